@@ -1,0 +1,157 @@
+"""Plain CPU oracle for paged decode attention (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code with the HIP library and never imports it.
+
+  oracle.c          binary64 decode attention through block tables, the slot
+                    scatter (reshape_and_cache) and the whole-block copy
+                    (copy_blocks); built here with gcc, single-threaded.
+  alloc_model.py    the block allocator (free list, reference counts, fork,
+                    append with copy-on-write, free) in plain Python.
+  place.py          helpers that build pools and tables with the model allocator
+                    and the oracle's scatter/copy, for a workload batch.
+
+Sources: the four pages on vLLM's PagedAttention — "PagedAttention" concept
+report (compassingai.com) §5 (block table, base + offset addressing), §6
+(reference counts, copy-on-write), §8 (dot product, softmax, weighted sum of
+values; outer loop over blocks, inner over tokens), §11 (free list); "vLLM
+PagedAttention 技术深度解析" (kwkr.cn) §1.2.2 (allocation flow) and §1.3.2
+(sharing); the KV-cache/paging tutorial (wmrh.cn) "KV cache" and "paged
+attention" parts (newest token's K/V computed at the step; shared blocks with
+reference counts 2 and 3).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import tempfile
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+_STATUS = {0: "ok", 1: "bad argument", 2: "index out of range", 3: "out of memory"}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(mutant: int = 0, out: Optional[str] = None) -> str:
+    """Compile oracle.c with gcc (-O2, strict IEEE, no fast-math). Returns the path."""
+    out = out or _LIB
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+           f"-DORACLE_MUTANT={int(mutant)}", _SRC, "-lm", "-o", out + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _needs_build(path: str) -> bool:
+    return not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC)
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, path: Optional[str] = None):
+        path = path or _LIB
+        if path == _LIB and _needs_build(path):
+            build()
+        self._lib = ctypes.CDLL(path)
+        vp, i32p, dp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)
+        ci, cd = ctypes.c_int, ctypes.c_double
+        self._lib.oracle_decode.argtypes = [dp, vp, vp, vp, i32p, ci, i32p, ci, ci, ci, ci, ci, ci, cd, ci]
+        self._lib.oracle_reshape_and_cache.argtypes = [vp, vp, vp, vp, i32p, ci, ci, ci, ci, ci, ci]
+        self._lib.oracle_copy_blocks.argtypes = [vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci]
+        self._lib.oracle_load.argtypes = [vp, ctypes.c_int64, ci]
+        self._lib.oracle_load.restype = cd
+        for f in ("oracle_decode", "oracle_reshape_and_cache", "oracle_copy_blocks"):
+            getattr(self._lib, f).restype = ctypes.c_int
+
+    @staticmethod
+    def _check(rc: int, what: str):
+        if rc != 0:
+            raise OracleError(f"{what}: {_STATUS.get(rc, rc)}")
+
+    @staticmethod
+    def _i32(a) -> np.ndarray:
+        return np.ascontiguousarray(a, dtype=np.int32)
+
+    def load(self, arr: np.ndarray, dtype: str) -> np.ndarray:
+        """Decode stored values to float64 with the oracle's own decoder."""
+        a = np.ascontiguousarray(arr)
+        out = np.empty(a.size, np.float64)
+        for i in range(a.size):
+            out[i] = self._lib.oracle_load(a.ctypes.data, i, DTYPE_CODE[dtype])
+        return out.reshape(a.shape)
+
+    def decode(self, query, key_cache, value_cache, block_tables, context_lens, scale: float,
+               dtype: str, num_kv_heads: Optional[int] = None) -> np.ndarray:
+        """out[S][H_q][d] in float64.  Pools are [num_blocks][H_kv][B][d]."""
+        q = np.ascontiguousarray(query)
+        kc = np.ascontiguousarray(key_cache)
+        vc = np.ascontiguousarray(value_cache)
+        bt = self._i32(block_tables)
+        cl = self._i32(context_lens)
+        S, Hq, d = q.shape
+        nb, Hkv, B, d2 = kc.shape
+        assert d2 == d and vc.shape == kc.shape and bt.shape[0] == S and cl.shape == (S,)
+        if num_kv_heads is not None:
+            assert num_kv_heads == Hkv
+        out = np.zeros((S, Hq, d), np.float64)
+        rc = self._lib.oracle_decode(
+            out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), q.ctypes.data, kc.ctypes.data,
+            vc.ctypes.data, bt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), bt.shape[1],
+            cl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), S, Hq, Hkv, d, B, nb, float(scale),
+            DTYPE_CODE[dtype])
+        self._check(rc, "oracle_decode")
+        return out
+
+    def reshape_and_cache(self, key, value, key_cache, value_cache, slot_mapping, dtype: str):
+        """In-place scatter of key/value [N][H_kv][d] into the pools."""
+        k = np.ascontiguousarray(key)
+        v = np.ascontiguousarray(value)
+        sm = self._i32(slot_mapping)
+        assert key_cache.flags.c_contiguous and value_cache.flags.c_contiguous
+        nb, Hkv, B, d = key_cache.shape
+        N = sm.shape[0]
+        assert k.shape == (N, Hkv, d) and v.shape == k.shape
+        rc = self._lib.oracle_reshape_and_cache(
+            k.ctypes.data, v.ctypes.data, key_cache.ctypes.data, value_cache.ctypes.data,
+            sm.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), N, Hkv, d, B, nb, DTYPE_CODE[dtype])
+        self._check(rc, "oracle_reshape_and_cache")
+
+    def copy_blocks(self, key_cache, value_cache, src, dst, dtype: str):
+        """In-place whole-block copies src[i] -> dst[i] in both pools."""
+        s = self._i32(src)
+        t = self._i32(dst)
+        assert key_cache.flags.c_contiguous and value_cache.flags.c_contiguous
+        nb, Hkv, B, d = key_cache.shape
+        rc = self._lib.oracle_copy_blocks(
+            key_cache.ctypes.data, value_cache.ctypes.data,
+            s.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(s), Hkv, d, B, nb,
+            DTYPE_CODE[dtype])
+        self._check(rc, "oracle_copy_blocks")
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def build_mutant(mutant: int) -> Oracle:
+    """An oracle with one planted mistake (tests of the pins only)."""
+    d = tempfile.mkdtemp(prefix="oracle_mutant_")
+    return Oracle(build(mutant, os.path.join(d, f"liboracle_m{mutant}.so")))

@@ -1,0 +1,96 @@
+"""Oracle-side construction of workload batches (allocator replay, scatter, copies)."""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import workloads as W
+from oracle import place
+
+
+def _logical(batch):
+    """Per sequence: all its tokens' K and V in order (prompt, private, current)."""
+    w = batch.workload
+    ks = {s: [] for s in range(w.num_seqs)}
+    vs = {s: [] for s in range(w.num_seqs)}
+    appends = [op for op in batch.script if op.kind == "append"]
+    group_prompt = {}
+    for i, op in enumerate(appends):
+        if w.lengths == "prefix" and op.seq % w.samples == 0 and op.seq not in group_prompt:
+            group_prompt[op.seq] = i
+            continue
+        ks[op.seq].append(batch.append_k[i])
+        vs[op.seq].append(batch.append_v[i])
+    if w.lengths == "prefix":
+        for s in range(w.num_seqs):
+            i = group_prompt[(s // w.samples) * w.samples]
+            ks[s].insert(0, batch.append_k[i])
+            vs[s].insert(0, batch.append_v[i])
+    return ({s: np.concatenate(v) for s, v in ks.items()},
+            {s: np.concatenate(v) for s, v in vs.items()})
+
+
+def _f64(a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).double()
+    return torch.from_numpy(a.astype(np.float64))
+
+
+def _sdpa(batch):
+    w = batch.workload
+    K, V = _logical(batch)
+    out = np.zeros((w.num_seqs, w.num_q_heads, w.head_dim))
+    for s in range(w.num_seqs):
+        q = _f64(batch.q[s], w.dtype)[None, :, None, :]
+        k = _f64(K[s], w.dtype).permute(1, 0, 2)[None].contiguous()
+        v = _f64(V[s], w.dtype).permute(1, 0, 2)[None].contiguous()
+        out[s] = F.scaled_dot_product_attention(
+            q, k, v, scale=w.scale, enable_gqa=w.num_q_heads != w.num_kv_heads)[0, :, 0].numpy()
+    return out
+
+
+SMALL = {
+    "tiny_fp32": W.WORKLOADS["tiny_fp32"],
+    "prefix_small": W.scaled(W.WORKLOADS["prefix_sharing"], num_seqs=6, groups=2, samples=3,
+                             prefix_base=20, private_max=6, block_size=4, num_blocks=64,
+                             num_q_heads=4, num_kv_heads=2, head_dim=8),
+    "gqa_small": W.scaled(W.WORKLOADS["llama70b_gqa"], num_seqs=3, low=100, high=300,
+                          num_blocks=64, block_size=16, num_q_heads=16, num_kv_heads=2,
+                          head_dim=16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_decode_step_equals_attention_over_logical_tokens(name):
+    batch = W.make_batch(SMALL[name])
+    out, p = place.decode_step(batch)
+    assert np.all(np.isfinite(out))
+    assert np.max(np.abs(out - _sdpa(batch))) <= 1e-12
+    assert np.array_equal(p.context_lens, batch.lengths.context_lens)
+
+
+def test_prefix_construction_raises_one_copy_per_extra_sample():
+    w = SMALL["prefix_small"]
+    batch = W.make_batch(w)
+    p = place.place(batch)
+    assert len(p.cow_src) == w.groups * (w.samples - 1)
+    # every copy's source is its group's partly filled last prompt block
+    for j in range(w.groups):
+        srcs = set(p.cow_src[j * (w.samples - 1):(j + 1) * (w.samples - 1)].tolist())
+        assert len(srcs) == 1
+    st = p.alloc.stats()
+    assert st["shared_blocks"] == w.groups * (int(batch.lengths.prefix_lens[0]) // w.block_size)
+
+
+def test_identity_layout_gives_consecutive_blocks():
+    w = W.WORKLOADS["tiny_fp32"]
+    p = place.place(W.make_batch(w, identity=True))
+    flat = [b for row in p.block_tables for b in row if b >= 0]
+    assert flat == list(range(len(flat)))
+
+
+def test_full_size_lengths_match_the_recipe():
+    """The seeded draws of every workload (only the length step)."""
+    sums = {n: int(W.draw_lengths(w)[0].context_lens.sum()) for n, w in W.WORKLOADS.items()}
+    assert sums == {"tiny_fp32": 134, "llama7b": 46958, "llama13b_long": 95677,
+                    "prefix_sharing": 93983, "llama70b_gqa": 191507}
