@@ -1,0 +1,199 @@
+/*
+ * pa.h — C ABI of libpa: paged decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow four web pages on vLLM's PagedAttention:
+ *   [kwkr]   "vLLM PagedAttention 技术深度解析" (kwkr.cn/news/58438)
+ *   [wmrh]   KV cache / memory paging / paged attention tutorial (wmrh.cn/news/286280)
+ *   [5ulink] "PagedAttention 深度解析：vLLM 连续批处理与显存分页的工程奇迹" (5ulink.com)
+ *   [cpai]   "PagedAttention" concept report (compassingai.com/zh-hant/concept/pagedattention)
+ *
+ * Data layout (one attention layer):
+ *   key_cache, value_cache  [num_blocks][num_kv_heads][block_size][head_dim] of `dtype`:
+ *                           the physical block pool; one (block, head) tile is
+ *                           block_size * head_dim contiguous elements ([cpai] §5).
+ *   block_tables            int32 [num_seqs][max_blocks_per_seq]: entry j of row s is the
+ *                           physical block that holds tokens [j*B, (j+1)*B) of sequence s
+ *                           ([cpai] §5, [5ulink] §二); entries past ceil(ctx/B) are never
+ *                           read (pad them with -1).
+ *   context_lens            int32 [num_seqs]: tokens of sequence s, including the one being
+ *                           decoded, whose K/V must already be in the cache ([wmrh] "KV cache").
+ *   slot_mapping            int32 [num_tokens]: slot = physical_block * block_size + offset;
+ *                           a negative slot marks a padding token and is skipped.
+ *   query, out              [num_seqs][num_q_heads][head_dim] of `dtype`; query head h reads
+ *                           KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Supported: dtype f32 / f16 / bf16; head_dim 64 or 128; block_size 16, 32, 64 or 128;
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}.
+ *
+ * Ownership and ordering: every device pointer is borrowed from the caller and must
+ * stay valid until the work queued on `stream` (a hipStream_t; NULL = the null stream)
+ * has finished.  Device calls only validate host-visible arguments, enqueue kernels and
+ * return; they never allocate, free or synchronise.  Work on one stream runs in order,
+ * which is what makes it safe to reuse a freed block at once ([kwkr] §1.3.2).
+ *
+ * Errors: every call returns a pa_status.  Argument errors are reported before anything
+ * is enqueued.  Faults in device data cannot be reported synchronously; instead the
+ * kernels never touch memory outside the pools, and a sequence whose table holds an
+ * entry outside [0, num_blocks) for a token < ctx, or whose ctx is negative (or, with
+ * partitions, larger than max_context_len), gets NaN in every element of its output
+ * ([cpai] §13: bounds are checked in the kernel as well as by the scheduler).
+ * pa_check_tables validates host copies of the tables beforehand.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID = 1,     /* bad argument, unknown sequence, double free */
+    PA_ERR_BOUNDS = 2,      /* index outside the pool or the table */
+    PA_ERR_OOM = 3,         /* no free block left ([cpai] §13); state unchanged */
+    PA_ERR_UNSUPPORTED = 4, /* dtype / head_dim / block_size / group not built */
+    PA_ERR_HIP = 5          /* the HIP runtime reported an error (see pa_last_error) */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Decode-attention variants (pa_decode's `variant` argument). */
+typedef enum pa_variant {
+    PA_VARIANT_AUTO = 0, /* MFMA when the group size is >= 2 and dtype is 16-bit, else VALU */
+    PA_VARIANT_VALU = 1, /* vector-ALU kernel: one wavefront row per token */
+    PA_VARIANT_MFMA = 2  /* matrix-core kernel for grouped-query heads (16-bit only) */
+} pa_variant;
+
+/* Static text for a status code. */
+const char *pa_status_str(int status);
+/* Detail of the last failed call on this thread ("" if none). */
+const char *pa_last_error(void);
+/* ABI version (incremented on any incompatible change). */
+int pa_abi_version(void);
+
+/* ------------------------------------------------------------------ device ops */
+
+/*
+ * Bytes of scratch pa_decode needs for a given partition size (0 when
+ * partition_size == 0).  Partials are kept in fp32: for every sequence, query head
+ * and partition a running max, a sum of weights and head_dim weighted sums.
+ */
+size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+                                 int max_context_len, int partition_size);
+
+/*
+ * Decode attention over the paged cache ([cpai] §8: scores of the query against every
+ * cached key, softmax, weighted sum of the values; the kernel walks the block table):
+ *   out[s][h] = sum_t softmax_t(scale * <query[s][h], K_t>) * V_t,  t < context_lens[s]
+ * with K_t, V_t read at block block_tables[s][t / B], slot t % B, KV head h / g.
+ * Softmax and accumulation run in fp32; out is rounded to `dtype` (round to nearest
+ * even).  context_lens[s] == 0 gives zeros.
+ *
+ * partition_size == 0: one pass per (sequence, KV head).  Otherwise a multiple of
+ * block_size (and of 16): each partition of that many tokens is reduced on its own
+ * and a second kernel merges the partials with log-sum-exp weights; `workspace`
+ * must then hold pa_decode_workspace_bytes(...) bytes of device memory and
+ * max_context_len must bound every context_lens[s].
+ * `variant` selects the kernel (pa_variant).
+ */
+int pa_decode(void *out, const void *query, const void *key_cache, const void *value_cache,
+              const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+              int num_blocks, int max_context_len, float scale, int dtype, int partition_size,
+              int variant, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Write the newest tokens' K/V into their slots ([wmrh] "KV cache": at a decode step
+ * only the newest token's K and V are computed and cached; [cpai] §5 base + offset):
+ *   key_cache[slot / B][k][slot % B][:] = key[i][k][:]   (same for value)
+ * for every token i with 0 <= slot_mapping[i] < num_blocks * B; a bitwise copy.
+ * key, value: device [num_tokens][num_kv_heads][head_dim]; slot_mapping device.
+ */
+int pa_reshape_and_cache(const void *key, const void *value, void *key_cache, void *value_cache,
+                         const int32_t *slot_mapping, int num_tokens, int num_kv_heads,
+                         int head_dim, int block_size, int num_blocks, int dtype, void *stream);
+
+/*
+ * Copy-on-write block copies ([cpai] §6: before a write into a shared block, a new
+ * block gets a copy of its content): for every pair p, the whole block src[p] (all KV
+ * heads, all slots) of both pools is copied onto block dst[p], bit for bit.
+ * src, dst: device int32 [num_pairs].  A pair with an id outside [0, num_blocks) is
+ * skipped.  The dst ids must be distinct and must not appear among the src ids (the
+ * allocator's pairs always are); pa_check_copy_pairs checks host copies.
+ */
+int pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *src, const int32_t *dst,
+                   int num_pairs, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                   int dtype, void *stream);
+
+/* Host-side checks ([cpai] §13).  PA_ERR_BOUNDS names the first offending entry in
+ * pa_last_error. */
+int pa_check_tables(const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                    int max_blocks_per_seq, int block_size, int num_blocks);
+int pa_check_copy_pairs(const int32_t *src, const int32_t *dst, int num_pairs, int num_blocks);
+
+/* ------------------------------------------------------------ host allocator */
+
+/*
+ * Block allocator ([kwkr] §1.2.2 allocation flow, §1.3.2 sharing; [cpai] §6 reference
+ * counts and copy-on-write, §11 free list, §13 out-of-memory).  An opaque handle owned
+ * by the library; all calls on one handle are serialised by an internal mutex.
+ * Free blocks form a LIFO stack whose pops return 0, 1, 2, ... unless set otherwise;
+ * blocks released by pa_alloc_free_seq are pushed in table order.
+ */
+typedef struct pa_allocator pa_allocator;
+
+typedef struct pa_alloc_stats {
+    int64_t total_blocks;
+    int64_t used_blocks;    /* reference count > 0 */
+    int64_t free_blocks;
+    int64_t shared_blocks;  /* reference count > 1 */
+    int64_t num_seqs;
+    int64_t logical_tokens; /* sum of context lengths */
+    int64_t stored_tokens;  /* filled slots, counting a shared block once */
+    int64_t wasted_slots;   /* used_blocks * B - stored_tokens */
+} pa_alloc_stats;
+
+int pa_alloc_create(int num_blocks, int block_size, pa_allocator **out);
+void pa_alloc_destroy(pa_allocator *a);
+/* Pops return ids[0], ids[1], ...: ids must be a permutation of [0, num_blocks) and
+ * no block may be in use. */
+int pa_alloc_set_free_order(pa_allocator *a, const int32_t *ids, int n);
+int pa_alloc_new_seq(pa_allocator *a, int64_t *seq);
+/*
+ * Reserve the slot of seq's next token.  A full (or missing) last block takes a free
+ * block.  A partly filled last block that is shared (count > 1) is replaced by a
+ * fresh block and (*cow_src, *cow_dst) name the copy to run with pa_copy_blocks
+ * before the write; otherwise both are -1.  With no free block: PA_ERR_OOM and no
+ * change.
+ */
+int pa_alloc_append_slot(pa_allocator *a, int64_t seq, int32_t *slot, int32_t *cow_src,
+                         int32_t *cow_dst);
+/*
+ * n appends in order (seqs[i] may repeat).  slots[i] receives each slot; the copies
+ * raised are written to cow_src/cow_dst (capacity n) and counted in *num_cow.  Stops at
+ * the first failure; *num_done (may be NULL) = appends that succeeded.
+ */
+int pa_alloc_append_slots(pa_allocator *a, const int64_t *seqs, int n, int32_t *slots,
+                          int32_t *cow_src, int32_t *cow_dst, int *num_cow, int *num_done);
+/* New sequence sharing all of parent's blocks (each count + 1), same length. */
+int pa_alloc_fork(pa_allocator *a, int64_t parent, int64_t *child);
+/* Release the sequence; blocks whose count drops to 0 return to the free stack. */
+int pa_alloc_free_seq(pa_allocator *a, int64_t seq);
+/* One table: up to cap entries to out; *num_blocks and *context_len may be NULL. */
+int pa_alloc_block_table(pa_allocator *a, int64_t seq, int32_t *out, int cap, int *num_blocks,
+                         int *context_len);
+/* Padded tables of n sequences: out [n][max_blocks_per_seq] (-1 padding) and
+ * context_lens [n]; PA_ERR_BOUNDS if a table is longer than max_blocks_per_seq. */
+int pa_alloc_block_tables(pa_allocator *a, const int64_t *seqs, int n, int32_t *out,
+                          int max_blocks_per_seq, int32_t *context_lens);
+int pa_alloc_refcount(pa_allocator *a, int32_t block, int *refcount);
+int pa_alloc_get_stats(pa_allocator *a, pa_alloc_stats *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,303 @@
+"""Thin Python binding of libpa (paged decode attention for MI355X / gfx950).
+
+Argument marshalling only: every function passes torch tensors' data pointers,
+sizes and the current HIP stream to the C entry point of the same name in
+include/pa.h, and raises PaError on a non-zero status.  The compute runs in the
+HIP kernels of libpa.so; there is no fallback.  Build it with
+`python -m paged_kv_cache_308_amd.build` (or __graft_entry__.build()).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_BOUNDS, PA_ERR_OOM, PA_ERR_UNSUPPORTED, PA_ERR_HIP = range(6)
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
+
+# Every symbol include/pa.h declares (checked by the tests).
+EXPORTS = (
+    "pa_status_str", "pa_last_error", "pa_abi_version", "pa_decode_workspace_bytes", "pa_decode",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_check_tables", "pa_check_copy_pairs",
+    "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_set_free_order", "pa_alloc_new_seq",
+    "pa_alloc_append_slot", "pa_alloc_append_slots", "pa_alloc_fork", "pa_alloc_free_seq",
+    "pa_alloc_block_table", "pa_alloc_block_tables", "pa_alloc_refcount", "pa_alloc_get_stats",
+)
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {_lib().pa_status_str(status).decode()} ({detail})")
+        self.status = status
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "total_blocks", "used_blocks", "free_blocks", "shared_blocks", "num_seqs",
+        "logical_tokens", "stored_tokens", "wasted_slots")]
+
+
+_L = None
+
+
+def _lib():
+    global _L
+    if _L is not None:
+        return _L
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m paged_kv_cache_308_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    ip = ctypes.POINTER(ctypes.c_int)
+    sig = {
+        "pa_status_str": (ctypes.c_char_p, [i32]),
+        "pa_last_error": (ctypes.c_char_p, []),
+        "pa_abi_version": (i32, []),
+        "pa_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "pa_decode": (i32, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                            i32, i32, i32, vp, sz, vp]),
+        "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
+        "pa_copy_blocks": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
+        "pa_check_tables": (i32, [i32p, i32p, i32, i32, i32, i32]),
+        "pa_check_copy_pairs": (i32, [i32p, i32p, i32, i32]),
+        "pa_alloc_create": (i32, [i32, i32, ctypes.POINTER(vp)]),
+        "pa_alloc_destroy": (None, [vp]),
+        "pa_alloc_set_free_order": (i32, [vp, i32p, i32]),
+        "pa_alloc_new_seq": (i32, [vp, i64p]),
+        "pa_alloc_append_slot": (i32, [vp, i64, i32p, i32p, i32p]),
+        "pa_alloc_append_slots": (i32, [vp, i64p, i32, i32p, i32p, i32p, ip, ip]),
+        "pa_alloc_fork": (i32, [vp, i64, i64p]),
+        "pa_alloc_free_seq": (i32, [vp, i64]),
+        "pa_alloc_block_table": (i32, [vp, i64, i32p, i32, ip, ip]),
+        "pa_alloc_block_tables": (i32, [vp, i64p, i32, i32p, i32, i32p]),
+        "pa_alloc_refcount": (i32, [vp, ctypes.c_int32, ip]),
+        "pa_alloc_get_stats": (i32, [vp, ctypes.POINTER(_Stats)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _L = L
+    return L
+
+
+def _check(rc: int, where: str):
+    if rc != PA_OK:
+        raise PaError(rc, where, _lib().pa_last_error().decode())
+
+
+# ----------------------------------------------------------------- device ops
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    return {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}[t.dtype]
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _dev(t, name, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                              max_context_len: int, partition_size: int) -> int:
+    return _lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                            partition_size)
+
+
+def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale: float,
+              max_context_len: int = 0, partition_size: int = 0, variant: int = PA_VARIANT_AUTO,
+              workspace=None, stream=None):
+    """out/query [S][H_q][d]; pools [num_blocks][H_kv][B][d]; tables int32 [S][max_blocks]."""
+    torch = _torch()
+    S, Hq, d = query.shape
+    nb, Hkv, B, d2 = key_cache.shape
+    if d2 != d or value_cache.shape != key_cache.shape or out.shape != query.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables / context_lens shape")
+    for t in (query, key_cache, value_cache, out):
+        if t.dtype != query.dtype:
+            raise ValueError("query, pools and out must share one dtype")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib().pa_decode(
+        _dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, d, B, nb,
+        int(max_context_len), float(scale), dtype_code(query), int(partition_size), int(variant),
+        ws_ptr, ws_bytes, _stream(stream))
+    _check(rc, "pa_decode")
+    return out
+
+
+def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=None):
+    """key/value [N][H_kv][d] -> pools [num_blocks][H_kv][B][d] at slot_mapping (int32 [N])."""
+    torch = _torch()
+    N, Hkv, d = key.shape
+    nb, Hkv2, B, d2 = key_cache.shape
+    if (Hkv2, d2) != (Hkv, d) or value.shape != key.shape or value_cache.shape != key_cache.shape:
+        raise ValueError("shape mismatch")
+    if slot_mapping.shape != (N,):
+        raise ValueError("slot_mapping shape")
+    rc = _lib().pa_reshape_and_cache(
+        _dev(key, "key", key_cache.dtype), _dev(value, "value", key_cache.dtype),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache", key_cache.dtype),
+        _dev(slot_mapping, "slot_mapping", torch.int32), N, Hkv, d, B, nb, dtype_code(key_cache),
+        _stream(stream))
+    _check(rc, "pa_reshape_and_cache")
+
+
+def pa_copy_blocks(key_cache, value_cache, src, dst, stream=None):
+    """Whole-block copies src[i] -> dst[i] (int32 device tensors) in both pools."""
+    torch = _torch()
+    nb, Hkv, B, d = key_cache.shape
+    if value_cache.shape != key_cache.shape or src.shape != dst.shape or src.dim() != 1:
+        raise ValueError("shape mismatch")
+    rc = _lib().pa_copy_blocks(
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache", key_cache.dtype),
+        _dev(src, "src", torch.int32), _dev(dst, "dst", torch.int32), src.shape[0], Hkv, d, B, nb,
+        dtype_code(key_cache), _stream(stream))
+    _check(rc, "pa_copy_blocks")
+
+
+# ------------------------------------------------------------------ host checks
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+def _p32(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def pa_check_tables(block_tables, context_lens, block_size: int, num_blocks: int) -> None:
+    bt, cl = _i32(block_tables), _i32(context_lens)
+    _check(_lib().pa_check_tables(_p32(bt), _p32(cl), bt.shape[0], bt.shape[1], block_size,
+                                  num_blocks), "pa_check_tables")
+
+
+def pa_check_copy_pairs(src, dst, num_blocks: int) -> None:
+    s, d = _i32(src), _i32(dst)
+    _check(_lib().pa_check_copy_pairs(_p32(s), _p32(d), len(s), num_blocks), "pa_check_copy_pairs")
+
+
+# ------------------------------------------------------------- host allocator
+
+class Allocator:
+    """Owner of a pa_allocator handle; methods are the pa_alloc_* calls."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        h = ctypes.c_void_p()
+        _check(_lib().pa_alloc_create(num_blocks, block_size, ctypes.byref(h)), "pa_alloc_create")
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self):
+        if self._h:
+            _lib().pa_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_free_order(self, ids: Sequence[int]) -> None:
+        a = _i32(ids)
+        _check(_lib().pa_alloc_set_free_order(self._h, _p32(a), len(a)), "pa_alloc_set_free_order")
+
+    def new_seq(self) -> int:
+        s = ctypes.c_int64()
+        _check(_lib().pa_alloc_new_seq(self._h, ctypes.byref(s)), "pa_alloc_new_seq")
+        return s.value
+
+    def append_slot(self, seq: int):
+        """Returns (slot, (src, dst) or None)."""
+        slot, cs, cd = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib().pa_alloc_append_slot(self._h, seq, ctypes.byref(slot), ctypes.byref(cs),
+                                           ctypes.byref(cd)), "pa_alloc_append_slot")
+        return slot.value, ((cs.value, cd.value) if cs.value >= 0 else None)
+
+    def append_slots(self, seqs):
+        """Appends in order; returns (slots int32 [n], cow_src int32 [k], cow_dst int32 [k])."""
+        s = np.ascontiguousarray(np.asarray(seqs), dtype=np.int64)
+        n = len(s)
+        slots = np.empty(n, np.int32)
+        cs = np.empty(max(n, 1), np.int32)
+        cd = np.empty(max(n, 1), np.int32)
+        ncow, done = ctypes.c_int(), ctypes.c_int()
+        rc = _lib().pa_alloc_append_slots(
+            self._h, s.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, _p32(slots), _p32(cs),
+            _p32(cd), ctypes.byref(ncow), ctypes.byref(done))
+        _check(rc, f"pa_alloc_append_slots (done {done.value} of {n})")
+        return slots, cs[:ncow.value].copy(), cd[:ncow.value].copy()
+
+    def fork(self, parent: int) -> int:
+        c = ctypes.c_int64()
+        _check(_lib().pa_alloc_fork(self._h, parent, ctypes.byref(c)), "pa_alloc_fork")
+        return c.value
+
+    def free_seq(self, seq: int) -> None:
+        _check(_lib().pa_alloc_free_seq(self._h, seq), "pa_alloc_free_seq")
+
+    def block_table(self, seq: int):
+        n, ctx = ctypes.c_int(), ctypes.c_int()
+        # first call sizes the table (PA_ERR_BOUNDS with cap 0 is expected)
+        rc = _lib().pa_alloc_block_table(self._h, seq, None, 0, ctypes.byref(n), ctypes.byref(ctx))
+        if rc not in (PA_OK, PA_ERR_BOUNDS):
+            _check(rc, "pa_alloc_block_table")
+        out = np.empty(max(n.value, 1), np.int32)
+        _check(_lib().pa_alloc_block_table(self._h, seq, _p32(out), n.value, None, None),
+               "pa_alloc_block_table")
+        return out[:n.value].tolist(), ctx.value
+
+    def block_tables(self, seqs, max_blocks_per_seq: int):
+        s = np.ascontiguousarray(np.asarray(seqs), dtype=np.int64)
+        out = np.empty((len(s), max_blocks_per_seq), np.int32)
+        cl = np.empty(len(s), np.int32)
+        _check(_lib().pa_alloc_block_tables(self._h, s.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                            len(s), _p32(out), max_blocks_per_seq, _p32(cl)),
+               "pa_alloc_block_tables")
+        return out, cl
+
+    def refcount(self, block: int) -> int:
+        r = ctypes.c_int()
+        _check(_lib().pa_alloc_refcount(self._h, block, ctypes.byref(r)), "pa_alloc_refcount")
+        return r.value
+
+    def stats(self) -> dict:
+        st = _Stats()
+        _check(_lib().pa_alloc_get_stats(self._h, ctypes.byref(st)), "pa_alloc_get_stats")
+        return {n: getattr(st, n) for n, _ in _Stats._fields_}
+
+
+def abi_version() -> int:
+    return _lib().pa_abi_version()

@@ -1,0 +1,233 @@
+// C ABI entry points of libpa: argument validation, variant choice, launches.
+// Nothing here allocates device memory or synchronises; see pa.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+namespace pa {
+
+static thread_local char g_err[512];
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+int check_launch(const char *what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return PA_OK;
+}
+
+static int elem_bytes(int dtype) {
+    return dtype == PA_F32 ? 4 : (dtype == PA_F16 || dtype == PA_BF16) ? 2 : 0;
+}
+
+static bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_layout(int S, int Hq, int d, int P, void *ws, float **m, float **l, float **acc) {
+    const size_t n = (size_t)S * Hq * P;
+    const size_t bm = align256(n * sizeof(float));
+    const size_t bacc = align256(n * (size_t)d * sizeof(float));
+    if (ws) {
+        char *p = (char *)ws;
+        *m = (float *)p;
+        *l = (float *)(p + bm);
+        *acc = (float *)(p + 2 * bm);
+    }
+    return 2 * bm + bacc;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char *pa_status_str(int status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_INVALID: return "invalid argument";
+        case PA_ERR_BOUNDS: return "index out of bounds";
+        case PA_ERR_OOM: return "out of blocks";
+        case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case PA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *pa_last_error(void) { return g_err; }
+
+int pa_abi_version(void) { return 1; }
+
+static int max_partitions_for(int max_context_len, int partition_size) {
+    if (partition_size == 0) return 1;
+    return max_context_len <= 0 ? 1 : (max_context_len + partition_size - 1) / partition_size;
+}
+
+size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
+                                 int partition_size) {
+    if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+    return workspace_layout(num_seqs, num_q_heads, head_dim,
+                            max_partitions_for(max_context_len, partition_size), nullptr, nullptr,
+                            nullptr, nullptr);
+}
+
+int pa_decode(void *out, const void *query, const void *key_cache, const void *value_cache,
+              const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+              int num_blocks, int max_context_len, float scale, int dtype, int partition_size,
+              int variant, void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+        max_blocks_per_seq <= 0)
+        return fail(PA_ERR_INVALID, "bad sizes: S=%d Hq=%d Hkv=%d blocks=%d max_blocks=%d",
+                    num_seqs, num_q_heads, num_kv_heads, num_blocks, max_blocks_per_seq);
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+        return fail(PA_ERR_INVALID, "NULL device pointer");
+    if (elem_bytes(dtype) == 0) return fail(PA_ERR_UNSUPPORTED, "dtype %d", dtype);
+    if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d", head_dim);
+    if (!pow2_in(block_size, 16, 128)) return fail(PA_ERR_UNSUPPORTED, "block_size %d", block_size);
+    if (num_q_heads % num_kv_heads)
+        return fail(PA_ERR_INVALID, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+                    num_kv_heads);
+    const int group = num_q_heads / num_kv_heads;
+    if (!pow2_in(group, 1, 16)) return fail(PA_ERR_UNSUPPORTED, "group size %d", group);
+    if ((int64_t)num_blocks * num_kv_heads * block_size * head_dim > ((int64_t)1 << 40))
+        return fail(PA_ERR_UNSUPPORTED, "pool too large");
+    if (!(scale == scale)) return fail(PA_ERR_INVALID, "scale is NaN");
+    if (partition_size < 0 || (partition_size > 0 && (partition_size % block_size || partition_size % 16)))
+        return fail(PA_ERR_INVALID, "partition_size %d must be 0 or a multiple of block_size %d and 16",
+                    partition_size, block_size);
+    if (partition_size > 0 && max_context_len <= 0)
+        return fail(PA_ERR_INVALID, "max_context_len %d with partitions", max_context_len);
+    if (variant < PA_VARIANT_AUTO || variant > PA_VARIANT_MFMA)
+        return fail(PA_ERR_INVALID, "variant %d", variant);
+
+    DecodeArgs a{};
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.num_blocks = num_blocks;
+    a.partition_size = partition_size;
+    a.max_partitions = max_partitions_for(max_context_len, partition_size);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.dtype = dtype;
+    a.stream = stream;
+    if (partition_size > 0) {
+        const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, a.max_partitions,
+                                             nullptr, nullptr, nullptr, nullptr);
+        if (!workspace || workspace_bytes < need)
+            return fail(PA_ERR_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+        workspace_layout(num_seqs, num_q_heads, head_dim, a.max_partitions, workspace, &a.ws_max,
+                         &a.ws_sum, &a.ws_acc);
+    }
+    const bool mfma_ok = mfma_supported(dtype, head_dim, block_size, group);
+    if (variant == PA_VARIANT_MFMA) {
+        if (!mfma_ok)
+            return fail(PA_ERR_UNSUPPORTED, "MFMA kernel needs 16-bit dtype and group >= 2 (group %d)",
+                        group);
+        return launch_decode_mfma(a);
+    }
+    if (variant == PA_VARIANT_AUTO && mfma_ok && group >= 2) return launch_decode_mfma(a);
+    return launch_decode_valu(a);
+}
+
+int pa_reshape_and_cache(const void *key, const void *value, void *key_cache, void *value_cache,
+                         const int32_t *slot_mapping, int num_tokens, int num_kv_heads,
+                         int head_dim, int block_size, int num_blocks, int dtype, void *stream) {
+    clear_error();
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "dtype %d", dtype);
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID, "bad sizes");
+    if ((head_dim * eb) % 16) return fail(PA_ERR_UNSUPPORTED, "head_dim * elem_bytes must be a multiple of 16");
+    if ((int64_t)num_blocks * block_size > INT32_MAX) return fail(PA_ERR_INVALID, "slot ids overflow int32");
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+        return fail(PA_ERR_INVALID, "NULL device pointer");
+    return launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                                    num_kv_heads, head_dim, block_size, num_blocks, eb, stream);
+}
+
+int pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *src, const int32_t *dst,
+                   int num_pairs, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                   int dtype, void *stream) {
+    clear_error();
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "dtype %d", dtype);
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID, "bad sizes");
+    if (((int64_t)num_kv_heads * block_size * head_dim * eb) % 16)
+        return fail(PA_ERR_UNSUPPORTED, "block bytes must be a multiple of 16");
+    if (num_pairs == 0) return PA_OK;
+    if (!key_cache || !value_cache || !src || !dst) return fail(PA_ERR_INVALID, "NULL device pointer");
+    return launch_copy_blocks(key_cache, value_cache, src, dst, num_pairs, num_kv_heads, head_dim,
+                              block_size, num_blocks, eb, stream);
+}
+
+int pa_check_tables(const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
+                    int max_blocks_per_seq, int block_size, int num_blocks) {
+    clear_error();
+    if (num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0 ||
+        (num_seqs && (!block_tables || !context_lens)))
+        return fail(PA_ERR_INVALID, "bad argument");
+    for (int s = 0; s < num_seqs; ++s) {
+        const int n = context_lens[s];
+        if (n < 0) return fail(PA_ERR_INVALID, "context_lens[%d] = %d", s, n);
+        const int nb = (n + block_size - 1) / block_size;
+        if (nb > max_blocks_per_seq)
+            return fail(PA_ERR_BOUNDS, "sequence %d needs %d blocks > %d", s, nb, max_blocks_per_seq);
+        for (int j = 0; j < nb; ++j) {
+            const int32_t b = block_tables[(int64_t)s * max_blocks_per_seq + j];
+            if (b < 0 || b >= num_blocks)
+                return fail(PA_ERR_BOUNDS, "block_tables[%d][%d] = %d outside [0, %d)", s, j, b, num_blocks);
+        }
+    }
+    return PA_OK;
+}
+
+int pa_check_copy_pairs(const int32_t *src, const int32_t *dst, int num_pairs, int num_blocks) {
+    clear_error();
+    if (num_pairs < 0 || num_blocks <= 0 || (num_pairs && (!src || !dst)))
+        return fail(PA_ERR_INVALID, "bad argument");
+    // 1 = seen as src, 2 = seen as dst
+    char *mark = (char *)calloc((size_t)num_blocks, 1);
+    if (!mark) return fail(PA_ERR_OOM, "host allocation failed");
+    int rc = PA_OK;
+    for (int p = 0; p < num_pairs && rc == PA_OK; ++p) {
+        if (src[p] < 0 || src[p] >= num_blocks || dst[p] < 0 || dst[p] >= num_blocks)
+            rc = fail(PA_ERR_BOUNDS, "pair %d (%d -> %d) outside [0, %d)", p, src[p], dst[p], num_blocks);
+    }
+    for (int p = 0; p < num_pairs && rc == PA_OK; ++p) mark[src[p]] |= 1;
+    for (int p = 0; p < num_pairs && rc == PA_OK; ++p) {
+        if (mark[dst[p]] & 1) rc = fail(PA_ERR_INVALID, "pair %d: dst %d is also a src", p, dst[p]);
+        else if (mark[dst[p]] & 2) rc = fail(PA_ERR_INVALID, "pair %d: dst %d repeated", p, dst[p]);
+        else mark[dst[p]] |= 2;
+    }
+    free(mark);
+    return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal declarations shared by the libpa sources (not part of the ABI).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// Record a message for pa_last_error() and return `status`.
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clear the thread's last error.
+void clear_error();
+
+// Everything a decode launch needs (validated by the dispatcher).
+struct DecodeArgs {
+    void *out;
+    const void *query;
+    const void *key_cache;
+    const void *value_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    float *ws_max;   // [S][H_q][P] running max (log2 domain), partitioned runs only
+    float *ws_sum;   // [S][H_q][P] sum of weights
+    float *ws_acc;   // [S][H_q][P][d] weighted value sums
+    int max_blocks_per_seq;
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int head_dim;
+    int block_size;
+    int num_blocks;
+    int partition_size;  // 0 = one pass
+    int max_partitions;  // grid extent along partitions (1 for one pass)
+    float scale_log2;    // scale * log2(e)
+    int dtype;
+    void *stream;
+};
+
+// Workspace partition for `a` (pointers into `ws`); returns bytes needed.
+size_t workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_partitions,
+                        void *ws, float **m, float **l, float **acc);
+
+// Kernel launchers (return PA_OK, PA_ERR_UNSUPPORTED or PA_ERR_HIP).
+int launch_decode_valu(const DecodeArgs &a);
+int launch_decode_mfma(const DecodeArgs &a);
+bool mfma_supported(int dtype, int head_dim, int block_size, int group);
+int launch_reshape_and_cache(const void *key, const void *value, void *key_cache,
+                             void *value_cache, const int32_t *slot_mapping, int num_tokens,
+                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             int elem_bytes, void *stream);
+int launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *src, const int32_t *dst,
+                       int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                       int num_blocks, int elem_bytes, void *stream);
+
+// Map a HIP error after a launch to PA_ERR_HIP with its text.
+int check_launch(const char *what);
+
+}  // namespace pa

@@ -1,0 +1,140 @@
+// Device helpers shared by the decode kernels (gfx950 / wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Storage element types.
+struct F32 {
+    static constexpr int bytes = 4;
+};
+struct F16 {
+    static constexpr int bytes = 2;
+};
+struct BF16 {
+    static constexpr int bytes = 2;
+};
+
+// 16 stored bytes -> fp32 values.
+template <typename T>
+__device__ inline void to_f32(const u32x4 &w, float (&f)[16 / T::bytes]);
+
+template <>
+__device__ inline void to_f32<F32>(const u32x4 &w, float (&f)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+}
+template <>
+__device__ inline void to_f32<F16>(const u32x4 &w, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t x = w[i];  // bit_cast of a vector element would read element 0
+        const f16x2 h = __builtin_bit_cast(f16x2, x);
+        f[2 * i] = (float)h[0];
+        f[2 * i + 1] = (float)h[1];
+    }
+}
+template <>
+__device__ inline void to_f32<BF16>(const u32x4 &w, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+// Dot product of two 16-byte slices, fp32 result.  16-bit types use the packed
+// dot instructions (two products summed into an fp32 accumulator per op).
+template <typename T>
+__device__ inline float dot16(const u32x4 &a, const u32x4 &b);
+
+template <>
+__device__ inline float dot16<F32>(const u32x4 &a, const u32x4 &b) {
+    float s = __uint_as_float(a[0]) * __uint_as_float(b[0]);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) s = fmaf(__uint_as_float(a[i]), __uint_as_float(b[i]), s);
+    return s;
+}
+template <>
+__device__ inline float dot16<F16>(const u32x4 &a, const u32x4 &b) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t x = a[i], y = b[i];  // scalar copies: see to_f32<F16>
+        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, y), s, false);
+    }
+    return s;
+}
+template <>
+__device__ inline float dot16<BF16>(const u32x4 &a, const u32x4 &b) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t x = a[i], y = b[i];  // scalar copies: see to_f32<F16>
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), s,
+                                            false);
+    }
+    return s;
+}
+
+// DPP lane exchange inside 16-lane rows.
+template <int CTRL>
+__device__ inline float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over groups of N adjacent lanes (N = 8, 16, 32); every lane of a group gets the
+// same bits (each step adds a value to its mirror image, which commutes exactly).
+template <int N>
+__device__ inline float row_sum(float v) {
+    static_assert(N == 8 || N == 16 || N == 32, "group size");
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+    v += dpp<0x141>(v);  // row_half_mirror: the other quad of each 8
+    if (N >= 16) v += dpp<0x140>(v);  // row_mirror: the other half of each 16
+    if (N >= 32) v += __shfl_xor(v, 16);
+    return v;
+}
+
+// 2^x on the hardware transcendental unit (exact 1 at 0, 0 at -inf).
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup w is dispatched to XCD w % 8.  Number work items so that each XCD runs
+// a contiguous range of them.
+__device__ inline int xcd_remap(int w, int n) {
+    constexpr int NX = 8;
+    const int x = w % NX, k = w / NX;
+    const int q = n / NX, r = n % NX;
+    return x * q + (x < r ? x : r) + k;
+}
+
+// Round fp32 to the output type (round to nearest even) and store element i.
+template <typename T>
+__device__ inline void store_out(void *out, int64_t i, float v);
+
+template <>
+__device__ inline void store_out<F32>(void *out, int64_t i, float v) {
+    ((float *)out)[i] = v;
+}
+template <>
+__device__ inline void store_out<F16>(void *out, int64_t i, float v) {
+    ((_Float16 *)out)[i] = (_Float16)v;
+}
+template <>
+__device__ inline void store_out<BF16>(void *out, int64_t i, float v) {
+    uint32_t u = __float_as_uint(v);
+    uint16_t r;
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        r = 0x7fc0;  // NaN
+    else
+        r = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    ((uint16_t *)out)[i] = r;
+}
+
+}  // namespace pa

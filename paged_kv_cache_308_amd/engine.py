@@ -1,0 +1,110 @@
+"""Paged KV cache: device block pools plus the host allocator, driving libpa.
+
+One decode step, in stream order ("vLLM PagedAttention 技术深度解析" (kwkr.cn)
+§1.2.2 allocation flow; "PagedAttention" concept report (compassingai.com) §6
+copy-on-write, §8 attention over the block table; the KV-cache tutorial
+(wmrh.cn): only the newest token's K/V are computed at a step):
+  1. host: reserve a slot for every sequence's new token (a new block when the
+     last one is full, a copy-on-write pair when it is shared);
+  2. host -> device: the step's slots, tables and lengths;
+  3. device: pa_copy_blocks for the pairs, pa_reshape_and_cache for the new K/V,
+     pa_decode over the tables.
+Python only marshals arguments and keeps host bookkeeping; all device work runs in
+libpa's kernels on the caller's stream.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (PA_VARIANT_AUTO, Allocator, pa_copy_blocks, pa_decode, pa_decode_workspace_bytes,
+               pa_reshape_and_cache)
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
+                 dtype: torch.dtype, device="cuda", fill: Optional[float] = None):
+        self.num_blocks, self.num_kv_heads = num_blocks, num_kv_heads
+        self.head_dim, self.block_size, self.dtype = head_dim, block_size, dtype
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        self.key_cache = torch.empty(shape, dtype=dtype, device=device)
+        self.value_cache = torch.empty(shape, dtype=dtype, device=device)
+        if fill is not None:
+            self.key_cache.fill_(fill)
+            self.value_cache.fill_(fill)
+        self.alloc = Allocator(num_blocks, block_size)
+        self.device = torch.device(device)
+
+    # host allocator -------------------------------------------------------
+    def set_free_order(self, ids: Sequence[int]) -> None:
+        self.alloc.set_free_order(ids)
+
+    def new_seq(self) -> int:
+        return self.alloc.new_seq()
+
+    def fork(self, parent: int) -> int:
+        return self.alloc.fork(parent)
+
+    def free_seq(self, seq: int) -> None:
+        self.alloc.free_seq(seq)
+
+    def reserve(self, seqs: Sequence[int]):
+        """One new token per entry of `seqs` (in order).
+        Returns (slots, cow_src, cow_dst) as int32 numpy arrays."""
+        return self.alloc.append_slots(seqs)
+
+    def tables(self, seqs: Sequence[int], max_blocks_per_seq: Optional[int] = None):
+        if max_blocks_per_seq is None:
+            max_blocks_per_seq = max(1, max(len(self.alloc.block_table(s)[0]) for s in seqs))
+        return self.alloc.block_tables(seqs, max_blocks_per_seq)
+
+    # device ----------------------------------------------------------------
+    def upload(self, a: np.ndarray) -> torch.Tensor:
+        return torch.from_numpy(np.ascontiguousarray(a)).to(self.device, non_blocking=False)
+
+    def copy(self, cow_src, cow_dst, stream=None) -> None:
+        if len(cow_src):
+            pa_copy_blocks(self.key_cache, self.value_cache, _as_dev(cow_src, self.device),
+                           _as_dev(cow_dst, self.device), stream)
+
+    def write(self, key: torch.Tensor, value: torch.Tensor, slots, stream=None) -> None:
+        pa_reshape_and_cache(key, value, self.key_cache, self.value_cache,
+                             _as_dev(slots, self.device), stream)
+
+    def workspace(self, num_seqs: int, num_q_heads: int, max_context_len: int,
+                  partition_size: int) -> Optional[torch.Tensor]:
+        n = pa_decode_workspace_bytes(num_seqs, num_q_heads, self.head_dim, max_context_len,
+                                      partition_size)
+        return torch.empty(n, dtype=torch.uint8, device=self.device) if n else None
+
+    def attend(self, query, block_tables, context_lens, scale: float, out=None,
+               partition_size: int = 0, max_context_len: int = 0, variant: int = PA_VARIANT_AUTO,
+               workspace=None, stream=None) -> torch.Tensor:
+        out = torch.empty_like(query) if out is None else out
+        if partition_size and workspace is None:
+            workspace = self.workspace(query.shape[0], query.shape[1], max_context_len,
+                                       partition_size)
+        pa_decode(out, query, self.key_cache, self.value_cache, block_tables, context_lens, scale,
+                  max_context_len=max_context_len, partition_size=partition_size, variant=variant,
+                  workspace=workspace, stream=stream)
+        return out
+
+
+def _as_dev(a, device) -> torch.Tensor:
+    if isinstance(a, torch.Tensor):
+        return a if a.device.type != "cpu" else a.to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+def to_torch(a: np.ndarray, dtype: str) -> torch.Tensor:
+    """Storage numpy array (f32 / f16 / bf16 bits as uint16) -> CPU tensor."""
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    return torch.from_numpy(a)
+
+
+TORCH_DTYPE: Dict[str, torch.dtype] = {"f32": torch.float32, "f16": torch.float16,
+                                       "bf16": torch.bfloat16}

@@ -1,0 +1,100 @@
+"""Build a decode batch on the device by replaying an allocator script.
+
+The script is a list of operations ('new', seq) / ('fork', parent, child) /
+('append', seq, n) and every append carries the K/V of its n tokens.  Placement
+order: prompts; then the copy-on-write copies the appends raised; then every
+sequence's later tokens except its newest one.  The newest tokens are what a
+decode step writes (DeviceBatch.step).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import PA_VARIANT_AUTO
+from .engine import TORCH_DTYPE, PagedKVCache, to_torch
+
+
+@dataclasses.dataclass
+class DeviceBatch:
+    cache: PagedKVCache
+    query: torch.Tensor  # [S][H_q][d]
+    new_key: torch.Tensor  # [S][H_kv][d]
+    new_value: torch.Tensor
+    slot_mapping: torch.Tensor  # int32 [S]: newest token of each sequence
+    block_tables: torch.Tensor  # int32 [S][max_blocks]
+    context_lens: torch.Tensor  # int32 [S]
+    cow_src: np.ndarray
+    cow_dst: np.ndarray
+    host_tables: np.ndarray
+    host_context_lens: np.ndarray
+    max_context_len: int
+    scale: float
+
+    def step(self, partition_size: int = 0, variant: int = PA_VARIANT_AUTO, out=None,
+             workspace=None, stream=None) -> torch.Tensor:
+        """The decode step: newest K/V into their slots, then attention."""
+        self.cache.write(self.new_key, self.new_value, self.slot_mapping, stream)
+        return self.attend(partition_size, variant, out, workspace, stream)
+
+    def attend(self, partition_size: int = 0, variant: int = PA_VARIANT_AUTO, out=None,
+               workspace=None, stream=None) -> torch.Tensor:
+        return self.cache.attend(self.query, self.block_tables, self.context_lens, self.scale,
+                                 out=out, partition_size=partition_size,
+                                 max_context_len=self.max_context_len, variant=variant,
+                                 workspace=workspace, stream=stream)
+
+
+def replay(batch, poison: bool = True, device="cuda",
+           num_blocks: Optional[int] = None) -> DeviceBatch:
+    """`batch` carries .workload (sizes), .free_order, .script, .q, .append_k, .append_v."""
+    w = batch.workload
+    tdt = TORCH_DTYPE[w.dtype]
+    cache = PagedKVCache(num_blocks or w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, tdt,
+                         device, fill=float("nan") if poison else 0.0)
+    cache.set_free_order(batch.free_order)
+    ids = {}
+    slots: List[np.ndarray] = []
+    src, dst = [], []
+    for op in batch.script:
+        if op.kind == "new":
+            ids[op.seq] = cache.new_seq()
+        elif op.kind == "fork":
+            ids[op.arg] = cache.fork(ids[op.seq])
+        else:
+            s, cs, cd = cache.reserve([ids[op.seq]] * op.arg)
+            slots.append(s)
+            src += cs.tolist()
+            dst += cd.tolist()
+    appends = [op for op in batch.script if op.kind == "append"]
+    last = {}
+    for i, op in enumerate(appends):
+        last[op.seq] = i
+
+    def dev(a):
+        return to_torch(a, w.dtype).to(device)
+
+    for i, op in enumerate(appends):
+        if last[op.seq] != i:
+            cache.write(dev(batch.append_k[i]), dev(batch.append_v[i]), slots[i])
+    cow_src = np.asarray(src, np.int32)
+    cow_dst = np.asarray(dst, np.int32)
+    cache.copy(cow_src, cow_dst)
+    S = w.num_seqs
+    newest = np.empty(S, np.int32)
+    nk = np.empty((S, w.num_kv_heads, w.head_dim), batch.append_k[0].dtype)
+    nv = np.empty_like(nk)
+    for seq, i in last.items():
+        if appends[i].arg > 1:
+            cache.write(dev(batch.append_k[i][:-1]), dev(batch.append_v[i][:-1]), slots[i][:-1])
+        newest[seq] = slots[i][-1]
+        nk[seq] = batch.append_k[i][-1]
+        nv[seq] = batch.append_v[i][-1]
+    seq_ids = [ids[s] for s in range(S)]
+    bt, cl = cache.tables(seq_ids)
+    return DeviceBatch(cache, dev(batch.q), dev(nk), dev(nv), cache.upload(newest),
+                       cache.upload(bt), cache.upload(cl), cow_src, cow_dst, bt, cl,
+                       int(cl.max()) if S else 0, w.scale)

@@ -1,0 +1,292 @@
+"""HIP path against the oracle on the GPU (through the C ABI).
+
+Bars: bitwise for the block operations and the pools they write; max-abs 1e-5 for
+fp32 attention and 2e-2 for fp16 / bf16 attention (output rounded to the storage
+type, oracle in binary64, unrounded).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_308_amd as pa
+import workloads as W
+from oracle import place
+from oracle_pins import Case
+from paged_kv_cache_308_amd.engine import TORCH_DTYPE, to_torch
+from paged_kv_cache_308_amd.replay import replay
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
+VALU, MFMA, AUTO = pa.PA_VARIANT_VALU, pa.PA_VARIANT_MFMA, pa.PA_VARIANT_AUTO
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def bits(t: torch.Tensor) -> bytes:
+    return t.cpu().contiguous().view(torch.uint8).numpy().tobytes()
+
+
+def np_bits(a: np.ndarray) -> bytes:
+    return np.ascontiguousarray(a).tobytes()
+
+
+HAVE_MFMA = False  # the matrix-core kernel is checked once it is built
+
+
+def variants(Hq, Hkv, dtype):
+    vs = [VALU]
+    if HAVE_MFMA and Hq // Hkv >= 2 and dtype != "f32":
+        vs.append(MFMA)
+    return vs
+
+
+def variants_for(w):
+    return variants(w.num_q_heads, w.num_kv_heads, w.dtype)
+
+
+# ----------------------------------------------------------- small workloads
+
+SMALL = {
+    "tiny_fp32": W.WORKLOADS["tiny_fp32"],
+    "mha_f16": W.scaled(W.WORKLOADS["llama7b"], num_seqs=8, num_q_heads=8, num_kv_heads=8,
+                        num_blocks=1200, partition_size=128),
+    "long_bf16": W.scaled(W.WORKLOADS["llama13b_long"], num_seqs=4, num_q_heads=8, num_kv_heads=8,
+                          low=600, high=1100, num_blocks=400, partition_size=256),
+    "prefix_f16": W.scaled(W.WORKLOADS["prefix_sharing"], num_seqs=10, groups=2, samples=5,
+                           num_q_heads=8, num_kv_heads=8, prefix_base=64, private_max=40,
+                           num_blocks=256, partition_size=64),
+    "gqa_bf16": W.scaled(W.WORKLOADS["llama70b_gqa"], num_seqs=3, num_q_heads=16, num_kv_heads=2,
+                         low=300, high=700, num_blocks=64, partition_size=256),
+    "gqa_f16_b16": W.scaled(W.WORKLOADS["llama70b_gqa"], num_seqs=3, num_q_heads=8,
+                            num_kv_heads=2, low=100, high=300, num_blocks=128, block_size=16,
+                            dtype="f16", partition_size=64),
+    "f16_d64_b32": W.scaled(W.WORKLOADS["llama7b"], num_seqs=5, num_q_heads=4, num_kv_heads=4,
+                            head_dim=64, block_size=32, num_blocks=300, partition_size=64),
+    "f32_d128_b64_g4": W.scaled(W.WORKLOADS["llama70b_gqa"], num_seqs=3, num_q_heads=8,
+                                num_kv_heads=2, low=50, high=200, num_blocks=32, block_size=64,
+                                dtype="f32", partition_size=128),
+    "bf16_d64_b128_g16": W.scaled(W.WORKLOADS["llama70b_gqa"], num_seqs=2, num_q_heads=16,
+                                  num_kv_heads=1, head_dim=64, low=200, high=400, num_blocks=16,
+                                  partition_size=256),
+}
+
+
+@pytest.fixture(scope="module")
+def oracle_steps():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            batch = W.make_batch(SMALL[name])
+            out, p = place.decode_step(batch)
+            cache[name] = (batch, out, p)
+        return cache[name]
+    return get
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_workload(name, oracle_steps):
+    w = SMALL[name]
+    batch, want, placed = oracle_steps(name)
+    for P in sorted({0, w.partition_size}):
+        for v in variants_for(w):
+            say(f"[gpu] small {name} P={P} variant={v}")
+            db = replay(batch)
+            assert np.array_equal(db.host_tables, placed.block_tables)
+            assert np.array_equal(db.cow_src, placed.cow_src)
+            assert np.array_equal(db.cow_dst, placed.cow_dst)
+            got = db.step(partition_size=P, variant=v)
+            torch.cuda.synchronize()
+            err = np.max(np.abs(f64(got) - want))
+            assert err <= TOL[w.dtype], (name, P, v, err)
+            # the pools after the step: bit for bit what the oracle's scatter/copy wrote
+            assert bits(db.cache.key_cache) == np_bits(placed.key_cache)
+            assert bits(db.cache.value_cache) == np_bits(placed.value_cache)
+
+
+# ----------------------------------------------------------------- edge cases
+
+
+def _upload_case(c: Case):
+    dt = TORCH_DTYPE[c.dtype]
+    dev = lambda a: to_torch(a, c.dtype).cuda()
+    q = dev(c.q)
+    kc, vc = dev(c.kc), dev(c.vc)
+    bt = torch.from_numpy(c.tables).cuda()
+    cl = torch.from_numpy(c.ctx).cuda()
+    assert kc.dtype == dt
+    return q, kc, vc, bt, cl
+
+
+def _run_case(c: Case, P, variant, max_ctx=None, tables=None):
+    q, kc, vc, bt, cl = _upload_case(c)
+    if tables is not None:
+        bt = torch.from_numpy(tables).cuda()
+    out = torch.empty_like(q)
+    mc = int(c.ctx.max()) if max_ctx is None else max_ctx
+    ws = None
+    if P:
+        n = pa.pa_decode_workspace_bytes(q.shape[0], q.shape[1], c.d, mc, P)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    pa.pa_decode(out, q, kc, vc, bt, cl, c.scale, max_context_len=mc, partition_size=P,
+                 variant=variant, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+EDGE_LENS = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1000]
+
+EDGE_SHAPES = [
+    # Hq, Hkv, d, B, dtype
+    (4, 4, 128, 16, "f16"),
+    (4, 4, 64, 16, "f32"),
+    (8, 1, 128, 16, "bf16"),
+    (8, 2, 64, 32, "f16"),
+    (16, 16, 128, 128, "bf16"),
+    (32, 2, 128, 64, "bf16"),
+    (4, 2, 128, 16, "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_edge_lengths(shape):
+    Hq, Hkv, d, B, dt = shape
+    rng = np.random.default_rng(7)
+    c = Case(rng, EDGE_LENS, Hq, Hkv, d, B, dt)
+    want = c.run(oracle.default())
+    for P in (0, 64, 512) if B <= 64 else (0, 128, 512):
+        for v in variants(Hq, Hkv, dt):
+            say(f"[gpu] edge {shape} P={P} variant={v}")
+            got = _run_case(c, P, v)
+            err = np.max(np.abs(f64(got) - want))
+            assert err <= TOL[dt], (shape, P, v, err)
+            assert torch.all(got[0] == 0)  # empty context
+            # one token: exactly that token's V
+            g = Hq // Hkv
+            v1 = to_torch(c.v[1], dt)[0]  # [Hkv][d]
+            assert bits(got[1]) == bits(v1.repeat_interleave(g, dim=0))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_identity_and_permuted_tables_are_bit_identical(dt):
+    lens = [100, 37, 513, 16, 1]
+    outs = []
+    for identity in (True, False):
+        rng = np.random.default_rng(11)
+        c = Case(rng, lens, 8, 2, 128, 16, dt, identity=identity)
+        for P in (0, 64):
+            say(f"[gpu] identity={identity} {dt} P={P}")
+            outs.append((P, bits(_run_case(c, P, VALU))))
+    assert outs[0] == outs[2] and outs[1] == outs[3]
+
+
+@pytest.mark.parametrize("P", [0, 64])
+def test_bad_table_entry_gives_nan_for_that_sequence_only(P):
+    rng = np.random.default_rng(12)
+    c = Case(rng, [40, 50, 60], 4, 4, 128, 16, "f16")
+    clean = _run_case(c, P, VALU)
+    for bad in (-1, c.num_blocks, 1 << 30):
+        t = c.tables.copy()
+        t[1, 2] = bad
+        say(f"[gpu] bad entry {bad} P={P}")
+        got = _run_case(c, P, VALU, tables=t)
+        assert torch.isnan(got[1]).all()
+        assert bits(got[0]) == bits(clean[0]) and bits(got[2]) == bits(clean[2])
+
+
+def test_context_longer_than_max_context_len_gives_nan():
+    rng = np.random.default_rng(13)
+    c = Case(rng, [100, 300], 4, 4, 128, 16, "bf16")
+    say("[gpu] ctx > max_context_len")
+    got = _run_case(c, 64, VALU, max_ctx=128)
+    assert torch.isnan(got[1]).all() and not torch.isnan(got[0]).any()
+
+
+def test_reshape_and_cache_bitwise():
+    rng = np.random.default_rng(14)
+    for dt, nb, H, B, d in (("f16", 40, 8, 16, 128), ("f32", 9, 2, 64, 64), ("bf16", 7, 16, 128, 128)):
+        N = nb * B // 3
+        slots = rng.choice(nb * B, size=N, replace=False).astype(np.int32)
+        slots[::7] = -1
+        slots[3] = nb * B + 5  # past the pool: skipped
+        key = W.round_to(rng.standard_normal((N, H, d), dtype=np.float32), dt)
+        val = W.round_to(rng.standard_normal((N, H, d), dtype=np.float32), dt)
+        kc = W.round_to(rng.standard_normal((nb, H, B, d), dtype=np.float32), dt)
+        vc = W.round_to(rng.standard_normal((nb, H, B, d), dtype=np.float32), dt)
+        gk, gv = to_torch(kc, dt).cuda(), to_torch(vc, dt).cuda()
+        say(f"[gpu] reshape_and_cache {dt} N={N}")
+        pa.pa_reshape_and_cache(to_torch(key, dt).cuda(), to_torch(val, dt).cuda(), gk, gv,
+                                torch.from_numpy(slots).cuda())
+        torch.cuda.synchronize()
+        ok = slots.copy()
+        ok[3] = -1
+        oracle.default().reshape_and_cache(key, val, kc, vc, ok, dt)
+        assert bits(gk) == np_bits(kc) and bits(gv) == np_bits(vc)
+
+
+def test_copy_blocks_bitwise():
+    rng = np.random.default_rng(15)
+    for dt, nb, H, B, d in (("f16", 64, 32, 16, 128), ("f32", 20, 4, 32, 64), ("bf16", 30, 8, 128, 128)):
+        kc = W.round_to(rng.standard_normal((nb, H, B, d), dtype=np.float32), dt)
+        vc = W.round_to(rng.standard_normal((nb, H, B, d), dtype=np.float32), dt)
+        ids = rng.permutation(nb).astype(np.int32)
+        n = nb // 3
+        src, dst = ids[:n].copy(), ids[n:2 * n].copy()
+        gk, gv = to_torch(kc, dt).cuda(), to_torch(vc, dt).cuda()
+        s_dev = torch.from_numpy(np.append(src, nb + 3).astype(np.int32)).cuda()  # last pair skipped
+        d_dev = torch.from_numpy(np.append(dst, 0).astype(np.int32)).cuda()
+        say(f"[gpu] copy_blocks {dt} pairs={n}")
+        pa.pa_copy_blocks(gk, gv, s_dev, d_dev)
+        torch.cuda.synchronize()
+        oracle.default().copy_blocks(kc, vc, src, dst, dt)
+        assert bits(gk) == np_bits(kc) and bits(gv) == np_bits(vc)
+
+
+# ------------------------------------------------------------ full-size workloads
+
+
+def _sample(ctx: np.ndarray, k: int = 6):
+    order = np.argsort(ctx, kind="stable")
+    pick = {int(order[0]), int(order[-1])}
+    rng = np.random.default_rng(99)
+    for s in rng.permutation(len(ctx)):
+        if len(pick) >= k:
+            break
+        pick.add(int(s))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", ["llama7b", "llama13b_long", "llama70b_gqa", "prefix_sharing"])
+def test_full_size_sampled(name):
+    """Whole batch on the GPU in the benchmark's launch setup; oracle on a sample of
+    sequences (attention does not depend on where blocks sit, so the oracle may
+    place its sub-batch in its own pool)."""
+    w = W.WORKLOADS[name]
+    say(f"[gpu] full-size {name}: generating")
+    batch = W.make_batch(w)
+    db = replay(batch)
+    variant = AUTO
+    say(f"[gpu] full-size {name}: step P={w.partition_size}")
+    got = f64(db.step(partition_size=w.partition_size, variant=variant))
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(got))
+    if w.lengths == "prefix":
+        want, p = place.decode_step(batch)
+        assert np.array_equal(db.host_tables, p.block_tables) and len(db.cow_src) == 64
+        err = np.max(np.abs(got - want))
+    else:
+        seqs = _sample(batch.lengths.context_lens)
+        want, _ = place.decode_step(W.make_batch(w, seqs=seqs))
+        err = np.max(np.abs(got[seqs] - want))
+    say(f"[gpu] full-size {name}: max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
