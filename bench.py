@@ -1,0 +1,248 @@
+"""Paged decode attention benchmark on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b]
+
+A step is one decode step of the whole batch on the device, inputs resident in
+HBM: the copy-on-write block copies the step raised (prefix_sharing only), the
+newest tokens' K/V scattered into their slots (pa_reshape_and_cache), and decode
+attention over the block tables (pa_decode, with context partitions and their
+log-sum-exp merge when the workload uses them).  Steps rotate over R replicas of
+the batch in separate allocations, so no step finds the previous one's K/V in the
+last-level cache.
+
+Printed: one JSON line.  value = effective KV GB/s of the whole step
+(sum_s ctx_s * 2 * H_kv * d * esz / step time); also decode seqs/s, the decode
+call alone, its roofline against 8 TB/s, the same kernels on an identity
+(physically contiguous) layout, the host allocator's cost per step, and the
+oracle's CPU time on the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+REPLICAS = 3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama7b")
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--no-identity", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, ctx: np.ndarray) -> dict:
+    """Bytes one decode call must move: K/V of every cached token, q in, out, the
+    table entries it reads and the lengths."""
+    esz = w.elem_bytes
+    kv = int(ctx.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * esz
+    qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * esz
+    tbl = 4 * int(np.sum((ctx.astype(np.int64) + w.block_size - 1) // w.block_size)) + 4 * w.num_seqs
+    return {"kv": kv, "total": kv + qo + tbl}
+
+
+def build_replicas(args, w, batch, identity: bool):
+    import torch
+    from paged_kv_cache_308_amd.replay import replay
+    import workloads as W
+    b = batch
+    if identity:
+        b = W.Batch(batch.workload, batch.lengths, np.arange(w.num_blocks, dtype=np.int32),
+                    batch.script, batch.q, batch.append_k, batch.append_v)
+    reps = []
+    for r in range(REPLICAS):
+        db = replay(b, poison=False)
+        ws = db.cache.workspace(w.num_seqs, w.num_q_heads, db.max_context_len, args.P)
+        src = torch.from_numpy(db.cow_src).cuda()
+        dst = torch.from_numpy(db.cow_dst).cuda()
+        out = torch.empty_like(db.query)
+        reps.append((db, ws, src, dst, out))
+    torch.cuda.synchronize()
+    return reps
+
+
+def run_steps(args, reps, n_steps: int, record: bool):
+    """Returns (total ms, per-step decode ms list, per-step pre-decode ms list)."""
+    import torch
+    from paged_kv_cache_308_amd import pa_copy_blocks
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)] if record else None
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(st)
+    for k in range(n_steps):
+        db, ws, src, dst, out = reps[k % len(reps)]
+        if record:
+            evs[k][0].record(st)
+        if src.numel():
+            pa_copy_blocks(db.cache.key_cache, db.cache.value_cache, src, dst, st)
+        db.cache.write(db.new_key, db.new_value, db.slot_mapping, st)
+        if record:
+            evs[k][1].record(st)
+        db.attend(args.P, args.variant, out=out, workspace=ws, stream=st)
+        if record:
+            evs[k][2].record(st)
+    t1.record(st)
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    if not record:
+        return total, [], []
+    dec = [a[1].elapsed_time(a[2]) for a in evs]
+    pre = [a[0].elapsed_time(a[1]) for a in evs]
+    return total, dec, pre
+
+
+def host_alloc_cost(w, batch, steps: int = 50) -> float:
+    """Microseconds per step for the host allocator to reserve every sequence's
+    next slot (pa_alloc_append_slots over the batch)."""
+    import paged_kv_cache_308_amd as pa
+    a = pa.Allocator(w.num_blocks, w.block_size)
+    a.set_free_order(batch.free_order)
+    ids = {}
+    for op in batch.script:
+        if op.kind == "new":
+            ids[op.seq] = a.new_seq()
+        elif op.kind == "fork":
+            ids[op.arg] = a.fork(ids[op.seq])
+        else:
+            a.append_slots([ids[op.seq]] * op.arg)
+    seqs = [ids[s] for s in range(w.num_seqs)]
+    t = time.perf_counter()
+    for _ in range(steps):
+        a.append_slots(seqs)
+    return (time.perf_counter() - t) / steps * 1e6
+
+
+def cpu_baseline(args, w, batch, kv_bytes: int) -> dict:
+    """The oracle (binary64, one thread) on the same step, timed on this host."""
+    from oracle import place
+    import oracle
+    p = place.place(batch, poison=False)
+    o = oracle.default()
+    o.reshape_and_cache(p.new_key, p.new_value, p.key_cache, p.value_cache, p.slot_mapping, w.dtype)
+    t = time.perf_counter()
+    o.decode(batch.q, p.key_cache, p.value_cache, p.block_tables, p.context_lens, w.scale, w.dtype)
+    dt = time.perf_counter() - t
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole {w.name} decode step ({w.num_seqs} sequences, all heads), "
+                      f"oracle decode call only, {dt:.2f} s on one thread of {cpu}",
+            "seconds": round(dt, 3), "seqs_per_s": round(w.num_seqs / dt, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(sequences, KV heads and context partitions shard without communication; "
+              "run one process per GPU)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    import paged_kv_cache_308_amd as pa  # noqa: F401  (fails loudly without libpa.so)
+    pa._lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = W.WORKLOADS[args.workload]
+    args.P = w.partition_size if args.partition_size is None else args.partition_size
+    log(args, f"[bench] {w.name}: generating inputs")
+    batch = W.make_batch(w)
+    ctx = batch.lengths.context_lens
+    ab = algorithmic_bytes(w, ctx)
+    log(args, f"[bench] placing {REPLICAS} replicas")
+    reps = build_replicas(args, w, batch, identity=False)
+
+    log(args, f"[bench] warmup {args.warmup}")
+    run_steps(args, reps, args.warmup, record=False)
+    log(args, f"[bench] timing {args.steps} steps")
+    total_ms, dec_ms, pre_ms = run_steps(args, reps, args.steps, record=True)
+    ms_step = total_ms / args.steps
+    dec_avg = float(np.mean(dec_ms))
+    log(args, f"[bench] {ms_step * 1e3:.1f} us/step, decode {dec_avg * 1e3:.1f} us")
+
+    ident = None
+    if not args.no_identity:
+        del reps
+        torch.cuda.empty_cache()
+        reps_i = build_replicas(args, w, batch, identity=True)
+        run_steps(args, reps_i, args.warmup, record=False)
+        _, dec_i, _ = run_steps(args, reps_i, args.steps, record=True)
+        ident = float(np.mean(dec_i))
+        del reps_i
+        torch.cuda.empty_cache()
+        log(args, f"[bench] identity layout decode {ident * 1e3:.1f} us")
+
+    alloc_us = host_alloc_cost(w, batch)
+    cpu = None if args.no_cpu else cpu_baseline(args, w, batch, ab["kv"])
+
+    gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
+    achieved = ab["total"] / (dec_avg * 1e-3) / 1e9
+    kernels = "decode_valu_kernel" + (" + lse_merge_kernel" if args.P else "")
+    line = {
+        "metric": "paged decode attn: effective KV HBM GB/s (% of peak) and decode seqs/sec",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "num_blocks": w.num_blocks,
+                   "sum_context_lens": int(ctx.sum()), "max_context_len": int(ctx.max()),
+                   "partition_size": args.P, "variant": args.variant,
+                   "kv_bytes_per_step": ab["kv"], "replicas": REPLICAS},
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "decode_us": round(dec_avg * 1e3, 2),
+        "pre_decode_us": round(float(np.mean(pre_ms)) * 1e3, 2),
+        "decode_kv_gbs": round(ab["kv"] / (dec_avg * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "kernel": kernels, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": ab["total"], "traffic": None},
+        "identity_decode_us": None if ident is None else round(ident * 1e3, 2),
+        "paged_vs_identity": None if ident is None else round(ident / dec_avg, 4),
+        "host_alloc_us_per_step": round(alloc_us, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

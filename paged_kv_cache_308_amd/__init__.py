@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpa.so")
+# PA_LIBRARY selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_BOUNDS, PA_ERR_OOM, PA_ERR_UNSUPPORTED, PA_ERR_HIP = range(6)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2

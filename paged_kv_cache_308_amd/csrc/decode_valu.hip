@@ -22,9 +22,10 @@
 //    loads are in flight while the current one is reduced);
 //  * at the end the rows of a wave, then the waves of the workgroup (through LDS),
 //    are merged with log-sum-exp weights;
-//  * workgroup ids are remapped so that consecutive work items (the same KV head
-//    and partition of consecutive sequences) run on the same XCD and share its L2
-//    when their tables point at the same blocks (shared prefixes).
+//  * workgroup ids are remapped so that each XCD runs a contiguous range of work
+//    items (partition fastest, then sequence, then KV head): the XCDs get equal
+//    shares, and consecutive sequences of one KV head share an XCD's L2 when their
+//    tables point at the same blocks (shared prefixes).
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -33,7 +34,14 @@
 namespace pa {
 namespace {
 
-constexpr int NW = 4;  // waves per workgroup
+#ifndef PA_VALU_WAVES
+#define PA_VALU_WAVES 8
+#endif
+#ifndef PA_VALU_LOADS
+#define PA_VALU_LOADS 4
+#endif
+constexpr int NW = PA_VALU_WAVES;  // waves per workgroup
+constexpr int NL = PA_VALU_LOADS;  // wave loads (of K and of V) per chunk
 
 template <typename T, int D, int G, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
@@ -46,20 +54,23 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
     constexpr int EPL = 16 / EB;            // elements per lane per row
     constexpr int LPT = D * EB / 16;        // lanes per token row
     constexpr int TPW = 64 / LPT;           // token rows per wave load
-    constexpr int NL = 4;                   // wave loads per chunk
     constexpr int C = NL * TPW;             // tokens per chunk
     constexpr int ROW_BYTES = D * EB;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform: keeps table lookups on the scalar unit and branches scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row = lane / LPT;
     const int col = lane % LPT;
 
+    // work item order: partition fastest, then sequence, then KV head, so every XCD's
+    // contiguous range holds whole sequences (balanced) and a head's sequences are
+    // neighbours (shared-prefix siblings land on one XCD)
     const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int s = L % num_seqs;
-    const int rest = L / num_seqs;
-    const int kvh = rest % num_kv_heads;
-    const int part = rest / num_kv_heads;
+    const int part = L % max_partitions;
+    const int rest = L / max_partitions;
+    const int s = rest % num_seqs;
+    const int kvh = rest / num_seqs;
     const int num_q_heads = num_kv_heads * G;
 
     const int ctx = context_lens[s];
@@ -96,21 +107,29 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
     const bool has_tail = (ntok % C) != 0;
 
     // Byte offset of the first row of wave load i of chunk c (uniform), or -1 when the
-    // load lies past `end` or its table entry is outside the pool.
+    // load lies past `end` or its table entry is outside the pool.  The last block
+    // looked up is remembered: the loads of a chunk usually share one block.
+    int cached_lb = -1;
+    int64_t cached_base = -1;
     auto load_offset = [&](int c, int i) -> int64_t {
         const int tok = start + c * C + i * TPW;
         if (tok >= end) return -1;
         const int lb = tok >> log2_block;
-        if (lb >= max_blocks_per_seq) {  // context longer than the table row
-            bad = true;
-            return -1;
+        if (lb != cached_lb) {
+            cached_lb = lb;
+            cached_base = -1;
+            if (lb >= max_blocks_per_seq) {  // context longer than the table row
+                bad = true;
+            } else {
+                const int32_t pb = table[lb];
+                if (pb < 0 || pb >= num_blocks)
+                    bad = true;
+                else
+                    cached_base = (int64_t)pb * block_bytes + head_off;
+            }
         }
-        const int32_t pb = table[lb];
-        if (pb < 0 || pb >= num_blocks) {
-            bad = true;
-            return -1;
-        }
-        return (int64_t)pb * block_bytes + head_off + (int64_t)(tok & (block_size - 1)) * ROW_BYTES;
+        if (cached_base < 0) return -1;
+        return cached_base + (int64_t)(tok & (block_size - 1)) * ROW_BYTES;
     };
 
     struct Chunk {
@@ -121,8 +140,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
         for (int i = 0; i < NL; ++i) {
             const int64_t off = load_offset(c, i);
             if (off >= 0) {
-                b.k[i] = *(const u32x4 *)(key_cache + off + lane * 16);
-                b.v[i] = *(const u32x4 *)(value_cache + off + lane * 16);
+                // K/V are read once per step: non-temporal loads keep them from
+                // displacing reusable lines in the caches (measured +8-10%)
+                b.k[i] = __builtin_nontemporal_load((const u32x4 *)(key_cache + off + lane * 16));
+                b.v[i] = __builtin_nontemporal_load((const u32x4 *)(value_cache + off + lane * 16));
             } else {
                 b.k[i] = u32x4{0, 0, 0, 0};
                 b.v[i] = u32x4{0, 0, 0, 0};

@@ -80,7 +80,7 @@ class Workload:
 WORKLOADS: Dict[str, Workload] = {
     "tiny_fp32": Workload("tiny_fp32", 1, 4, 4, 4, 64, 16, 32, "f32", 0, "fixed",
                           fixed_lengths=(1, 16, 17, 100)),
-    "llama7b": Workload("llama7b", 2, 64, 32, 32, 128, 16, 40000, "f16", 512, "lognormal"),
+    "llama7b": Workload("llama7b", 2, 64, 32, 32, 128, 16, 40000, "f16", 0, "lognormal"),
     "llama13b_long": Workload("llama13b_long", 3, 32, 40, 40, 128, 16, 16384, "bf16", 512,
                               "uniform", low=2048, high=4096),
     "prefix_sharing": Workload("prefix_sharing", 4, 80, 32, 32, 128, 16, 8192, "f16", 512,
