@@ -338,12 +338,9 @@ int launch_t(const DecodeArgs &a) {
                            (const uint8_t *)a.value_cache, a.block_tables, a.context_lens, a.ws_max,
                            a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads,
                            log2b, a.num_blocks, a.partition_size, a.max_partitions, a.scale_log2);
-        int rc = check_launch("decode_valu (partitions)");
+        const int rc = check_launch("decode_valu (partitions)");
         if (rc != PA_OK) return rc;
-        hipLaunchKernelGGL((lse_merge_kernel<T, D>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
-                           st, a.out, a.ws_max, a.ws_sum, a.ws_acc, a.context_lens, a.num_q_heads,
-                           a.partition_size, a.max_partitions);
-        return check_launch("lse_merge");
+        return launch_lse_merge(a);
     }
     hipLaunchKernelGGL((decode_valu_kernel<T, D, G, false>), dim3(grid), dim3(NW * 64), 0, st,
                        a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
@@ -372,7 +369,29 @@ int by_dim(const DecodeArgs &a) {
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d", a.head_dim);
 }
 
+template <typename T, int D>
+int merge_t(const DecodeArgs &a) {
+    hipLaunchKernelGGL((lse_merge_kernel<T, D>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
+                       (hipStream_t)a.stream, a.out, a.ws_max, a.ws_sum, a.ws_acc, a.context_lens,
+                       a.num_q_heads, a.partition_size, a.max_partitions);
+    return check_launch("lse_merge");
+}
+
+template <typename T>
+int merge_dim(const DecodeArgs &a) {
+    return a.head_dim == 64 ? merge_t<T, 64>(a) : merge_t<T, 128>(a);
+}
+
 }  // namespace
+
+int launch_lse_merge(const DecodeArgs &a) {
+    switch (a.dtype) {
+        case PA_F32: return merge_dim<F32>(a);
+        case PA_F16: return merge_dim<F16>(a);
+        case PA_BF16: return merge_dim<BF16>(a);
+    }
+    return fail(PA_ERR_UNSUPPORTED, "dtype %d", a.dtype);
+}
 
 int launch_decode_valu(const DecodeArgs &a) {
     switch (a.dtype) {

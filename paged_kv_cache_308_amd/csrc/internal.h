@@ -45,6 +45,8 @@ size_t workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_par
 // Kernel launchers (return PA_OK, PA_ERR_UNSUPPORTED or PA_ERR_HIP).
 int launch_decode_valu(const DecodeArgs &a);
 int launch_decode_mfma(const DecodeArgs &a);
+// Log-sum-exp merge of partition partials into `out` (after a partitioned decode).
+int launch_lse_merge(const DecodeArgs &a);
 bool mfma_supported(int dtype, int head_dim, int block_size, int group);
 int launch_reshape_and_cache(const void *key, const void *value, void *key_cache,
                              void *value_cache, const int32_t *slot_mapping, int num_tokens,

@@ -40,7 +40,7 @@ def np_bits(a: np.ndarray) -> bytes:
     return np.ascontiguousarray(a).tobytes()
 
 
-HAVE_MFMA = False  # the matrix-core kernel is checked once it is built
+HAVE_MFMA = True
 
 
 def variants(Hq, Hkv, dtype):

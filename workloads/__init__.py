@@ -86,7 +86,7 @@ WORKLOADS: Dict[str, Workload] = {
     "prefix_sharing": Workload("prefix_sharing", 4, 80, 32, 32, 128, 16, 8192, "f16", 512,
                                "prefix", groups=16, samples=5, prefix_base=1024,
                                private_max=256),
-    "llama70b_gqa": Workload("llama70b_gqa", 5, 32, 64, 8, 128, 128, 4096, "bf16", 512,
+    "llama70b_gqa": Workload("llama70b_gqa", 5, 32, 64, 8, 128, 128, 4096, "bf16", 0,
                              "uniform", low=4096, high=8192),
 }
 
