@@ -17,9 +17,11 @@
 //    which is exactly a P^T operand once the k order is chosen to match (no shuffle);
 //  * the O^T fragment holds one head per lane column, so the online-softmax rescale
 //    and the final division use per-lane values;
-//  * V must be read transposed (8 tokens of one d per lane): each wave stages its V
-//    rows in its own LDS region (rows padded by 32 bytes so the 4 rows read together
-//    fall in different banks) and reads them back 16 bits at a time.
+//  * V must be read transposed (8 tokens of one d per lane): each wave copies its V
+//    rows HBM -> LDS with direct 16-byte LDS loads (global_load_lds_dwordx4, no
+//    register staging) into its own double-buffered region, 1 KiB per wave load with
+//    32 bytes of padding after each KiB so the four rows read together fall in
+//    different banks, and reads them back 16 bits at a time.
 // Softmax runs in fp32 (online, exp2 domain).  P enters the second product rounded to
 // the storage type; the normaliser sums the rounded weights, so numerator and
 // denominator use the same weights.  Accumulation is fp32.
@@ -84,9 +86,11 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
     constexpr int ROW = D * 2;            // bytes per token row
     constexpr int NKK = D / 32;           // 32-wide d steps of the score product
     constexpr int NN = D / 16;            // 16-row d fragments of the output
-    constexpr int LROW = ROW + 32;        // padded LDS row stride (bytes)
-    constexpr int VL = 16 * ROW / 1024;   // 16-byte wave loads per 16-token V tile
-    constexpr int STAGE = CT * LROW;      // LDS bytes per wave
+    constexpr int VL = 16 * ROW / 1024;   // 1 KiB wave loads per 16-token V tile
+    constexpr int RPK = 1024 / ROW;       // token rows per KiB
+    constexpr int KSTR = 1024 + 32;       // LDS stride of one KiB group (padded)
+    constexpr int STAGE = 2 * VL * KSTR;  // LDS bytes of one chunk's V
+    constexpr int WAVE_LDS = 2 * STAGE;   // double-buffered
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -108,9 +112,9 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
         end = min(ctx, start + partition_size);
     }
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[MW * STAGE];
-    static_assert((2 * MW * G + MW * G * D) * 4 <= MW * STAGE, "merge area must fit the staging area");
-    uint8_t *stage = lds + wave * STAGE;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[MW * WAVE_LDS];
+    static_assert((2 * MW * G + MW * G * D) * 4 <= MW * WAVE_LDS, "merge area must fit the staging area");
+    uint8_t *wave_lds = lds + wave * WAVE_LDS;
 
     const int block_size = 1 << log2_block;
     const int32_t *table = block_tables + (int64_t)s * max_blocks_per_seq;
@@ -136,7 +140,10 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
     const int ntok = ctx < 0 ? 0 : end - start;
     const int nchunks = (ntok + CT - 1) / CT;
 
-    // byte offset of the first row of 16-token tile `tt` of chunk c, or -1
+    // Byte offset of the first row of 16-token tile `tt` of chunk c, or -1.  A tile with
+    // no data (past `end`, or a bad entry) reads block 0's first rows instead (inside
+    // the pool; masked like any row past `end`): no branch around a load, because one
+    // makes the compiler wait for every outstanding load.
     auto tile_base = [&](int c, int tt) -> int64_t {
         const int tok = start + c * CT + 16 * tt;
         if (tok >= end) return -1;
@@ -153,41 +160,35 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
         return (int64_t)pb * block_bytes + head_off + (int64_t)(tok & (block_size - 1)) * ROW;
     };
 
+    // a chunk's K operands live in registers; its V rows go to LDS stage `st`
     struct Chunk {
         u32x4 k[2][NKK];
-        u32x4 v[2][VL];
     };
-    auto issue = [&](Chunk &b, int c) {
+    auto issue = [&](Chunk &b, int c, int st) {
+        uint8_t *stage = wave_lds + st * STAGE;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const int64_t base = tile_base(c, tt);
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                b.k[tt][kk] = base >= 0 ? __builtin_nontemporal_load((const u32x4 *)(key_cache + base + n * ROW + (32 * kk + 8 * q) * 2))
-                                        : u32x4{0, 0, 0, 0};
+            int64_t base = tile_base(c, tt);
+            base = base < 0 ? 0 : base;
 #pragma unroll
             for (int i = 0; i < VL; ++i)
-                b.v[tt][i] = base >= 0 ? __builtin_nontemporal_load((const u32x4 *)(value_cache + base + i * 1024 + lane * 16))
-                                       : u32x4{0, 0, 0, 0};
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(value_cache + base + i * 1024 + lane * 16),
+                    (__attribute__((address_space(3))) void *)(stage + (tt * VL + i) * KSTR), 16, 0, 0);
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+                b.k[tt][kk] = kv_load(
+                    (const u32x4 *)(key_cache + base + n * ROW + (32 * kk + 8 * q) * 2));
         }
     };
-    auto consume = [&](const Chunk &b, int c) {
+    // LDS address of V[row r of the chunk][byte col]
+    auto v_at = [&](const uint8_t *stage, int r, int col) -> const uint8_t * {
+        return stage + (r / RPK) * KSTR + (r % RPK) * ROW + col;
+    };
+    auto consume = [&](const Chunk &b, int c, int st) {
+        const uint8_t *stage = wave_lds + st * STAGE;
         const int tok0 = start + c * CT;
         const bool tail = tok0 + CT > end;
-        // stage V rows in LDS (rows past `end` as zeros: 0 * NaN would poison the product)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int i = 0; i < VL; ++i) {
-                const int byte = i * 1024 + lane * 16;
-                const int r = 16 * tt + byte / ROW;
-                u32x4 w = b.v[tt][i];
-                if (tail && tok0 + r >= end) w = u32x4{0, 0, 0, 0};
-                *(u32x4 *)(stage + r * LROW + (byte % ROW)) = w;
-            }
         // scores S^T: lane holds tokens 16 tt + 4 q + i of head n
         float sc[2][4];
 #pragma unroll
@@ -229,9 +230,20 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
         const u32x4 pb = u32x4{pk[0], pk[1], pk[2], pk[3]};
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn) o[nn] *= alpha;
+        // this chunk's V rows have landed in LDS: its V loads were issued before its K
+        // loads, which the score product above already waited for
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (tail) {
+            // rows past `end` as zeros: 0 * NaN would poison the product
+            for (int r = max(0, end - tok0); r < CT; ++r)
+                for (int col = lane * 4; col < ROW; col += 256)
+                    *(uint32_t *)v_at(stage, r, col) = 0u;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
         // V^T operand per 16-row d fragment: lane reads V[t(q, j)][16 nn + n]
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn) {
@@ -239,28 +251,39 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
                 const int t0 = j < 4 ? 4 * q + j : 16 + 4 * q + (j - 4);
-                const uint16_t a = *(const uint16_t *)(stage + t0 * LROW + (16 * nn + n) * 2);
-                const uint16_t c2 = *(const uint16_t *)(stage + (t0 + 1) * LROW + (16 * nn + n) * 2);
+                const uint16_t a = *(const uint16_t *)v_at(stage, t0, (16 * nn + n) * 2);
+                const uint16_t c2 = *(const uint16_t *)v_at(stage, t0 + 1, (16 * nn + n) * 2);
                 vk[j / 2] = (uint32_t)a | ((uint32_t)c2 << 16);
             }
             o[nn] = Mma<T>::run(u32x4{vk[0], vk[1], vk[2], vk[3]}, pb, o[nn]);
         }
+        // the stage is rewritten by a later chunk's loads: finish reading it first
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
     {
+        // this wave's chunks are wave, wave + MW, ...; the steady-state loop always has
+        // a next chunk to prefetch (see tile_base), the last one or two run after it
+        const int mine = nchunks > wave ? (nchunks - wave + MW - 1) / MW : 0;
         Chunk A, Bf;
-        int c = wave;
-        if (c < nchunks) issue(A, c);
-        while (c < nchunks) {
-            int cn = c + MW;
-            if (cn < nchunks) issue(Bf, cn);
-            consume(A, c);
-            c = cn;
-            if (c >= nchunks) break;
-            cn = c + MW;
-            if (cn < nchunks) issue(A, cn);
-            consume(Bf, c);
-            c = cn;
+        if (mine > 0) {
+            issue(A, wave, 0);
+            int j = 0;
+            for (; j + 2 < mine; j += 2) {
+                issue(Bf, wave + (j + 1) * MW, 1);
+                consume(A, wave + j * MW, 0);
+                issue(A, wave + (j + 2) * MW, 0);
+                consume(Bf, wave + (j + 1) * MW, 1);
+            }
+            if (j + 1 < mine) {
+                issue(Bf, wave + (j + 1) * MW, 1);
+                consume(A, wave + j * MW, 0);
+                consume(Bf, wave + (j + 1) * MW, 1);
+            } else {
+                consume(A, wave + j * MW, 0);
+            }
         }
     }
 

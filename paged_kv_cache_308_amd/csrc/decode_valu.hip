@@ -109,6 +109,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
     // Byte offset of the first row of wave load i of chunk c (uniform), or -1 when the
     // load lies past `end` or its table entry is outside the pool.  The last block
     // looked up is remembered: the loads of a chunk usually share one block.
+    // A load with no data (past `end` in the tail chunk, or through a bad entry) reads
+    // block 0's first rows instead (always inside the pool; masked or discarded
+    // later): no branch around a load, because one makes the compiler wait for every
+    // outstanding load.
     int cached_lb = -1;
     int64_t cached_base = -1;
     auto load_offset = [&](int c, int i) -> int64_t {
@@ -138,16 +142,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
     auto issue = [&](Chunk &b, int c) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const int64_t off = load_offset(c, i);
-            if (off >= 0) {
-                // K/V are read once per step: non-temporal loads keep them from
-                // displacing reusable lines in the caches (measured +8-10%)
-                b.k[i] = __builtin_nontemporal_load((const u32x4 *)(key_cache + off + lane * 16));
-                b.v[i] = __builtin_nontemporal_load((const u32x4 *)(value_cache + off + lane * 16));
-            } else {
-                b.k[i] = u32x4{0, 0, 0, 0};
-                b.v[i] = u32x4{0, 0, 0, 0};
-            }
+            int64_t off = load_offset(c, i);
+            off = off < 0 ? 0 : off;
+            b.k[i] = kv_load((const u32x4 *)(key_cache + off + lane * 16));
+            b.v[i] = kv_load((const u32x4 *)(value_cache + off + lane * 16));
         }
     };
     auto consume = [&](const Chunk &b, int c, bool tail) {
@@ -197,20 +195,28 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
     };
 
     // double-buffered walk over this wave's full chunks: wave, wave + NW, ...
+    // This wave's full chunks are wave, wave + NW, ...  The steady-state loop always
+    // has a next chunk to prefetch, so its loads are unconditional and the compiler
+    // waits only for the chunk being reduced; the last one or two run after it.
     {
+        const int mine = nfull > wave ? (nfull - wave + NW - 1) / NW : 0;
         Chunk A, Bf;
-        int c = wave;
-        if (c < nfull) issue(A, c);
-        while (c < nfull) {
-            int cn = c + NW;
-            if (cn < nfull) issue(Bf, cn);
-            consume(A, c, false);
-            c = cn;
-            if (c >= nfull) break;
-            cn = c + NW;
-            if (cn < nfull) issue(A, cn);
-            consume(Bf, c, false);
-            c = cn;
+        if (mine > 0) {
+            issue(A, wave);
+            int j = 0;
+            for (; j + 2 < mine; j += 2) {
+                issue(Bf, wave + (j + 1) * NW);
+                consume(A, wave + j * NW, false);
+                issue(A, wave + (j + 2) * NW);
+                consume(Bf, wave + (j + 1) * NW, false);
+            }
+            if (j + 1 < mine) {
+                issue(Bf, wave + (j + 1) * NW);
+                consume(A, wave + j * NW, false);
+                consume(Bf, wave + (j + 1) * NW, false);
+            } else {
+                consume(A, wave + j * NW, false);
+            }
         }
         if (has_tail && (nfull % NW) == wave) {
             issue(A, nfull);
