@@ -32,6 +32,33 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 REPLICAS = 3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_sources_digest() -> str:
+    """sha256 over the HIP/C++ sources of libpa (names and contents, sorted)."""
+    import hashlib
+    d = os.path.join(ROOT, "paged_kv_cache_308_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None
+    when the kernels have changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("sources_sha256") != kernel_sources_digest():
+        return None
+    return rec["bytes_per_launch"]
 
 
 def parse():
@@ -45,6 +72,9 @@ def parse():
     ap.add_argument("--no-identity", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     return ap.parse_args()
 
 
@@ -170,6 +200,16 @@ def main():
               "run one process per GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return
     import workloads as W
     import paged_kv_cache_308_amd as pa  # noqa: F401  (fails loudly without libpa.so)
     pa._lib()
@@ -238,7 +278,7 @@ def main():
         "decode_kv_gbs": round(ab["kv"] / (dec_avg * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": kernels, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": ab["total"], "traffic": None},
+                     "bytes_per_launch": ab["total"], "traffic": measured_traffic(w.name)},
         "identity_decode_us": None if ident is None else round(ident * 1e3, 2),
         "paged_vs_identity": None if ident is None else round(ident / dec_avg, 4),
         "host_alloc_us_per_step": round(alloc_us, 2),

@@ -60,11 +60,17 @@ typedef enum pa_status {
 
 typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
 
-/* Decode-attention variants (pa_decode's `variant` argument). */
+/* Decode-attention variants (pa_decode's `variant` argument): a kernel choice in the
+ * low 4 bits, optionally OR-ed with PA_DECODE_SHARED_KV. */
 typedef enum pa_variant {
     PA_VARIANT_AUTO = 0, /* MFMA when the group size is >= 2 and dtype is 16-bit, else VALU */
     PA_VARIANT_VALU = 1, /* vector-ALU kernel: one wavefront row per token */
-    PA_VARIANT_MFMA = 2  /* matrix-core kernel for grouped-query heads (16-bit only) */
+    PA_VARIANT_MFMA = 2, /* matrix-core kernel for grouped-query heads (16-bit only) */
+    /* Hint: the batch's tables share physical blocks (forked sequences, shared prefixes,
+     * [cpai] §6).  K/V are then read with cacheable loads so sequences that read the same
+     * block can hit in L2; without it they are read non-temporally, which is faster when
+     * every block is read once per step.  Results are identical either way. */
+    PA_DECODE_SHARED_KV = 16
 } pa_variant;
 
 /* Static text for a status code. */

@@ -21,6 +21,7 @@ LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 PA_OK, PA_ERR_INVALID, PA_ERR_BOUNDS, PA_ERR_OOM, PA_ERR_UNSUPPORTED, PA_ERR_HIP = range(6)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
+PA_DECODE_SHARED_KV = 16
 
 # Every symbol include/pa.h declares (checked by the tests).
 EXPORTS = (

@@ -36,6 +36,35 @@ static bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int launch_decode_valu(const DecodeArgs &a) {
+    switch (a.dtype) {
+        case PA_F32: return launch_decode_valu_f32(a);
+        case PA_F16: return launch_decode_valu_f16(a);
+        case PA_BF16: return launch_decode_valu_bf16(a);
+    }
+    return fail(PA_ERR_UNSUPPORTED, "dtype %d", a.dtype);
+}
+
+int launch_lse_merge(const DecodeArgs &a) {
+    switch (a.dtype) {
+        case PA_F32: return launch_lse_merge_f32(a);
+        case PA_F16: return launch_lse_merge_f16(a);
+        case PA_BF16: return launch_lse_merge_bf16(a);
+    }
+    return fail(PA_ERR_UNSUPPORTED, "dtype %d", a.dtype);
+}
+
+bool mfma_supported(int dtype, int head_dim, int block_size, int group) {
+    return (dtype == PA_F16 || dtype == PA_BF16) && (head_dim == 64 || head_dim == 128) &&
+           block_size >= 16 && (group == 2 || group == 4 || group == 8 || group == 16);
+}
+
+int launch_decode_mfma(const DecodeArgs &a) {
+    if (a.dtype == PA_F16) return launch_decode_mfma_f16(a);
+    if (a.dtype == PA_BF16) return launch_decode_mfma_bf16(a);
+    return fail(PA_ERR_UNSUPPORTED, "MFMA dtype %d", a.dtype);
+}
+
 size_t workspace_layout(int S, int Hq, int d, int P, void *ws, float **m, float **l, float **acc) {
     const size_t n = (size_t)S * Hq * P;
     const size_t bm = align256(n * sizeof(float));
@@ -113,7 +142,8 @@ int pa_decode(void *out, const void *query, const void *key_cache, const void *v
                     partition_size, block_size);
     if (partition_size > 0 && max_context_len <= 0)
         return fail(PA_ERR_INVALID, "max_context_len %d with partitions", max_context_len);
-    if (variant < PA_VARIANT_AUTO || variant > PA_VARIANT_MFMA)
+    const int kernel_choice = variant & 15;
+    if (kernel_choice > PA_VARIANT_MFMA || (variant & ~(15 | PA_DECODE_SHARED_KV)))
         return fail(PA_ERR_INVALID, "variant %d", variant);
 
     DecodeArgs a{};
@@ -133,6 +163,7 @@ int pa_decode(void *out, const void *query, const void *key_cache, const void *v
     a.partition_size = partition_size;
     a.max_partitions = max_partitions_for(max_context_len, partition_size);
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.cached_kv = (variant & PA_DECODE_SHARED_KV) != 0;
     a.dtype = dtype;
     a.stream = stream;
     if (partition_size > 0) {
@@ -144,13 +175,13 @@ int pa_decode(void *out, const void *query, const void *key_cache, const void *v
                          &a.ws_sum, &a.ws_acc);
     }
     const bool mfma_ok = mfma_supported(dtype, head_dim, block_size, group);
-    if (variant == PA_VARIANT_MFMA) {
+    if (kernel_choice == PA_VARIANT_MFMA) {
         if (!mfma_ok)
             return fail(PA_ERR_UNSUPPORTED, "MFMA kernel needs 16-bit dtype and group >= 2 (group %d)",
                         group);
         return launch_decode_mfma(a);
     }
-    if (variant == PA_VARIANT_AUTO && mfma_ok && group >= 2) return launch_decode_mfma(a);
+    if (kernel_choice == PA_VARIANT_AUTO && mfma_ok && group >= 2) return launch_decode_mfma(a);
     return launch_decode_valu(a);
 }
 

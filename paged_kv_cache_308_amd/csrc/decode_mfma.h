@@ -1,3 +1,4 @@
+#pragma once
 // Grouped-query paged decode attention on the matrix cores (gfx950 MFMA).
 //
 // What is computed is the same as the vector kernel ("PagedAttention" concept report
@@ -34,7 +35,7 @@
 #include "kernel_common.h"
 
 namespace pa {
-namespace {
+namespace mfma {
 
 #ifndef PA_MFMA_WAVES
 #define PA_MFMA_WAVES 4
@@ -76,7 +77,7 @@ struct Mma<BF16> {
     }
 };
 
-template <typename T, int D, int G, bool SPLIT>
+template <typename T, int D, int G, bool SPLIT, bool NT>
 __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
     void *__restrict__ out, const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
     const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
                     (__attribute__((address_space(3))) void *)(stage + (tt * VL + i) * KSTR), 16, 0, 0);
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk)
-                b.k[tt][kk] = kv_load(
+                b.k[tt][kk] = kv_load<NT>(
                     (const u32x4 *)(key_cache + base + n * ROW + (32 * kk + 8 * q) * 2));
         }
     };
@@ -342,14 +343,14 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
     }
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool NT>
 int launch_t(const DecodeArgs &a) {
     const int log2b = __builtin_ctz(a.block_size);
     const bool split = a.partition_size > 0;
     const unsigned grid = (unsigned)a.num_seqs * a.num_kv_heads * (split ? a.max_partitions : 1);
     hipStream_t st = (hipStream_t)a.stream;
     if (split) {
-        hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, true>), dim3(grid), dim3(MW * 64), 0, st,
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, true, NT>), dim3(grid), dim3(MW * 64), 0, st,
                            a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
                            (const uint8_t *)a.value_cache, a.block_tables, a.context_lens, a.ws_max,
                            a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads,
@@ -358,7 +359,7 @@ int launch_t(const DecodeArgs &a) {
         if (rc != PA_OK) return rc;
         return launch_lse_merge(a);
     }
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, false>), dim3(grid), dim3(MW * 64), 0, st,
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, false, NT>), dim3(grid), dim3(MW * 64), 0, st,
                        a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
                        (const uint8_t *)a.value_cache, a.block_tables, a.context_lens, nullptr,
                        nullptr, nullptr, a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads, log2b,
@@ -366,13 +367,18 @@ int launch_t(const DecodeArgs &a) {
     return check_launch("decode_mfma");
 }
 
+template <typename T, int D, int G>
+int by_cache(const DecodeArgs &a) {
+    return a.cached_kv ? launch_t<T, D, G, false>(a) : launch_t<T, D, G, true>(a);
+}
+
 template <typename T, int D>
 int by_group(const DecodeArgs &a) {
     switch (a.num_q_heads / a.num_kv_heads) {
-        case 2: return launch_t<T, D, 2>(a);
-        case 4: return launch_t<T, D, 4>(a);
-        case 8: return launch_t<T, D, 8>(a);
-        case 16: return launch_t<T, D, 16>(a);
+        case 2: return by_cache<T, D, 2>(a);
+        case 4: return by_cache<T, D, 4>(a);
+        case 8: return by_cache<T, D, 8>(a);
+        case 16: return by_cache<T, D, 16>(a);
     }
     return fail(PA_ERR_UNSUPPORTED, "MFMA group %d", a.num_q_heads / a.num_kv_heads);
 }
@@ -384,17 +390,6 @@ int by_dim(const DecodeArgs &a) {
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d", a.head_dim);
 }
 
-}  // namespace
-
-bool mfma_supported(int dtype, int head_dim, int block_size, int group) {
-    return (dtype == PA_F16 || dtype == PA_BF16) && (head_dim == 64 || head_dim == 128) &&
-           block_size >= 16 && (group == 2 || group == 4 || group == 8 || group == 16);
-}
-
-int launch_decode_mfma(const DecodeArgs &a) {
-    if (a.dtype == PA_F16) return by_dim<F16>(a);
-    if (a.dtype == PA_BF16) return by_dim<BF16>(a);
-    return fail(PA_ERR_UNSUPPORTED, "MFMA dtype %d", a.dtype);
-}
+}  // namespace mfma
 
 }  // namespace pa

@@ -1,0 +1,8 @@
+// BF16 instantiations of the matrix-core decode kernels (see decode_mfma.h).
+#include "decode_mfma.h"
+
+namespace pa {
+
+int launch_decode_mfma_bf16(const DecodeArgs &a) { return mfma::by_dim<BF16>(a); }
+
+}  // namespace pa

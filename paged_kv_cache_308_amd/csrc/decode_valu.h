@@ -1,3 +1,4 @@
+#pragma once
 // Paged decode attention on the vector ALUs (gfx950), one pass or split by context
 // partition, and the log-sum-exp merge of partition partials.
 //
@@ -32,7 +33,7 @@
 #include "kernel_common.h"
 
 namespace pa {
-namespace {
+namespace valu {
 
 #ifndef PA_VALU_WAVES
 #define PA_VALU_WAVES 8
@@ -43,7 +44,7 @@ namespace {
 constexpr int NW = PA_VALU_WAVES;  // waves per workgroup
 constexpr int NL = PA_VALU_LOADS;  // wave loads (of K and of V) per chunk
 
-template <typename T, int D, int G, bool SPLIT>
+template <typename T, int D, int G, bool SPLIT, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
     void *__restrict__ out, const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
     const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
@@ -144,8 +145,8 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
         for (int i = 0; i < NL; ++i) {
             int64_t off = load_offset(c, i);
             off = off < 0 ? 0 : off;
-            b.k[i] = kv_load((const u32x4 *)(key_cache + off + lane * 16));
-            b.v[i] = kv_load((const u32x4 *)(value_cache + off + lane * 16));
+            b.k[i] = kv_load<NT>((const u32x4 *)(key_cache + off + lane * 16));
+            b.v[i] = kv_load<NT>((const u32x4 *)(value_cache + off + lane * 16));
         }
     };
     auto consume = [&](const Chunk &b, int c, bool tail) {
@@ -332,14 +333,14 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(
     }
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool NT>
 int launch_t(const DecodeArgs &a) {
     const int log2b = __builtin_ctz(a.block_size);
     const bool split = a.partition_size > 0;
     const unsigned grid = (unsigned)a.num_seqs * a.num_kv_heads * (split ? a.max_partitions : 1);
     hipStream_t st = (hipStream_t)a.stream;
     if (split) {
-        hipLaunchKernelGGL((decode_valu_kernel<T, D, G, true>), dim3(grid), dim3(NW * 64), 0, st,
+        hipLaunchKernelGGL((decode_valu_kernel<T, D, G, true, NT>), dim3(grid), dim3(NW * 64), 0, st,
                            a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
                            (const uint8_t *)a.value_cache, a.block_tables, a.context_lens, a.ws_max,
                            a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads,
@@ -348,7 +349,7 @@ int launch_t(const DecodeArgs &a) {
         if (rc != PA_OK) return rc;
         return launch_lse_merge(a);
     }
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, G, false>), dim3(grid), dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, G, false, NT>), dim3(grid), dim3(NW * 64), 0, st,
                        a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
                        (const uint8_t *)a.value_cache, a.block_tables, a.context_lens, nullptr,
                        nullptr, nullptr, a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads, log2b,
@@ -356,14 +357,19 @@ int launch_t(const DecodeArgs &a) {
     return check_launch("decode_valu");
 }
 
+template <typename T, int D, int G>
+int by_cache(const DecodeArgs &a) {
+    return a.cached_kv ? launch_t<T, D, G, false>(a) : launch_t<T, D, G, true>(a);
+}
+
 template <typename T, int D>
 int by_group(const DecodeArgs &a) {
     switch (a.num_q_heads / a.num_kv_heads) {
-        case 1: return launch_t<T, D, 1>(a);
-        case 2: return launch_t<T, D, 2>(a);
-        case 4: return launch_t<T, D, 4>(a);
-        case 8: return launch_t<T, D, 8>(a);
-        case 16: return launch_t<T, D, 16>(a);
+        case 1: return by_cache<T, D, 1>(a);
+        case 2: return by_cache<T, D, 2>(a);
+        case 4: return by_cache<T, D, 4>(a);
+        case 8: return by_cache<T, D, 8>(a);
+        case 16: return by_cache<T, D, 16>(a);
     }
     return fail(PA_ERR_UNSUPPORTED, "group %d", a.num_q_heads / a.num_kv_heads);
 }
@@ -388,24 +394,6 @@ int merge_dim(const DecodeArgs &a) {
     return a.head_dim == 64 ? merge_t<T, 64>(a) : merge_t<T, 128>(a);
 }
 
-}  // namespace
-
-int launch_lse_merge(const DecodeArgs &a) {
-    switch (a.dtype) {
-        case PA_F32: return merge_dim<F32>(a);
-        case PA_F16: return merge_dim<F16>(a);
-        case PA_BF16: return merge_dim<BF16>(a);
-    }
-    return fail(PA_ERR_UNSUPPORTED, "dtype %d", a.dtype);
-}
-
-int launch_decode_valu(const DecodeArgs &a) {
-    switch (a.dtype) {
-        case PA_F32: return by_dim<F32>(a);
-        case PA_F16: return by_dim<F16>(a);
-        case PA_BF16: return by_dim<BF16>(a);
-    }
-    return fail(PA_ERR_UNSUPPORTED, "dtype %d", a.dtype);
-}
+}  // namespace valu
 
 }  // namespace pa

@@ -34,6 +34,7 @@ struct DecodeArgs {
     int partition_size;  // 0 = one pass
     int max_partitions;  // grid extent along partitions (1 for one pass)
     float scale_log2;    // scale * log2(e)
+    bool cached_kv;      // K/V through cacheable loads (blocks shared between sequences)
     int dtype;
     void *stream;
 };
@@ -55,6 +56,16 @@ int launch_reshape_and_cache(const void *key, const void *value, void *key_cache
 int launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *src, const int32_t *dst,
                        int num_pairs, int num_kv_heads, int head_dim, int block_size,
                        int num_blocks, int elem_bytes, void *stream);
+
+// Per-dtype launchers (one translation unit each).
+int launch_decode_valu_f32(const DecodeArgs &a);
+int launch_decode_valu_f16(const DecodeArgs &a);
+int launch_decode_valu_bf16(const DecodeArgs &a);
+int launch_lse_merge_f32(const DecodeArgs &a);
+int launch_lse_merge_f16(const DecodeArgs &a);
+int launch_lse_merge_bf16(const DecodeArgs &a);
+int launch_decode_mfma_f16(const DecodeArgs &a);
+int launch_decode_mfma_bf16(const DecodeArgs &a);
 
 // Map a HIP error after a launch to PA_ERR_HIP with its text.
 int check_launch(const char *what);

@@ -83,19 +83,15 @@ __device__ inline float dot16<BF16>(const u32x4 &a, const u32x4 &b) {
     return s;
 }
 
-// K/V rows are read once per decode step: non-temporal loads keep them from
-// displacing reusable lines (measured +8-10% on streaming batches).  Building with
-// -DPA_KV_NONTEMPORAL=0 gives plain loads, which let sequences that share prefix
-// blocks hit in L2 instead.
-#ifndef PA_KV_NONTEMPORAL
-#define PA_KV_NONTEMPORAL 1
-#endif
+// K/V rows are read once per decode step unless blocks are shared between sequences:
+// non-temporal loads keep them from displacing reusable lines (measured +8-10% on
+// streaming batches); plain loads let sequences that share prefix blocks hit in L2.
+template <bool NT>
 __device__ inline u32x4 kv_load(const u32x4 *p) {
-#if PA_KV_NONTEMPORAL
-    return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
 }
 
 // DPP lane exchange inside 16-lane rows.

@@ -14,7 +14,7 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-from . import PA_VARIANT_AUTO
+from . import PA_DECODE_SHARED_KV, PA_VARIANT_AUTO
 from .engine import TORCH_DTYPE, PagedKVCache, to_torch
 
 
@@ -33,6 +33,7 @@ class DeviceBatch:
     host_context_lens: np.ndarray
     max_context_len: int
     scale: float
+    shared: bool = False  # tables share physical blocks: pass the cache hint
 
     def step(self, partition_size: int = 0, variant: int = PA_VARIANT_AUTO, out=None,
              workspace=None, stream=None) -> torch.Tensor:
@@ -42,6 +43,8 @@ class DeviceBatch:
 
     def attend(self, partition_size: int = 0, variant: int = PA_VARIANT_AUTO, out=None,
                workspace=None, stream=None) -> torch.Tensor:
+        if self.shared:
+            variant |= PA_DECODE_SHARED_KV
         return self.cache.attend(self.query, self.block_tables, self.context_lens, self.scale,
                                  out=out, partition_size=partition_size,
                                  max_context_len=self.max_context_len, variant=variant,
@@ -97,4 +100,5 @@ def replay(batch, poison: bool = True, device="cuda",
     bt, cl = cache.tables(seq_ids)
     return DeviceBatch(cache, dev(batch.q), dev(nk), dev(nv), cache.upload(newest),
                        cache.upload(bt), cache.upload(cl), cow_src, cow_dst, bt, cl,
-                       int(cl.max()) if S else 0, w.scale)
+                       int(cl.max()) if S else 0, w.scale,
+                       cache.alloc.stats()["shared_blocks"] > 0)

@@ -190,6 +190,26 @@ def test_identity_and_permuted_tables_are_bit_identical(dt):
     assert outs[0] == outs[2] and outs[1] == outs[3]
 
 
+def test_shared_kv_hint_changes_nothing_but_the_cache_policy():
+    """PA_DECODE_SHARED_KV selects cacheable loads; the result is bit-identical."""
+    batch = W.make_batch(SMALL["prefix_f16"])
+    for v in (VALU, AUTO):
+        outs = []
+        for hint in (0, pa.PA_DECODE_SHARED_KV):
+            db = replay(batch)
+            db.shared = False
+            say(f"[gpu] shared-kv hint={hint} variant={v}")
+            outs.append(bits(db.step(partition_size=64, variant=v | hint)))
+        assert outs[0] == outs[1]
+    g = W.make_batch(SMALL["gqa_bf16"])
+    outs = []
+    for hint in (0, pa.PA_DECODE_SHARED_KV):
+        db = replay(g)
+        say(f"[gpu] shared-kv hint={hint} mfma")
+        outs.append(bits(db.step(partition_size=0, variant=MFMA | hint)))
+    assert outs[0] == outs[1]
+
+
 @pytest.mark.parametrize("P", [0, 64])
 def test_bad_table_entry_gives_nan_for_that_sequence_only(P):
     rng = np.random.default_rng(12)

@@ -199,6 +199,8 @@ def _decode(**kw):
     (dict(P=512, maxctx=0), pa.PA_ERR_INVALID),
     (dict(variant=2, dtype=pa.PA_F32, Hq=16, Hkv=8), pa.PA_ERR_UNSUPPORTED),
     (dict(variant=5), pa.PA_ERR_INVALID),
+    (dict(variant=32), pa.PA_ERR_INVALID),
+    (dict(variant=pa.PA_DECODE_SHARED_KV | 3), pa.PA_ERR_INVALID),
     (dict(out=None), pa.PA_ERR_INVALID),
     (dict(nb=0), pa.PA_ERR_INVALID),
     (dict(scale=float("nan")), pa.PA_ERR_INVALID),
