@@ -82,12 +82,17 @@ int pa_abi_version(void);
 
 /* ------------------------------------------------------------------ device ops */
 
+/* pa_decode's partition_size for the balanced split (see pa_decode). */
+#define PA_PARTITION_BALANCED (-1)
+
 /*
  * Bytes of scratch pa_decode needs for a given partition size (0 when
- * partition_size == 0).  Partials are kept in fp32: for every sequence, query head
- * and partition a running max, a sum of weights and head_dim weighted sums.
+ * partition_size == 0).  Partials are kept in fp32: a running max, a sum of weights
+ * and head_dim weighted sums per query head, for every (sequence, partition) or, with
+ * PA_PARTITION_BALANCED, for every wave the current device can hold plus every
+ * (sequence, KV head); the balanced size therefore depends on the current device.
  */
-size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                  int max_context_len, int partition_size);
 
 /*
@@ -98,11 +103,15 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
  * Softmax and accumulation run in fp32; out is rounded to `dtype` (round to nearest
  * even).  context_lens[s] == 0 gives zeros.
  *
- * partition_size == 0: one pass per (sequence, KV head).  Otherwise a multiple of
- * block_size (and of 16): each partition of that many tokens is reduced on its own
- * and a second kernel merges the partials with log-sum-exp weights; `workspace`
- * must then hold pa_decode_workspace_bytes(...) bytes of device memory and
- * max_context_len must bound every context_lens[s].
+ * partition_size == 0: one pass per (sequence, KV head).  A multiple of block_size
+ * (and of 16): each partition of that many tokens is reduced on its own and a second
+ * kernel merges the partials with log-sum-exp weights; max_context_len must bound
+ * every context_lens[s].  PA_PARTITION_BALANCED (vector kernel, at most 4096
+ * sequences): the batch's work, as one list of 16-token chunks over KV heads and
+ * sequences, is cut into equal ranges for all the waves the device holds at once,
+ * whatever the length mix; each wave writes a partial per (sequence, KV head) it
+ * touches and a second kernel merges them.  With partitions `workspace` must hold
+ * pa_decode_workspace_bytes(...) bytes of device memory (contents need not be set).
  * `variant` selects the kernel (pa_variant).
  */
 int pa_decode(void *out, const void *query, const void *key_cache, const void *value_cache,

@@ -22,6 +22,7 @@ PA_OK, PA_ERR_INVALID, PA_ERR_BOUNDS, PA_ERR_OOM, PA_ERR_UNSUPPORTED, PA_ERR_HIP
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 PA_DECODE_SHARED_KV = 16
+PA_PARTITION_BALANCED = -1
 
 # Every symbol include/pa.h declares (checked by the tests).
 EXPORTS = (
@@ -63,7 +64,7 @@ def _lib():
         "pa_status_str": (ctypes.c_char_p, [i32]),
         "pa_last_error": (ctypes.c_char_p, []),
         "pa_abi_version": (i32, []),
-        "pa_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "pa_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
         "pa_decode": (i32, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                             i32, i32, i32, vp, sz, vp]),
         "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
@@ -125,10 +126,10 @@ def _dev(t, name, dtype=None):
     return t.data_ptr()
 
 
-def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                               max_context_len: int, partition_size: int) -> int:
-    return _lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
-                                            partition_size)
+    return _lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            max_context_len, partition_size)
 
 
 def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale: float,

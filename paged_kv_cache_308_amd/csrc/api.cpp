@@ -78,6 +78,31 @@ size_t workspace_layout(int S, int Hq, int d, int P, void *ws, float **m, float 
     return 2 * bm + bacc;
 }
 
+size_t workspace_layout_balanced(int S, int Hq, int Hkv, int d, int W, void *ws, int32_t **hdr,
+                                 float **m, float **l, float **acc) {
+    const size_t bh = align256((size_t)(4 + S + 1) * sizeof(int32_t));
+    const size_t n = ((size_t)W + (size_t)Hkv * S) * (size_t)(Hq / Hkv);
+    const size_t bm = align256(n * sizeof(float));
+    const size_t bacc = align256(n * (size_t)d * sizeof(float));
+    if (ws) {
+        char *p = (char *)ws;
+        *hdr = (int32_t *)p;
+        *m = (float *)(p + bh);
+        *l = (float *)(p + bh + bm);
+        *acc = (float *)(p + bh + 2 * bm);
+    }
+    return bh + 2 * bm + bacc;
+}
+
+int device_max_waves() {
+    int dev = 0, cus = 0, threads = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&threads, hipDeviceAttributeMaxThreadsPerMultiProcessor, dev) != hipSuccess)
+        return 0;
+    return cus * (threads / 64);
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -98,16 +123,25 @@ const char *pa_status_str(int status) {
 
 const char *pa_last_error(void) { return g_err; }
 
-int pa_abi_version(void) { return 1; }
+int pa_abi_version(void) { return 2; }
 
 static int max_partitions_for(int max_context_len, int partition_size) {
     if (partition_size == 0) return 1;
     return max_context_len <= 0 ? 1 : (max_context_len + partition_size - 1) / partition_size;
 }
 
-size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
-                                 int partition_size) {
-    if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_context_len, int partition_size) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        num_q_heads % num_kv_heads)
+        return 0;
+    if (partition_size == PA_PARTITION_BALANCED) {
+        const int w = device_max_waves();
+        if (w <= 0) return 0;
+        return workspace_layout_balanced(num_seqs, num_q_heads, num_kv_heads, head_dim, w, nullptr,
+                                         nullptr, nullptr, nullptr, nullptr);
+    }
+    if (partition_size <= 0) return 0;
     return workspace_layout(num_seqs, num_q_heads, head_dim,
                             max_partitions_for(max_context_len, partition_size), nullptr, nullptr,
                             nullptr, nullptr);
@@ -137,9 +171,14 @@ int pa_decode(void *out, const void *query, const void *key_cache, const void *v
     if ((int64_t)num_blocks * num_kv_heads * block_size * head_dim > ((int64_t)1 << 40))
         return fail(PA_ERR_UNSUPPORTED, "pool too large");
     if (!(scale == scale)) return fail(PA_ERR_INVALID, "scale is NaN");
-    if (partition_size < 0 || (partition_size > 0 && (partition_size % block_size || partition_size % 16)))
-        return fail(PA_ERR_INVALID, "partition_size %d must be 0 or a multiple of block_size %d and 16",
+    const bool balanced = partition_size == PA_PARTITION_BALANCED;
+    if ((partition_size < 0 && !balanced) ||
+        (partition_size > 0 && (partition_size % block_size || partition_size % 16)))
+        return fail(PA_ERR_INVALID,
+                    "partition_size %d must be 0, PA_PARTITION_BALANCED or a multiple of block_size %d and 16",
                     partition_size, block_size);
+    if (balanced && num_seqs > kBalancedMaxSeqs)
+        return fail(PA_ERR_UNSUPPORTED, "balanced split takes at most %d sequences", kBalancedMaxSeqs);
     if (partition_size > 0 && max_context_len <= 0)
         return fail(PA_ERR_INVALID, "max_context_len %d with partitions", max_context_len);
     const int kernel_choice = variant & 15;
@@ -166,7 +205,18 @@ int pa_decode(void *out, const void *query, const void *key_cache, const void *v
     a.cached_kv = (variant & PA_DECODE_SHARED_KV) != 0;
     a.dtype = dtype;
     a.stream = stream;
-    if (partition_size > 0) {
+    if (balanced) {
+        // partial slots for every wave the device can hold at once
+        const int w = device_max_waves();
+        if (w <= 0) return fail(PA_ERR_HIP, "device properties unavailable");
+        const size_t need = workspace_layout_balanced(num_seqs, num_q_heads, num_kv_heads, head_dim, w,
+                                                      nullptr, nullptr, nullptr, nullptr, nullptr);
+        if (!workspace || workspace_bytes < need)
+            return fail(PA_ERR_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+        a.max_workers = w;
+        workspace_layout_balanced(num_seqs, num_q_heads, num_kv_heads, head_dim, w, workspace, &a.ws_hdr,
+                                  &a.ws_max, &a.ws_sum, &a.ws_acc);
+    } else if (partition_size > 0) {
         const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, a.max_partitions,
                                              nullptr, nullptr, nullptr, nullptr);
         if (!workspace || workspace_bytes < need)
@@ -176,12 +226,13 @@ int pa_decode(void *out, const void *query, const void *key_cache, const void *v
     }
     const bool mfma_ok = mfma_supported(dtype, head_dim, block_size, group);
     if (kernel_choice == PA_VARIANT_MFMA) {
+        if (balanced) return fail(PA_ERR_UNSUPPORTED, "balanced split runs on the vector kernel");
         if (!mfma_ok)
             return fail(PA_ERR_UNSUPPORTED, "MFMA kernel needs 16-bit dtype and group >= 2 (group %d)",
                         group);
         return launch_decode_mfma(a);
     }
-    if (kernel_choice == PA_VARIANT_AUTO && mfma_ok && group >= 2) return launch_decode_mfma(a);
+    if (kernel_choice == PA_VARIANT_AUTO && mfma_ok && group >= 2 && !balanced) return launch_decode_mfma(a);
     return launch_decode_valu(a);
 }
 

@@ -44,6 +44,84 @@ namespace valu {
 constexpr int NW = PA_VALU_WAVES;  // waves per workgroup
 constexpr int NL = PA_VALU_LOADS;  // wave loads (of K and of V) per chunk
 
+// One chunk of the online softmax for this lane's token rows.  k[i], v[i] hold this
+// lane's 16 bytes of token row `tok_row0 + i * TPW` (rows at or past `end` are masked
+// when `tail`).  m, l, acc: fp32 running max (exp2 domain), sum of weights and
+// weighted value sums of this lane's rows, for each of the G query heads.
+template <typename T, int G, int NL, int LPT, int TPW>
+__device__ inline void chunk_update(const u32x4 (&qv)[G], const u32x4 (&k)[NL], const u32x4 (&v)[NL],
+                                    int tok_row0, int end, bool tail, float scale_log2,
+                                    float (&m)[G], float (&l)[G], float (&acc)[G][16 / T::bytes]) {
+    constexpr int EPL = 16 / T::bytes;
+    float sc[G][NL];
+    bool valid[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        valid[i] = !tail || (tok_row0 + i * TPW < end);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float dot = row_sum<LPT>(dot16<T>(qv[g], k[i]));
+            sc[g][i] = valid[i] ? dot * scale_log2 : -INFINITY;
+        }
+    }
+    float vf[NL][EPL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        u32x4 w = v[i];
+        if (tail && !valid[i]) w = u32x4{0, 0, 0, 0};  // never multiply a slot past ctx
+        to_f32<T>(w, vf[i]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float cm = sc[g][0];
+#pragma unroll
+        for (int i = 1; i < NL; ++i) cm = fmaxf(cm, sc[g][i]);
+        const float mn = fmaxf(m[g], cm);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        const float alpha = fast_exp2(m[g] - ms);
+        float p[NL], psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            p[i] = fast_exp2(sc[g][i] - ms);
+            psum += p[i];
+        }
+        l[g] = l[g] * alpha + psum;
+        m[g] = mn;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            float a = acc[g][e] * alpha;
+#pragma unroll
+            for (int i = 0; i < NL; ++i) a = fmaf(p[i], vf[i][e], a);
+            acc[g][e] = a;
+        }
+    }
+}
+
+// Merge the states of a wave's token rows (lanes col, col + LPT, ... hold the same
+// dims) with log-sum-exp weights; afterwards every row holds the wave's state.
+template <int G, int EPL, int LPT>
+__device__ inline void merge_rows(float (&m)[G], float (&l)[G], float (&acc)[G][EPL]) {
+#pragma unroll
+    for (int step = LPT; step < 64; step <<= 1) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float mo = __shfl_xor(m[g], step);
+            const float lo = __shfl_xor(l[g], step);
+            const float mn = fmaxf(m[g], mo);
+            const float ms = mn == -INFINITY ? 0.f : mn;
+            const float a = fast_exp2(m[g] - ms);
+            const float bsc = fast_exp2(mo - ms);
+            l[g] = l[g] * a + lo * bsc;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const float ao = __shfl_xor(acc[g][e], step);
+                acc[g][e] = acc[g][e] * a + ao * bsc;
+            }
+            m[g] = mn;
+        }
+    }
+}
+
 template <typename T, int D, int G, bool SPLIT, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
     void *__restrict__ out, const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
@@ -150,52 +228,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
         }
     };
     auto consume = [&](const Chunk &b, int c, bool tail) {
-        const int tok0 = start + c * C + row;
-        float sc[G][NL];
-        bool valid[NL];
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            valid[i] = !tail || (tok0 + i * TPW < end);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float dot = row_sum<LPT>(dot16<T>(qv[g], b.k[i]));
-                sc[g][i] = valid[i] ? dot * scale_log2 : -INFINITY;
-            }
-        }
-        float vf[NL][EPL];
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            u32x4 w = b.v[i];
-            if (tail && !valid[i]) w = u32x4{0, 0, 0, 0};  // never multiply a slot past ctx
-            to_f32<T>(w, vf[i]);
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float cm = sc[g][0];
-#pragma unroll
-            for (int i = 1; i < NL; ++i) cm = fmaxf(cm, sc[g][i]);
-            const float mn = fmaxf(m[g], cm);
-            const float ms = mn == -INFINITY ? 0.f : mn;
-            const float alpha = fast_exp2(m[g] - ms);
-            float p[NL], psum = 0.f;
-#pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                p[i] = fast_exp2(sc[g][i] - ms);
-                psum += p[i];
-            }
-            l[g] = l[g] * alpha + psum;
-            m[g] = mn;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                float a = acc[g][e] * alpha;
-#pragma unroll
-                for (int i = 0; i < NL; ++i) a = fmaf(p[i], vf[i][e], a);
-                acc[g][e] = a;
-            }
-        }
+        chunk_update<T, G, NL, LPT, TPW>(qv, b.k, b.v, start + c * C + row, end, tail, scale_log2, m, l,
+                                         acc);
     };
 
-    // double-buffered walk over this wave's full chunks: wave, wave + NW, ...
     // This wave's full chunks are wave, wave + NW, ...  The steady-state loop always
     // has a next chunk to prefetch, so its loads are unconditional and the compiler
     // waits only for the chunk being reduced; the last one or two run after it.
@@ -225,26 +261,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
         }
     }
 
-    // merge the rows of this wave (lanes col, col + LPT, ... hold the same dims)
-#pragma unroll
-    for (int step = LPT; step < 64; step <<= 1) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mo = __shfl_xor(m[g], step);
-            const float lo = __shfl_xor(l[g], step);
-            const float mn = fmaxf(m[g], mo);
-            const float ms = mn == -INFINITY ? 0.f : mn;
-            const float a = fast_exp2(m[g] - ms);
-            const float bsc = fast_exp2(mo - ms);
-            l[g] = l[g] * a + lo * bsc;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const float ao = __shfl_xor(acc[g][e], step);
-                acc[g][e] = acc[g][e] * a + ao * bsc;
-            }
-            m[g] = mn;
-        }
-    }
+    merge_rows<G, EPL, LPT>(m, l, acc);
 
     // merge the waves through LDS
     __shared__ float sm_m[NW][G], sm_l[NW][G], sm_acc[NW][G][D];
@@ -333,8 +350,312 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(
     }
 }
 
+// ------------------------------------------------------------------ balanced split
+//
+// All work of the batch is one ordered list of chunks (KV head, then sequence, then
+// C-token chunk).  Each of the W resident waves takes an equal contiguous range of it
+// and streams it with the same double-buffered pipeline, so no wave waits for a long
+// sequence and no sequence waits for a free wave.  When a wave finishes the part of a
+// (sequence, KV head) item that lies in its range it writes that item's partial
+// (running max, sum, weighted value sums per query head) to slot `wave + item`: ranges
+// and items are both ordered, so two (wave, item) pairs that share a slot would need
+// a later wave on an earlier item, which cannot happen.  balanced_merge_kernel then
+// combines each item's partials with log-sum-exp weights.
+//
+// Workspace header (int32), written by workgroup 0: [0] chunks per KV head, [1] chunks
+// per wave, [2] waves, [4 + s] chunks of the sequences before s (s = 0..S).
+
+constexpr int NWB = 4;               // waves per workgroup of the balanced kernel
+constexpr int BAL_MAX_SEQS = 4096;   // sequences per batch in balanced mode
+constexpr int BAL_HDR = 4;           // header ints before the prefix
+
+template <typename T, int D, int G, bool NT>
+__global__ __launch_bounds__(NWB * 64) void decode_balanced_kernel(
+    const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
+    const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, int32_t *__restrict__ ws_hdr, float *__restrict__ ws_max,
+    float *__restrict__ ws_sum, float *__restrict__ ws_acc, int max_blocks_per_seq, int num_seqs,
+    int num_kv_heads, int log2_block, int num_blocks, float scale_log2) {
+    constexpr int EB = T::bytes;
+    constexpr int EPL = 16 / EB;
+    constexpr int LPT = D * EB / 16;
+    constexpr int TPW = 64 / LPT;
+    constexpr int C = NL * TPW;
+    constexpr int ROW_BYTES = D * EB;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row = lane / LPT;
+    const int col = lane % LPT;
+    const int S = num_seqs;
+    const int num_q_heads = num_kv_heads * G;
+
+    // chunks per sequence and their prefix, in LDS (wave 0 scans 64 sequences a step)
+    __shared__ int sm_pre[BAL_MAX_SEQS + 1];
+    if (wave == 0) {
+        int carry = 0;
+        for (int base = 0; base < S; base += 64) {
+            const int s = base + lane;
+            const int c = s < S ? context_lens[s] : 0;
+            int v = c > 0 ? (c + C - 1) / C : 0;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(v, o);
+                if (lane >= o) v += t;
+            }
+            if (s < S) sm_pre[s + 1] = carry + v;
+            carry += __shfl(v, 63);
+        }
+        if (lane == 0) sm_pre[0] = 0;
+    }
+    __syncthreads();
+    auto pre = [&](int s) -> int { return __builtin_amdgcn_readfirstlane(sm_pre[s]); };
+
+    const int per_head = pre(S);
+    const int total = per_head * num_kv_heads;
+    const int W = gridDim.x * NWB;
+    const int per = (total + W - 1) / W;
+    if (blockIdx.x == 0) {
+        if (threadIdx.x == 0) {
+            ws_hdr[0] = per_head;
+            ws_hdr[1] = per;
+            ws_hdr[2] = W;
+            ws_hdr[3] = 0;
+        }
+        for (int t = threadIdx.x; t <= S; t += NWB * 64) ws_hdr[BAL_HDR + t] = sm_pre[t];
+    }
+    // consecutive workers share an XCD (shared-prefix siblings are neighbours in the list)
+    const int w = xcd_remap(blockIdx.x, gridDim.x) * NWB + wave;
+    const int g_begin = w * per;
+    const int g_end = min(total, g_begin + per);
+    if (per == 0 || g_begin >= total) return;
+
+    // position in the list: KV head, sequence, chunk of the sequence
+    struct Pos {
+        int kvh, s, c, n, ctx;
+    };
+    auto locate = [&](int g) -> Pos {
+        Pos p;
+        p.kvh = g / per_head;
+        const int r = g - p.kvh * per_head;
+        int lo = 0, hi = S - 1;  // smallest s with pre(s + 1) > r
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (pre(mid + 1) > r)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        p.s = lo;
+        p.c = r - pre(lo);
+        p.n = pre(lo + 1) - pre(lo);
+        p.ctx = context_lens[lo];
+        return p;
+    };
+    auto advance = [&](Pos &p) {
+        if (++p.c < p.n) return;
+        p.c = 0;
+        do {
+            if (++p.s == S) {
+                p.s = 0;
+                ++p.kvh;
+            }
+            p.n = pre(p.s + 1) - pre(p.s);
+        } while (p.n == 0 && p.kvh < num_kv_heads);
+        p.ctx = context_lens[p.s];
+    };
+
+    const int block_size = 1 << log2_block;
+    const int64_t block_bytes = (int64_t)num_kv_heads * block_size * ROW_BYTES;
+
+    struct Chunk {
+        u32x4 q[G], k[NL], v[NL];
+        Pos p;
+        bool bad;
+    };
+    // Loads of chunk p.  As in the partitioned kernel every chunk issues the same loads
+    // (rows past ctx, a bad table entry or a position past the list read block 0's first
+    // rows and are masked or discarded), so the compiler's waits stay exact.
+    auto issue = [&](Chunk &b, const Pos &p) {
+        b.p = p;
+        b.bad = false;
+        const bool live = p.kvh < num_kv_heads;
+        const int s = live ? p.s : 0;
+        const int kvh = live ? p.kvh : 0;
+        const int32_t *table = block_tables + (int64_t)s * max_blocks_per_seq;
+        int cached_lb = -1;
+        int64_t cached_base = 0;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int tok = p.c * C + i * TPW;
+            int64_t off = 0;
+            if (live && tok < p.ctx) {
+                const int lb = tok >> log2_block;
+                if (lb != cached_lb) {
+                    cached_lb = lb;
+                    cached_base = -1;
+                    if (lb < max_blocks_per_seq) {
+                        const int32_t pb = table[lb];
+                        if (pb >= 0 && pb < num_blocks)
+                            cached_base = (int64_t)pb * block_bytes + (int64_t)kvh * block_size * ROW_BYTES;
+                    }
+                }
+                if (cached_base < 0)
+                    b.bad = true;
+                else
+                    off = cached_base + (int64_t)(tok & (block_size - 1)) * ROW_BYTES;
+            }
+            b.k[i] = kv_load<NT>((const u32x4 *)(key_cache + off + lane * 16));
+            b.v[i] = kv_load<NT>((const u32x4 *)(value_cache + off + lane * 16));
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            b.q[g] = *(const u32x4 *)(query + ((int64_t)(s * num_q_heads + kvh * G + g) * D + col * EPL) * EB);
+    };
+
+    float m[G], l[G], acc[G][EPL];
+    auto reset = [&]() {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            m[g] = -INFINITY;
+            l[g] = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+        }
+    };
+    reset();
+    bool item_bad = false;
+
+    auto consume = [&](const Chunk &b, int g) {
+        const Pos &p = b.p;
+        const int tok0 = p.c * C;
+        chunk_update<T, G, NL, LPT, TPW>(b.q, b.k, b.v, tok0 + row, p.ctx, tok0 + C > p.ctx, scale_log2, m,
+                                         l, acc);
+        item_bad |= b.bad;
+        if (p.c == p.n - 1 || g == g_end - 1) {
+            // this wave's share of the item is complete: write its partial
+            merge_rows<G, EPL, LPT>(m, l, acc);
+            const int64_t slot = (int64_t)w + p.kvh * S + p.s;
+            if (row == 0) {
+#pragma unroll
+                for (int gg = 0; gg < G; ++gg) {
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) ws_acc[(slot * G + gg) * D + col * EPL + e] = acc[gg][e];
+                    if (col == 0) {
+                        ws_max[slot * G + gg] = item_bad ? NAN : m[gg];
+                        ws_sum[slot * G + gg] = l[gg];
+                    }
+                }
+            }
+            reset();
+            item_bad = false;
+        }
+    };
+
+    const int mine = g_end - g_begin;
+    Pos ip = locate(g_begin);  // position of the next chunk to issue
+    Chunk A, Bf;
+    issue(A, ip);
+    advance(ip);
+    int j = 0;
+    for (; j + 2 < mine; j += 2) {
+        issue(Bf, ip);
+        advance(ip);
+        consume(A, g_begin + j);
+        issue(A, ip);
+        advance(ip);
+        consume(Bf, g_begin + j + 1);
+    }
+    if (j + 1 < mine) {
+        issue(Bf, ip);
+        consume(A, g_begin + j);
+        consume(Bf, g_begin + j + 1);
+    } else {
+        consume(A, g_begin + j);
+    }
+}
+
+// Combine the partials of one (sequence, query head) written by the waves whose
+// ranges cover it: out = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64) void balanced_merge_kernel(
+    void *__restrict__ out, const int32_t *__restrict__ ws_hdr, const float *__restrict__ ws_max,
+    const float *__restrict__ ws_sum, const float *__restrict__ ws_acc,
+    const int32_t *__restrict__ context_lens, int num_seqs, int num_kv_heads) {
+    const int num_q_heads = num_kv_heads * G;
+    const int sh = blockIdx.x;
+    const int s = sh / num_q_heads;
+    const int h = sh - s * num_q_heads;
+    const int kvh = h / G;
+    const int gg = h - kvh * G;
+    const int64_t obase = (int64_t)sh * D;
+    const int ctx = context_lens[s];
+    const int per_head = ws_hdr[0];
+    const int per = ws_hdr[1];
+    const int first = ws_hdr[BAL_HDR + s];
+    const int n = ws_hdr[BAL_HDR + s + 1] - first;
+    if (ctx < 0 || n == 0) {
+        for (int j = threadIdx.x; j < D; j += 64) store_out<T>(out, obase + j, ctx < 0 ? NAN : 0.f);
+        return;
+    }
+    const int g0 = kvh * per_head + first;
+    const int w0 = g0 / per, w1 = (g0 + n - 1) / per;
+    const int64_t item = (int64_t)kvh * num_seqs + s;
+    float M = -INFINITY;
+    bool bad = false;
+    for (int w = w0; w <= w1; ++w) {
+        const float x = ws_max[(w + item) * G + gg];
+        bad |= x != x;
+        M = fmaxf(M, x);
+    }
+    const float Ms = M == -INFINITY ? 0.f : M;
+    float Lsum = 0.f;
+    for (int w = w0; w <= w1; ++w) Lsum += ws_sum[(w + item) * G + gg] * fast_exp2(ws_max[(w + item) * G + gg] - Ms);
+    for (int j = threadIdx.x; j < D; j += 64) {
+        float A = 0.f;
+        for (int w = w0; w <= w1; ++w)
+            A += fast_exp2(ws_max[(w + item) * G + gg] - Ms) * ws_acc[((w + item) * G + gg) * D + j];
+        float o = Lsum > 0.f ? A / Lsum : 0.f;
+        if (bad) o = NAN;
+        store_out<T>(out, obase + j, o);
+    }
+}
+
+// Waves of one balanced launch: as many as can be resident at once on this device.
+template <typename K>
+int balanced_workers(K kernel) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)kernel, NWB * 64, 0) != hipSuccess)
+        return 0;
+    return cus * (per_cu > 0 ? per_cu : 1) * NWB;
+}
+
+template <typename T, int D, int G, bool NT>
+int launch_balanced(const DecodeArgs &a) {
+    auto kernel = decode_balanced_kernel<T, D, G, NT>;
+    static int workers = 0;  // per instantiation; the library runs on one device type
+    if (workers == 0) workers = balanced_workers(kernel);
+    if (workers <= 0) return fail(PA_ERR_HIP, "occupancy query failed");
+    if (workers > a.max_workers) workers = a.max_workers - a.max_workers % NWB;
+    hipStream_t st = (hipStream_t)a.stream;
+    hipLaunchKernelGGL(kernel, dim3(workers / NWB), dim3(NWB * 64), 0, st, (const uint8_t *)a.query,
+                       (const uint8_t *)a.key_cache, (const uint8_t *)a.value_cache, a.block_tables,
+                       a.context_lens, a.ws_hdr, a.ws_max, a.ws_sum, a.ws_acc, a.max_blocks_per_seq,
+                       a.num_seqs, a.num_kv_heads, __builtin_ctz(a.block_size), a.num_blocks,
+                       a.scale_log2);
+    int rc = check_launch("decode_balanced");
+    if (rc != PA_OK) return rc;
+    hipLaunchKernelGGL((balanced_merge_kernel<T, D, G>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0, st,
+                       a.out, a.ws_hdr, a.ws_max, a.ws_sum, a.ws_acc, a.context_lens, a.num_seqs,
+                       a.num_kv_heads);
+    return check_launch("balanced_merge");
+}
+
 template <typename T, int D, int G, bool NT>
 int launch_t(const DecodeArgs &a) {
+    if (a.partition_size < 0) return launch_balanced<T, D, G, NT>(a);
     const int log2b = __builtin_ctz(a.block_size);
     const bool split = a.partition_size > 0;
     const unsigned grid = (unsigned)a.num_seqs * a.num_kv_heads * (split ? a.max_partitions : 1);

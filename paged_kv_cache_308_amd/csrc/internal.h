@@ -24,6 +24,8 @@ struct DecodeArgs {
     float *ws_max;   // [S][H_q][P] running max (log2 domain), partitioned runs only
     float *ws_sum;   // [S][H_q][P] sum of weights
     float *ws_acc;   // [S][H_q][P][d] weighted value sums
+    int32_t *ws_hdr; // balanced split: list header and per-sequence chunk prefix
+    int max_workers; // balanced split: partial slots reserved for this many waves
     int max_blocks_per_seq;
     int num_seqs;
     int num_q_heads;
@@ -42,6 +44,13 @@ struct DecodeArgs {
 // Workspace partition for `a` (pointers into `ws`); returns bytes needed.
 size_t workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_partitions,
                         void *ws, float **m, float **l, float **acc);
+// Balanced split: header ints then (waves + H_kv * S) partial slots of G heads.
+size_t workspace_layout_balanced(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_workers, void *ws, int32_t **hdr, float **m, float **l,
+                                 float **acc);
+// Most waves the current device can hold at once (0 if unknown).
+int device_max_waves();
+constexpr int kBalancedMaxSeqs = 4096;
 
 // Kernel launchers (return PA_OK, PA_ERR_UNSUPPORTED or PA_ERR_HIP).
 int launch_decode_valu(const DecodeArgs &a);

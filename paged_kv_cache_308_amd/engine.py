@@ -75,8 +75,8 @@ class PagedKVCache:
 
     def workspace(self, num_seqs: int, num_q_heads: int, max_context_len: int,
                   partition_size: int) -> Optional[torch.Tensor]:
-        n = pa_decode_workspace_bytes(num_seqs, num_q_heads, self.head_dim, max_context_len,
-                                      partition_size)
+        n = pa_decode_workspace_bytes(num_seqs, num_q_heads, self.num_kv_heads, self.head_dim,
+                                      max_context_len, partition_size)
         return torch.empty(n, dtype=torch.uint8, device=self.device) if n else None
 
     def attend(self, query, block_tables, context_lens, scale: float, out=None,

@@ -22,6 +22,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
 VALU, MFMA, AUTO = pa.PA_VARIANT_VALU, pa.PA_VARIANT_MFMA, pa.PA_VARIANT_AUTO
+BAL = pa.PA_PARTITION_BALANCED
 
 
 def say(*a):
@@ -43,15 +44,15 @@ def np_bits(a: np.ndarray) -> bytes:
 HAVE_MFMA = True
 
 
-def variants(Hq, Hkv, dtype):
+def variants(Hq, Hkv, dtype, P=0):
     vs = [VALU]
-    if HAVE_MFMA and Hq // Hkv >= 2 and dtype != "f32":
+    if HAVE_MFMA and Hq // Hkv >= 2 and dtype != "f32" and P != BAL:
         vs.append(MFMA)
     return vs
 
 
-def variants_for(w):
-    return variants(w.num_q_heads, w.num_kv_heads, w.dtype)
+def variants_for(w, P=0):
+    return variants(w.num_q_heads, w.num_kv_heads, w.dtype, P)
 
 
 # ----------------------------------------------------------- small workloads
@@ -98,8 +99,8 @@ def oracle_steps():
 def test_small_workload(name, oracle_steps):
     w = SMALL[name]
     batch, want, placed = oracle_steps(name)
-    for P in sorted({0, w.partition_size}):
-        for v in variants_for(w):
+    for P in sorted({0, w.partition_size, BAL}):
+        for v in variants_for(w, P):
             say(f"[gpu] small {name} P={P} variant={v}")
             db = replay(batch)
             assert np.array_equal(db.host_tables, placed.block_tables)
@@ -136,7 +137,7 @@ def _run_case(c: Case, P, variant, max_ctx=None, tables=None):
     mc = int(c.ctx.max()) if max_ctx is None else max_ctx
     ws = None
     if P:
-        n = pa.pa_decode_workspace_bytes(q.shape[0], q.shape[1], c.d, mc, P)
+        n = pa.pa_decode_workspace_bytes(q.shape[0], q.shape[1], c.Hkv, c.d, mc, P)
         ws = torch.empty(n, dtype=torch.uint8, device="cuda")
     pa.pa_decode(out, q, kc, vc, bt, cl, c.scale, max_context_len=mc, partition_size=P,
                  variant=variant, workspace=ws)
@@ -164,8 +165,8 @@ def test_edge_lengths(shape):
     rng = np.random.default_rng(7)
     c = Case(rng, EDGE_LENS, Hq, Hkv, d, B, dt)
     want = c.run(oracle.default())
-    for P in (0, 64, 512) if B <= 64 else (0, 128, 512):
-        for v in variants(Hq, Hkv, dt):
+    for P in (0, 64, 512, BAL) if B <= 64 else (0, 128, 512, BAL):
+        for v in variants(Hq, Hkv, dt, P):
             say(f"[gpu] edge {shape} P={P} variant={v}")
             got = _run_case(c, P, v)
             err = np.max(np.abs(f64(got) - want))
@@ -184,10 +185,10 @@ def test_identity_and_permuted_tables_are_bit_identical(dt):
     for identity in (True, False):
         rng = np.random.default_rng(11)
         c = Case(rng, lens, 8, 2, 128, 16, dt, identity=identity)
-        for P in (0, 64):
+        for P in (0, 64, BAL):
             say(f"[gpu] identity={identity} {dt} P={P}")
             outs.append((P, bits(_run_case(c, P, VALU))))
-    assert outs[0] == outs[2] and outs[1] == outs[3]
+    assert outs[0] == outs[3] and outs[1] == outs[4] and outs[2] == outs[5]
 
 
 def test_shared_kv_hint_changes_nothing_but_the_cache_policy():
@@ -210,7 +211,7 @@ def test_shared_kv_hint_changes_nothing_but_the_cache_policy():
     assert outs[0] == outs[1]
 
 
-@pytest.mark.parametrize("P", [0, 64])
+@pytest.mark.parametrize("P", [0, 64, BAL])
 def test_bad_table_entry_gives_nan_for_that_sequence_only(P):
     rng = np.random.default_rng(12)
     c = Case(rng, [40, 50, 60], 4, 4, 128, 16, "f16")

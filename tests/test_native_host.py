@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(pa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert pa.abi_version() == 1
+    assert pa.abi_version() == 2
 
 
 # -------------------------------------------------------------- allocator parity
@@ -194,6 +194,8 @@ def _decode(**kw):
     (dict(Hq=12, Hkv=8), pa.PA_ERR_INVALID),
     (dict(Hq=8 * 32, Hkv=8), pa.PA_ERR_UNSUPPORTED),
     (dict(P=24), pa.PA_ERR_INVALID),
+    (dict(P=-2), pa.PA_ERR_INVALID),
+    (dict(P=-1, S=5000), pa.PA_ERR_UNSUPPORTED),
     (dict(P=512, ws=None), pa.PA_ERR_INVALID),
     (dict(P=512, ws=FAKE, wsb=16), pa.PA_ERR_INVALID),
     (dict(P=512, maxctx=0), pa.PA_ERR_INVALID),
@@ -216,10 +218,11 @@ def test_empty_batch_is_a_no_op():
 
 def test_workspace_size():
     S, Hq, d = 32, 40, 128
-    n = pa.pa_decode_workspace_bytes(S, Hq, d, 4096, 512)
+    n = pa.pa_decode_workspace_bytes(S, Hq, Hq, d, 4096, 512)
     parts = 8
     assert n >= S * Hq * parts * (d + 2) * 4 and n < S * Hq * parts * (d + 2) * 4 + 1024
-    assert pa.pa_decode_workspace_bytes(S, Hq, d, 4096, 0) == 0
+    assert pa.pa_decode_workspace_bytes(S, Hq, Hq, d, 4096, 0) == 0
+    assert pa.pa_decode_workspace_bytes(S, Hq, 7, d, 4096, 512) == 0  # 40 heads not a multiple of 7
 
 
 def test_block_ops_reject_before_launch():
