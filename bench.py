@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--no-identity", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--swap", type=int, default=0, metavar="N",
+                    help="instead of decode: move N sequences' blocks to pinned host memory and "
+                         "back (pa_swap_blocks) and report both directions' GB/s")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -192,6 +195,45 @@ def cpu_baseline(args, w, batch, kv_bytes: int) -> dict:
             "seconds": round(dt, 3), "seqs_per_s": round(w.num_seqs / dt, 3)}
 
 
+def swap_bench(args, w, batch) -> dict:
+    """Block swap (preemption data mover): N sequences out to pinned host memory and back."""
+    import torch
+    from paged_kv_cache_308_amd import pa_swap_blocks
+    from paged_kv_cache_308_amd.engine import HostKVPool
+    from paged_kv_cache_308_amd.replay import replay
+    db = replay(batch, poison=False)
+    cache = db.cache
+    n = min(args.swap, w.num_seqs)
+    tables = [cache.alloc.block_table(db.seq_ids[s])[0] for s in range(n)]
+    src = np.concatenate([np.asarray(t, np.int32) for t in tables])
+    nblk = len(src)
+    host = HostKVPool(nblk, w.num_kv_heads, w.head_dim, w.block_size, cache.dtype)
+    dev_ids = torch.from_numpy(src).cuda()
+    host_ids = torch.arange(nblk, dtype=torch.int32, device="cuda")
+    nbytes = 2 * nblk * w.num_kv_heads * w.block_size * w.head_dim * w.elem_bytes
+    st = torch.cuda.current_stream()
+    res = {}
+    for name, (a, b, s_, d_) in {
+            "out": ((cache.key_cache, cache.value_cache), (host.key_cache, host.value_cache), dev_ids, host_ids),
+            "in": ((host.key_cache, host.value_cache), (cache.key_cache, cache.value_cache), host_ids, dev_ids)}.items():
+        for _ in range(2):
+            pa_swap_blocks(a[0], a[1], b[0], b[1], s_, d_, st)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(args.steps):
+            pa_swap_blocks(a[0], a[1], b[0], b[1], s_, d_, st)
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        res[name] = {"ms": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+    return {"metric": "block swap GB/s (device <-> pinned host, pa_swap_blocks)",
+            "value": res["out"]["GBps"], "unit": "GB/s", "higher_is_better": True,
+            "n_gpus": 1, "steps": args.steps, "dtype": w.dtype, "data": "synthetic",
+            "config": {"workload": w.name, "sequences": n, "blocks": nblk, "bytes": nbytes},
+            "swap_out": res["out"], "swap_in": res["in"]}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -220,6 +262,9 @@ def main():
     batch = W.make_batch(w)
     ctx = batch.lengths.context_lens
     ab = algorithmic_bytes(w, ctx)
+    if args.swap:
+        print(json.dumps(swap_bench(args, w, batch)), flush=True)
+        return
     log(args, f"[bench] placing {REPLICAS} replicas")
     reps = build_replicas(args, w, batch, identity=False)
 

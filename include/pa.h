@@ -143,6 +143,20 @@ int pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *src, const
                    int num_pairs, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                    int dtype, void *stream);
 
+/*
+ * Move whole blocks between two different pools of the same shape (per block: all KV
+ * heads, all slots, bit for bit): dst_*[dst[p]] = src_*[src[p]] for both K and V.
+ * Either pool may be device memory or pinned host memory mapped into the device's
+ * address space (hipHostMalloc / a pinned tensor): this is the swap-out and swap-in
+ * data mover for preemption ([cpai] §6 and §11: a request's blocks move to CPU memory
+ * under memory pressure and come back when it is rescheduled).  src, dst: int32
+ * [num_pairs] readable by the device.  A pair with an id outside its pool is skipped.
+ */
+int pa_swap_blocks(const void *src_key_cache, const void *src_value_cache, void *dst_key_cache,
+                   void *dst_value_cache, const int32_t *src, const int32_t *dst, int num_pairs,
+                   int num_kv_heads, int head_dim, int block_size, int src_num_blocks,
+                   int dst_num_blocks, int dtype, void *stream);
+
 /* Host-side checks ([cpai] §13).  PA_ERR_BOUNDS names the first offending entry in
  * pa_last_error. */
 int pa_check_tables(const int32_t *block_tables, const int32_t *context_lens, int num_seqs,
@@ -193,6 +207,10 @@ int pa_alloc_append_slot(pa_allocator *a, int64_t seq, int32_t *slot, int32_t *c
  */
 int pa_alloc_append_slots(pa_allocator *a, const int64_t *seqs, int n, int32_t *slots,
                           int32_t *cow_src, int32_t *cow_dst, int *num_cow, int *num_done);
+/* New sequence of num_tokens tokens on ceil(num_tokens / B) fresh blocks (count 1),
+ * whose ids are written to block_ids in table order (capacity cap): the receiving end
+ * of a swap.  With too few free blocks: PA_ERR_OOM and no change. */
+int pa_alloc_adopt(pa_allocator *a, int num_tokens, int64_t *seq, int32_t *block_ids, int cap);
 /* New sequence sharing all of parent's blocks (each count + 1), same length. */
 int pa_alloc_fork(pa_allocator *a, int64_t parent, int64_t *child);
 /* Release the sequence; blocks whose count drops to 0 return to the free stack. */

@@ -4,8 +4,9 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package.  It shares no code with the HIP library and never imports it.
 
   oracle.c          binary64 decode attention through block tables, the slot
-                    scatter (reshape_and_cache) and the whole-block copy
-                    (copy_blocks); built here with gcc, single-threaded.
+                    scatter (reshape_and_cache), the whole-block copy
+                    (copy_blocks) and the block move between two pools
+                    (swap_blocks); built here with gcc, single-threaded.
   alloc_model.py    the block allocator (free list, reference counts, fork,
                     append with copy-on-write, free) in plain Python.
   place.py          helpers that build pools and tables with the model allocator
@@ -69,9 +70,12 @@ class Oracle:
         self._lib.oracle_decode.argtypes = [dp, vp, vp, vp, i32p, ci, i32p, ci, ci, ci, ci, ci, ci, cd, ci]
         self._lib.oracle_reshape_and_cache.argtypes = [vp, vp, vp, vp, i32p, ci, ci, ci, ci, ci, ci]
         self._lib.oracle_copy_blocks.argtypes = [vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci]
+        self._lib.oracle_swap_blocks.argtypes = [vp, vp, vp, vp, i32p, i32p, ci, ci, ci, ci, ci, ci,
+                                                 ci]
         self._lib.oracle_load.argtypes = [vp, ctypes.c_int64, ci]
         self._lib.oracle_load.restype = cd
-        for f in ("oracle_decode", "oracle_reshape_and_cache", "oracle_copy_blocks"):
+        for f in ("oracle_decode", "oracle_reshape_and_cache", "oracle_copy_blocks",
+                  "oracle_swap_blocks"):
             getattr(self._lib, f).restype = ctypes.c_int
 
     @staticmethod
@@ -139,6 +143,22 @@ class Oracle:
             t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(s), Hkv, d, B, nb,
             DTYPE_CODE[dtype])
         self._check(rc, "oracle_copy_blocks")
+
+    def swap_blocks(self, src_k, src_v, dst_k, dst_v, src, dst, dtype: str):
+        """In-place whole-block moves src pools[src[i]] -> dst pools[dst[i]]."""
+        s_ = self._i32(src)
+        t = self._i32(dst)
+        for a in (src_k, src_v, dst_k, dst_v):
+            assert a.flags.c_contiguous
+        ns, Hkv, B, d = src_k.shape
+        nd = dst_k.shape[0]
+        assert dst_k.shape[1:] == (Hkv, B, d)
+        rc = self._lib.oracle_swap_blocks(
+            src_k.ctypes.data, src_v.ctypes.data, dst_k.ctypes.data, dst_v.ctypes.data,
+            s_.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(s_), Hkv, d, B, ns, nd,
+            DTYPE_CODE[dtype])
+        self._check(rc, "oracle_swap_blocks")
 
 
 _default: Optional[Oracle] = None

@@ -13,6 +13,9 @@ What the pages fix:
     explicit out-of-memory error instead of failing the running requests.
   - KV-cache/paging tutorial (wmrh.cn), "paged attention" part: forked requests
     point at the same physical blocks with count 2 (three beams: count 3).
+  - "PagedAttention" concept report §6 and §11: under memory pressure a request's
+    blocks move to CPU memory and back; `adopt` is the receiving end of such a move
+    (a sequence of n tokens on fresh blocks).
 
 Readings (pages silent): the free list is a LIFO stack whose pops initially return
 0, 1, 2, ... (or a given order); blocks released by free_seq are pushed in table
@@ -89,6 +92,19 @@ class ModelAllocator:
             return b * B + n % B, (last, b)
         self.ctx[sid] = n + 1
         return last * B + n % B, None
+
+    def adopt(self, num_tokens: int):
+        """A sequence of num_tokens tokens on fresh blocks (the receiving end of a swap)."""
+        n = -(-num_tokens // self.block_size)
+        if n > len(self.free):
+            raise OutOfBlocks()
+        sid = self.new_seq()
+        for _ in range(n):
+            b = self.free.pop()
+            self.ref[b] = 1
+            self.tables[sid].append(b)
+        self.ctx[sid] = num_tokens
+        return sid, list(self.tables[sid])
 
     def fork(self, parent: int) -> int:
         table = self._seq(parent)

@@ -261,3 +261,27 @@ int oracle_copy_blocks(void *key_cache, void *value_cache, const int32_t *src, c
     }
     return ORACLE_OK;
 }
+
+/*
+ * Whole-block moves between two different pools of the same block shape ("PagedAttention"
+ * concept report §6 and §11: a request's blocks move to CPU memory under pressure and
+ * back later): for each pair p, block src[p] of (src_k, src_v) is copied onto block
+ * dst[p] of (dst_k, dst_v), bit for bit.  ORACLE_BAD_INDEX if an id is out of range.
+ */
+int oracle_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                       const int32_t *src, const int32_t *dst, int num_pairs, int num_kv_heads,
+                       int head_dim, int block_size, int src_blocks, int dst_blocks, int dtype)
+{
+    const int eb = elem_bytes(dtype);
+    if (eb == 0 || num_pairs < 0) return ORACLE_BAD_ARG;
+    const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
+    for (int p = 0; p < num_pairs; ++p) {
+        if (src[p] < 0 || src[p] >= src_blocks || dst[p] < 0 || dst[p] >= dst_blocks)
+            return ORACLE_BAD_INDEX;
+        memcpy((char *)dst_k + dst[p] * block_bytes, (const char *)src_k + src[p] * block_bytes,
+               (size_t)block_bytes);
+        memcpy((char *)dst_v + dst[p] * block_bytes, (const char *)src_v + src[p] * block_bytes,
+               (size_t)block_bytes);
+    }
+    return ORACLE_OK;
+}

@@ -27,7 +27,8 @@ PA_PARTITION_BALANCED = -1
 # Every symbol include/pa.h declares (checked by the tests).
 EXPORTS = (
     "pa_status_str", "pa_last_error", "pa_abi_version", "pa_decode_workspace_bytes", "pa_decode",
-    "pa_reshape_and_cache", "pa_copy_blocks", "pa_check_tables", "pa_check_copy_pairs",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_check_tables",
+    "pa_check_copy_pairs", "pa_alloc_adopt",
     "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_set_free_order", "pa_alloc_new_seq",
     "pa_alloc_append_slot", "pa_alloc_append_slots", "pa_alloc_fork", "pa_alloc_free_seq",
     "pa_alloc_block_table", "pa_alloc_block_tables", "pa_alloc_refcount", "pa_alloc_get_stats",
@@ -69,6 +70,8 @@ def _lib():
                             i32, i32, i32, vp, sz, vp]),
         "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
         "pa_copy_blocks": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
+        "pa_swap_blocks": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]),
+        "pa_alloc_adopt": (i32, [vp, i32, i64p, i32p, i32]),
         "pa_check_tables": (i32, [i32p, i32p, i32, i32, i32, i32]),
         "pa_check_copy_pairs": (i32, [i32p, i32p, i32, i32]),
         "pa_alloc_create": (i32, [i32, i32, ctypes.POINTER(vp)]),
@@ -190,6 +193,37 @@ def pa_copy_blocks(key_cache, value_cache, src, dst, stream=None):
     _check(rc, "pa_copy_blocks")
 
 
+def _any_ptr(t, name):
+    """Device or pinned-host tensor: its address (readable by the device)."""
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    return t.data_ptr()
+
+
+def pa_swap_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache, src, dst,
+                   stream=None):
+    """Whole-block moves between two pools (device or pinned host); src/dst int32 ids."""
+    torch = _torch()
+    ns, Hkv, B, d = src_key_cache.shape
+    nd = dst_key_cache.shape[0]
+    if (src_value_cache.shape != src_key_cache.shape or dst_key_cache.shape[1:] != (Hkv, B, d)
+            or dst_value_cache.shape != dst_key_cache.shape or src.shape != dst.shape):
+        raise ValueError("shape mismatch")
+    for t in (src_value_cache, dst_key_cache, dst_value_cache):
+        if t.dtype != src_key_cache.dtype:
+            raise ValueError("pools must share one dtype")
+    if src.dtype != torch.int32 or dst.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    rc = _lib().pa_swap_blocks(
+        _any_ptr(src_key_cache, "src_key_cache"), _any_ptr(src_value_cache, "src_value_cache"),
+        _any_ptr(dst_key_cache, "dst_key_cache"), _any_ptr(dst_value_cache, "dst_value_cache"),
+        _any_ptr(src, "src"), _any_ptr(dst, "dst"), src.shape[0], Hkv, d, B, ns, nd,
+        dtype_code(src_key_cache), _stream(stream))
+    _check(rc, "pa_swap_blocks")
+
+
 # ------------------------------------------------------------------ host checks
 
 def _i32(a) -> np.ndarray:
@@ -262,6 +296,15 @@ class Allocator:
             _p32(cd), ctypes.byref(ncow), ctypes.byref(done))
         _check(rc, f"pa_alloc_append_slots (done {done.value} of {n})")
         return slots, cs[:ncow.value].copy(), cd[:ncow.value].copy()
+
+    def adopt(self, num_tokens: int):
+        """New sequence of num_tokens tokens on fresh blocks: (seq, block ids)."""
+        n = -(-num_tokens // self.block_size)
+        ids = np.empty(max(n, 1), np.int32)
+        sq = ctypes.c_int64()
+        _check(_lib().pa_alloc_adopt(self._h, num_tokens, ctypes.byref(sq), _p32(ids), n),
+               "pa_alloc_adopt")
+        return sq.value, ids[:n].copy()
 
     def fork(self, parent: int) -> int:
         c = ctypes.c_int64()

@@ -153,6 +153,27 @@ int pa_alloc_append_slots(pa_allocator *a, const int64_t *seqs, int n, int32_t *
     return PA_OK;
 }
 
+int pa_alloc_adopt(pa_allocator *a, int num_tokens, int64_t *seq, int32_t *block_ids, int cap) {
+    if (!a || !seq || num_tokens < 0 || cap < 0 || (cap > 0 && !block_ids))
+        return pa::fail(PA_ERR_INVALID, "bad argument");
+    std::lock_guard<std::mutex> g(a->mu);
+    const int64_t n = ((int64_t)num_tokens + a->block_size - 1) / a->block_size;
+    if (n > cap) return pa::fail(PA_ERR_BOUNDS, "%lld blocks exceed cap %d", (long long)n, cap);
+    if (n > (int64_t)a->free_stack.size())
+        return pa::fail(PA_ERR_OOM, "%lld blocks wanted, %zu free", (long long)n, a->free_stack.size());
+    pa_allocator::Seq sq;
+    sq.ctx = num_tokens;
+    for (int64_t j = 0; j < n; ++j) {
+        const int32_t b = a->pop();
+        sq.table.push_back(b);
+        block_ids[j] = b;
+    }
+    const int64_t id = a->next_id++;
+    a->seqs.emplace(id, std::move(sq));
+    *seq = id;
+    return PA_OK;
+}
+
 int pa_alloc_fork(pa_allocator *a, int64_t parent, int64_t *child) {
     if (!a || !child) return pa::fail(PA_ERR_INVALID, "NULL argument");
     std::lock_guard<std::mutex> g(a->mu);

@@ -265,8 +265,30 @@ int pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *src, const
         return fail(PA_ERR_UNSUPPORTED, "block bytes must be a multiple of 16");
     if (num_pairs == 0) return PA_OK;
     if (!key_cache || !value_cache || !src || !dst) return fail(PA_ERR_INVALID, "NULL device pointer");
-    return launch_copy_blocks(key_cache, value_cache, src, dst, num_pairs, num_kv_heads, head_dim,
-                              block_size, num_blocks, eb, stream);
+    return launch_move_blocks(key_cache, value_cache, key_cache, value_cache, src, dst, num_pairs,
+                              num_kv_heads, head_dim, block_size, num_blocks, num_blocks, eb, stream);
+}
+
+int pa_swap_blocks(const void *src_key_cache, const void *src_value_cache, void *dst_key_cache,
+                   void *dst_value_cache, const int32_t *src, const int32_t *dst, int num_pairs,
+                   int num_kv_heads, int head_dim, int block_size, int src_num_blocks,
+                   int dst_num_blocks, int dtype, void *stream) {
+    clear_error();
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "dtype %d", dtype);
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || src_num_blocks <= 0 ||
+        dst_num_blocks <= 0)
+        return fail(PA_ERR_INVALID, "bad sizes");
+    if (((int64_t)num_kv_heads * block_size * head_dim * eb) % 16)
+        return fail(PA_ERR_UNSUPPORTED, "block bytes must be a multiple of 16");
+    if (num_pairs == 0) return PA_OK;
+    if (!src_key_cache || !src_value_cache || !dst_key_cache || !dst_value_cache || !src || !dst)
+        return fail(PA_ERR_INVALID, "NULL pointer");
+    if (src_key_cache == dst_key_cache || src_value_cache == dst_value_cache)
+        return fail(PA_ERR_INVALID, "source and destination pools must differ (use pa_copy_blocks)");
+    return launch_move_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache, src, dst,
+                              num_pairs, num_kv_heads, head_dim, block_size, src_num_blocks,
+                              dst_num_blocks, eb, stream);
 }
 
 int pa_check_tables(const int32_t *block_tables, const int32_t *context_lens, int num_seqs,

@@ -38,22 +38,25 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     }
 }
 
+// Whole-block moves between two pools (which may be the same pool).
 // "PagedAttention" concept report (compassingai.com) §6: before a write into a shared
-// block, a fresh block receives a copy of its content.  grid = (word groups, pairs,
-// pool); each workgroup moves 4 words per lane (16 KiB) of one block of one pool.
+// block, a fresh block receives a copy of its content; §6 and §11: under memory
+// pressure a request's blocks are moved out to CPU memory and moved back later.
+// grid = (word groups, pairs, pool); each workgroup moves 4 words per lane (16 KiB)
+// of one block of one pool.  A pair with an id outside its pool is skipped.
 constexpr int COPY_THREADS = 256;
 constexpr int COPY_UNROLL = 4;
 
-__global__ __launch_bounds__(COPY_THREADS) void copy_blocks_kernel(
-    u32x4 *__restrict__ key_cache, u32x4 *__restrict__ value_cache, const int32_t *__restrict__ src,
-    const int32_t *__restrict__ dst, int64_t words_per_block, int num_blocks) {
+__global__ __launch_bounds__(COPY_THREADS) void move_blocks_kernel(
+    const u32x4 *src_key, const u32x4 *src_value, u32x4 *dst_key, u32x4 *dst_value,
+    const int32_t *__restrict__ src, const int32_t *__restrict__ dst, int64_t words_per_block,
+    int src_blocks, int dst_blocks) {
     const int pair = blockIdx.y;
     const int32_t s = src[pair];
     const int32_t d = dst[pair];
-    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
-    u32x4 *pool = blockIdx.z == 0 ? key_cache : value_cache;
-    const u32x4 *from = pool + (int64_t)s * words_per_block;
-    u32x4 *to = pool + (int64_t)d * words_per_block;
+    if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks) return;
+    const u32x4 *from = (blockIdx.z == 0 ? src_key : src_value) + (int64_t)s * words_per_block;
+    u32x4 *to = (blockIdx.z == 0 ? dst_key : dst_value) + (int64_t)d * words_per_block;
     const int64_t base = (int64_t)blockIdx.x * COPY_THREADS * COPY_UNROLL + threadIdx.x;
     u32x4 w[COPY_UNROLL];
 #pragma unroll
@@ -84,26 +87,22 @@ int launch_reshape_and_cache(const void *key, const void *value, void *key_cache
     return check_launch("reshape_and_cache");
 }
 
-int launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *src, const int32_t *dst,
-                       int num_pairs, int num_kv_heads, int head_dim, int block_size,
-                       int num_blocks, int elem_bytes, void *stream) {
+int launch_move_blocks(const void *src_key, const void *src_value, void *dst_key, void *dst_value,
+                       const int32_t *src, const int32_t *dst, int num_pairs, int num_kv_heads,
+                       int head_dim, int block_size, int src_blocks, int dst_blocks, int elem_bytes,
+                       void *stream) {
     const int64_t words = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes / 16;
     const int64_t per_wg = COPY_THREADS * COPY_UNROLL;
     const unsigned gx = (unsigned)((words + per_wg - 1) / per_wg);
-    if (num_pairs > 65535) {
-        // grid.y is limited; split the pair list
-        int rc = PA_OK;
-        for (int off = 0; off < num_pairs && rc == PA_OK; off += 65535) {
-            const int n = num_pairs - off < 65535 ? num_pairs - off : 65535;
-            rc = launch_copy_blocks(key_cache, value_cache, src + off, dst + off, n, num_kv_heads,
-                                    head_dim, block_size, num_blocks, elem_bytes, stream);
-        }
-        return rc;
+    for (int off = 0; off < num_pairs; off += 65535) {  // grid.y is limited
+        const int n = num_pairs - off < 65535 ? num_pairs - off : 65535;
+        hipLaunchKernelGGL(move_blocks_kernel, dim3(gx, n, 2), dim3(COPY_THREADS), 0, (hipStream_t)stream,
+                           (const u32x4 *)src_key, (const u32x4 *)src_value, (u32x4 *)dst_key,
+                           (u32x4 *)dst_value, src + off, dst + off, words, src_blocks, dst_blocks);
+        const int rc = check_launch("move_blocks");
+        if (rc != PA_OK) return rc;
     }
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, num_pairs, 2), dim3(COPY_THREADS), 0,
-                       (hipStream_t)stream, (u32x4 *)key_cache, (u32x4 *)value_cache, src, dst,
-                       words, num_blocks);
-    return check_launch("copy_blocks");
+    return PA_OK;
 }
 
 }  // namespace pa

@@ -62,9 +62,10 @@ int launch_reshape_and_cache(const void *key, const void *value, void *key_cache
                              void *value_cache, const int32_t *slot_mapping, int num_tokens,
                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
                              int elem_bytes, void *stream);
-int launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *src, const int32_t *dst,
-                       int num_pairs, int num_kv_heads, int head_dim, int block_size,
-                       int num_blocks, int elem_bytes, void *stream);
+int launch_move_blocks(const void *src_key, const void *src_value, void *dst_key, void *dst_value,
+                       const int32_t *src, const int32_t *dst, int num_pairs, int num_kv_heads,
+                       int head_dim, int block_size, int src_blocks, int dst_blocks, int elem_bytes,
+                       void *stream);
 
 // Per-dtype launchers (one translation unit each).
 int launch_decode_valu_f32(const DecodeArgs &a);

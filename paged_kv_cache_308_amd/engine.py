@@ -20,7 +20,7 @@ import numpy as np
 import torch
 
 from . import (PA_VARIANT_AUTO, Allocator, pa_copy_blocks, pa_decode, pa_decode_workspace_bytes,
-               pa_reshape_and_cache)
+               pa_reshape_and_cache, pa_swap_blocks)
 
 
 class PagedKVCache:
@@ -90,6 +90,47 @@ class PagedKVCache:
                   max_context_len=max_context_len, partition_size=partition_size, variant=variant,
                   workspace=workspace, stream=stream)
         return out
+
+
+class HostKVPool:
+    """Swap space: a block pool of the same shape in pinned host memory (the device
+    reads and writes it directly) with its own allocator ("PagedAttention" concept
+    report §6 and §11: under memory pressure a request's blocks move to CPU memory and
+    come back when it is rescheduled)."""
+
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
+                 dtype: torch.dtype):
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        self.key_cache = torch.empty(shape, dtype=dtype, pin_memory=True)
+        self.value_cache = torch.empty(shape, dtype=dtype, pin_memory=True)
+        self.alloc = Allocator(num_blocks, block_size)
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+
+def swap_out(cache: PagedKVCache, host: HostKVPool, seq: int, stream=None) -> int:
+    """Move `seq`'s blocks to host memory and release them on the device; returns the
+    sequence's id in the host pool.  Stream order keeps the freed device blocks from
+    being overwritten before the copy has read them."""
+    table, ctx = cache.alloc.block_table(seq)
+    hseq, hids = host.alloc.adopt(ctx)
+    if len(table):
+        pa_swap_blocks(cache.key_cache, cache.value_cache, host.key_cache, host.value_cache,
+                       _as_dev(np.asarray(table, np.int32), cache.device),
+                       _as_dev(hids, cache.device), stream)
+    cache.free_seq(seq)
+    return hseq
+
+
+def swap_in(cache: PagedKVCache, host: HostKVPool, hseq: int, stream=None) -> int:
+    """Move a swapped-out sequence back onto fresh device blocks; returns its new id."""
+    table, ctx = host.alloc.block_table(hseq)
+    seq, ids = cache.alloc.adopt(ctx)
+    if len(table):
+        pa_swap_blocks(host.key_cache, host.value_cache, cache.key_cache, cache.value_cache,
+                       _as_dev(np.asarray(table, np.int32), cache.device),
+                       _as_dev(ids, cache.device), stream)
+    host.alloc.free_seq(hseq)
+    return seq
 
 
 def _as_dev(a, device) -> torch.Tensor:

@@ -34,6 +34,7 @@ class DeviceBatch:
     max_context_len: int
     scale: float
     shared: bool = False  # tables share physical blocks: pass the cache hint
+    seq_ids: Optional[List[int]] = None  # allocator id of each batch sequence
 
     def step(self, partition_size: int = 0, variant: int = PA_VARIANT_AUTO, out=None,
              workspace=None, stream=None) -> torch.Tensor:
@@ -101,4 +102,4 @@ def replay(batch, poison: bool = True, device="cuda",
     return DeviceBatch(cache, dev(batch.q), dev(nk), dev(nv), cache.upload(newest),
                        cache.upload(bt), cache.upload(cl), cow_src, cow_dst, bt, cl,
                        int(cl.max()) if S else 0, w.scale,
-                       cache.alloc.stats()["shared_blocks"] > 0)
+                       cache.alloc.stats()["shared_blocks"] > 0, seq_ids)

@@ -310,6 +310,27 @@ def pin_copy(o):
         assert kc.tobytes() == wk.tobytes() and vc.tobytes() == wv.tobytes()
 
 
+def pin_swap(o):
+    """Moves between two pools equal numpy dst[dst_ids] = src[src_ids], bitwise; the
+    source pools are untouched."""
+    rng = np.random.default_rng(114)
+    for dt in ("f32", "f16", "bf16"):
+        H, B, d = 2, 4, 8
+        sk = W.round_to(rng.standard_normal((10, H, B, d), dtype=np.float32), dt)
+        sv = W.round_to(rng.standard_normal((10, H, B, d), dtype=np.float32), dt)
+        dk = W.round_to(rng.standard_normal((7, H, B, d), dtype=np.float32), dt)
+        dv = W.round_to(rng.standard_normal((7, H, B, d), dtype=np.float32), dt)
+        src = rng.choice(10, 5, replace=False).astype(np.int32)
+        dst = rng.choice(7, 5, replace=False).astype(np.int32)
+        wk, wv = dk.copy(), dv.copy()
+        wk[dst] = sk[src]
+        wv[dst] = sv[src]
+        sk0, sv0 = sk.copy(), sv.copy()
+        o.swap_blocks(sk, sv, dk, dv, src, dst, dt)
+        assert dk.tobytes() == wk.tobytes() and dv.tobytes() == wv.tobytes()
+        assert sk.tobytes() == sk0.tobytes() and sv.tobytes() == sv0.tobytes()
+
+
 def pin_page3_request(o):
     """The 100-token request of 5ulink §二 through its table [5,2,7,0,12,3,9]
     equals attention over its 100 tokens laid out contiguously."""
@@ -356,4 +377,5 @@ def pin_dtype_decode(o):
 
 ORACLE_PINS = [pin_sdpa, pin_brute, pin_permutation, pin_ctx1, pin_equal_keys, pin_dominant,
                pin_shared_prefix, pin_nan_poison, pin_empty, pin_bad_index, pin_reshape, pin_copy,
+               pin_swap,
                pin_page3_request, pin_dtype_decode]

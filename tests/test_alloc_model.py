@@ -106,6 +106,22 @@ def test_out_of_blocks_changes_nothing():
     assert (list(a.free), list(a.ref), a.block_table(x), a.stats()) == before
 
 
+def test_adopt_takes_fresh_blocks_and_is_all_or_nothing():
+    """The receiving end of a swap: n tokens on ceil(n/B) fresh blocks, count 1."""
+    a = ModelAllocator(6, 4)
+    sid, ids = a.adopt(9)
+    assert ids == [0, 1, 2] and a.block_table(sid) == ([0, 1, 2], 9)
+    assert all(a.refcount(b) == 1 for b in ids)
+    before = (list(a.free), list(a.ref), a.stats())
+    with pytest.raises(OutOfBlocks):
+        a.adopt(13)  # 4 blocks, 3 free
+    assert (list(a.free), list(a.ref), a.stats()) == before
+    slot, cow = a.append_slot(sid)  # continues in the last adopted block
+    assert slot == 2 * 4 + 1 and cow is None
+    s2, ids2 = a.adopt(0)
+    assert ids2 == [] and a.block_table(s2) == ([], 0)
+
+
 def test_invalid_operations():
     a = ModelAllocator(4, 4)
     with pytest.raises(InvalidOp):
@@ -122,7 +138,7 @@ def test_invalid_operations():
 
 
 @settings(max_examples=60, deadline=None)
-@given(st.lists(st.tuples(st.sampled_from(["new", "append", "fork", "free"]),
+@given(st.lists(st.tuples(st.sampled_from(["new", "append", "fork", "free", "adopt"]),
                           st.integers(0, 50), st.integers(1, 9)), max_size=60),
        st.sampled_from([1, 2, 4, 16]))
 def test_reference_counts_are_conserved(ops, B):
@@ -138,6 +154,8 @@ def test_reference_counts_are_conserved(ops, B):
                     a.append_slot(s)
             elif kind == "fork":
                 live.append(a.fork(live[pick % len(live)]))
+            elif kind == "adopt":
+                live.append(a.adopt(n * 3)[0])
             else:
                 a.free_seq(live.pop(pick % len(live)))
         except OutOfBlocks:

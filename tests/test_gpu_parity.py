@@ -273,6 +273,55 @@ def test_copy_blocks_bitwise():
         assert bits(gk) == np_bits(kc) and bits(gv) == np_bits(vc)
 
 
+def test_swap_out_and_in_round_trip():
+    """Three sequences (two of them sharing prompt blocks) go to pinned host memory, their
+    device blocks are reused and overwritten, and they come back: the host copy equals the
+    oracle's move bit for bit, and attention afterwards is bit-identical to before."""
+    from paged_kv_cache_308_amd.engine import HostKVPool, swap_in, swap_out
+    w = SMALL["prefix_f16"]
+    batch = W.make_batch(w)
+    db = replay(batch)
+    before = bits(db.step(partition_size=0, variant=VALU))
+    cache = db.cache
+    host = HostKVPool(300, w.num_kv_heads, w.head_dim, w.block_size, TORCH_DTYPE[w.dtype])
+    host.key_cache.fill_(0.0)
+    host.value_cache.fill_(0.0)
+    moved = [1, 3, 6]
+    kc0 = cache.key_cache.cpu().numpy().view(np.uint16)
+    vc0 = cache.value_cache.cpu().numpy().view(np.uint16)
+    want_k = host.key_cache.numpy().view(np.uint16).copy()
+    want_v = host.value_cache.numpy().view(np.uint16).copy()
+    hseqs = []
+    for s_ in moved:
+        table, _ = cache.alloc.block_table(db.seq_ids[s_])
+        say(f"[gpu] swap out seq {s_} ({len(table)} blocks)")
+        h = swap_out(cache, host, db.seq_ids[s_])
+        htable, _ = host.alloc.block_table(h)
+        oracle.default().swap_blocks(kc0, vc0, want_k, want_v, np.asarray(table, np.int32),
+                                     np.asarray(htable, np.int32), w.dtype)
+        hseqs.append(h)
+    torch.cuda.synchronize()
+    assert host.key_cache.numpy().view(np.uint16).tobytes() == want_k.tobytes()
+    assert host.value_cache.numpy().view(np.uint16).tobytes() == want_v.tobytes()
+    # reuse the released device blocks for junk
+    junk = cache.new_seq()
+    n_free = cache.alloc.stats()["free_blocks"]
+    slots, _, _ = cache.reserve([junk] * (n_free * w.block_size))
+    rnd = torch.randn(len(slots), w.num_kv_heads, w.head_dim, device="cuda").to(TORCH_DTYPE[w.dtype])
+    cache.write(rnd, rnd, slots)
+    cache.free_seq(junk)
+    for s_, h in zip(moved, hseqs):
+        say(f"[gpu] swap in seq {s_}")
+        db.seq_ids[s_] = swap_in(cache, host, h)
+    bt, cl = cache.tables(db.seq_ids, db.host_tables.shape[1])
+    assert np.array_equal(cl, db.host_context_lens)
+    db.block_tables = torch.from_numpy(bt).cuda()
+    db.shared = False
+    after = bits(db.attend(partition_size=0, variant=VALU))
+    torch.cuda.synchronize()
+    assert after == before
+
+
 # ------------------------------------------------------------ full-size workloads
 
 

@@ -63,6 +63,17 @@ def _run_both(num_blocks, B, ops, order=None):
         elif kind == "fork":
             a, b = live[pick % len(live)]
             live.append((nat.fork(a), mod.fork(b)))
+        elif kind == "adopt":
+            try:
+                sb, ib = mod.adopt(n * 3)
+            except OutOfBlocks:
+                with pytest.raises(pa.PaError) as e:
+                    nat.adopt(n * 3)
+                assert e.value.status == pa.PA_ERR_OOM
+                continue
+            sa, ia = nat.adopt(n * 3)
+            assert ia.tolist() == ib
+            live.append((sa, sb))
         else:
             a, b = live.pop(pick % len(live))
             nat.free_seq(a)
@@ -76,7 +87,7 @@ def _run_both(num_blocks, B, ops, order=None):
 
 
 @settings(max_examples=80, deadline=None)
-@given(st.lists(st.tuples(st.sampled_from(["new", "append", "fork", "free"]),
+@given(st.lists(st.tuples(st.sampled_from(["new", "append", "fork", "free", "adopt"]),
                           st.integers(0, 50), st.integers(1, 12)), max_size=50),
        st.sampled_from([1, 4, 16]), st.booleans())
 def test_native_allocator_matches_model(ops, B, permuted):
@@ -236,3 +247,11 @@ def test_block_ops_reject_before_launch():
     assert L.pa_copy_blocks(FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 10, pa.PA_F16, None) == pa.PA_OK
     assert L.pa_copy_blocks(FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 16, 10, 9, None) == \
         pa.PA_ERR_UNSUPPORTED
+    # swap: same pool on both sides, zero pairs, bad dtype
+    assert L.pa_swap_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 16, 10, 10, pa.PA_F16,
+                            None) == pa.PA_ERR_INVALID
+    other = ctypes.c_void_p(0x2000)
+    assert L.pa_swap_blocks(FAKE, FAKE, other, other, FAKE, FAKE, 0, 8, 128, 16, 10, 10, pa.PA_F16,
+                            None) == pa.PA_OK
+    assert L.pa_swap_blocks(FAKE, FAKE, other, other, FAKE, FAKE, 2, 8, 128, 16, 10, 10, 9,
+                            None) == pa.PA_ERR_UNSUPPORTED
