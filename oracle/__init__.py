@@ -6,7 +6,9 @@ this package.  It shares no code with the HIP library and never imports it.
   oracle.c          binary64 decode attention through block tables, the slot
                     scatter (reshape_and_cache), the whole-block copy
                     (copy_blocks) and the block move between two pools
-                    (swap_blocks); built here with gcc, single-threaded.
+                    (swap_blocks); the same for pools of OCP E4M3 codes with a
+                    scale per (block, KV head) (decode_fp8, reshape_and_cache_fp8,
+                    fp8_value, fp8_encode); built here with gcc, single-threaded.
   alloc_model.py    the block allocator (free list, reference counts, fork,
                     append with copy-on-write, free) in plain Python.
   place.py          helpers that build pools and tables with the model allocator
@@ -35,7 +37,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
 _STATUS = {0: "ok", 1: "bad argument", 2: "index out of range", 3: "out of memory"}
 
 
@@ -74,8 +76,17 @@ class Oracle:
                                                  ci]
         self._lib.oracle_load.argtypes = [vp, ctypes.c_int64, ci]
         self._lib.oracle_load.restype = cd
+        fp = ctypes.POINTER(ctypes.c_float)
+        self._lib.oracle_decode_fp8.argtypes = [dp, vp, vp, vp, fp, fp, i32p, ci, i32p, ci, ci, ci,
+                                                ci, ci, ci, cd, ci]
+        self._lib.oracle_reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, fp, fp, i32p, ci, ci,
+                                                           ci, ci, ci, ci]
+        self._lib.oracle_fp8_value.argtypes = [ctypes.c_uint8]
+        self._lib.oracle_fp8_value.restype = cd
+        self._lib.oracle_fp8_encode.argtypes = [ctypes.c_float]
+        self._lib.oracle_fp8_encode.restype = ctypes.c_uint8
         for f in ("oracle_decode", "oracle_reshape_and_cache", "oracle_copy_blocks",
-                  "oracle_swap_blocks"):
+                  "oracle_swap_blocks", "oracle_decode_fp8", "oracle_reshape_and_cache_fp8"):
             getattr(self._lib, f).restype = ctypes.c_int
 
     @staticmethod
@@ -116,6 +127,66 @@ class Oracle:
             DTYPE_CODE[dtype])
         self._check(rc, "oracle_decode")
         return out
+
+    @staticmethod
+    def _f32(a) -> np.ndarray:
+        return np.ascontiguousarray(a, dtype=np.float32)
+
+    def fp8_value(self, codes) -> np.ndarray:
+        """E4M3 codes (uint8) -> float64 values."""
+        c = np.asarray(codes, np.uint8)
+        return np.array([self._lib.oracle_fp8_value(int(x)) for x in c.ravel()],
+                        np.float64).reshape(c.shape)
+
+    def fp8_encode(self, y) -> np.ndarray:
+        """float32 numbers -> nearest E4M3 codes (ties to even, saturating)."""
+        y = np.asarray(y, np.float32)
+        return np.array([self._lib.oracle_fp8_encode(float(x)) for x in y.ravel()],
+                        np.uint8).reshape(y.shape)
+
+    def decode_fp8(self, query, key_cache, value_cache, k_scales, v_scales, block_tables,
+                   context_lens, scale: float, qdtype: str) -> np.ndarray:
+        """Decode over E4M3 pools (uint8 [num_blocks][H_kv][B][d]) with float32 scales
+        [num_blocks][H_kv]; query f16 / bf16 [S][H_q][d].  Returns float64."""
+        q = np.ascontiguousarray(query)
+        kc = np.ascontiguousarray(key_cache, dtype=np.uint8)
+        vc = np.ascontiguousarray(value_cache, dtype=np.uint8)
+        ks, vs = self._f32(k_scales), self._f32(v_scales)
+        bt = self._i32(block_tables)
+        cl = self._i32(context_lens)
+        S, Hq, d = q.shape
+        nb, Hkv, B, d2 = kc.shape
+        assert d2 == d and vc.shape == kc.shape and ks.shape == (nb, Hkv) and vs.shape == ks.shape
+        out = np.zeros((S, Hq, d), np.float64)
+        fp = ctypes.POINTER(ctypes.c_float)
+        rc = self._lib.oracle_decode_fp8(
+            out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), q.ctypes.data, kc.ctypes.data,
+            vc.ctypes.data, ks.ctypes.data_as(fp), vs.ctypes.data_as(fp),
+            bt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), bt.shape[1],
+            cl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), S, Hq, Hkv, d, B, nb, float(scale),
+            DTYPE_CODE[qdtype])
+        self._check(rc, "oracle_decode_fp8")
+        return out
+
+    def reshape_and_cache_fp8(self, key, value, key_cache, value_cache, k_scales, v_scales,
+                              slot_mapping, src_dtype: str):
+        """In-place scatter of key/value [N][H_kv][d] (src_dtype) into E4M3 pools."""
+        k = np.ascontiguousarray(key)
+        v = np.ascontiguousarray(value)
+        sm = self._i32(slot_mapping)
+        assert key_cache.dtype == np.uint8 and value_cache.dtype == np.uint8
+        assert key_cache.flags.c_contiguous and value_cache.flags.c_contiguous
+        ks, vs = self._f32(k_scales), self._f32(v_scales)
+        nb, Hkv, B, d = key_cache.shape
+        N = sm.shape[0]
+        assert k.shape == (N, Hkv, d) and v.shape == k.shape and ks.shape == (nb, Hkv)
+        fp = ctypes.POINTER(ctypes.c_float)
+        rc = self._lib.oracle_reshape_and_cache_fp8(
+            k.ctypes.data, v.ctypes.data, key_cache.ctypes.data, value_cache.ctypes.data,
+            ks.ctypes.data_as(fp), vs.ctypes.data_as(fp),
+            sm.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), N, Hkv, d, B, nb,
+            DTYPE_CODE[src_dtype])
+        self._check(rc, "oracle_reshape_and_cache_fp8")
 
     def reshape_and_cache(self, key, value, key_cache, value_cache, slot_mapping, dtype: str):
         """In-place scatter of key/value [N][H_kv][d] into the pools."""

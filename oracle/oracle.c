@@ -7,8 +7,10 @@
  * HIP library; the two meet only through the seeded input generators.
  *
  * Everything is single-threaded, unblocked and unfused, and every floating
- * point step runs in IEEE binary64.  Stored f32 / f16 / bf16 values are decoded
- * to binary64 exactly (every such value is representable).
+ * point step runs in IEEE binary64.  Stored f32 / f16 / bf16 / E4M3 values are
+ * decoded to binary64 exactly (every such value is representable).  The one
+ * binary32 step is the division that picks an E4M3 code (reshape into E4M3
+ * pools), done in the precision the device decides it in.
  *
  * Sources (four web pages on vLLM's PagedAttention):
  *  - "PagedAttention" concept report (compassingai.com), §5: the cache is cut
@@ -30,6 +32,10 @@
  *  - query head h reads KV head h / (H_q / H_kv).
  *  - a context of length 0 yields an all-zero output.
  *  - slot = physical_block * B + offset; a negative slot is skipped.
+ *  - compressed pools (kwkr.cn §1.5 quantising older blocks; compassingai.com §15
+ *    lossy block compression): OCP E4M3 codes with one fp32 scale per (physical
+ *    block, KV head) for K and one for V; encoding rounds to nearest, ties to the
+ *    even code, and saturates at +-448.
  *
  * ORACLE_MUTANT (compile-time, tests only) plants one known mistake so the test
  * suite can show that its pins catch it; the shipped build defines it as 0.
@@ -43,7 +49,7 @@
 #define ORACLE_MUTANT 0
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_FP8 = 3 };
 enum { ORACLE_OK = 0, ORACLE_BAD_ARG = 1, ORACLE_BAD_INDEX = 2, ORACLE_NO_MEM = 3 };
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
@@ -71,8 +77,72 @@ static double bf16_bits_to_f64(uint16_t b)
     return (double)f;
 }
 
+/*
+ * OCP 8-bit floating point, E4M3 variant without infinities: 1 sign bit, 4 exponent
+ * bits (bias 7), 3 fraction bits.  Exponent field 0 holds zero and the subnormals
+ * frac * 2^-9; the fraction pattern 111 with exponent field 1111 is NaN (0x7F, 0xFF);
+ * every other code is (1 + frac/8) * 2^(e-7), up to 448.
+ */
+double oracle_fp8_value(uint8_t c)
+{
+    const int sign = c >> 7;
+    const int expo = (c >> 3) & 15;
+    const int frac = c & 7;
+    double v;
+    if (expo == 15 && frac == 7)
+        return NAN;
+#if ORACLE_MUTANT == 11
+    if (expo == 0)
+        v = ldexp((double)frac, -10);                /* planted: bias 8 */
+    else
+        v = ldexp((double)(8 + frac), expo - 11);
+#else
+    if (expo == 0)
+        v = ldexp((double)frac, -9);                 /* (frac / 8) * 2^(1-7) */
+    else
+        v = ldexp((double)(8 + frac), expo - 10);    /* (1 + frac/8) * 2^(e-7) */
+#endif
+    return sign ? -v : v;
+}
+
+/*
+ * The E4M3 code nearest to y, found by trying every finite code; of two equally near
+ * codes the one with an even code (fraction bit 0) wins.  Magnitudes of 448 and above
+ * (infinity too) give the largest finite code of y's sign; NaN gives 0x7F; the sign of
+ * a zero result is y's sign.
+ */
+uint8_t oracle_fp8_encode(float y)
+{
+    if (y != y)
+        return 0x7F;
+    const uint8_t sign = signbit(y) ? 0x80 : 0;
+    const double a = fabs((double)y);
+#if ORACLE_MUTANT == 14
+    if (a >= 464.0)
+        return 0x7F;                                  /* planted: no saturation */
+#endif
+    if (a >= 448.0)
+        return sign | 0x7E;
+    int best = 0;
+    double best_dist = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        const double dist = fabs(oracle_fp8_value((uint8_t)c) - a);
+#if ORACLE_MUTANT == 13
+        if (dist <= best_dist) {                      /* planted: ties away from zero */
+#else
+        if (dist < best_dist || (dist == best_dist && (c & 1) == 0)) {
+#endif
+            best = c;
+            best_dist = dist;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
 double oracle_load(const void *base, int64_t idx, int dtype)
 {
+    if (dtype == ORACLE_FP8)
+        return oracle_fp8_value(((const uint8_t *)base)[idx]);
     if (dtype == ORACLE_F32) {
         float f;
         memcpy(&f, (const char *)base + idx * 4, 4);
@@ -85,7 +155,14 @@ double oracle_load(const void *base, int64_t idx, int dtype)
 
 static int elem_bytes(int dtype)
 {
-    return dtype == ORACLE_F32 ? 4 : (dtype == ORACLE_F16 || dtype == ORACLE_BF16) ? 2 : 0;
+    return dtype == ORACLE_F32 ? 4 : (dtype == ORACLE_F16 || dtype == ORACLE_BF16) ? 2
+                                     : dtype == ORACLE_FP8 ? 1 : 0;
+}
+
+/* Query and output types: the 16- and 32-bit floating point formats. */
+static int is_wide(int dtype)
+{
+    return dtype == ORACLE_F32 || dtype == ORACLE_F16 || dtype == ORACLE_BF16;
 }
 
 /* Element offset of K or V for (physical block b, kv head k, in-block slot o, dim j). */
@@ -100,22 +177,34 @@ static int64_t pool_index(int64_t b, int k, int o, int j, int Hkv, int B, int d)
 }
 
 /*
+ * Scale of the stored values of physical block pb, KV head k: 1 for pools in the
+ * query's type; for E4M3 pools the per-(block, head) factor from `scales`
+ * ([num_blocks][H_kv]).
+ */
+static double block_scale(const float *scales, int64_t pb, int k, int Hkv)
+{
+    return scales ? (double)scales[pb * Hkv + k] : 1.0;
+}
+
+/*
  * out[s][h][:]  (binary64, [S][H_q][d]) for every sequence s and query head h:
  *   n   = context_lens[s]
  *   x_t = scale * sum_j q[s][h][j] * K(t)[j]            for t < n
  *   p_t = exp(x_t - max_t x_t),   Z = sum_t p_t
  *   out = sum_t p_t * V(t) / Z
  * where K(t), V(t) are read at physical block block_tables[s][t / B], slot t % B,
- * KV head h / (H_q / H_kv).  Returns ORACLE_BAD_INDEX if a table entry needed
- * for t < n is outside [0, num_blocks) or t / B reaches max_blocks_per_seq.
+ * KV head h / (H_q / H_kv), and multiplied by that block's scale (E4M3 pools).
+ * Returns ORACLE_BAD_INDEX if a table entry needed for t < n is outside
+ * [0, num_blocks) or t / B reaches max_blocks_per_seq.
  */
-int oracle_decode(double *out, const void *query, const void *key_cache, const void *value_cache,
-                  const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
-                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                  int num_blocks, double scale, int dtype)
+static int decode_impl(double *out, const void *query, const void *key_cache, const void *value_cache,
+                       const float *k_scales, const float *v_scales, const int32_t *block_tables,
+                       int max_blocks_per_seq, const int32_t *context_lens, int num_seqs,
+                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                       int num_blocks, double scale, int qdtype, int kvdtype)
 {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-        num_q_heads % num_kv_heads != 0 || elem_bytes(dtype) == 0)
+        num_q_heads % num_kv_heads != 0 || !is_wide(qdtype) || elem_bytes(kvdtype) == 0)
         return ORACLE_BAD_ARG;
     const int g = num_q_heads / num_kv_heads;
     const int d = head_dim, B = block_size, Hkv = num_kv_heads;
@@ -148,10 +237,15 @@ int oracle_decode(double *out, const void *query, const void *key_cache, const v
                 if (lb >= max_blocks_per_seq) { free(x); return ORACLE_BAD_INDEX; }
                 const int64_t pb = block_tables[(int64_t)s * max_blocks_per_seq + lb];
                 if (pb < 0 || pb >= num_blocks) { free(x); return ORACLE_BAD_INDEX; }
+#if ORACLE_MUTANT == 15
+                const double ks = block_scale(k_scales, lb, k, Hkv);  /* planted: logical block */
+#else
+                const double ks = block_scale(k_scales, pb, k, Hkv);
+#endif
                 double dot = 0.0;
                 for (int j = 0; j < d; ++j)
-                    dot += oracle_load(query, q_row + j, dtype) *
-                           oracle_load(key_cache, pool_index(pb, k, off, j, Hkv, B, d), dtype);
+                    dot += oracle_load(query, q_row + j, qdtype) *
+                           (oracle_load(key_cache, pool_index(pb, k, off, j, Hkv, B, d), kvdtype) * ks);
 #if ORACLE_MUTANT == 1
                 x[t] = dot;                   /* planted: scale dropped */
 #else
@@ -192,7 +286,12 @@ int oracle_decode(double *out, const void *query, const void *key_cache, const v
 #else
                     const void *vsrc = value_cache;
 #endif
-                    acc += x[t] * oracle_load(vsrc, pool_index(pb, k, t % B, j, Hkv, B, d), dtype);
+#if ORACLE_MUTANT == 12
+                    const double vs = block_scale(k_scales, pb, k, Hkv);  /* planted: K's scale */
+#else
+                    const double vs = block_scale(v_scales, pb, k, Hkv);
+#endif
+                    acc += x[t] * (oracle_load(vsrc, pool_index(pb, k, t % B, j, Hkv, B, d), kvdtype) * vs);
                 }
                 o_row[j] = acc / Z;
             }
@@ -200,6 +299,39 @@ int oracle_decode(double *out, const void *query, const void *key_cache, const v
         free(x);
     }
     return ORACLE_OK;
+}
+
+/* Decode over pools stored in the query's type (f32, f16 or bf16). */
+int oracle_decode(double *out, const void *query, const void *key_cache, const void *value_cache,
+                  const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                  int num_blocks, double scale, int dtype)
+{
+    if (!is_wide(dtype))
+        return ORACLE_BAD_ARG;
+    return decode_impl(out, query, key_cache, value_cache, NULL, NULL, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, num_blocks, scale, dtype, dtype);
+}
+
+/*
+ * Decode over E4M3 pools: a stored code c of block pb, head k stands for
+ * value(c) * k_scales[pb][k] (keys) or value(c) * v_scales[pb][k] (values); the query
+ * is f16 or bf16 (qdtype).  Compressing cached blocks to fewer bits is the direction
+ * of "vLLM PagedAttention 技术深度解析" (kwkr.cn) §1.5 and of the "PagedAttention"
+ * concept report §15; the format and the per-block scale are this oracle's reading.
+ */
+int oracle_decode_fp8(double *out, const void *query, const void *key_cache, const void *value_cache,
+                      const float *k_scales, const float *v_scales, const int32_t *block_tables,
+                      int max_blocks_per_seq, const int32_t *context_lens, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                      double scale, int qdtype)
+{
+    if (!k_scales || !v_scales)
+        return ORACLE_BAD_ARG;
+    return decode_impl(out, query, key_cache, value_cache, k_scales, v_scales, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, block_size, num_blocks, scale, qdtype, ORACLE_FP8);
 }
 
 /*
@@ -231,6 +363,43 @@ int oracle_reshape_and_cache(const void *key, const void *value, void *key_cache
                 memcpy((char *)key_cache + dst * eb, (const char *)key + src * eb, eb);
                 memcpy((char *)value_cache + dst * eb, (const char *)value + src * eb, eb);
             }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * The slot scatter into E4M3 pools: element x (key/value in src_dtype) of token i, KV
+ * head k goes to block b = slot / B as oracle_fp8_encode(x / scale), scale taken from
+ * k_scales[b][k] (keys) or v_scales[b][k] (values); the division is one binary32
+ * division, so that the code is decided in the precision the device uses.
+ */
+int oracle_reshape_and_cache_fp8(const void *key, const void *value, uint8_t *key_cache,
+                                 uint8_t *value_cache, const float *k_scales, const float *v_scales,
+                                 const int32_t *slot_mapping, int num_tokens, int num_kv_heads,
+                                 int head_dim, int block_size, int num_blocks, int src_dtype)
+{
+    if (!is_wide(src_dtype) || num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || !k_scales || !v_scales)
+        return ORACLE_BAD_ARG;
+    for (int i = 0; i < num_tokens; ++i) {
+        const int64_t slot = slot_mapping[i];
+        if (slot < 0) continue;
+        const int64_t b = slot / block_size, off = slot % block_size;
+        if (b >= num_blocks) return ORACLE_BAD_INDEX;
+        for (int k = 0; k < num_kv_heads; ++k) {
+            const float ks = k_scales[b * num_kv_heads + k];
+            const float vs = v_scales[b * num_kv_heads + k];
+            for (int j = 0; j < head_dim; ++j) {
+                const int64_t src = ((int64_t)i * num_kv_heads + k) * head_dim + j;
+                const int64_t dst = pool_index(b, k, (int)off, j, num_kv_heads, block_size, head_dim);
+                const float xk = (float)oracle_load(key, src, src_dtype);
+                const float xv = (float)oracle_load(value, src, src_dtype);
+                const float yk = xk / ks;
+                const float yv = xv / vs;
+                key_cache[dst] = oracle_fp8_encode(yk);
+                value_cache[dst] = oracle_fp8_encode(yv);
+            }
+        }
     }
     return ORACLE_OK;
 }

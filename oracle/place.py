@@ -1,8 +1,9 @@
 """Build pools and tables for a workload batch on the oracle side (TEST INFRASTRUCTURE).
 
 Replays the batch's allocator script on the model allocator, scatters every
-token with the oracle's reshape_and_cache, applies the copy-on-write pairs with
-the oracle's copy_blocks, and returns everything the oracle's decode needs.
+token with the oracle's reshape_and_cache (reshape_and_cache_fp8 for E4M3 pools),
+applies the copy-on-write pairs with the oracle's copy_blocks (E4M3 blocks take
+their scales along), and returns everything the oracle's decode needs.
 Step order (the decode step of the KV-cache/paging tutorial (wmrh.cn): only the
 newest token's K/V are written, then attention runs over all cached tokens):
   1. earlier tokens of every sequence are placed (prompt, then private tokens,
@@ -34,6 +35,26 @@ class Placed:
     cow_src: np.ndarray  # int32: copy-on-write pairs in the order they arose
     cow_dst: np.ndarray
     alloc: ModelAllocator
+    k_scales: Optional[np.ndarray] = None  # E4M3 pools: float32 [num_blocks][H_kv]
+    v_scales: Optional[np.ndarray] = None
+
+    def write(self, key, value, slots, src_dtype: str) -> None:
+        """Scatter tokens (src_dtype) into the pools with the oracle's scatter."""
+        o = _default_oracle()
+        if self.k_scales is None:
+            o.reshape_and_cache(key, value, self.key_cache, self.value_cache, slots, src_dtype)
+        else:
+            o.reshape_and_cache_fp8(key, value, self.key_cache, self.value_cache, self.k_scales,
+                                    self.v_scales, slots, src_dtype)
+
+    def copy(self, src, dst, kv_dtype: str) -> None:
+        """Whole-block copies; E4M3 blocks take their scales along."""
+        o = _default_oracle()
+        o.copy_blocks(self.key_cache, self.value_cache, src, dst, kv_dtype)
+        if self.k_scales is not None:
+            nb, H = self.k_scales.shape
+            o.copy_blocks(self.k_scales.reshape(nb, H, 1, 1), self.v_scales.reshape(nb, H, 1, 1),
+                          src, dst, "f32")
 
 
 def replay(batch: W.Batch):
@@ -63,18 +84,26 @@ def replay(batch: W.Batch):
 
 def place(batch: W.Batch, poison: bool = True) -> Placed:
     """Pools with every token placed except each sequence's newest one."""
-    o = _default_oracle()
     w = batch.workload
     a, sids, slots, cow = replay(batch)
     shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
-    npd = W.storage_np_dtype(w.dtype)
-    fill = W.nan_bits(w.dtype) if poison else npd(0)
-    kc = np.full(shape, fill, dtype=npd)
-    vc = np.full(shape, fill, dtype=npd)
+    npd = W.storage_np_dtype(w.kv)
+    fill = W.nan_bits(w.kv) if poison else npd(0)
     S = w.num_seqs
+    if cow:
+        src = np.array([c[0] for c in cow], np.int32)
+        dst = np.array([c[1] for c in cow], np.int32)
+    else:
+        src = np.zeros(0, np.int32)
+        dst = np.zeros(0, np.int32)
+    qnp = W.storage_np_dtype(w.dtype)
     newest_slot = np.full(S, -1, np.int32)
-    newest_k = np.zeros((S, w.num_kv_heads, w.head_dim), npd)
+    newest_k = np.zeros((S, w.num_kv_heads, w.head_dim), qnp)
     newest_v = np.zeros_like(newest_k)
+    p = Placed(np.full(shape, fill, dtype=npd), np.full(shape, fill, dtype=npd), None, None,
+               newest_slot, newest_k, newest_v, src, dst, a)
+    if w.kv == "fp8":
+        p.k_scales, p.v_scales = W.fp8_scales(w)
     appends = [op for op in batch.script if op.kind == "append"]
     # prompts first; then the copy-on-write copies; then each sequence's private
     # tokens (all of its last append but the newest token)
@@ -83,19 +112,12 @@ def place(batch: W.Batch, poison: bool = True) -> Placed:
         last_append_of[op.seq] = i
     prompt_like = [i for i, op in enumerate(appends) if last_append_of[op.seq] != i]
     for i in prompt_like:
-        o.reshape_and_cache(batch.append_k[i], batch.append_v[i], kc, vc, slots[i], w.dtype)
-    if cow:
-        src = np.array([c[0] for c in cow], np.int32)
-        dst = np.array([c[1] for c in cow], np.int32)
-    else:
-        src = np.zeros(0, np.int32)
-        dst = np.zeros(0, np.int32)
-    o.copy_blocks(kc, vc, src, dst, w.dtype)
+        p.write(batch.append_k[i], batch.append_v[i], slots[i], w.dtype)
+    p.copy(src, dst, w.kv)
     for seq, i in last_append_of.items():
         n = appends[i].arg
         if n > 1:
-            o.reshape_and_cache(batch.append_k[i][:-1], batch.append_v[i][:-1], kc, vc,
-                                slots[i][:-1], w.dtype)
+            p.write(batch.append_k[i][:-1], batch.append_v[i][:-1], slots[i][:-1], w.dtype)
         newest_slot[seq] = slots[i][-1]
         newest_k[seq] = batch.append_k[i][-1]
         newest_v[seq] = batch.append_v[i][-1]
@@ -106,7 +128,8 @@ def place(batch: W.Batch, poison: bool = True) -> Placed:
         t, n = a.block_table(sids[s])
         bt[s, :len(t)] = t
         cl[s] = n
-    return Placed(kc, vc, bt, cl, newest_slot, newest_k, newest_v, src, dst, a)
+    p.block_tables, p.context_lens = bt, cl
+    return p
 
 
 def decode_step(batch: W.Batch, placed: Optional[Placed] = None, poison: bool = True):
@@ -115,7 +138,11 @@ def decode_step(batch: W.Batch, placed: Optional[Placed] = None, poison: bool = 
     o = _default_oracle()
     w = batch.workload
     p = placed or place(batch, poison)
-    o.reshape_and_cache(p.new_key, p.new_value, p.key_cache, p.value_cache, p.slot_mapping, w.dtype)
-    out = o.decode(batch.q, p.key_cache, p.value_cache, p.block_tables, p.context_lens,
-                   w.scale, w.dtype)
+    p.write(p.new_key, p.new_value, p.slot_mapping, w.dtype)
+    if p.k_scales is None:
+        out = o.decode(batch.q, p.key_cache, p.value_cache, p.block_tables, p.context_lens,
+                       w.scale, w.dtype)
+    else:
+        out = o.decode_fp8(batch.q, p.key_cache, p.value_cache, p.k_scales, p.v_scales,
+                           p.block_tables, p.context_lens, w.scale, w.dtype)
     return out, p

@@ -17,6 +17,10 @@ of the oracle with a planted mistake (see test_oracle_pins.py).  The facts used:
              (5ulink §二), computed through its table, equals attention over the
              same 100 tokens laid out contiguously.
   brute      pure-Python loops through the table on tiny inputs.
+  E4M3       torch's float8_e4m3fn for the value of every code and for rounding
+             (clamped to +-448 first: the saturating reading), every midpoint
+             between neighbouring codes (ties to even), the round trip of every
+             finite code, and torch SDPA over dequantised tokens for the decode.
 """
 from __future__ import annotations
 
@@ -375,7 +379,162 @@ def pin_dtype_decode(o):
     assert np.array_equal(o.load(x, "f32"), x.astype(np.float64))
 
 
+# ---------------------------------------------------------------------------
+# E4M3 pools with a scale per (physical block, KV head)
+
+
+def torch_fp8_values() -> np.ndarray:
+    """float64 value of each of the 256 E4M3 codes, decoded by torch."""
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def torch_fp8_encode(y) -> np.ndarray:
+    """Codes for float32 numbers: torch's round-to-nearest-even cast after clamping to
+    +-448 (NaN stays NaN and becomes 0x7F)."""
+    t = torch.from_numpy(np.ascontiguousarray(y, np.float32))
+    codes = t.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    codes[np.isnan(np.asarray(y))] = 0x7F
+    return codes
+
+
+def pin_fp8_codes(o):
+    """Every E4M3 code decodes to torch's value (NaN at 0x7F / 0xFF only), with the
+    format's landmarks: 1.0 = 0x38, 448 = 0x7E, 2^-6 = 0x08, 2^-9 = 0x01."""
+    c = np.arange(256, dtype=np.uint8)
+    got = o.fp8_value(c)
+    assert np.array_equal(got, torch_fp8_values(), equal_nan=True)
+    assert [i for i in range(256) if np.isnan(got[i])] == [0x7F, 0xFF]
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9
+    assert got[0xBC] == -1.5 and np.signbit(got[0x80]) and got[0x80] == 0.0
+
+
+def pin_fp8_encode(o):
+    """Rounding to E4M3 equals torch's cast after clamping to +-448: random numbers over
+    many magnitudes, every midpoint between neighbouring codes (ties go to the even
+    code), the saturation edge, zeros, infinities and NaN; finite codes round-trip."""
+    vals = torch_fp8_values()
+    finite = [c for c in range(0x7F)]  # 0x00..0x7E
+    mids = [(vals[c] + vals[c + 1]) / 2 for c in finite[:-1]]
+    rng = np.random.default_rng(120)
+    ys = np.concatenate([
+        np.asarray(mids, np.float32), -np.asarray(mids, np.float32),
+        (rng.standard_normal(4000) * np.exp2(rng.uniform(-14, 10, 4000))).astype(np.float32),
+        np.array([447.9, 448.0, 455.9, 456.0, 463.99, 464.0, 500.0, 1e30, np.inf, -np.inf, -464.0,
+                  0.0, -0.0, 1e-30, -1e-30, 2.0 ** -10, 3 * 2.0 ** -11, np.nan], np.float32)])
+    got = o.fp8_encode(ys)
+    want = torch_fp8_encode(ys)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(ys[i]), int(got[i]), int(want[i])) for i in bad[:5]]
+    # midpoint ties land on the even neighbour
+    for c, m in zip(finite[:-1], mids):
+        assert int(o.fp8_encode(np.float32(m))) % 2 == 0, (c, m)
+    codes = np.array(finite + [0x80 + c for c in finite], np.uint8)
+    assert np.array_equal(o.fp8_encode(vals[codes].astype(np.float32)), codes)
+
+
+class Fp8Case:
+    """E4M3 pools with random per-(block, KV head) scales, placed through a random
+    permutation of blocks; slots past each context hold the NaN code."""
+
+    def __init__(self, rng, lens, Hq, Hkv, d, B, qdtype):
+        self.lens = [int(x) for x in lens]
+        self.Hq, self.Hkv, self.d, self.B, self.qdtype = Hq, Hkv, d, B, qdtype
+        self.dtype = qdtype  # of the query (Case.f64 reads it)
+        nblk = [-(-n // B) for n in self.lens]
+        self.num_blocks = sum(nblk) + 3
+        self.scale = float(np.float32(1.0 / math.sqrt(d)))
+        S = len(self.lens)
+        self.q = W.round_to(rng.standard_normal((S, Hq, d), dtype=np.float32), qdtype)
+        self.ks = np.exp2(rng.uniform(-7, -4, (self.num_blocks, Hkv))).astype(np.float32)
+        self.vs = np.exp2(rng.uniform(-7, -4, (self.num_blocks, Hkv))).astype(np.float32)
+        ids = rng.permutation(self.num_blocks)
+        self.max_blocks = max(1, max(nblk))
+        self.tables = np.full((S, self.max_blocks), -1, np.int32)
+        pos = 0
+        for s, nb in enumerate(nblk):
+            self.tables[s, :nb] = ids[pos:pos + nb]
+            pos += nb
+        shape = (self.num_blocks, Hkv, B, d)
+        self.kc = np.full(shape, 0x7F, np.uint8)
+        self.vc = np.full(shape, 0x7F, np.uint8)
+        vals = torch_fp8_values()
+        self.kf, self.vf = [], []  # dequantised tokens [n][H_kv][d] in logical order
+        for s, n in enumerate(self.lens):
+            kcodes = torch_fp8_encode(rng.standard_normal((n, Hkv, d), dtype=np.float32) * 60)
+            vcodes = torch_fp8_encode(rng.standard_normal((n, Hkv, d), dtype=np.float32) * 60)
+            kf = np.empty((n, Hkv, d))
+            vf = np.empty((n, Hkv, d))
+            for t in range(n):
+                b = self.tables[s, t // B]
+                self.kc[b, :, t % B, :] = kcodes[t]
+                self.vc[b, :, t % B, :] = vcodes[t]
+                kf[t] = vals[kcodes[t]] * self.ks[b][:, None].astype(np.float64)
+                vf[t] = vals[vcodes[t]] * self.vs[b][:, None].astype(np.float64)
+            self.kf.append(kf)
+            self.vf.append(vf)
+        self.ctx = np.asarray(self.lens, np.int32)
+
+    def run(self, o):
+        return o.decode_fp8(self.q, self.kc, self.vc, self.ks, self.vs, self.tables, self.ctx,
+                            self.scale, self.qdtype)
+
+    def sdpa(self):
+        out = np.zeros((len(self.lens), self.Hq, self.d))
+        qf = Case.f64(self, self.q)
+        for s, n in enumerate(self.lens):
+            if n == 0:
+                continue
+            q = torch.from_numpy(qf[s])[None, :, None, :]
+            k = torch.from_numpy(self.kf[s]).permute(1, 0, 2)[None].contiguous()
+            v = torch.from_numpy(self.vf[s]).permute(1, 0, 2)[None].contiguous()
+            out[s] = F.scaled_dot_product_attention(q, k, v, scale=self.scale,
+                                                    enable_gqa=self.Hq != self.Hkv)[0, :, 0, :].numpy()
+        return out
+
+
+def pin_fp8_sdpa(o):
+    """Decode over E4M3 pools equals torch SDPA over the dequantised tokens (code value
+    times the scale of the block and head holding it), in logical order."""
+    rng = np.random.default_rng(121)
+    for lens, Hq, Hkv, d, B, qdt in (([1, 5, 16, 33], 2, 2, 8, 4, "f16"),
+                                     ([40, 7], 8, 2, 16, 8, "bf16"),
+                                     ([0, 70], 4, 1, 32, 16, "f16")):
+        c = Fp8Case(rng, lens, Hq, Hkv, d, B, qdt)
+        got, want = c.run(o), c.sdpa()
+        assert np.max(np.abs(got - want)) <= 1e-12, (lens, Hq, Hkv, d, B, qdt)
+
+
+def pin_fp8_reshape(o):
+    """The E4M3 scatter equals numpy fancy indexing of torch's clamped cast of
+    x / scale (one float32 division) into the slots; untouched slots keep their bytes."""
+    rng = np.random.default_rng(122)
+    for dt, nb, H, B, d in (("f16", 6, 2, 4, 8), ("bf16", 5, 3, 8, 16), ("f32", 4, 1, 2, 4)):
+        N = nb * B // 2
+        slots = rng.choice(nb * B, size=N, replace=False).astype(np.int32)
+        slots[::5] = -1
+        key = W.round_to(rng.standard_normal((N, H, d), dtype=np.float32) * 8, dt)
+        val = W.round_to(rng.standard_normal((N, H, d), dtype=np.float32) * 8, dt)
+        key.reshape(-1)[:3] = W.round_to(np.array([1e4, -1e4, 0.0], np.float32), dt)
+        ks = np.exp2(rng.uniform(-6, -2, (nb, H))).astype(np.float32)
+        vs = np.exp2(rng.uniform(-6, -2, (nb, H))).astype(np.float32)
+        kc = rng.integers(0, 256, (nb, H, B, d)).astype(np.uint8)
+        vc = rng.integers(0, 256, (nb, H, B, d)).astype(np.uint8)
+        wk, wv = kc.copy(), vc.copy()
+        keep = slots >= 0
+        tmp = Case.__new__(Case)
+        tmp.dtype = dt
+        for want, x, sc in ((wk, key, ks), (wv, val, vs)):
+            xf = tmp.f64(x).astype(np.float32)  # exact: every source value fits
+            for i in np.nonzero(keep)[0]:
+                b, off = divmod(int(slots[i]), B)
+                y = (torch.from_numpy(xf[i]) / torch.from_numpy(sc[b])[:, None]).numpy()
+                want[b, :, off, :] = torch_fp8_encode(y)
+        o.reshape_and_cache_fp8(key, val, kc, vc, ks, vs, slots, dt)
+        assert kc.tobytes() == wk.tobytes() and vc.tobytes() == wv.tobytes(), dt
+
+
 ORACLE_PINS = [pin_sdpa, pin_brute, pin_permutation, pin_ctx1, pin_equal_keys, pin_dominant,
                pin_shared_prefix, pin_nan_poison, pin_empty, pin_bad_index, pin_reshape, pin_copy,
                pin_swap,
-               pin_page3_request, pin_dtype_decode]
+               pin_page3_request, pin_dtype_decode, pin_fp8_codes, pin_fp8_encode, pin_fp8_sdpa,
+               pin_fp8_reshape]

@@ -26,6 +26,11 @@ MUTANTS = {
     8: "slot split into block/offset the wrong way round",
     9: "block copy skips the value pool",
     10: "sign of the exponent flipped",
+    11: "E4M3 exponent bias 8",
+    12: "values scaled by the key scale",
+    13: "E4M3 ties rounded away from zero",
+    14: "E4M3 encode without saturation",
+    15: "key scale taken from the logical block",
 }
 
 

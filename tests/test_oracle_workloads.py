@@ -93,4 +93,37 @@ def test_full_size_lengths_match_the_recipe():
     """The seeded draws of every workload (only the length step)."""
     sums = {n: int(W.draw_lengths(w)[0].context_lens.sum()) for n, w in W.WORKLOADS.items()}
     assert sums == {"tiny_fp32": 134, "llama7b": 46958, "llama13b_long": 95677,
-                    "prefix_sharing": 93983, "llama70b_gqa": 191507}
+                    "prefix_sharing": 93983, "llama70b_gqa": 191507, "llama7b_fp8": 46958}
+
+
+def test_fp8_prefix_step_equals_attention_over_dequantised_tokens():
+    """E4M3 pools with per-(block, head) scales, copy-on-write included: each token of
+    each sequence stands for torch's E4M3 rounding of x / s times s, s the final scale
+    of the block holding it (a copied block carries its source's scale)."""
+    from oracle_pins import torch_fp8_encode, torch_fp8_values
+    w = W.scaled(SMALL["prefix_small"], kv_dtype="fp8", dtype="f16")
+    batch = W.make_batch(w)
+    out, p = place.decode_step(batch)
+    assert len(p.cow_src) > 0 and np.all(np.isfinite(out))
+    vals = torch_fp8_values()
+    K, V = _logical(batch)
+    ref = np.zeros_like(out)
+    g = w.num_q_heads // w.num_kv_heads
+    for s in range(w.num_seqs):
+        n = int(p.context_lens[s])
+        blocks = p.block_tables[s, np.arange(n) // w.block_size]
+        kq = np.empty((n, w.num_kv_heads, w.head_dim))
+        vq = np.empty_like(kq)
+        for t in range(n):
+            ks = p.k_scales[blocks[t]][:, None]
+            vs = p.v_scales[blocks[t]][:, None]
+            kx = (torch.from_numpy(K[s][t].astype(np.float32)) / torch.from_numpy(ks)).numpy()
+            vx = (torch.from_numpy(V[s][t].astype(np.float32)) / torch.from_numpy(vs)).numpy()
+            kq[t] = vals[torch_fp8_encode(kx)] * ks.astype(np.float64)
+            vq[t] = vals[torch_fp8_encode(vx)] * vs.astype(np.float64)
+        q = _f64(batch.q[s], w.dtype)[None, :, None, :]
+        ref[s] = F.scaled_dot_product_attention(
+            q, torch.from_numpy(kq).permute(1, 0, 2)[None].contiguous(),
+            torch.from_numpy(vq).permute(1, 0, 2)[None].contiguous(), scale=w.scale,
+            enable_gqa=g > 1)[0, :, 0].numpy()
+    assert np.max(np.abs(out - ref)) <= 1e-12

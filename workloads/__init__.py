@@ -23,6 +23,9 @@ Workloads (shapes and length mixes of the serving examples on the pages):
   - llama70b_gqa    70B-shaped GQA: 32 seqs, 64 query / 8 KV heads, d=128, B=128,
                     bf16, 4,096 blocks, lengths uniform in [4096, 8192], 512-token
                     partitions.
+  - llama7b_fp8     llama7b (same seed, lengths and numbers) with the pools held as
+                    OCP E4M3 codes and one fp32 scale per (block, KV head) for K and
+                    for V; query, new K/V and output stay fp16.
 
 Draw recipe (numpy PCG64):
   base stream  default_rng(seed): (1) length parameters, (2) free order =
@@ -34,6 +37,9 @@ Draw recipe (numpy PCG64):
                prompt (prefix_sharing only).
   values       standard_normal(float32) rounded to the storage type with
                round-to-nearest-even; bf16 is returned as raw uint16 bits.
+  E4M3 scales  default_rng(SeedSequence([seed, 3])): K scales then V scales,
+               [num_blocks][H_kv] float32, each 2^u with u uniform in [-7, -5]
+               (448 * scale spans 3.5 to 14 standard deviations of the values).
 """
 from __future__ import annotations
 
@@ -66,6 +72,7 @@ class Workload:
     samples: int = 0  # prefix: samples per prompt
     prefix_base: int = 0  # prefix: shared prompt = prefix_base + U{1..block_size-1}
     private_max: int = 0  # prefix: private tokens U{0..private_max}
+    kv_dtype: str = ""  # pool storage type; "" = the query's type, "fp8" = E4M3 codes
 
     @property
     def scale(self) -> float:
@@ -75,6 +82,15 @@ class Workload:
     @property
     def elem_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
+
+    @property
+    def kv(self) -> str:
+        """Storage type of the K/V pools."""
+        return self.kv_dtype or self.dtype
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return 1 if self.kv == "fp8" else self.elem_bytes
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -88,6 +104,8 @@ WORKLOADS: Dict[str, Workload] = {
                                private_max=256),
     "llama70b_gqa": Workload("llama70b_gqa", 5, 32, 64, 8, 128, 128, 4096, "bf16", 0,
                              "uniform", low=4096, high=8192),
+    "llama7b_fp8": Workload("llama7b_fp8", 2, 64, 32, 32, 128, 16, 40000, "f16", 0, "lognormal",
+                            kv_dtype="fp8"),
 }
 
 
@@ -116,11 +134,21 @@ def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def nan_bits(dtype: str):
     """A quiet NaN in the storage representation (for poisoning unused slots)."""
-    return {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(0x7FC0)}[dtype]
+    return {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(0x7FC0),
+            "fp8": np.uint8(0x7F)}[dtype]
 
 
 def storage_np_dtype(dtype: str):
-    return {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
+    return {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}[dtype]
+
+
+def fp8_scales(w: Workload):
+    """K and V scales [num_blocks][H_kv] float32 of an E4M3 workload."""
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, 3]))
+    shape = (w.num_blocks, w.num_kv_heads)
+    ks = np.exp2(rng.uniform(-7.0, -5.0, shape)).astype(np.float32)
+    vs = np.exp2(rng.uniform(-7.0, -5.0, shape)).astype(np.float32)
+    return ks, vs
 
 
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
