@@ -88,11 +88,14 @@ def log(args, *a):
 
 def algorithmic_bytes(w, ctx: np.ndarray) -> dict:
     """Bytes one decode call must move: K/V of every cached token, q in, out, the
-    table entries it reads and the lengths."""
-    esz = w.elem_bytes
-    kv = int(ctx.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * esz
-    qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * esz
-    tbl = 4 * int(np.sum((ctx.astype(np.int64) + w.block_size - 1) // w.block_size)) + 4 * w.num_seqs
+    table entries it reads and the lengths (E4M3 pools: also the K and V scale of every
+    (block, KV head) it reads)."""
+    kv = int(ctx.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * w.kv_elem_bytes
+    qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * w.elem_bytes
+    blocks = int(np.sum((ctx.astype(np.int64) + w.block_size - 1) // w.block_size))
+    tbl = 4 * blocks + 4 * w.num_seqs
+    if w.kv == "fp8":
+        tbl += 8 * blocks * w.num_kv_heads
     return {"kv": kv, "total": kv + qo + tbl}
 
 
@@ -119,7 +122,6 @@ def build_replicas(args, w, batch, identity: bool):
 def run_steps(args, reps, n_steps: int, record: bool):
     """Returns (total ms, per-step decode ms list, per-step pre-decode ms list)."""
     import torch
-    from paged_kv_cache_308_amd import pa_copy_blocks
     st = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
             torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)] if record else None
@@ -132,7 +134,7 @@ def run_steps(args, reps, n_steps: int, record: bool):
         if record:
             evs[k][0].record(st)
         if src.numel():
-            pa_copy_blocks(db.cache.key_cache, db.cache.value_cache, src, dst, st)
+            db.cache.copy(src, dst, st)
         db.cache.write(db.new_key, db.new_value, db.slot_mapping, st)
         if record:
             evs[k][1].record(st)
@@ -176,9 +178,14 @@ def cpu_baseline(args, w, batch, kv_bytes: int) -> dict:
     import oracle
     p = place.place(batch, poison=False)
     o = oracle.default()
-    o.reshape_and_cache(p.new_key, p.new_value, p.key_cache, p.value_cache, p.slot_mapping, w.dtype)
+    p.write(p.new_key, p.new_value, p.slot_mapping, w.dtype)
     t = time.perf_counter()
-    o.decode(batch.q, p.key_cache, p.value_cache, p.block_tables, p.context_lens, w.scale, w.dtype)
+    if w.kv == "fp8":
+        o.decode_fp8(batch.q, p.key_cache, p.value_cache, p.k_scales, p.v_scales, p.block_tables,
+                     p.context_lens, w.scale, w.dtype)
+    else:
+        o.decode(batch.q, p.key_cache, p.value_cache, p.block_tables, p.context_lens, w.scale,
+                 w.dtype)
     dt = time.perf_counter() - t
     cpu = platform.processor() or platform.machine()
     try:
@@ -210,7 +217,7 @@ def swap_bench(args, w, batch) -> dict:
     host = HostKVPool(nblk, w.num_kv_heads, w.head_dim, w.block_size, cache.dtype)
     dev_ids = torch.from_numpy(src).cuda()
     host_ids = torch.arange(nblk, dtype=torch.int32, device="cuda")
-    nbytes = 2 * nblk * w.num_kv_heads * w.block_size * w.head_dim * w.elem_bytes
+    nbytes = 2 * nblk * w.num_kv_heads * w.block_size * w.head_dim * w.kv_elem_bytes
     st = torch.cuda.current_stream()
     res = {}
     for name, (a, b, s_, d_) in {
@@ -294,7 +301,7 @@ def main():
     gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
     achieved = ab["total"] / (dec_avg * 1e-3) / 1e9
     g = w.num_q_heads // w.num_kv_heads
-    mfma = args.variant == 2 or (args.variant == 0 and g >= 2 and w.dtype != "f32")
+    mfma = w.kv != "fp8" and (args.variant == 2 or (args.variant == 0 and g >= 2 and w.dtype != "f32"))
     kernels = ("decode_mfma_kernel" if mfma else "decode_valu_kernel") + \
         (" + lse_merge_kernel" if args.P else "")
     line = {
@@ -308,9 +315,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "fp8_e4m3" if w.kv == "fp8" else w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+        "config": {"workload": w.name, "kv_dtype": w.kv, "query_dtype": w.dtype,
+                   "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "num_blocks": w.num_blocks,
                    "sum_context_lens": int(ctx.sum()), "max_context_len": int(ctx.max()),

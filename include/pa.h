@@ -23,7 +23,9 @@
  *                           KV head h / (num_q_heads / num_kv_heads).
  *
  * Supported: dtype f32 / f16 / bf16; head_dim 64 or 128; block_size 16, 32, 64 or 128;
- * num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}.
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}.  Compressed pools (pa_decode_fp8,
+ * pa_reshape_and_cache_fp8) hold one-byte E4M3 codes with an fp32 scale per
+ * (physical block, KV head); their query and output are f16 or bf16.
  *
  * Ownership and ordering: every device pointer is borrowed from the caller and must
  * stay valid until the work queued on `stream` (a hipStream_t; NULL = the null stream)
@@ -58,7 +60,10 @@ typedef enum pa_status {
     PA_ERR_HIP = 5          /* the HIP runtime reported an error (see pa_last_error) */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* PA_FP8_E4M3: one-byte OCP E4M3 codes (no infinities; 0x7F / 0xFF are NaN; largest
+ * finite 448).  Pool storage only: accepted by pa_copy_blocks and pa_swap_blocks, and
+ * the pool type of pa_decode_fp8 / pa_reshape_and_cache_fp8. */
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Decode-attention variants (pa_decode's `variant` argument): a kernel choice in the
  * low 4 bits, optionally OR-ed with PA_DECODE_SHARED_KV. */
@@ -137,7 +142,10 @@ int pa_reshape_and_cache(const void *key, const void *value, void *key_cache, vo
  * heads, all slots) of both pools is copied onto block dst[p], bit for bit.
  * src, dst: device int32 [num_pairs].  A pair with an id outside [0, num_blocks) is
  * skipped.  The dst ids must be distinct and must not appear among the src ids (the
- * allocator's pairs always are); pa_check_copy_pairs checks host copies.
+ * allocator's pairs always are); pa_check_copy_pairs checks host copies.  A block's
+ * bytes (num_kv_heads * block_size * head_dim * element size) must be a multiple of 4:
+ * the per-(block, KV head) scales of E4M3 pools are moved with the same call, as pools
+ * of PA_F32 with head_dim = block_size = 1.
  */
 int pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *src, const int32_t *dst,
                    int num_pairs, int num_kv_heads, int head_dim, int block_size, int num_blocks,
@@ -156,6 +164,46 @@ int pa_swap_blocks(const void *src_key_cache, const void *src_value_cache, void 
                    void *dst_value_cache, const int32_t *src, const int32_t *dst, int num_pairs,
                    int num_kv_heads, int head_dim, int block_size, int src_num_blocks,
                    int dst_num_blocks, int dtype, void *stream);
+
+/* ------------------------------------------------------- compressed (E4M3) pools */
+
+/*
+ * Compressed KV blocks ([kwkr] §1.5: quantising older blocks, dynamic precision;
+ * [cpai] §15: lossy compression of physical blocks to raise the effective capacity).
+ * The pools hold PA_FP8_E4M3 codes in the usual [num_blocks][num_kv_heads][B][d]
+ * layout, and k_scales / v_scales (device fp32 [num_blocks][num_kv_heads]) give each
+ * (physical block, KV head) tile its own scale: a key code c of block b, head k stands
+ * for value(c) * k_scales[b][k] (values likewise with v_scales).  The caller owns the
+ * scales: it sets a block's scales before the block's first write and moves them with
+ * the block (pa_copy_blocks / pa_swap_blocks on the scale arrays, see there).
+ */
+
+/*
+ * E4M3 counterpart of pa_reshape_and_cache: element x of key[i][k][:] (dtype f32, f16
+ * or bf16) is stored in block b = slot / B as the E4M3 code nearest to
+ * y = x / k_scales[b][k] (one correctly rounded fp32 division): round to nearest, ties
+ * to the even code, |y| >= 448 (infinities too) saturating to +-448, NaN to 0x7F.
+ * Values likewise with v_scales.  Slots outside [0, num_blocks * B) are skipped.
+ */
+int pa_reshape_and_cache_fp8(const void *key, const void *value, void *key_cache, void *value_cache,
+                             const float *k_scales, const float *v_scales,
+                             const int32_t *slot_mapping, int num_tokens, int num_kv_heads,
+                             int head_dim, int block_size, int num_blocks, int dtype, void *stream);
+
+/*
+ * pa_decode over E4M3 pools: the same attention with K_t = value(code) * k_scale and
+ * V_t = value(code) * v_scale of the block and KV head holding token t.  query and out
+ * are `dtype` (PA_F16 or PA_BF16); codes are widened exactly, products and softmax run
+ * in fp32.  Every other argument, partitioning, the workspace and the error behaviour
+ * are those of pa_decode; the vector kernel serves every variant (PA_VARIANT_MFMA
+ * returns PA_ERR_UNSUPPORTED), and group sizes go up to 8.
+ */
+int pa_decode_fp8(void *out, const void *query, const void *key_cache, const void *value_cache,
+                  const float *k_scales, const float *v_scales, const int32_t *block_tables,
+                  int max_blocks_per_seq, const int32_t *context_lens, int num_seqs,
+                  int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                  int max_context_len, float scale, int dtype, int partition_size, int variant,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Host-side checks ([cpai] §13).  PA_ERR_BOUNDS names the first offending entry in
  * pa_last_error. */

@@ -123,10 +123,17 @@ uint8_t oracle_fp8_encode(float y)
 #endif
     if (a >= 448.0)
         return sign | 0x7E;
+    static double value[0x7F];  /* oracle_fp8_value of the finite non-negative codes */
+    static int have_values = 0;
+    if (!have_values) {
+        for (int c = 0; c <= 0x7E; ++c)
+            value[c] = oracle_fp8_value((uint8_t)c);
+        have_values = 1;
+    }
     int best = 0;
     double best_dist = INFINITY;
     for (int c = 0; c <= 0x7E; ++c) {
-        const double dist = fabs(oracle_fp8_value((uint8_t)c) - a);
+        const double dist = fabs(value[c] - a);
 #if ORACLE_MUTANT == 13
         if (dist <= best_dist) {                      /* planted: ties away from zero */
 #else

@@ -82,8 +82,9 @@ def replay(batch: W.Batch):
     return a, sids, slots, cow
 
 
-def place(batch: W.Batch, poison: bool = True) -> Placed:
-    """Pools with every token placed except each sequence's newest one."""
+def place(batch: W.Batch, poison: bool = True, fp8_scales=None) -> Placed:
+    """Pools with every token placed except each sequence's newest one.  E4M3 pools take
+    the workload's block scales unless `fp8_scales` = (k, v) [num_blocks][H_kv] is given."""
     w = batch.workload
     a, sids, slots, cow = replay(batch)
     shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
@@ -103,7 +104,9 @@ def place(batch: W.Batch, poison: bool = True) -> Placed:
     p = Placed(np.full(shape, fill, dtype=npd), np.full(shape, fill, dtype=npd), None, None,
                newest_slot, newest_k, newest_v, src, dst, a)
     if w.kv == "fp8":
-        p.k_scales, p.v_scales = W.fp8_scales(w)
+        ks, vs = fp8_scales if fp8_scales is not None else W.fp8_scales(w)
+        p.k_scales = np.array(ks, np.float32)
+        p.v_scales = np.array(vs, np.float32)
     appends = [op for op in batch.script if op.kind == "append"]
     # prompts first; then the copy-on-write copies; then each sequence's private
     # tokens (all of its last append but the newest token)
@@ -132,12 +135,13 @@ def place(batch: W.Batch, poison: bool = True) -> Placed:
     return p
 
 
-def decode_step(batch: W.Batch, placed: Optional[Placed] = None, poison: bool = True):
+def decode_step(batch: W.Batch, placed: Optional[Placed] = None, poison: bool = True,
+                fp8_scales=None):
     """The oracle's decode step: scatter the newest tokens, then attention.
     Returns (out float64 [S][H_q][d], placed)."""
     o = _default_oracle()
     w = batch.workload
-    p = placed or place(batch, poison)
+    p = placed or place(batch, poison, fp8_scales)
     p.write(p.new_key, p.new_value, p.slot_mapping, w.dtype)
     if p.k_scales is None:
         out = o.decode(batch.q, p.key_cache, p.value_cache, p.block_tables, p.context_lens,

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_BOUNDS, PA_ERR_OOM, PA_ERR_UNSUPPORTED, PA_ERR_HIP = range(6)
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 PA_DECODE_SHARED_KV = 16
 PA_PARTITION_BALANCED = -1
@@ -28,6 +28,7 @@ PA_PARTITION_BALANCED = -1
 EXPORTS = (
     "pa_status_str", "pa_last_error", "pa_abi_version", "pa_decode_workspace_bytes", "pa_decode",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_check_tables",
+    "pa_reshape_and_cache_fp8", "pa_decode_fp8",
     "pa_check_copy_pairs", "pa_alloc_adopt",
     "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_set_free_order", "pa_alloc_new_seq",
     "pa_alloc_append_slot", "pa_alloc_append_slots", "pa_alloc_fork", "pa_alloc_free_seq",
@@ -69,6 +70,10 @@ def _lib():
         "pa_decode": (i32, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                             i32, i32, i32, vp, sz, vp]),
         "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
+        "pa_reshape_and_cache_fp8": (i32, [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                           vp]),
+        "pa_decode_fp8": (i32, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                i32, f32, i32, i32, i32, vp, sz, vp]),
         "pa_copy_blocks": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
         "pa_swap_blocks": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]),
         "pa_alloc_adopt": (i32, [vp, i32, i64p, i32p, i32]),
@@ -108,8 +113,10 @@ def _torch():
 
 
 def dtype_code(t) -> int:
+    """pa_dtype of a tensor; E4M3 pools are torch.uint8 (raw codes) or float8_e4m3fn."""
     torch = _torch()
-    return {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}[t.dtype]
+    return {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
+            torch.uint8: PA_FP8_E4M3, torch.float8_e4m3fn: PA_FP8_E4M3}[t.dtype]
 
 
 def _stream(stream) -> int:
@@ -161,6 +168,62 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
         ws_ptr, ws_bytes, _stream(stream))
     _check(rc, "pa_decode")
     return out
+
+
+def _is_fp8(t) -> bool:
+    return dtype_code(t) == PA_FP8_E4M3
+
+
+def pa_decode_fp8(out, query, key_cache, value_cache, k_scales, v_scales, block_tables, context_lens,
+                  scale: float, max_context_len: int = 0, partition_size: int = 0,
+                  variant: int = PA_VARIANT_AUTO, workspace=None, stream=None):
+    """E4M3 pools (uint8 [num_blocks][H_kv][B][d]) with float32 scales [num_blocks][H_kv];
+    out/query f16 or bf16 [S][H_q][d]."""
+    torch = _torch()
+    S, Hq, d = query.shape
+    nb, Hkv, B, d2 = key_cache.shape
+    if d2 != d or value_cache.shape != key_cache.shape or out.shape != query.shape:
+        raise ValueError("shape mismatch")
+    if not (_is_fp8(key_cache) and _is_fp8(value_cache)) or out.dtype != query.dtype:
+        raise ValueError("pools must hold E4M3 codes; out must match the query's dtype")
+    if k_scales.shape != (nb, Hkv) or v_scales.shape != (nb, Hkv):
+        raise ValueError("scales must be [num_blocks][H_kv]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables / context_lens shape")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib().pa_decode_fp8(
+        _dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(k_scales, "k_scales", torch.float32),
+        _dev(v_scales, "v_scales", torch.float32), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, d, B, nb,
+        int(max_context_len), float(scale), dtype_code(query), int(partition_size), int(variant),
+        ws_ptr, ws_bytes, _stream(stream))
+    _check(rc, "pa_decode_fp8")
+    return out
+
+
+def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, k_scales, v_scales, slot_mapping,
+                             stream=None):
+    """key/value [N][H_kv][d] (f32 / f16 / bf16) -> E4M3 pools at slot_mapping (int32 [N]),
+    each element divided by its block's scale and rounded to the nearest code."""
+    torch = _torch()
+    N, Hkv, d = key.shape
+    nb, Hkv2, B, d2 = key_cache.shape
+    if (Hkv2, d2) != (Hkv, d) or value.shape != key.shape or value_cache.shape != key_cache.shape:
+        raise ValueError("shape mismatch")
+    if not (_is_fp8(key_cache) and _is_fp8(value_cache)):
+        raise ValueError("pools must hold E4M3 codes")
+    if k_scales.shape != (nb, Hkv) or v_scales.shape != (nb, Hkv) or slot_mapping.shape != (N,):
+        raise ValueError("scales / slot_mapping shape")
+    rc = _lib().pa_reshape_and_cache_fp8(
+        _dev(key, "key"), _dev(value, "value", key.dtype), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(k_scales, "k_scales", torch.float32),
+        _dev(v_scales, "v_scales", torch.float32), _dev(slot_mapping, "slot_mapping", torch.int32), N,
+        Hkv, d, B, nb, dtype_code(key), _stream(stream))
+    _check(rc, "pa_reshape_and_cache_fp8")
 
 
 def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=None):

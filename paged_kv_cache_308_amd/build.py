@@ -14,12 +14,15 @@ BUILD = os.path.join(ROOT, "_build", "libpa")
 LIB = os.path.join(HERE, "libpa.so")
 
 SOURCES = ["api.cpp", "allocator.cpp", "cache_ops.hip", "decode_valu_f32.hip", "decode_valu_f16.hip",
-           "decode_valu_bf16.hip", "decode_mfma_f16.hip", "decode_mfma_bf16.hip"]
+           "decode_valu_bf16.hip", "decode_valu_fp8_f16.hip", "decode_valu_fp8_bf16.hip",
+           "decode_mfma_f16.hip", "decode_mfma_bf16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
-# packed-fp32 instructions stay off: hipcc may form them from plain float code
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# packed-fp32 instructions stay off: hipcc may form them from plain float code.
+# fp32 division is correctly rounded (the E4M3 scatter picks codes from x / scale).
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-fhip-fp32-correctly-rounded-divide-sqrt"]
 
 
 def _compile(src: str, extra) -> str:

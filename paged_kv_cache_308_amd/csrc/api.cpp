@@ -28,15 +28,24 @@ int check_launch(const char *what) {
     return PA_OK;
 }
 
+// Element bytes of the query / output types (0 for anything else).
 static int elem_bytes(int dtype) {
     return dtype == PA_F32 ? 4 : (dtype == PA_F16 || dtype == PA_BF16) ? 2 : 0;
 }
+
+// Element bytes of every pool type (block moves are bitwise).
+static int pool_elem_bytes(int dtype) { return dtype == PA_FP8_E4M3 ? 1 : elem_bytes(dtype); }
 
 static bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int launch_decode_valu(const DecodeArgs &a) {
+    if (a.kv_fp8) {
+        if (a.dtype == PA_F16) return launch_decode_valu_fp8_f16(a);
+        if (a.dtype == PA_BF16) return launch_decode_valu_fp8_bf16(a);
+        return fail(PA_ERR_UNSUPPORTED, "E4M3 pools with query dtype %d", a.dtype);
+    }
     switch (a.dtype) {
         case PA_F32: return launch_decode_valu_f32(a);
         case PA_F16: return launch_decode_valu_f16(a);
@@ -123,7 +132,7 @@ const char *pa_status_str(int status) {
 
 const char *pa_last_error(void) { return g_err; }
 
-int pa_abi_version(void) { return 2; }
+int pa_abi_version(void) { return 3; }
 
 static int max_partitions_for(int max_context_len, int partition_size) {
     if (partition_size == 0) return 1;
@@ -147,27 +156,29 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
                             nullptr, nullptr);
 }
 
-int pa_decode(void *out, const void *query, const void *key_cache, const void *value_cache,
-              const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
-              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-              int num_blocks, int max_context_len, float scale, int dtype, int partition_size,
-              int variant, void *workspace, size_t workspace_bytes, void *stream) {
-    clear_error();
+// Validation, workspace carving and kernel choice shared by pa_decode and pa_decode_fp8.
+static int decode_common(DecodeArgs &a, int max_context_len, float scale, int variant, void *workspace,
+                         size_t workspace_bytes) {
+    const int num_seqs = a.num_seqs, num_q_heads = a.num_q_heads, num_kv_heads = a.num_kv_heads;
+    const int head_dim = a.head_dim, block_size = a.block_size, num_blocks = a.num_blocks;
+    const int partition_size = a.partition_size, dtype = a.dtype;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
-        max_blocks_per_seq <= 0)
+        a.max_blocks_per_seq <= 0)
         return fail(PA_ERR_INVALID, "bad sizes: S=%d Hq=%d Hkv=%d blocks=%d max_blocks=%d",
-                    num_seqs, num_q_heads, num_kv_heads, num_blocks, max_blocks_per_seq);
+                    num_seqs, num_q_heads, num_kv_heads, num_blocks, a.max_blocks_per_seq);
     if (num_seqs == 0) return PA_OK;
-    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    if (!a.out || !a.query || !a.key_cache || !a.value_cache || !a.block_tables || !a.context_lens)
         return fail(PA_ERR_INVALID, "NULL device pointer");
-    if (elem_bytes(dtype) == 0) return fail(PA_ERR_UNSUPPORTED, "dtype %d", dtype);
+    if (a.kv_fp8 && (!a.k_scales || !a.v_scales)) return fail(PA_ERR_INVALID, "NULL scale array");
+    if (elem_bytes(dtype) == 0 || (a.kv_fp8 && dtype == PA_F32))
+        return fail(PA_ERR_UNSUPPORTED, "dtype %d", dtype);
     if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d", head_dim);
     if (!pow2_in(block_size, 16, 128)) return fail(PA_ERR_UNSUPPORTED, "block_size %d", block_size);
     if (num_q_heads % num_kv_heads)
         return fail(PA_ERR_INVALID, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
                     num_kv_heads);
     const int group = num_q_heads / num_kv_heads;
-    if (!pow2_in(group, 1, 16)) return fail(PA_ERR_UNSUPPORTED, "group size %d", group);
+    if (!pow2_in(group, 1, a.kv_fp8 ? 8 : 16)) return fail(PA_ERR_UNSUPPORTED, "group size %d", group);
     if ((int64_t)num_blocks * num_kv_heads * block_size * head_dim > ((int64_t)1 << 40))
         return fail(PA_ERR_UNSUPPORTED, "pool too large");
     if (!(scale == scale)) return fail(PA_ERR_INVALID, "scale is NaN");
@@ -185,26 +196,9 @@ int pa_decode(void *out, const void *query, const void *key_cache, const void *v
     if (kernel_choice > PA_VARIANT_MFMA || (variant & ~(15 | PA_DECODE_SHARED_KV)))
         return fail(PA_ERR_INVALID, "variant %d", variant);
 
-    DecodeArgs a{};
-    a.out = out;
-    a.query = query;
-    a.key_cache = key_cache;
-    a.value_cache = value_cache;
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.num_seqs = num_seqs;
-    a.num_q_heads = num_q_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.head_dim = head_dim;
-    a.block_size = block_size;
-    a.num_blocks = num_blocks;
-    a.partition_size = partition_size;
     a.max_partitions = max_partitions_for(max_context_len, partition_size);
     a.scale_log2 = scale * 1.4426950408889634f;
     a.cached_kv = (variant & PA_DECODE_SHARED_KV) != 0;
-    a.dtype = dtype;
-    a.stream = stream;
     if (balanced) {
         // partial slots for every wave the device can hold at once
         const int w = device_max_waves();
@@ -224,8 +218,9 @@ int pa_decode(void *out, const void *query, const void *key_cache, const void *v
         workspace_layout(num_seqs, num_q_heads, head_dim, a.max_partitions, workspace, &a.ws_max,
                          &a.ws_sum, &a.ws_acc);
     }
-    const bool mfma_ok = mfma_supported(dtype, head_dim, block_size, group);
+    const bool mfma_ok = !a.kv_fp8 && mfma_supported(dtype, head_dim, block_size, group);
     if (kernel_choice == PA_VARIANT_MFMA) {
+        if (a.kv_fp8) return fail(PA_ERR_UNSUPPORTED, "E4M3 pools run on the vector kernel");
         if (balanced) return fail(PA_ERR_UNSUPPORTED, "balanced split runs on the vector kernel");
         if (!mfma_ok)
             return fail(PA_ERR_UNSUPPORTED, "MFMA kernel needs 16-bit dtype and group >= 2 (group %d)",
@@ -234,6 +229,59 @@ int pa_decode(void *out, const void *query, const void *key_cache, const void *v
     }
     if (kernel_choice == PA_VARIANT_AUTO && mfma_ok && group >= 2 && !balanced) return launch_decode_mfma(a);
     return launch_decode_valu(a);
+}
+
+static DecodeArgs decode_args(void *out, const void *query, const void *key_cache, const void *value_cache,
+                              const int32_t *block_tables, int max_blocks_per_seq,
+                              const int32_t *context_lens, int num_seqs, int num_q_heads,
+                              int num_kv_heads, int head_dim, int block_size, int num_blocks, int dtype,
+                              int partition_size, void *stream) {
+    DecodeArgs a{};
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.num_blocks = num_blocks;
+    a.partition_size = partition_size;
+    a.dtype = dtype;
+    a.stream = stream;
+    return a;
+}
+
+int pa_decode(void *out, const void *query, const void *key_cache, const void *value_cache,
+              const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+              int num_blocks, int max_context_len, float scale, int dtype, int partition_size,
+              int variant, void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    DecodeArgs a = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                               context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               num_blocks, dtype, partition_size, stream);
+    return decode_common(a, max_context_len, scale, variant, workspace, workspace_bytes);
+}
+
+int pa_decode_fp8(void *out, const void *query, const void *key_cache, const void *value_cache,
+                  const float *k_scales, const float *v_scales, const int32_t *block_tables,
+                  int max_blocks_per_seq, const int32_t *context_lens, int num_seqs,
+                  int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                  int max_context_len, float scale, int dtype, int partition_size, int variant,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    DecodeArgs a = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                               context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               num_blocks, dtype, partition_size, stream);
+    a.kv_fp8 = true;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    return decode_common(a, max_context_len, scale, variant, workspace, workspace_bytes);
 }
 
 int pa_reshape_and_cache(const void *key, const void *value, void *key_cache, void *value_cache,
@@ -253,16 +301,34 @@ int pa_reshape_and_cache(const void *key, const void *value, void *key_cache, vo
                                     num_kv_heads, head_dim, block_size, num_blocks, eb, stream);
 }
 
+int pa_reshape_and_cache_fp8(const void *key, const void *value, void *key_cache, void *value_cache,
+                             const float *k_scales, const float *v_scales,
+                             const int32_t *slot_mapping, int num_tokens, int num_kv_heads,
+                             int head_dim, int block_size, int num_blocks, int dtype, void *stream) {
+    clear_error();
+    if (elem_bytes(dtype) == 0) return fail(PA_ERR_UNSUPPORTED, "source dtype %d", dtype);
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID, "bad sizes");
+    if (head_dim % 4) return fail(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 4");
+    if ((int64_t)num_blocks * block_size > INT32_MAX) return fail(PA_ERR_INVALID, "slot ids overflow int32");
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !key_cache || !value_cache || !k_scales || !v_scales || !slot_mapping)
+        return fail(PA_ERR_INVALID, "NULL device pointer");
+    return launch_reshape_and_cache_fp8(key, value, key_cache, value_cache, k_scales, v_scales,
+                                        slot_mapping, num_tokens, num_kv_heads, head_dim, block_size,
+                                        num_blocks, dtype, stream);
+}
+
 int pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *src, const int32_t *dst,
                    int num_pairs, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                    int dtype, void *stream) {
     clear_error();
-    const int eb = elem_bytes(dtype);
+    const int eb = pool_elem_bytes(dtype);
     if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "dtype %d", dtype);
     if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
         return fail(PA_ERR_INVALID, "bad sizes");
-    if (((int64_t)num_kv_heads * block_size * head_dim * eb) % 16)
-        return fail(PA_ERR_UNSUPPORTED, "block bytes must be a multiple of 16");
+    if (((int64_t)num_kv_heads * block_size * head_dim * eb) % 4)
+        return fail(PA_ERR_UNSUPPORTED, "block bytes must be a multiple of 4");
     if (num_pairs == 0) return PA_OK;
     if (!key_cache || !value_cache || !src || !dst) return fail(PA_ERR_INVALID, "NULL device pointer");
     return launch_move_blocks(key_cache, value_cache, key_cache, value_cache, src, dst, num_pairs,
@@ -274,13 +340,13 @@ int pa_swap_blocks(const void *src_key_cache, const void *src_value_cache, void 
                    int num_kv_heads, int head_dim, int block_size, int src_num_blocks,
                    int dst_num_blocks, int dtype, void *stream) {
     clear_error();
-    const int eb = elem_bytes(dtype);
+    const int eb = pool_elem_bytes(dtype);
     if (eb == 0) return fail(PA_ERR_UNSUPPORTED, "dtype %d", dtype);
     if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || src_num_blocks <= 0 ||
         dst_num_blocks <= 0)
         return fail(PA_ERR_INVALID, "bad sizes");
-    if (((int64_t)num_kv_heads * block_size * head_dim * eb) % 16)
-        return fail(PA_ERR_UNSUPPORTED, "block bytes must be a multiple of 16");
+    if (((int64_t)num_kv_heads * block_size * head_dim * eb) % 4)
+        return fail(PA_ERR_UNSUPPORTED, "block bytes must be a multiple of 4");
     if (num_pairs == 0) return PA_OK;
     if (!src_key_cache || !src_value_cache || !dst_key_cache || !dst_value_cache || !src || !dst)
         return fail(PA_ERR_INVALID, "NULL pointer");

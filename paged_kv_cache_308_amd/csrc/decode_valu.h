@@ -29,6 +29,8 @@
 //    tables point at the same blocks (shared prefixes).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "internal.h"
 #include "kernel_common.h"
 
@@ -41,18 +43,112 @@ namespace valu {
 #ifndef PA_VALU_LOADS
 #define PA_VALU_LOADS 4
 #endif
+#ifndef PA_FP8_LOADS
+#define PA_FP8_LOADS 2
+#endif
 constexpr int NW = PA_VALU_WAVES;  // waves per workgroup
 constexpr int NL = PA_VALU_LOADS;  // wave loads (of K and of V) per chunk
 
+// Wave loads per chunk for a storage policy and group size.  E4M3 pools: two (measured
+// on llama-7B-shaped batches: 73 us against 85 us with four, whose 136 registers per
+// lane leave room for one workgroup per CU instead of two), and one with 8 query heads
+// per KV head, whose widened codes and state need the registers.
+template <typename KV, int G>
+constexpr int loads_per_chunk() {
+    return KV::scaled ? (G >= 8 ? PA_FP8_LOADS / 2 : PA_FP8_LOADS) : NL;
+}
+
+// How the kernels read one lane's slice of a token row (SB bytes of K or V).
+//  SameKV<T>:     pools in the query's type T; 16-byte slices of 16 / sizeof(T)
+//                 elements.
+//  E4M3KV<T, SB>: pools of E4M3 codes with a scale per (block, KV head); query and
+//                 output in T (f16 or bf16).  Slices of SB = 16 or 8 codes: 8 halves
+//                 the value sums a lane holds per query head, which keeps grouped
+//                 heads (4 or 8 per KV head) in registers.  Codes are widened exactly
+//                 to T pairs for the packed dot products and to fp32 for the value
+//                 sums; the block scales are applied to the score (keys) and to the
+//                 token's weight (values).
+template <typename T>
+struct SameKV {
+    using Q = T;
+    using Word = u32x4;
+    static constexpr int slice_bytes = 16;
+    static constexpr int kv_bytes = T::bytes;
+    static constexpr int epl = 16 / T::bytes;
+    static constexpr bool scaled = false;
+    struct QSlice {
+        u32x4 w;
+    };
+    __device__ static QSlice load_q(const uint8_t *p) { return {*(const u32x4 *)p}; }
+    __device__ static float dot(const QSlice &q, const Word &k) { return dot16<T>(q.w, k); }
+    __device__ static void values(const Word &v, float (&f)[epl]) { to_f32<T>(v, f); }
+    // elements 4j .. 4j+3 of the slice
+    __device__ static void values4(const Word &v, int j, float (&f)[4]) {
+        float all[epl];
+        to_f32<T>(v, all);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = all[4 * j + e];
+    }
+};
+
+template <typename T, int SB>
+struct E4M3KV {
+    static_assert(T::bytes == 2, "E4M3 pools take a 16-bit query");
+    static_assert(SB == 16 || SB == 8, "slice bytes");
+    using Q = T;
+    using Word = typename std::conditional<SB == 16, u32x4, u32x2>::type;
+    static constexpr int slice_bytes = SB;
+    static constexpr int kv_bytes = 1;
+    static constexpr int epl = SB;
+    static constexpr bool scaled = true;
+    struct QSlice {
+        u32x4 w[SB / 8];  // SB elements of T
+    };
+    __device__ static QSlice load_q(const uint8_t *p) {
+        QSlice q;
+#pragma unroll
+        for (int i = 0; i < SB / 8; ++i) q.w[i] = *(const u32x4 *)(p + 16 * i);
+        return q;
+    }
+    // codes 8j .. 8j+7 of the slice widened to four T pairs
+    __device__ static u32x4 widen8(const Word &k, int j) {
+        const uint32_t a = k[2 * j], b = k[2 * j + 1];  // scalar copies: see to_f32<F16>
+        return u32x4{e4m3_pair<T>(a, false), e4m3_pair<T>(a, true), e4m3_pair<T>(b, false),
+                     e4m3_pair<T>(b, true)};
+    }
+    __device__ static float dot(const QSlice &q, const Word &k) {
+        float s = dot16<T>(q.w[0], widen8(k, 0));
+        if constexpr (SB == 16) s += dot16<T>(q.w[1], widen8(k, 1));
+        return s;
+    }
+    __device__ static void values(const Word &v, float (&f)[SB]) { e4m3_to_f32<SB / 4>(v, f); }
+    // codes 4j .. 4j+3 of the slice
+    __device__ static void values4(const Word &v, int j, float (&f)[4]) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const uint32_t x = v[j];  // scalar copy: see to_f32<F16>
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, true);
+        f[0] = lo[0];
+        f[1] = lo[1];
+        f[2] = hi[0];
+        f[3] = hi[1];
+    }
+};
+
 // One chunk of the online softmax for this lane's token rows.  k[i], v[i] hold this
-// lane's 16 bytes of token row `tok_row0 + i * TPW` (rows at or past `end` are masked
-// when `tail`).  m, l, acc: fp32 running max (exp2 domain), sum of weights and
-// weighted value sums of this lane's rows, for each of the G query heads.
-template <typename T, int G, int NL, int LPT, int TPW>
-__device__ inline void chunk_update(const u32x4 (&qv)[G], const u32x4 (&k)[NL], const u32x4 (&v)[NL],
-                                    int tok_row0, int end, bool tail, float scale_log2,
-                                    float (&m)[G], float (&l)[G], float (&acc)[G][16 / T::bytes]) {
-    constexpr int EPL = 16 / T::bytes;
+// lane's slice of token row `tok_row0 + i * TPW` (rows at or past `end` are masked
+// when `tail`).  ksl[i]: factor from the dot product to the exp2-domain score of the
+// rows of load i (scale * log2(e), times the block's key scale for E4M3 pools);
+// vsc[i]: their value scale (E4M3 pools only).  m, l, acc: fp32 running max (exp2
+// domain), sum of weights and weighted value sums of this lane's rows, for each of the
+// G query heads.
+template <typename KV, int G, int NL, int LPT, int TPW>
+__device__ inline void chunk_update(const typename KV::QSlice (&qv)[G], const typename KV::Word (&k)[NL],
+                                    const typename KV::Word (&v)[NL], const float (&ksl)[NL],
+                                    const float (&vsc)[NL],
+                                    int tok_row0, int end, bool tail, float (&m)[G], float (&l)[G],
+                                    float (&acc)[G][KV::epl]) {
+    constexpr int EPL = KV::epl;
     float sc[G][NL];
     bool valid[NL];
 #pragma unroll
@@ -60,17 +156,13 @@ __device__ inline void chunk_update(const u32x4 (&qv)[G], const u32x4 (&k)[NL], 
         valid[i] = !tail || (tok_row0 + i * TPW < end);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const float dot = row_sum<LPT>(dot16<T>(qv[g], k[i]));
-            sc[g][i] = valid[i] ? dot * scale_log2 : -INFINITY;
+            const float dot = row_sum<LPT>(KV::dot(qv[g], k[i]));
+            sc[g][i] = valid[i] ? dot * ksl[i] : -INFINITY;
         }
     }
-    float vf[NL][EPL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        u32x4 w = v[i];
-        if (tail && !valid[i]) w = u32x4{0, 0, 0, 0};  // never multiply a slot past ctx
-        to_f32<T>(w, vf[i]);
-    }
+    // weights, then the value sums: acc = acc * alpha + sum_i p_i v_i, element by element
+    // in token order; values are widened four at a time, once for all G heads
+    float p[G][NL];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         float cm = sc[g][0];
@@ -79,20 +171,35 @@ __device__ inline void chunk_update(const u32x4 (&qv)[G], const u32x4 (&k)[NL], 
         const float mn = fmaxf(m[g], cm);
         const float ms = mn == -INFINITY ? 0.f : mn;
         const float alpha = fast_exp2(m[g] - ms);
-        float p[NL], psum = 0.f;
+        float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            p[i] = fast_exp2(sc[g][i] - ms);
-            psum += p[i];
+            p[g][i] = fast_exp2(sc[g][i] - ms);
+            psum += p[g][i];
+            if constexpr (KV::scaled) p[g][i] *= vsc[i];  // weight of the dequantised value
         }
         l[g] = l[g] * alpha + psum;
         m[g] = mn;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            float a = acc[g][e] * alpha;
+        for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+    }
+    typename KV::Word w[NL];
 #pragma unroll
-            for (int i = 0; i < NL; ++i) a = fmaf(p[i], vf[i][e], a);
-            acc[g][e] = a;
+    for (int i = 0; i < NL; ++i) {
+        w[i] = v[i];
+        if (tail && !valid[i]) w[i] = typename KV::Word{};  // never multiply a slot past ctx
+    }
+#pragma unroll
+    for (int j = 0; j < EPL / 4; ++j) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            float f[4];
+            KV::values4(w[i], j, f);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[g][4 * j + e] = fmaf(p[g][i], f[e], acc[g][4 * j + e]);
+            }
         }
     }
 }
@@ -122,19 +229,43 @@ __device__ inline void merge_rows(float (&m)[G], float (&l)[G], float (&acc)[G][
     }
 }
 
-template <typename T, int D, int G, bool SPLIT, bool NT>
-__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
+// Launch shape of the partitioned / one-pass kernel per storage policy and group size
+// (the macros exist for tuning builds; the defaults are the measured best).
+#ifndef PA_FP8_WAVES
+#define PA_FP8_WAVES 8
+#endif
+#ifndef PA_FP8_WAVES_PER_EU
+#define PA_FP8_WAVES_PER_EU 1
+#endif
+template <typename KV, int G>
+constexpr int waves_per_group() {
+    return KV::scaled ? PA_FP8_WAVES : NW;
+}
+// Waves per SIMD the register allocation must allow (1 = no constraint).
+template <typename KV, int G>
+constexpr int min_waves_per_eu() {
+    return KV::scaled ? PA_FP8_WAVES_PER_EU : 1;
+}
+
+template <typename KV, int D, int G, bool SPLIT, bool NT>
+__global__ __launch_bounds__((waves_per_group<KV, G>() * 64))
+__attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu_kernel(
     void *__restrict__ out, const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
-    const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
+    const uint8_t *__restrict__ value_cache, const float *__restrict__ k_scales,
+    const float *__restrict__ v_scales, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_max, float *__restrict__ ws_sum,
     float *__restrict__ ws_acc, int max_blocks_per_seq, int num_seqs, int num_kv_heads,
     int log2_block, int num_blocks, int partition_size, int max_partitions, float scale_log2) {
-    constexpr int EB = T::bytes;
-    constexpr int EPL = 16 / EB;            // elements per lane per row
-    constexpr int LPT = D * EB / 16;        // lanes per token row
+    using T = typename KV::Q;
+    constexpr int NWG = waves_per_group<KV, G>();
+    constexpr int QB = T::bytes;            // query / output element bytes
+    constexpr int EPL = KV::epl;            // elements per lane per row
+    constexpr int SB = KV::slice_bytes;
+    constexpr int ROW_BYTES = D * KV::kv_bytes;
+    constexpr int LPT = ROW_BYTES / SB;     // lanes per token row
     constexpr int TPW = 64 / LPT;           // token rows per wave load
-    constexpr int C = NL * TPW;             // tokens per chunk
-    constexpr int ROW_BYTES = D * EB;
+    constexpr int NLK = loads_per_chunk<KV, G>();
+    constexpr int C = NLK * TPW;             // tokens per chunk
 
     const int lane = threadIdx.x & 63;
     // wave-uniform: keeps table lookups on the scalar unit and branches scalar
@@ -166,10 +297,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
     const int64_t block_bytes = (int64_t)num_kv_heads * block_size * ROW_BYTES;
 
     // this lane's slice of every query head of the group
-    u32x4 qv[G];
+    typename KV::QSlice qv[G];
 #pragma unroll
     for (int g = 0; g < G; ++g)
-        qv[g] = *(const u32x4 *)(query + ((int64_t)(s * num_q_heads + kvh * G + g) * D + col * EPL) * EB);
+        qv[g] = KV::load_q(query + ((int64_t)(s * num_q_heads + kvh * G + g) * D + col * EPL) * QB);
 
     float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -194,6 +325,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
     // outstanding load.
     int cached_lb = -1;
     int64_t cached_base = -1;
+    float cached_ks = 0.f, cached_vs = 0.f;  // E4M3 pools: the block's scales
     auto load_offset = [&](int c, int i) -> int64_t {
         const int tok = start + c * C + i * TPW;
         if (tok >= end) return -1;
@@ -205,10 +337,15 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
                 bad = true;
             } else {
                 const int32_t pb = table[lb];
-                if (pb < 0 || pb >= num_blocks)
+                if (pb < 0 || pb >= num_blocks) {
                     bad = true;
-                else
+                } else {
                     cached_base = (int64_t)pb * block_bytes + head_off;
+                    if constexpr (KV::scaled) {
+                        cached_ks = k_scales[(int64_t)pb * num_kv_heads + kvh];
+                        cached_vs = v_scales[(int64_t)pb * num_kv_heads + kvh];
+                    }
+                }
             }
         }
         if (cached_base < 0) return -1;
@@ -216,46 +353,53 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
     };
 
     struct Chunk {
-        u32x4 k[NL], v[NL];
+        typename KV::Word k[NLK], v[NLK];
+        float ksl[NLK], vsc[NLK];
     };
     auto issue = [&](Chunk &b, int c) {
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
+        for (int i = 0; i < NLK; ++i) {
             int64_t off = load_offset(c, i);
+            b.ksl[i] = scale_log2;
+            b.vsc[i] = 1.f;
+            if constexpr (KV::scaled) {
+                b.ksl[i] = off < 0 ? 0.f : scale_log2 * cached_ks;
+                b.vsc[i] = off < 0 ? 0.f : cached_vs;
+            }
             off = off < 0 ? 0 : off;
-            b.k[i] = kv_load<NT>((const u32x4 *)(key_cache + off + lane * 16));
-            b.v[i] = kv_load<NT>((const u32x4 *)(value_cache + off + lane * 16));
+            b.k[i] = kv_load<NT>((const typename KV::Word *)(key_cache + off + lane * SB));
+            b.v[i] = kv_load<NT>((const typename KV::Word *)(value_cache + off + lane * SB));
         }
     };
     auto consume = [&](const Chunk &b, int c, bool tail) {
-        chunk_update<T, G, NL, LPT, TPW>(qv, b.k, b.v, start + c * C + row, end, tail, scale_log2, m, l,
-                                         acc);
+        chunk_update<KV, G, NLK, LPT, TPW>(qv, b.k, b.v, b.ksl, b.vsc, start + c * C + row, end, tail, m, l,
+                                          acc);
     };
 
-    // This wave's full chunks are wave, wave + NW, ...  The steady-state loop always
+    // This wave's full chunks are wave, wave + NWG, ...  The steady-state loop always
     // has a next chunk to prefetch, so its loads are unconditional and the compiler
     // waits only for the chunk being reduced; the last one or two run after it.
     {
-        const int mine = nfull > wave ? (nfull - wave + NW - 1) / NW : 0;
+        const int mine = nfull > wave ? (nfull - wave + NWG - 1) / NWG : 0;
         Chunk A, Bf;
         if (mine > 0) {
             issue(A, wave);
             int j = 0;
             for (; j + 2 < mine; j += 2) {
-                issue(Bf, wave + (j + 1) * NW);
-                consume(A, wave + j * NW, false);
-                issue(A, wave + (j + 2) * NW);
-                consume(Bf, wave + (j + 1) * NW, false);
+                issue(Bf, wave + (j + 1) * NWG);
+                consume(A, wave + j * NWG, false);
+                issue(A, wave + (j + 2) * NWG);
+                consume(Bf, wave + (j + 1) * NWG, false);
             }
             if (j + 1 < mine) {
-                issue(Bf, wave + (j + 1) * NW);
-                consume(A, wave + j * NW, false);
-                consume(Bf, wave + (j + 1) * NW, false);
+                issue(Bf, wave + (j + 1) * NWG);
+                consume(A, wave + j * NWG, false);
+                consume(Bf, wave + (j + 1) * NWG, false);
             } else {
-                consume(A, wave + j * NW, false);
+                consume(A, wave + j * NWG, false);
             }
         }
-        if (has_tail && (nfull % NW) == wave) {
+        if (has_tail && (nfull % NWG) == wave) {
             issue(A, nfull);
             consume(A, nfull, true);
         }
@@ -264,7 +408,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
     merge_rows<G, EPL, LPT>(m, l, acc);
 
     // merge the waves through LDS
-    __shared__ float sm_m[NW][G], sm_l[NW][G], sm_acc[NW][G][D];
+    __shared__ float sm_m[NWG][G], sm_l[NWG][G], sm_acc[NWG][G][D];
     __shared__ int sm_bad;
     if (threadIdx.x == 0) sm_bad = 0;
     __syncthreads();
@@ -282,16 +426,16 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(
     }
     __syncthreads();
     const bool any_bad = sm_bad != 0;
-    for (int t = threadIdx.x; t < G * D; t += NW * 64) {
+    for (int t = threadIdx.x; t < G * D; t += NWG * 64) {
         const int g = t / D;
         const int j = t - g * D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][g]);
+        for (int w = 0; w < NWG; ++w) M = fmaxf(M, sm_m[w][g]);
         const float Ms = M == -INFINITY ? 0.f : M;
         float Lsum = 0.f, A = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
+        for (int w = 0; w < NWG; ++w) {
             const float f = fast_exp2(sm_m[w][g] - Ms);
             Lsum += sm_l[w][g] * f;
             A += sm_acc[w][g][j] * f;
@@ -369,19 +513,22 @@ constexpr int NWB = 4;               // waves per workgroup of the balanced kern
 constexpr int BAL_MAX_SEQS = 4096;   // sequences per batch in balanced mode
 constexpr int BAL_HDR = 4;           // header ints before the prefix
 
-template <typename T, int D, int G, bool NT>
+template <typename KV, int D, int G, bool NT>
 __global__ __launch_bounds__(NWB * 64) void decode_balanced_kernel(
     const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
-    const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
+    const uint8_t *__restrict__ value_cache, const float *__restrict__ k_scales,
+    const float *__restrict__ v_scales, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int32_t *__restrict__ ws_hdr, float *__restrict__ ws_max,
     float *__restrict__ ws_sum, float *__restrict__ ws_acc, int max_blocks_per_seq, int num_seqs,
     int num_kv_heads, int log2_block, int num_blocks, float scale_log2) {
-    constexpr int EB = T::bytes;
-    constexpr int EPL = 16 / EB;
-    constexpr int LPT = D * EB / 16;
+    constexpr int QB = KV::Q::bytes;
+    constexpr int EPL = KV::epl;
+    constexpr int SB = KV::slice_bytes;
+    constexpr int ROW_BYTES = D * KV::kv_bytes;
+    constexpr int LPT = ROW_BYTES / SB;
     constexpr int TPW = 64 / LPT;
-    constexpr int C = NL * TPW;
-    constexpr int ROW_BYTES = D * EB;
+    constexpr int NLK = loads_per_chunk<KV, G>();
+    constexpr int C = NLK * TPW;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -469,7 +616,9 @@ __global__ __launch_bounds__(NWB * 64) void decode_balanced_kernel(
     const int64_t block_bytes = (int64_t)num_kv_heads * block_size * ROW_BYTES;
 
     struct Chunk {
-        u32x4 q[G], k[NL], v[NL];
+        typename KV::QSlice q[G];
+        typename KV::Word k[NLK], v[NLK];
+        float ksl[NLK], vsc[NLK];
         Pos p;
         bool bad;
     };
@@ -485,10 +634,13 @@ __global__ __launch_bounds__(NWB * 64) void decode_balanced_kernel(
         const int32_t *table = block_tables + (int64_t)s * max_blocks_per_seq;
         int cached_lb = -1;
         int64_t cached_base = 0;
+        float cached_ks = 0.f, cached_vs = 0.f;
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
+        for (int i = 0; i < NLK; ++i) {
             const int tok = p.c * C + i * TPW;
             int64_t off = 0;
+            b.ksl[i] = scale_log2;
+            b.vsc[i] = 1.f;
             if (live && tok < p.ctx) {
                 const int lb = tok >> log2_block;
                 if (lb != cached_lb) {
@@ -496,21 +648,30 @@ __global__ __launch_bounds__(NWB * 64) void decode_balanced_kernel(
                     cached_base = -1;
                     if (lb < max_blocks_per_seq) {
                         const int32_t pb = table[lb];
-                        if (pb >= 0 && pb < num_blocks)
+                        if (pb >= 0 && pb < num_blocks) {
                             cached_base = (int64_t)pb * block_bytes + (int64_t)kvh * block_size * ROW_BYTES;
+                            if constexpr (KV::scaled) {
+                                cached_ks = k_scales[(int64_t)pb * num_kv_heads + kvh];
+                                cached_vs = v_scales[(int64_t)pb * num_kv_heads + kvh];
+                            }
+                        }
                     }
                 }
                 if (cached_base < 0)
                     b.bad = true;
                 else
                     off = cached_base + (int64_t)(tok & (block_size - 1)) * ROW_BYTES;
+                if constexpr (KV::scaled) {
+                    b.ksl[i] = scale_log2 * cached_ks;
+                    b.vsc[i] = cached_vs;
+                }
             }
-            b.k[i] = kv_load<NT>((const u32x4 *)(key_cache + off + lane * 16));
-            b.v[i] = kv_load<NT>((const u32x4 *)(value_cache + off + lane * 16));
+            b.k[i] = kv_load<NT>((const typename KV::Word *)(key_cache + off + lane * SB));
+            b.v[i] = kv_load<NT>((const typename KV::Word *)(value_cache + off + lane * SB));
         }
 #pragma unroll
         for (int g = 0; g < G; ++g)
-            b.q[g] = *(const u32x4 *)(query + ((int64_t)(s * num_q_heads + kvh * G + g) * D + col * EPL) * EB);
+            b.q[g] = KV::load_q(query + ((int64_t)(s * num_q_heads + kvh * G + g) * D + col * EPL) * QB);
     };
 
     float m[G], l[G], acc[G][EPL];
@@ -529,8 +690,8 @@ __global__ __launch_bounds__(NWB * 64) void decode_balanced_kernel(
     auto consume = [&](const Chunk &b, int g) {
         const Pos &p = b.p;
         const int tok0 = p.c * C;
-        chunk_update<T, G, NL, LPT, TPW>(b.q, b.k, b.v, tok0 + row, p.ctx, tok0 + C > p.ctx, scale_log2, m,
-                                         l, acc);
+        chunk_update<KV, G, NLK, LPT, TPW>(b.q, b.k, b.v, b.ksl, b.vsc, tok0 + row, p.ctx, tok0 + C > p.ctx,
+                                          m, l, acc);
         item_bad |= b.bad;
         if (p.c == p.n - 1 || g == g_end - 1) {
             // this wave's share of the item is complete: write its partial
@@ -632,73 +793,96 @@ int balanced_workers(K kernel) {
     return cus * (per_cu > 0 ? per_cu : 1) * NWB;
 }
 
-template <typename T, int D, int G, bool NT>
+template <typename KV, int D, int G, bool NT>
 int launch_balanced(const DecodeArgs &a) {
-    auto kernel = decode_balanced_kernel<T, D, G, NT>;
+    auto kernel = decode_balanced_kernel<KV, D, G, NT>;
     static int workers = 0;  // per instantiation; the library runs on one device type
     if (workers == 0) workers = balanced_workers(kernel);
     if (workers <= 0) return fail(PA_ERR_HIP, "occupancy query failed");
     if (workers > a.max_workers) workers = a.max_workers - a.max_workers % NWB;
     hipStream_t st = (hipStream_t)a.stream;
     hipLaunchKernelGGL(kernel, dim3(workers / NWB), dim3(NWB * 64), 0, st, (const uint8_t *)a.query,
-                       (const uint8_t *)a.key_cache, (const uint8_t *)a.value_cache, a.block_tables,
-                       a.context_lens, a.ws_hdr, a.ws_max, a.ws_sum, a.ws_acc, a.max_blocks_per_seq,
-                       a.num_seqs, a.num_kv_heads, __builtin_ctz(a.block_size), a.num_blocks,
-                       a.scale_log2);
+                       (const uint8_t *)a.key_cache, (const uint8_t *)a.value_cache, a.k_scales,
+                       a.v_scales, a.block_tables, a.context_lens, a.ws_hdr, a.ws_max, a.ws_sum, a.ws_acc,
+                       a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads, __builtin_ctz(a.block_size),
+                       a.num_blocks, a.scale_log2);
     int rc = check_launch("decode_balanced");
     if (rc != PA_OK) return rc;
-    hipLaunchKernelGGL((balanced_merge_kernel<T, D, G>), dim3(a.num_seqs * a.num_q_heads), dim3(64), 0, st,
-                       a.out, a.ws_hdr, a.ws_max, a.ws_sum, a.ws_acc, a.context_lens, a.num_seqs,
-                       a.num_kv_heads);
+    hipLaunchKernelGGL((balanced_merge_kernel<typename KV::Q, D, G>), dim3(a.num_seqs * a.num_q_heads),
+                       dim3(64), 0, st, a.out, a.ws_hdr, a.ws_max, a.ws_sum, a.ws_acc, a.context_lens,
+                       a.num_seqs, a.num_kv_heads);
     return check_launch("balanced_merge");
 }
 
-template <typename T, int D, int G, bool NT>
+template <typename KV, int D, int G, bool NT>
 int launch_t(const DecodeArgs &a) {
-    if (a.partition_size < 0) return launch_balanced<T, D, G, NT>(a);
+    if (a.partition_size < 0) return launch_balanced<KV, D, G, NT>(a);
     const int log2b = __builtin_ctz(a.block_size);
     const bool split = a.partition_size > 0;
     const unsigned grid = (unsigned)a.num_seqs * a.num_kv_heads * (split ? a.max_partitions : 1);
     hipStream_t st = (hipStream_t)a.stream;
     if (split) {
-        hipLaunchKernelGGL((decode_valu_kernel<T, D, G, true, NT>), dim3(grid), dim3(NW * 64), 0, st,
+        hipLaunchKernelGGL((decode_valu_kernel<KV, D, G, true, NT>), dim3(grid),
+                           dim3(waves_per_group<KV, G>() * 64), 0, st,
                            a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
-                           (const uint8_t *)a.value_cache, a.block_tables, a.context_lens, a.ws_max,
-                           a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads,
-                           log2b, a.num_blocks, a.partition_size, a.max_partitions, a.scale_log2);
+                           (const uint8_t *)a.value_cache, a.k_scales, a.v_scales, a.block_tables,
+                           a.context_lens, a.ws_max, a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs,
+                           a.num_kv_heads, log2b, a.num_blocks, a.partition_size, a.max_partitions,
+                           a.scale_log2);
         const int rc = check_launch("decode_valu (partitions)");
         if (rc != PA_OK) return rc;
         return launch_lse_merge(a);
     }
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, G, false, NT>), dim3(grid), dim3(NW * 64), 0, st,
+    hipLaunchKernelGGL((decode_valu_kernel<KV, D, G, false, NT>), dim3(grid),
+                       dim3(waves_per_group<KV, G>() * 64), 0, st,
                        a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
-                       (const uint8_t *)a.value_cache, a.block_tables, a.context_lens, nullptr,
-                       nullptr, nullptr, a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads, log2b,
-                       a.num_blocks, 0, 1, a.scale_log2);
+                       (const uint8_t *)a.value_cache, a.k_scales, a.v_scales, a.block_tables,
+                       a.context_lens, nullptr, nullptr, nullptr, a.max_blocks_per_seq, a.num_seqs,
+                       a.num_kv_heads, log2b, a.num_blocks, 0, 1, a.scale_log2);
     return check_launch("decode_valu");
 }
 
-template <typename T, int D, int G>
+template <typename KV, int D, int G>
 int by_cache(const DecodeArgs &a) {
-    return a.cached_kv ? launch_t<T, D, G, false>(a) : launch_t<T, D, G, true>(a);
+    return a.cached_kv ? launch_t<KV, D, G, false>(a) : launch_t<KV, D, G, true>(a);
 }
 
-template <typename T, int D>
+template <typename KV, int D>
 int by_group(const DecodeArgs &a) {
     switch (a.num_q_heads / a.num_kv_heads) {
-        case 1: return by_cache<T, D, 1>(a);
-        case 2: return by_cache<T, D, 2>(a);
-        case 4: return by_cache<T, D, 4>(a);
-        case 8: return by_cache<T, D, 8>(a);
-        case 16: return by_cache<T, D, 16>(a);
+        case 1: return by_cache<KV, D, 1>(a);
+        case 2: return by_cache<KV, D, 2>(a);
+        case 4: return by_cache<KV, D, 4>(a);
+        case 8: return by_cache<KV, D, 8>(a);
+        case 16: return by_cache<KV, D, 16>(a);
     }
     return fail(PA_ERR_UNSUPPORTED, "group %d", a.num_q_heads / a.num_kv_heads);
 }
 
-template <typename T>
+template <typename KV>
 int by_dim(const DecodeArgs &a) {
-    if (a.head_dim == 64) return by_group<T, 64>(a);
-    if (a.head_dim == 128) return by_group<T, 128>(a);
+    if (a.head_dim == 64) return by_group<KV, 64>(a);
+    if (a.head_dim == 128) return by_group<KV, 128>(a);
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d", a.head_dim);
+}
+
+// E4M3 pools: 16-code slices for 1 or 2 query heads per KV head, 8-code slices for 4
+// and 8 (a lane then holds 8 fp32 value sums per head, as with 16-bit pools).
+template <typename T, int D>
+int e4m3_by_group(const DecodeArgs &a) {
+    switch (a.num_q_heads / a.num_kv_heads) {
+        case 1: return by_cache<E4M3KV<T, 16>, D, 1>(a);
+        case 2: return by_cache<E4M3KV<T, 16>, D, 2>(a);
+        case 4: return by_cache<E4M3KV<T, 8>, D, 4>(a);
+        case 8: return by_cache<E4M3KV<T, 8>, D, 8>(a);
+    }
+    return fail(PA_ERR_UNSUPPORTED, "group %d with E4M3 pools", a.num_q_heads / a.num_kv_heads);
+}
+
+template <typename T>
+int e4m3_by_dim(const DecodeArgs &a) {
+    if (a.head_dim == 64) return e4m3_by_group<T, 64>(a);
+    if (a.head_dim == 128) return e4m3_by_group<T, 128>(a);
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d", a.head_dim);
 }
 

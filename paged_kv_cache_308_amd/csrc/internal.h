@@ -19,6 +19,8 @@ struct DecodeArgs {
     const void *query;
     const void *key_cache;
     const void *value_cache;
+    const float *k_scales;  // E4M3 pools: [num_blocks][H_kv] scales (else null)
+    const float *v_scales;
     const int32_t *block_tables;
     const int32_t *context_lens;
     float *ws_max;   // [S][H_q][P] running max (log2 domain), partitioned runs only
@@ -37,7 +39,8 @@ struct DecodeArgs {
     int max_partitions;  // grid extent along partitions (1 for one pass)
     float scale_log2;    // scale * log2(e)
     bool cached_kv;      // K/V through cacheable loads (blocks shared between sequences)
-    int dtype;
+    int dtype;           // query / output type
+    bool kv_fp8;         // pools hold E4M3 codes (k_scales / v_scales set)
     void *stream;
 };
 
@@ -62,6 +65,12 @@ int launch_reshape_and_cache(const void *key, const void *value, void *key_cache
                              void *value_cache, const int32_t *slot_mapping, int num_tokens,
                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
                              int elem_bytes, void *stream);
+// E4M3 scatter; src_dtype is the pa_dtype of key / value (f32, f16 or bf16).
+int launch_reshape_and_cache_fp8(const void *key, const void *value, void *key_cache,
+                                 void *value_cache, const float *k_scales, const float *v_scales,
+                                 const int32_t *slot_mapping, int num_tokens, int num_kv_heads,
+                                 int head_dim, int block_size, int num_blocks, int src_dtype,
+                                 void *stream);
 int launch_move_blocks(const void *src_key, const void *src_value, void *dst_key, void *dst_value,
                        const int32_t *src, const int32_t *dst, int num_pairs, int num_kv_heads,
                        int head_dim, int block_size, int src_blocks, int dst_blocks, int elem_bytes,
@@ -74,6 +83,8 @@ int launch_decode_valu_bf16(const DecodeArgs &a);
 int launch_lse_merge_f32(const DecodeArgs &a);
 int launch_lse_merge_f16(const DecodeArgs &a);
 int launch_lse_merge_bf16(const DecodeArgs &a);
+int launch_decode_valu_fp8_f16(const DecodeArgs &a);
+int launch_decode_valu_fp8_bf16(const DecodeArgs &a);
 int launch_decode_mfma_f16(const DecodeArgs &a);
 int launch_decode_mfma_bf16(const DecodeArgs &a);
 

@@ -7,6 +7,7 @@
 namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -86,8 +87,8 @@ __device__ inline float dot16<BF16>(const u32x4 &a, const u32x4 &b) {
 // K/V rows are read once per decode step unless blocks are shared between sequences:
 // non-temporal loads keep them from displacing reusable lines (measured +8-10% on
 // streaming batches); plain loads let sequences that share prefix blocks hit in L2.
-template <bool NT>
-__device__ inline u32x4 kv_load(const u32x4 *p) {
+template <bool NT, typename W>
+__device__ inline W kv_load(const W *p) {
     if constexpr (NT)
         return __builtin_nontemporal_load(p);
     else
@@ -100,17 +101,70 @@ __device__ inline float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over groups of N adjacent lanes (N = 8, 16, 32); every lane of a group gets the
-// same bits (each step adds a value to its mirror image, which commutes exactly).
+// Sum over groups of N adjacent lanes (N = 4, 8, 16, 32); every lane of a group gets
+// the same bits (each step adds a value to its mirror image, which commutes exactly).
 template <int N>
 __device__ inline float row_sum(float v) {
-    static_assert(N == 8 || N == 16 || N == 32, "group size");
+    static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
     v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
     v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
-    v += dpp<0x141>(v);  // row_half_mirror: the other quad of each 8
+    if (N >= 8) v += dpp<0x141>(v);  // row_half_mirror: the other quad of each 8
     if (N >= 16) v += dpp<0x140>(v);  // row_mirror: the other half of each 16
     if (N >= 32) v += __shfl_xor(v, 16);
     return v;
+}
+
+// ---------------------------------------------------------------- E4M3 codes
+// OCP E4M3 (bias 7, 3 fraction bits, no infinities, 0x7F / 0xFF NaN).  The gfx950
+// conversion instructions widen two codes at a time, exactly (every E4M3 value is an
+// f16, bf16 and f32 value); the scale operand is 1.
+
+// Codes 2h, 2h+1 of a 4-code word (h = 0, 1) widened to a 16-bit pair.
+template <typename T>
+__device__ inline uint32_t e4m3_pair(uint32_t w, bool hi);
+template <>
+__device__ inline uint32_t e4m3_pair<F16>(uint32_t w, bool hi) {
+    return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, false));
+}
+template <>
+__device__ inline uint32_t e4m3_pair<BF16>(uint32_t w, bool hi) {
+    return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
+}
+
+// 4 * N codes (N = 4: u32x4, N = 2: u32x2) -> fp32.
+template <int N, typename W>
+__device__ inline void e4m3_to_f32(const W &w, float (&f)[4 * N]) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t x = w[i];  // scalar copy: see to_f32<F16>
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, true);
+        f[4 * i] = lo[0];
+        f[4 * i + 1] = lo[1];
+        f[4 * i + 2] = hi[0];
+        f[4 * i + 3] = hi[1];
+    }
+}
+
+// The E4M3 code nearest to y: round to nearest, ties to the even code; |y| >= 448 and
+// infinities saturate to the largest finite code of y's sign; NaN gives 0x7F.
+__device__ inline uint32_t e4m3_encode(float y) {
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return 0x7fu;        // NaN
+    if (a >= 0x43e00000u) return sign | 0x7eu; // 448 = 1.75 * 2^8 and above
+    if (a < 0x3c800000u) {                      // below 2^-6: multiples of 2^-9
+        const float q = rintf(__uint_as_float(a) * 512.f);  // exact product, ties to even
+        return sign | (uint32_t)q;              // 8 -> 0x08 = 2^-6, the first normal
+    }
+    // normal: keep 3 of the 23 fraction bits, ties to even (a carry bumps the exponent)
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+    const uint32_t e = (r >> 23) - 120u;        // rebias 127 -> 7
+    return sign | (e << 3) | ((r >> 20) & 7u);
 }
 
 // 2^x on the hardware transcendental unit (exact 1 at 0, 0 at -inf).

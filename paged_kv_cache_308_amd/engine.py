@@ -19,21 +19,42 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (PA_VARIANT_AUTO, Allocator, pa_copy_blocks, pa_decode, pa_decode_workspace_bytes,
-               pa_reshape_and_cache, pa_swap_blocks)
+from . import (PA_VARIANT_AUTO, Allocator, pa_copy_blocks, pa_decode, pa_decode_fp8,
+               pa_decode_workspace_bytes, pa_reshape_and_cache, pa_reshape_and_cache_fp8,
+               pa_swap_blocks)
+
+FP8_NAN_CODE = 0x7F
+
+
+def _scale_pools(k_scales: torch.Tensor, v_scales: torch.Tensor):
+    """[num_blocks][H_kv] scale arrays viewed as pools of 1x1 float32 blocks, so the block
+    copy and swap calls move a block's scales with it."""
+    nb, h = k_scales.shape
+    return k_scales.view(nb, h, 1, 1), v_scales.view(nb, h, 1, 1)
 
 
 class PagedKVCache:
+    """Device K/V pools of one layer and the host allocator.  dtype=torch.uint8 holds
+    E4M3 codes, with k_scales / v_scales float32 [num_blocks][H_kv] (one per block and
+    KV head, set by the owner before a block's first write; default 1)."""
+
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int,
                  dtype: torch.dtype, device="cuda", fill: Optional[float] = None):
         self.num_blocks, self.num_kv_heads = num_blocks, num_kv_heads
         self.head_dim, self.block_size, self.dtype = head_dim, block_size, dtype
+        self.fp8 = dtype == torch.uint8
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
         self.key_cache = torch.empty(shape, dtype=dtype, device=device)
         self.value_cache = torch.empty(shape, dtype=dtype, device=device)
         if fill is not None:
+            if self.fp8:  # NaN poison is the NaN code; any other fill is zero
+                fill = FP8_NAN_CODE if fill != fill else 0
             self.key_cache.fill_(fill)
             self.value_cache.fill_(fill)
+        self.k_scales = self.v_scales = None
+        if self.fp8:
+            self.k_scales = torch.ones((num_blocks, num_kv_heads), dtype=torch.float32, device=device)
+            self.v_scales = torch.ones_like(self.k_scales)
         self.alloc = Allocator(num_blocks, block_size)
         self.device = torch.device(device)
 
@@ -66,12 +87,18 @@ class PagedKVCache:
 
     def copy(self, cow_src, cow_dst, stream=None) -> None:
         if len(cow_src):
-            pa_copy_blocks(self.key_cache, self.value_cache, _as_dev(cow_src, self.device),
-                           _as_dev(cow_dst, self.device), stream)
+            src, dst = _as_dev(cow_src, self.device), _as_dev(cow_dst, self.device)
+            pa_copy_blocks(self.key_cache, self.value_cache, src, dst, stream)
+            if self.fp8:
+                pa_copy_blocks(*_scale_pools(self.k_scales, self.v_scales), src, dst, stream)
 
     def write(self, key: torch.Tensor, value: torch.Tensor, slots, stream=None) -> None:
-        pa_reshape_and_cache(key, value, self.key_cache, self.value_cache,
-                             _as_dev(slots, self.device), stream)
+        if self.fp8:
+            pa_reshape_and_cache_fp8(key, value, self.key_cache, self.value_cache, self.k_scales,
+                                     self.v_scales, _as_dev(slots, self.device), stream)
+        else:
+            pa_reshape_and_cache(key, value, self.key_cache, self.value_cache,
+                                 _as_dev(slots, self.device), stream)
 
     def workspace(self, num_seqs: int, num_q_heads: int, max_context_len: int,
                   partition_size: int) -> Optional[torch.Tensor]:
@@ -86,9 +113,15 @@ class PagedKVCache:
         if partition_size and workspace is None:
             workspace = self.workspace(query.shape[0], query.shape[1], max_context_len,
                                        partition_size)
-        pa_decode(out, query, self.key_cache, self.value_cache, block_tables, context_lens, scale,
-                  max_context_len=max_context_len, partition_size=partition_size, variant=variant,
-                  workspace=workspace, stream=stream)
+        if self.fp8:
+            pa_decode_fp8(out, query, self.key_cache, self.value_cache, self.k_scales,
+                          self.v_scales, block_tables, context_lens, scale,
+                          max_context_len=max_context_len, partition_size=partition_size,
+                          variant=variant, workspace=workspace, stream=stream)
+        else:
+            pa_decode(out, query, self.key_cache, self.value_cache, block_tables, context_lens,
+                      scale, max_context_len=max_context_len, partition_size=partition_size,
+                      variant=variant, workspace=workspace, stream=stream)
         return out
 
 
@@ -103,6 +136,11 @@ class HostKVPool:
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
         self.key_cache = torch.empty(shape, dtype=dtype, pin_memory=True)
         self.value_cache = torch.empty(shape, dtype=dtype, pin_memory=True)
+        self.k_scales = self.v_scales = None
+        if dtype == torch.uint8:  # E4M3 codes: the blocks' scales travel with them
+            self.k_scales = torch.ones((num_blocks, num_kv_heads), dtype=torch.float32,
+                                       pin_memory=True)
+            self.v_scales = torch.ones_like(self.k_scales).pin_memory()
         self.alloc = Allocator(num_blocks, block_size)
         self.num_blocks, self.block_size = num_blocks, block_size
 
@@ -114,9 +152,13 @@ def swap_out(cache: PagedKVCache, host: HostKVPool, seq: int, stream=None) -> in
     table, ctx = cache.alloc.block_table(seq)
     hseq, hids = host.alloc.adopt(ctx)
     if len(table):
-        pa_swap_blocks(cache.key_cache, cache.value_cache, host.key_cache, host.value_cache,
-                       _as_dev(np.asarray(table, np.int32), cache.device),
-                       _as_dev(hids, cache.device), stream)
+        src = _as_dev(np.asarray(table, np.int32), cache.device)
+        dst = _as_dev(hids, cache.device)
+        pa_swap_blocks(cache.key_cache, cache.value_cache, host.key_cache, host.value_cache, src,
+                       dst, stream)
+        if cache.fp8:
+            pa_swap_blocks(*_scale_pools(cache.k_scales, cache.v_scales),
+                           *_scale_pools(host.k_scales, host.v_scales), src, dst, stream)
     cache.free_seq(seq)
     return hseq
 
@@ -126,9 +168,13 @@ def swap_in(cache: PagedKVCache, host: HostKVPool, hseq: int, stream=None) -> in
     table, ctx = host.alloc.block_table(hseq)
     seq, ids = cache.alloc.adopt(ctx)
     if len(table):
-        pa_swap_blocks(host.key_cache, host.value_cache, cache.key_cache, cache.value_cache,
-                       _as_dev(np.asarray(table, np.int32), cache.device),
-                       _as_dev(ids, cache.device), stream)
+        src = _as_dev(np.asarray(table, np.int32), cache.device)
+        dst = _as_dev(ids, cache.device)
+        pa_swap_blocks(host.key_cache, host.value_cache, cache.key_cache, cache.value_cache, src,
+                       dst, stream)
+        if cache.fp8:
+            pa_swap_blocks(*_scale_pools(host.k_scales, host.v_scales),
+                           *_scale_pools(cache.k_scales, cache.v_scales), src, dst, stream)
     host.alloc.free_seq(hseq)
     return seq
 
@@ -140,7 +186,7 @@ def _as_dev(a, device) -> torch.Tensor:
 
 
 def to_torch(a: np.ndarray, dtype: str) -> torch.Tensor:
-    """Storage numpy array (f32 / f16 / bf16 bits as uint16) -> CPU tensor."""
+    """Storage numpy array (f32 / f16 / bf16 bits as uint16 / E4M3 codes) -> CPU tensor."""
     a = np.ascontiguousarray(a)
     if dtype == "bf16":
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
@@ -148,4 +194,4 @@ def to_torch(a: np.ndarray, dtype: str) -> torch.Tensor:
 
 
 TORCH_DTYPE: Dict[str, torch.dtype] = {"f32": torch.float32, "f16": torch.float16,
-                                       "bf16": torch.bfloat16}
+                                       "bf16": torch.bfloat16, "fp8": torch.uint8}

@@ -54,11 +54,16 @@ class DeviceBatch:
 
 def replay(batch, poison: bool = True, device="cuda",
            num_blocks: Optional[int] = None) -> DeviceBatch:
-    """`batch` carries .workload (sizes), .free_order, .script, .q, .append_k, .append_v."""
+    """`batch` carries .workload (sizes), .free_order, .script, .q, .append_k, .append_v
+    (and .fp8_scales, the K and V block scales, when the workload's pools are E4M3)."""
     w = batch.workload
-    tdt = TORCH_DTYPE[w.dtype]
-    cache = PagedKVCache(num_blocks or w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, tdt,
-                         device, fill=float("nan") if poison else 0.0)
+    kv = getattr(w, "kv", w.dtype)
+    cache = PagedKVCache(num_blocks or w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
+                         TORCH_DTYPE[kv], device, fill=float("nan") if poison else 0.0)
+    if kv == "fp8":
+        ks, vs = batch.fp8_scales
+        cache.k_scales.copy_(torch.from_numpy(ks[:cache.num_blocks]))
+        cache.v_scales.copy_(torch.from_numpy(vs[:cache.num_blocks]))
     cache.set_free_order(batch.free_order)
     ids = {}
     slots: List[np.ndarray] = []

@@ -434,7 +434,9 @@ def pin_fp8_encode(o):
 
 class Fp8Case:
     """E4M3 pools with random per-(block, KV head) scales, placed through a random
-    permutation of blocks; slots past each context hold the NaN code."""
+    permutation of blocks; slots past each context hold the NaN code.  Tokens are
+    standard normal numbers x stored as torch's E4M3 rounding of x / s (s the scale of
+    the block and head holding them), so dequantised values are O(1)."""
 
     def __init__(self, rng, lens, Hq, Hkv, d, B, qdtype):
         self.lens = [int(x) for x in lens]
@@ -460,16 +462,19 @@ class Fp8Case:
         vals = torch_fp8_values()
         self.kf, self.vf = [], []  # dequantised tokens [n][H_kv][d] in logical order
         for s, n in enumerate(self.lens):
-            kcodes = torch_fp8_encode(rng.standard_normal((n, Hkv, d), dtype=np.float32) * 60)
-            vcodes = torch_fp8_encode(rng.standard_normal((n, Hkv, d), dtype=np.float32) * 60)
+            kx = rng.standard_normal((n, Hkv, d), dtype=np.float32)
+            vx = rng.standard_normal((n, Hkv, d), dtype=np.float32)
             kf = np.empty((n, Hkv, d))
             vf = np.empty((n, Hkv, d))
             for t in range(n):
                 b = self.tables[s, t // B]
-                self.kc[b, :, t % B, :] = kcodes[t]
-                self.vc[b, :, t % B, :] = vcodes[t]
-                kf[t] = vals[kcodes[t]] * self.ks[b][:, None].astype(np.float64)
-                vf[t] = vals[vcodes[t]] * self.vs[b][:, None].astype(np.float64)
+                ks, vs = self.ks[b][:, None], self.vs[b][:, None]
+                kcode = torch_fp8_encode((torch.from_numpy(kx[t]) / torch.from_numpy(ks)).numpy())
+                vcode = torch_fp8_encode((torch.from_numpy(vx[t]) / torch.from_numpy(vs)).numpy())
+                self.kc[b, :, t % B, :] = kcode
+                self.vc[b, :, t % B, :] = vcode
+                kf[t] = vals[kcode] * ks.astype(np.float64)
+                vf[t] = vals[vcode] * vs.astype(np.float64)
             self.kf.append(kf)
             self.vf.append(vf)
         self.ctx = np.asarray(self.lens, np.int32)

@@ -14,7 +14,7 @@ import oracle
 import paged_kv_cache_308_amd as pa
 import workloads as W
 from oracle import place
-from oracle_pins import Case
+from oracle_pins import Case, Fp8Case, torch_fp8_values
 from paged_kv_cache_308_amd.engine import TORCH_DTYPE, to_torch
 from paged_kv_cache_308_amd.replay import replay
 
@@ -52,6 +52,8 @@ def variants(Hq, Hkv, dtype, P=0):
 
 
 def variants_for(w, P=0):
+    if w.kv == "fp8":  # E4M3 pools run on the vector kernel
+        return [VALU, AUTO]
     return variants(w.num_q_heads, w.num_kv_heads, w.dtype, P)
 
 
@@ -79,6 +81,20 @@ SMALL = {
     "bf16_d64_b128_g16": W.scaled(W.WORKLOADS["llama70b_gqa"], num_seqs=2, num_q_heads=16,
                                   num_kv_heads=1, head_dim=64, low=200, high=400, num_blocks=16,
                                   partition_size=256),
+    # E4M3 pools with per-(block, KV head) scales
+    "fp8_mha_f16": W.scaled(W.WORKLOADS["llama7b_fp8"], num_seqs=8, num_q_heads=8, num_kv_heads=8,
+                            num_blocks=1200, partition_size=128),
+    "fp8_prefix_bf16": W.scaled(W.WORKLOADS["prefix_sharing"], num_seqs=10, groups=2, samples=5,
+                                num_q_heads=8, num_kv_heads=8, prefix_base=64, private_max=40,
+                                num_blocks=256, partition_size=64, dtype="bf16", kv_dtype="fp8"),
+    "fp8_gqa4_bf16": W.scaled(W.WORKLOADS["llama70b_gqa"], num_seqs=3, num_q_heads=16,
+                              num_kv_heads=4, low=300, high=700, num_blocks=96, block_size=16,
+                              partition_size=256, kv_dtype="fp8"),
+    "fp8_d64_g8_f16": W.scaled(W.WORKLOADS["llama70b_gqa"], num_seqs=3, num_q_heads=16,
+                               num_kv_heads=2, head_dim=64, low=100, high=300, num_blocks=64,
+                               block_size=32, dtype="f16", partition_size=64, kv_dtype="fp8"),
+    "fp8_d64_g2_f16": W.scaled(W.WORKLOADS["llama7b_fp8"], num_seqs=5, num_q_heads=8,
+                               num_kv_heads=4, head_dim=64, num_blocks=300, partition_size=64),
 }
 
 
@@ -113,6 +129,9 @@ def test_small_workload(name, oracle_steps):
             # the pools after the step: bit for bit what the oracle's scatter/copy wrote
             assert bits(db.cache.key_cache) == np_bits(placed.key_cache)
             assert bits(db.cache.value_cache) == np_bits(placed.value_cache)
+            if w.kv == "fp8":  # copied blocks took their scales along
+                assert bits(db.cache.k_scales) == np_bits(placed.k_scales)
+                assert bits(db.cache.v_scales) == np_bits(placed.v_scales)
 
 
 # ----------------------------------------------------------------- edge cases
@@ -322,6 +341,156 @@ def test_swap_out_and_in_round_trip():
     assert after == before
 
 
+# ------------------------------------------------------------------ E4M3 pools
+
+
+def _run_fp8_case(c: Fp8Case, P, variant=VALU, tables=None):
+    q = to_torch(c.q, c.qdtype).cuda()
+    kc = torch.from_numpy(c.kc).cuda()
+    vc = torch.from_numpy(c.vc).cuda()
+    ks = torch.from_numpy(c.ks).cuda()
+    vs = torch.from_numpy(c.vs).cuda()
+    bt = torch.from_numpy(c.tables if tables is None else tables).cuda()
+    cl = torch.from_numpy(c.ctx).cuda()
+    out = torch.empty_like(q)
+    mc = int(c.ctx.max())
+    ws = None
+    if P:
+        n = pa.pa_decode_workspace_bytes(q.shape[0], q.shape[1], c.Hkv, c.d, mc, P)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    pa.pa_decode_fp8(out, q, kc, vc, ks, vs, bt, cl, c.scale, max_context_len=mc, partition_size=P,
+                     variant=variant, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+FP8_EDGE_SHAPES = [
+    # Hq, Hkv, d, B, query dtype: groups 1, 2 (16-code slices) and 4, 8 (8-code slices)
+    (4, 4, 128, 16, "f16"),
+    (4, 2, 64, 16, "bf16"),
+    (8, 2, 128, 32, "f16"),
+    (8, 1, 64, 16, "bf16"),
+    (16, 2, 128, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", FP8_EDGE_SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_fp8_edge_lengths(shape):
+    Hq, Hkv, d, B, qdt = shape
+    rng = np.random.default_rng(21)
+    c = Fp8Case(rng, EDGE_LENS, Hq, Hkv, d, B, qdt)
+    want = c.run(oracle.default())
+    g = Hq // Hkv
+    for P in (0, 64, 512, BAL) if B <= 64 else (0, 128, 512, BAL):
+        say(f"[gpu] fp8 edge {shape} P={P}")
+        got = _run_fp8_case(c, P)
+        err = np.max(np.abs(f64(got) - want))
+        assert err <= TOL[qdt], (shape, P, err)
+        assert torch.all(got[0] == 0)  # empty context
+        # one token: its dequantised V (code value times the block's scale), rounded
+        b = int(c.tables[1, 0])
+        v1 = torch.from_numpy(torch_fp8_values()[c.vc[b, :, 0, :]] *
+                              c.vs[b][:, None].astype(np.float64))
+        assert torch.equal(got[1].cpu(), v1.to(got.dtype).repeat_interleave(g, dim=0))
+
+
+@pytest.mark.parametrize("P", [0, 64, BAL])
+def test_fp8_bad_table_entry_gives_nan_for_that_sequence_only(P):
+    rng = np.random.default_rng(22)
+    c = Fp8Case(rng, [40, 50, 60], 4, 4, 128, 16, "f16")
+    clean = _run_fp8_case(c, P)
+    t = c.tables.copy()
+    t[1, 2] = c.num_blocks
+    say(f"[gpu] fp8 bad entry P={P}")
+    got = _run_fp8_case(c, P, tables=t)
+    assert torch.isnan(got[1]).all()
+    assert bits(got[0]) == bits(clean[0]) and bits(got[2]) == bits(clean[2])
+
+
+def _fp8_special_values(rng, n):
+    """Every E4M3 value and every midpoint between neighbours (ties), both signs, the
+    saturation edge, zeros, infinities, NaN, then random numbers over many magnitudes."""
+    vals = torch_fp8_values()
+    finite = vals[:0x7F]
+    mids = (finite[:-1] + finite[1:]) / 2
+    special = np.concatenate([finite, mids, -finite, -mids,
+                              [447.0, 448.0, 455.0, 456.0, 463.0, 464.0, 500.0, 1e4, -1e4, np.inf,
+                               -np.inf, np.nan, 0.0, -0.0, 2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11]])
+    rest = rng.standard_normal(max(0, n - len(special))) * np.exp2(rng.uniform(-12, 10, max(0, n - len(special))))
+    return np.concatenate([special, rest])[:n].astype(np.float32)
+
+
+def test_reshape_and_cache_fp8_bitwise():
+    """E4M3 scatter against the oracle's brute-force nearest-code search: exact values,
+    ties, saturation, NaN / inf, with power-of-two scales (x / s exact) and random ones."""
+    rng = np.random.default_rng(23)
+    for dt, nb, H, B, d in (("f32", 12, 2, 16, 64), ("f16", 40, 8, 16, 128), ("bf16", 7, 4, 128, 128)):
+        N = nb * B // 2
+        slots = rng.choice(nb * B, size=N, replace=False).astype(np.int32)
+        slots[::7] = -1
+        slots[3] = nb * B + 5  # past the pool: skipped
+        vals = _fp8_special_values(rng, N * H * d).reshape(N, H, d)
+        key = W.round_to(vals, dt)
+        val = W.round_to(rng.permutation(vals.ravel()).reshape(N, H, d), dt)
+        ks = np.where(rng.random((nb, H)) < 0.5, np.exp2(rng.integers(-8, 3, (nb, H))),
+                      np.exp2(rng.uniform(-8, 2, (nb, H)))).astype(np.float32)
+        vs = np.exp2(rng.uniform(-8, 2, (nb, H))).astype(np.float32)
+        kc = rng.integers(0, 256, (nb, H, B, d)).astype(np.uint8)
+        vc = rng.integers(0, 256, (nb, H, B, d)).astype(np.uint8)
+        gk, gv = torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda()
+        say(f"[gpu] reshape_and_cache_fp8 {dt} N={N}")
+        pa.pa_reshape_and_cache_fp8(to_torch(key, dt).cuda(), to_torch(val, dt).cuda(), gk, gv,
+                                    torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda(),
+                                    torch.from_numpy(slots).cuda())
+        torch.cuda.synchronize()
+        ok = slots.copy()
+        ok[3] = -1
+        oracle.default().reshape_and_cache_fp8(key, val, kc, vc, ks, vs, ok, dt)
+        assert bits(gk) == np_bits(kc) and bits(gv) == np_bits(vc)
+
+
+def test_fp8_blocks_and_scales_copy_and_swap_bitwise():
+    """E4M3 pools move with pa_copy_blocks / pa_swap_blocks, and so do their scale arrays,
+    as pools of one float32 per (block, KV head): 4-byte words when H_kv * 4 is not a
+    multiple of 16."""
+    rng = np.random.default_rng(24)
+    for H in (2, 8):
+        nb, B, d = 30, 16, 128
+        kc = rng.integers(0, 256, (nb, H, B, d)).astype(np.uint8)
+        vc = rng.integers(0, 256, (nb, H, B, d)).astype(np.uint8)
+        ks = rng.random((nb, H, 1, 1)).astype(np.float32)
+        vs = rng.random((nb, H, 1, 1)).astype(np.float32)
+        ids = rng.permutation(nb).astype(np.int32)
+        src, dst = ids[:9].copy(), ids[9:18].copy()
+        g = [torch.from_numpy(a).cuda() for a in (kc, vc, ks, vs)]
+        sd, dd = torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda()
+        say(f"[gpu] fp8 copy H={H}")
+        pa.pa_copy_blocks(g[0], g[1], sd, dd)
+        pa.pa_copy_blocks(g[2], g[3], sd, dd)
+        torch.cuda.synchronize()
+        o = oracle.default()
+        o.copy_blocks(kc, vc, src, dst, "fp8")
+        o.copy_blocks(ks, vs, src, dst, "f32")
+        for t, a in zip(g, (kc, vc, ks, vs)):
+            assert bits(t) == np_bits(a)
+        # device -> pinned host
+        hk = torch.zeros((12, H, B, d), dtype=torch.uint8, pin_memory=True)
+        hv = torch.zeros_like(hk).pin_memory()
+        hks = torch.zeros((12, H, 1, 1), dtype=torch.float32, pin_memory=True)
+        hvs = torch.zeros_like(hks).pin_memory()
+        hs, hd = src[:5].copy(), rng.choice(12, 5, replace=False).astype(np.int32)
+        say(f"[gpu] fp8 swap H={H}")
+        pa.pa_swap_blocks(g[0], g[1], hk, hv, torch.from_numpy(hs).cuda(), torch.from_numpy(hd).cuda())
+        pa.pa_swap_blocks(g[2], g[3], hks, hvs, torch.from_numpy(hs).cuda(), torch.from_numpy(hd).cuda())
+        torch.cuda.synchronize()
+        wk, wv = np.zeros((12, H, B, d), np.uint8), np.zeros((12, H, B, d), np.uint8)
+        wks, wvs = np.zeros((12, H, 1, 1), np.float32), np.zeros((12, H, 1, 1), np.float32)
+        o.swap_blocks(kc, vc, wk, wv, hs, hd, "fp8")
+        o.swap_blocks(ks, vs, wks, wvs, hs, hd, "f32")
+        for t, a in zip((hk, hv, hks, hvs), (wk, wv, wks, wvs)):
+            assert t.numpy().tobytes() == a.tobytes()
+
+
 # ------------------------------------------------------------ full-size workloads
 
 
@@ -336,7 +505,24 @@ def _sample(ctx: np.ndarray, k: int = 6):
     return sorted(pick)
 
 
-@pytest.mark.parametrize("name", ["llama7b", "llama13b_long", "llama70b_gqa", "prefix_sharing"])
+def _sub_batch_scales(w, batch, sub, seqs):
+    """Block scales for a sub-batch placed by the oracle in its own pool: each of its
+    blocks takes the scale of the block that holds the same tokens in the full batch."""
+    ks_full, vs_full = W.fp8_scales(w)
+    a_full, sids, _, _ = place.replay(batch)
+    a_sub, sids_sub, _, _ = place.replay(sub)
+    ks, vs = ks_full.copy(), vs_full.copy()
+    for i, s in enumerate(seqs):
+        full_t, _ = a_full.block_table(sids[s])
+        sub_t, _ = a_sub.block_table(sids_sub[i])
+        for fb, sb in zip(full_t, sub_t):
+            ks[sb] = ks_full[fb]
+            vs[sb] = vs_full[fb]
+    return ks, vs
+
+
+@pytest.mark.parametrize("name", ["llama7b", "llama13b_long", "llama70b_gqa", "prefix_sharing",
+                                  "llama7b_fp8"])
 def test_full_size_sampled(name):
     """Whole batch on the GPU in the benchmark's launch setup; oracle on a sample of
     sequences (attention does not depend on where blocks sit, so the oracle may
@@ -356,7 +542,9 @@ def test_full_size_sampled(name):
         err = np.max(np.abs(got - want))
     else:
         seqs = _sample(batch.lengths.context_lens)
-        want, _ = place.decode_step(W.make_batch(w, seqs=seqs))
+        sub = W.make_batch(w, seqs=seqs)
+        scales = _sub_batch_scales(w, batch, sub, seqs) if w.kv == "fp8" else None
+        want, _ = place.decode_step(sub, fp8_scales=scales)
         err = np.max(np.abs(got[seqs] - want))
     say(f"[gpu] full-size {name}: max abs err {err:.3e}")
     assert err <= TOL[w.dtype]

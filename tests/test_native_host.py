@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(pa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert pa.abi_version() == 2
+    assert pa.abi_version() == 3
 
 
 # -------------------------------------------------------------- allocator parity
@@ -227,6 +227,34 @@ def test_empty_batch_is_a_no_op():
     assert _decode(S=0) == pa.PA_OK
 
 
+def _decode_fp8(**kw):
+    a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, maxb=4, cl=FAKE, S=2,
+             Hq=8, Hkv=8, d=128, B=16, nb=10, maxctx=64, scale=0.1, dtype=pa.PA_F16, P=0, variant=0,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return pa._lib().pa_decode_fp8(a["out"], a["query"], a["kc"], a["vc"], a["ks"], a["vs"], a["bt"],
+                                   a["maxb"], a["cl"], a["S"], a["Hq"], a["Hkv"], a["d"], a["B"],
+                                   a["nb"], a["maxctx"], a["scale"], a["dtype"], a["P"],
+                                   a["variant"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),        # E4M3 pools take a 16-bit query
+    (dict(dtype=pa.PA_FP8_E4M3), pa.PA_ERR_UNSUPPORTED),
+    (dict(ks=None), pa.PA_ERR_INVALID),
+    (dict(vs=None), pa.PA_ERR_INVALID),
+    (dict(Hq=16, Hkv=1), pa.PA_ERR_UNSUPPORTED),            # groups stop at 8
+    (dict(variant=pa.PA_VARIANT_MFMA, Hq=16, Hkv=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(d=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(P=24), pa.PA_ERR_INVALID),
+    (dict(P=512, ws=None), pa.PA_ERR_INVALID),
+])
+def test_decode_fp8_rejects_before_launch(kw, status):
+    assert _decode_fp8(**kw) == status
+    assert pa._lib().pa_last_error() != b""
+    assert _decode_fp8(S=0) == pa.PA_OK
+
+
 def test_workspace_size():
     S, Hq, d = 32, 40, 128
     n = pa.pa_decode_workspace_bytes(S, Hq, Hq, d, 4096, 512)
@@ -255,3 +283,19 @@ def test_block_ops_reject_before_launch():
                             None) == pa.PA_OK
     assert L.pa_swap_blocks(FAKE, FAKE, other, other, FAKE, FAKE, 2, 8, 128, 16, 10, 10, 9,
                             None) == pa.PA_ERR_UNSUPPORTED
+    # block bytes must be a multiple of 4: E4M3 pools of one 2-wide row, scale arrays of
+    # 1 to 3 heads (4-byte words) pass validation with zero pairs
+    assert L.pa_copy_blocks(FAKE, FAKE, FAKE, FAKE, 2, 1, 2, 1, 10, pa.PA_FP8_E4M3,
+                            None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_copy_blocks(FAKE, FAKE, FAKE, FAKE, 0, 3, 1, 1, 10, pa.PA_F32, None) == pa.PA_OK
+    assert L.pa_copy_blocks(FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 10, pa.PA_FP8_E4M3,
+                            None) == pa.PA_OK
+    # E4M3 scatter: the source must be f32 / f16 / bf16; head_dim a multiple of 4
+    assert L.pa_reshape_and_cache_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10,
+                                      pa.PA_FP8_E4M3, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_reshape_and_cache_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 6, 16, 10,
+                                      pa.PA_F16, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_reshape_and_cache_fp8(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 8, 128, 16, 10,
+                                      pa.PA_F16, None) == pa.PA_ERR_INVALID
+    assert L.pa_reshape_and_cache_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 10,
+                                      pa.PA_F16, None) == pa.PA_OK

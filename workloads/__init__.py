@@ -267,6 +267,11 @@ class Batch:
     append_k: List[np.ndarray]
     append_v: List[np.ndarray]
 
+    @property
+    def fp8_scales(self):
+        """K and V block scales of an E4M3 workload."""
+        return fp8_scales(self.workload)
+
 
 def make_batch(w: Workload, identity: bool = False, seqs=None) -> Batch:
     """Draw a whole batch.  `seqs` (plain workloads only) keeps just those
