@@ -35,16 +35,27 @@ REPLICAS = 3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_sources_digest() -> str:
-    """sha256 over the HIP/C++ sources of libpa (names and contents, sorted)."""
+# Sources the vector decode kernels are built from (their counters go stale when these change).
+DECODE_SOURCES = {
+    "f16": ["decode_valu.h", "kernel_common.h", "internal.h", "decode_valu_f16.hip"],
+    "bf16": ["decode_valu.h", "kernel_common.h", "internal.h", "decode_valu_bf16.hip"],
+    "f32": ["decode_valu.h", "kernel_common.h", "internal.h", "decode_valu_f32.hip"],
+    "fp8": ["decode_valu.h", "kernel_common.h", "internal.h", "decode_valu_fp8_f16.hip",
+            "decode_valu_fp8_bf16.hip"],
+    "mfma": ["decode_mfma.h", "kernel_common.h", "internal.h", "decode_mfma_f16.hip",
+             "decode_mfma_bf16.hip"],
+}
+
+
+def kernel_sources_digest(files) -> str:
+    """sha256 over the named libpa sources (names and contents, in the given order)."""
     import hashlib
     d = os.path.join(ROOT, "paged_kv_cache_308_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(name.encode())
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(f.read())
+    for name in files:
+        h.update(name.encode())
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -56,7 +67,7 @@ def measured_traffic(workload: str):
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("sources_sha256") != kernel_sources_digest():
+    if not rec or rec.get("sources_sha256") != kernel_sources_digest(rec.get("sources", [])):
         return None
     return rec["bytes_per_launch"]
 
