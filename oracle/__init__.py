@@ -8,7 +8,9 @@ this package.  It shares no code with the HIP library and never imports it.
                     (copy_blocks) and the block move between two pools
                     (swap_blocks); the same for pools of OCP E4M3 codes with a
                     scale per (block, KV head) (decode_fp8, reshape_and_cache_fp8,
-                    fp8_value, fp8_encode); built here with gcc, single-threaded.
+                    fp8_value, fp8_encode); causal attention of several query
+                    tokens per sequence (multi_query); built here with gcc,
+                    single-threaded.
   alloc_model.py    the block allocator (free list, reference counts, fork,
                     append with copy-on-write, free) in plain Python.
   place.py          helpers that build pools and tables with the model allocator
@@ -81,6 +83,9 @@ class Oracle:
                                                 ci, ci, ci, cd, ci]
         self._lib.oracle_reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, fp, fp, i32p, ci, ci,
                                                            ci, ci, ci, ci]
+        self._lib.oracle_multi_query.argtypes = [dp, vp, vp, vp, i32p, ci, i32p, i32p, ci, ci, ci, ci,
+                                                 ci, ci, cd, ci]
+        self._lib.oracle_multi_query.restype = ctypes.c_int
         self._lib.oracle_fp8_value.argtypes = [ctypes.c_uint8]
         self._lib.oracle_fp8_value.restype = cd
         self._lib.oracle_fp8_encode.argtypes = [ctypes.c_float]
@@ -187,6 +192,27 @@ class Oracle:
             sm.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), N, Hkv, d, B, nb,
             DTYPE_CODE[src_dtype])
         self._check(rc, "oracle_reshape_and_cache_fp8")
+
+    def multi_query(self, query, key_cache, value_cache, block_tables, context_lens, query_start,
+                    scale: float, dtype: str) -> np.ndarray:
+        """Causal attention of several query tokens per sequence (the last n_s positions
+        of each context).  query [T][H_q][d], query_start int32 [S+1].  Returns float64."""
+        q = np.ascontiguousarray(query)
+        kc = np.ascontiguousarray(key_cache)
+        vc = np.ascontiguousarray(value_cache)
+        bt, cl, qs = self._i32(block_tables), self._i32(context_lens), self._i32(query_start)
+        T, Hq, d = q.shape
+        nb, Hkv, B, d2 = kc.shape
+        S = cl.shape[0]
+        assert d2 == d and vc.shape == kc.shape and qs.shape == (S + 1,) and qs[-1] == T
+        out = np.zeros((T, Hq, d), np.float64)
+        p32 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        rc = self._lib.oracle_multi_query(
+            out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), q.ctypes.data, kc.ctypes.data,
+            vc.ctypes.data, p32(bt), bt.shape[1], p32(cl), p32(qs), S, Hq, Hkv, d, B, nb,
+            float(scale), DTYPE_CODE[dtype])
+        self._check(rc, "oracle_multi_query")
+        return out
 
     def reshape_and_cache(self, key, value, key_cache, value_cache, slot_mapping, dtype: str):
         """In-place scatter of key/value [N][H_kv][d] into the pools."""

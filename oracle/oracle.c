@@ -342,6 +342,83 @@ int oracle_decode_fp8(double *out, const void *query, const void *key_cache, con
 }
 
 /*
+ * Several query tokens per sequence over the paged cache (chunked prefill, a prefix-
+ * cache hit: "PagedAttention 深度解析" (5ulink.com) §六 item 5; the same gather through
+ * the block table as decode, "PagedAttention" concept report §5 and §8).  Sequence s
+ * owns query rows query_start[s] .. query_start[s+1]-1 (n_s of them, n_s <= ctx); row
+ * i of s is the token at position p = ctx - n_s + i, whose K/V are already cached, and
+ * it attends causally to the tokens t <= p:
+ *   out[row][h] = sum_{t <= p} softmax_t(scale * <q[row][h], K(t)>) * V(t).
+ * query, out: [T][H_q][d], T = query_start[num_seqs].
+ */
+int oracle_multi_query(double *out, const void *query, const void *key_cache, const void *value_cache,
+                       const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                       const int32_t *query_start, int num_seqs, int num_q_heads, int num_kv_heads,
+                       int head_dim, int block_size, int num_blocks, double scale, int dtype)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_q_heads % num_kv_heads != 0 || !is_wide(dtype) || query_start[0] != 0)
+        return ORACLE_BAD_ARG;
+    const int g = num_q_heads / num_kv_heads;
+    const int d = head_dim, B = block_size, Hkv = num_kv_heads;
+    for (int s = 0; s < num_seqs; ++s) {
+        const int n = context_lens[s];
+        const int nq = query_start[s + 1] - query_start[s];
+        if (n < 0 || nq < 0 || nq > n) return ORACLE_BAD_ARG;
+        for (int lb = 0; lb * B < n; ++lb) {
+            if (lb >= max_blocks_per_seq) return ORACLE_BAD_INDEX;
+            const int64_t pb = block_tables[(int64_t)s * max_blocks_per_seq + lb];
+            if (pb < 0 || pb >= num_blocks) return ORACLE_BAD_INDEX;
+        }
+        double *x = (double *)malloc(sizeof(double) * (n > 0 ? n : 1));
+        if (!x) return ORACLE_NO_MEM;
+        for (int i = 0; i < nq; ++i) {
+            const int64_t row = query_start[s] + i;
+#if ORACLE_MUTANT == 17
+            const int p = n - nq + i + 1;        /* planted: positions shifted by one */
+#else
+            const int p = n - nq + i;
+#endif
+#if ORACLE_MUTANT == 16
+            const int last = p - 1;              /* planted: a token does not see itself */
+#else
+            const int last = p;
+#endif
+            for (int h = 0; h < num_q_heads; ++h) {
+                const int k = h / g;
+                const int64_t q_row = (row * num_q_heads + h) * d;
+                double *o_row = out + (row * num_q_heads + h) * d;
+                double m = -INFINITY;
+                for (int t = 0; t <= last && t < n; ++t) {
+                    const int64_t pb = block_tables[(int64_t)s * max_blocks_per_seq + t / B];
+                    double dot = 0.0;
+                    for (int j = 0; j < d; ++j)
+                        dot += oracle_load(query, q_row + j, dtype) *
+                               oracle_load(key_cache, pool_index(pb, k, t % B, j, Hkv, B, d), dtype);
+                    x[t] = scale * dot;
+                    if (x[t] > m) m = x[t];
+                }
+                double Z = 0.0;
+                for (int t = 0; t <= last && t < n; ++t) {
+                    x[t] = exp(x[t] - m);
+                    Z += x[t];
+                }
+                for (int j = 0; j < d; ++j) {
+                    double acc = 0.0;
+                    for (int t = 0; t <= last && t < n; ++t) {
+                        const int64_t pb = block_tables[(int64_t)s * max_blocks_per_seq + t / B];
+                        acc += x[t] * oracle_load(value_cache, pool_index(pb, k, t % B, j, Hkv, B, d), dtype);
+                    }
+                    o_row[j] = Z > 0.0 ? acc / Z : 0.0;
+                }
+            }
+        }
+        free(x);
+    }
+    return ORACLE_OK;
+}
+
+/*
  * For every token i with slot = slot_mapping[i] >= 0: physical block slot / B,
  * in-block position slot % B; for every KV head k, copy key[i][k][:] into the key
  * pool and value[i][k][:] into the value pool at that place, bit for bit.

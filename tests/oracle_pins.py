@@ -538,8 +538,74 @@ def pin_fp8_reshape(o):
         assert kc.tobytes() == wk.tobytes() and vc.tobytes() == wv.tobytes(), dt
 
 
+# ---------------------------------------------------------------------------
+# several causal query tokens per sequence
+
+
+class MQCase(Case):
+    """A Case whose sequences also carry n_s query tokens (the last n_s positions)."""
+
+    def __init__(self, rng, lens, qlens, Hq, Hkv, d, B, dtype, **kw):
+        super().__init__(rng, lens, Hq, Hkv, d, B, dtype, **kw)
+        self.qlens = [int(x) for x in qlens]
+        assert all(0 <= a <= b for a, b in zip(self.qlens, self.lens))
+        self.qstart = np.concatenate([[0], np.cumsum(self.qlens)]).astype(np.int32)
+        T = int(self.qstart[-1])
+        self.mq = W.round_to(rng.standard_normal((T, Hq, d), dtype=np.float32), dtype)
+
+    def run_mq(self, o):
+        return o.multi_query(self.mq, self.kc, self.vc, self.tables, self.ctx, self.qstart,
+                             self.scale, self.dtype)
+
+    def sdpa_mq(self):
+        """torch SDPA (float64) with the causal mask t <= ctx - n_s + i, per sequence."""
+        out = np.zeros((int(self.qstart[-1]), self.Hq, self.d))
+        for s, (n, nq) in enumerate(zip(self.lens, self.qlens)):
+            if nq == 0:
+                continue
+            a, b = int(self.qstart[s]), int(self.qstart[s + 1])
+            q = torch.from_numpy(self.f64(self.mq[a:b])).permute(1, 0, 2)[None].contiguous()
+            k = torch.from_numpy(self.f64(self.k[s])).permute(1, 0, 2)[None].contiguous()
+            v = torch.from_numpy(self.f64(self.v[s])).permute(1, 0, 2)[None].contiguous()
+            pos = torch.arange(n - nq, n)[:, None]
+            mask = torch.arange(n)[None, :] <= pos
+            o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=self.scale,
+                                               enable_gqa=self.Hq != self.Hkv)
+            out[a:b] = o[0].permute(1, 0, 2).numpy()
+        return out
+
+
+def pin_mq_sdpa(o):
+    """Several query tokens per sequence equal torch SDPA with the causal mask over the
+    logical tokens (query i of n sits at position ctx - n + i)."""
+    rng = np.random.default_rng(130)
+    for lens, qlens, Hq, Hkv, d, B, dt in (([1, 5, 17, 40], [1, 5, 3, 17], 2, 2, 8, 4, "f32"),
+                                           ([33, 20], [33, 1], 8, 2, 16, 16, "bf16"),
+                                           ([70, 9, 0], [24, 9, 0], 4, 1, 32, 8, "f16")):
+        c = MQCase(rng, lens, qlens, Hq, Hkv, d, B, dt)
+        got, want = c.run_mq(o), c.sdpa_mq()
+        assert np.max(np.abs(got - want)) <= 1e-12, (lens, qlens, dt)
+
+
+def pin_mq_causal(o):
+    """A query token never sees later tokens: changing K and V after its position leaves
+    its output bit-identical; a chunk covering the whole context starts with V(0)."""
+    rng = np.random.default_rng(131)
+    c = MQCase(rng, [30], [30], 2, 2, 8, 4, "f32")
+    a = c.run_mq(o)
+    assert np.array_equal(a[0], c.v[0][0].astype(np.float64))
+    for cut in (5, 17):
+        c.k[0][cut + 1:] = rng.standard_normal(c.k[0][cut + 1:].shape, dtype=np.float32)
+        c.v[0][cut + 1:] = rng.standard_normal(c.v[0][cut + 1:].shape, dtype=np.float32)
+        c._put(0, c.kc, c.k[0])
+        c._put(0, c.vc, c.v[0])
+        b = c.run_mq(o)
+        assert np.array_equal(a[:cut + 1], b[:cut + 1]) and not np.array_equal(a[cut + 1:], b[cut + 1:])
+        a = b
+
+
 ORACLE_PINS = [pin_sdpa, pin_brute, pin_permutation, pin_ctx1, pin_equal_keys, pin_dominant,
                pin_shared_prefix, pin_nan_poison, pin_empty, pin_bad_index, pin_reshape, pin_copy,
                pin_swap,
                pin_page3_request, pin_dtype_decode, pin_fp8_codes, pin_fp8_encode, pin_fp8_sdpa,
-               pin_fp8_reshape]
+               pin_fp8_reshape, pin_mq_sdpa, pin_mq_causal]

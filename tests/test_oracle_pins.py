@@ -31,6 +31,8 @@ MUTANTS = {
     13: "E4M3 ties rounded away from zero",
     14: "E4M3 encode without saturation",
     15: "key scale taken from the logical block",
+    16: "a query token does not attend to itself",
+    17: "query positions shifted by one",
 }
 
 
