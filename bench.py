@@ -97,17 +97,21 @@ def log(args, *a):
         print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(w, ctx: np.ndarray) -> dict:
+def algorithmic_bytes(w, ctx: np.ndarray, unique_tokens: int = None) -> dict:
     """Bytes one decode call must move: K/V of every cached token, q in, out, the
     table entries it reads and the lengths (E4M3 pools: also the K and V scale of every
-    (block, KV head) it reads)."""
-    kv = int(ctx.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * w.kv_elem_bytes
+    (block, KV head) it reads).  kv / total count every sequence's tokens (the metric's
+    effective bytes); *_unique count a block shared by several sequences once, the
+    bytes that must come from HBM (the roofline's)."""
+    per_tok = 2 * w.num_kv_heads * w.head_dim * w.kv_elem_bytes
+    kv = int(ctx.astype(np.int64).sum()) * per_tok
     qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * w.elem_bytes
     blocks = int(np.sum((ctx.astype(np.int64) + w.block_size - 1) // w.block_size))
     tbl = 4 * blocks + 4 * w.num_seqs
     if w.kv == "fp8":
         tbl += 8 * blocks * w.num_kv_heads
-    return {"kv": kv, "total": kv + qo + tbl}
+    kv_u = kv if unique_tokens is None else unique_tokens * per_tok
+    return {"kv": kv, "total": kv + qo + tbl, "kv_unique": kv_u, "total_unique": kv_u + qo + tbl}
 
 
 def build_replicas(args, w, batch, identity: bool):
@@ -285,6 +289,8 @@ def main():
         return
     log(args, f"[bench] placing {REPLICAS} replicas")
     reps = build_replicas(args, w, batch, identity=False)
+    # tokens held in the pool (a block shared by several sequences counts once)
+    ab = algorithmic_bytes(w, ctx, reps[0][0].cache.alloc.stats()["stored_tokens"])
 
     log(args, f"[bench] warmup {args.warmup}")
     run_steps(args, reps, args.warmup, record=False)
@@ -310,7 +316,7 @@ def main():
     cpu = None if args.no_cpu else cpu_baseline(args, w, batch, ab["kv"])
 
     gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
-    achieved = ab["total"] / (dec_avg * 1e-3) / 1e9
+    achieved = ab["total_unique"] / (dec_avg * 1e-3) / 1e9
     g = w.num_q_heads // w.num_kv_heads
     mfma = w.kv != "fp8" and (args.variant == 2 or (args.variant == 0 and g >= 2 and w.dtype != "f32"))
     kernels = ("decode_mfma_kernel" if mfma else "decode_valu_kernel") + \
@@ -342,7 +348,7 @@ def main():
         "decode_kv_gbs": round(ab["kv"] / (dec_avg * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": kernels, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": ab["total"], "traffic": measured_traffic(w.name)},
+                     "bytes_per_launch": ab["total_unique"], "traffic": measured_traffic(w.name)},
         "identity_decode_us": None if ident is None else round(ident * 1e3, 2),
         "paged_vs_identity": None if ident is None else round(ident / dec_avg, 4),
         "host_alloc_us_per_step": round(alloc_us, 2),
