@@ -165,6 +165,26 @@ int pa_swap_blocks(const void *src_key_cache, const void *src_value_cache, void 
                    int num_kv_heads, int head_dim, int block_size, int src_num_blocks,
                    int dst_num_blocks, int dtype, void *stream);
 
+/*
+ * Several query tokens per sequence (chunked prefill, a prefix-cache hit: [5ulink] §六
+ * item 5), over the same paged cache and tables as pa_decode ([cpai] §5, §8).  Sequence
+ * s owns rows query_start[s] .. query_start[s+1]-1 of query and out ([T][num_q_heads]
+ * [head_dim] of `dtype`, T = num_query_tokens); with n_s such rows, row i is the token
+ * at position ctx_s - n_s + i, whose K/V must already be in the cache (written with
+ * pa_reshape_and_cache), and it attends causally:
+ *   out[row][h] = sum_{t <= ctx_s - n_s + i} softmax_t(scale * <query[row][h], K_t>) * V_t.
+ * query_start: device int32 [num_seqs + 1], nondecreasing from 0.  max_query_len must
+ * bound every n_s.  dtype f16 or bf16 (matrix cores); head_dim 64 or 128; group sizes
+ * 1 to 16.  A sequence with n_s > ctx_s, n_s > max_query_len, ctx_s < 0 or a needed
+ * table entry outside [0, num_blocks) gets NaN in its rows (rows past max_query_len are
+ * not written); rows outside [0, T) are never read or written.
+ */
+int pa_multi_query(void *out, const void *query, const void *key_cache, const void *value_cache,
+                   const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                   const int32_t *query_start, int num_seqs, int num_query_tokens, int max_query_len,
+                   int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                   float scale, int dtype, void *stream);
+
 /* ------------------------------------------------------- compressed (E4M3) pools */
 
 /*

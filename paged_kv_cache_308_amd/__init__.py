@@ -28,7 +28,7 @@ PA_PARTITION_BALANCED = -1
 EXPORTS = (
     "pa_status_str", "pa_last_error", "pa_abi_version", "pa_decode_workspace_bytes", "pa_decode",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_check_tables",
-    "pa_reshape_and_cache_fp8", "pa_decode_fp8",
+    "pa_reshape_and_cache_fp8", "pa_decode_fp8", "pa_multi_query",
     "pa_check_copy_pairs", "pa_alloc_adopt",
     "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_set_free_order", "pa_alloc_new_seq",
     "pa_alloc_append_slot", "pa_alloc_append_slots", "pa_alloc_fork", "pa_alloc_free_seq",
@@ -74,6 +74,8 @@ def _lib():
                                            vp]),
         "pa_decode_fp8": (i32, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
                                 i32, f32, i32, i32, i32, vp, sz, vp]),
+        "pa_multi_query": (i32, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                 i32, f32, i32, vp]),
         "pa_copy_blocks": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
         "pa_swap_blocks": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]),
         "pa_alloc_adopt": (i32, [vp, i32, i64p, i32p, i32]),
@@ -167,6 +169,32 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
         int(max_context_len), float(scale), dtype_code(query), int(partition_size), int(variant),
         ws_ptr, ws_bytes, _stream(stream))
     _check(rc, "pa_decode")
+    return out
+
+
+def pa_multi_query(out, query, key_cache, value_cache, block_tables, context_lens, query_start,
+                   scale: float, max_query_len: int, stream=None):
+    """Causal attention of several query tokens per sequence: query/out [T][H_q][d] (f16 or
+    bf16), query_start int32 [S+1] (sequence s owns rows query_start[s]..query_start[s+1]-1,
+    the last positions of its context)."""
+    torch = _torch()
+    T, Hq, d = query.shape
+    nb, Hkv, B, d2 = key_cache.shape
+    S = context_lens.shape[0]
+    if d2 != d or value_cache.shape != key_cache.shape or out.shape != query.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start.shape != (S + 1,):
+        raise ValueError("block_tables / query_start shape")
+    for t in (key_cache, value_cache, out):
+        if t.dtype != query.dtype:
+            raise ValueError("query, pools and out must share one dtype")
+    rc = _lib().pa_multi_query(
+        _dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        _dev(query_start, "query_start", torch.int32), S, T, int(max_query_len), Hq, Hkv, d, B, nb,
+        float(scale), dtype_code(query), _stream(stream))
+    _check(rc, "pa_multi_query")
     return out
 
 

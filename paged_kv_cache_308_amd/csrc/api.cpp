@@ -301,6 +301,42 @@ int pa_reshape_and_cache(const void *key, const void *value, void *key_cache, vo
                                     num_kv_heads, head_dim, block_size, num_blocks, eb, stream);
 }
 
+int pa_multi_query(void *out, const void *query, const void *key_cache, const void *value_cache,
+                   const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                   const int32_t *query_start, int num_seqs, int num_query_tokens, int max_query_len,
+                   int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                   float scale, int dtype, void *stream) {
+    clear_error();
+    if (num_seqs < 0 || num_query_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        num_blocks <= 0 || max_blocks_per_seq <= 0)
+        return fail(PA_ERR_INVALID, "bad sizes");
+    if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;
+    if (max_query_len <= 0) return fail(PA_ERR_INVALID, "max_query_len %d", max_query_len);
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens || !query_start)
+        return fail(PA_ERR_INVALID, "NULL device pointer");
+    if (dtype != PA_F16 && dtype != PA_BF16)
+        return fail(PA_ERR_UNSUPPORTED, "multi-query attention runs on the matrix cores: f16 or bf16, not %d",
+                    dtype);
+    if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d", head_dim);
+    if (!pow2_in(block_size, 16, 128)) return fail(PA_ERR_UNSUPPORTED, "block_size %d", block_size);
+    if (num_q_heads % num_kv_heads)
+        return fail(PA_ERR_INVALID, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+                    num_kv_heads);
+    const int group = num_q_heads / num_kv_heads;
+    if (!pow2_in(group, 1, 16)) return fail(PA_ERR_UNSUPPORTED, "group size %d", group);
+    if ((int64_t)num_blocks * num_kv_heads * block_size * head_dim > ((int64_t)1 << 40))
+        return fail(PA_ERR_UNSUPPORTED, "pool too large");
+    if (!(scale == scale)) return fail(PA_ERR_INVALID, "scale is NaN");
+    DecodeArgs a = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                               context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               num_blocks, dtype, 0, stream);
+    a.query_start = query_start;
+    a.num_query_tokens = num_query_tokens;
+    a.max_query_len = max_query_len;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return dtype == PA_F16 ? launch_multi_query_f16(a) : launch_multi_query_bf16(a);
+}
+
 int pa_reshape_and_cache_fp8(const void *key, const void *value, void *key_cache, void *value_cache,
                              const float *k_scales, const float *v_scales,
                              const int32_t *slot_mapping, int num_tokens, int num_kv_heads,

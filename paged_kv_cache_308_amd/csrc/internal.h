@@ -41,6 +41,10 @@ struct DecodeArgs {
     bool cached_kv;      // K/V through cacheable loads (blocks shared between sequences)
     int dtype;           // query / output type
     bool kv_fp8;         // pools hold E4M3 codes (k_scales / v_scales set)
+    // several query tokens per sequence (pa_multi_query)
+    const int32_t *query_start;  // [S + 1]: the sequence's rows of query / out
+    int num_query_tokens;        // rows of query / out
+    int max_query_len;           // bound on query_start[s + 1] - query_start[s]
     void *stream;
 };
 
@@ -86,6 +90,8 @@ int launch_lse_merge_bf16(const DecodeArgs &a);
 int launch_decode_valu_fp8_f16(const DecodeArgs &a);
 int launch_decode_valu_fp8_bf16(const DecodeArgs &a);
 int launch_decode_mfma_f16(const DecodeArgs &a);
+int launch_multi_query_f16(const DecodeArgs &a);
+int launch_multi_query_bf16(const DecodeArgs &a);
 int launch_decode_mfma_bf16(const DecodeArgs &a);
 
 // Map a HIP error after a launch to PA_ERR_HIP with its text.

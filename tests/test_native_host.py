@@ -227,6 +227,32 @@ def test_empty_batch_is_a_no_op():
     assert _decode(S=0) == pa.PA_OK
 
 
+def _mq(**kw):
+    a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, maxb=4, cl=FAKE, qs=FAKE, S=2, T=10, mql=8,
+             Hq=8, Hkv=8, d=128, B=16, nb=10, scale=0.1, dtype=pa.PA_F16, stream=None)
+    a.update(kw)
+    return pa._lib().pa_multi_query(a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["maxb"], a["cl"],
+                                    a["qs"], a["S"], a["T"], a["mql"], a["Hq"], a["Hkv"], a["d"], a["B"],
+                                    a["nb"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),   # matrix cores: 16-bit only
+    (dict(mql=0), pa.PA_ERR_INVALID),
+    (dict(qs=None), pa.PA_ERR_INVALID),
+    (dict(d=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(B=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(Hq=12, Hkv=8), pa.PA_ERR_INVALID),
+    (dict(Hq=64, Hkv=2), pa.PA_ERR_UNSUPPORTED),
+    (dict(T=-1), pa.PA_ERR_INVALID),
+    (dict(scale=float("nan")), pa.PA_ERR_INVALID),
+])
+def test_multi_query_rejects_before_launch(kw, status):
+    assert _mq(**kw) == status
+    assert pa._lib().pa_last_error() != b""
+    assert _mq(S=0) == pa.PA_OK and _mq(T=0) == pa.PA_OK
+
+
 def _decode_fp8(**kw):
     a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, maxb=4, cl=FAKE, S=2,
              Hq=8, Hkv=8, d=128, B=16, nb=10, maxctx=64, scale=0.1, dtype=pa.PA_F16, P=0, variant=0,
