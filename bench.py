@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # dense, MI355X
 REPLICAS = 3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -256,6 +257,102 @@ def swap_bench(args, w, batch) -> dict:
             "swap_out": res["out"], "swap_in": res["in"]}
 
 
+def mq_bench(args, w, batch) -> dict:
+    """Chunked prefill: each sequence's last query_len tokens are written into the cache
+    (pa_reshape_and_cache) and attend causally (pa_multi_query).  The roofline is the
+    matrix cores': 4 * d * H_q flops per (query token, visible key)."""
+    import torch
+    import paged_kv_cache_308_amd as pa
+    import workloads as W
+    from paged_kv_cache_308_amd.engine import to_torch
+    from paged_kv_cache_308_amd.replay import replay
+    ctx = batch.lengths.context_lens.astype(np.int64)
+    nq = np.minimum(ctx, w.query_len)
+    qstart = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    T = int(qstart[-1])
+    keys_seen = int(sum(int(((c - n + 1) + c) * n // 2) for c, n in zip(ctx, nq)))  # sum of pos + 1
+    flops = 4 * w.head_dim * w.num_q_heads * keys_seen
+    kv_bytes = int(ctx.sum()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    reps = []
+    for r in range(REPLICAS):
+        db = replay(batch, poison=False)
+        q = torch.cat([to_torch(W.chunk_queries(w, s, int(n)), w.dtype) for s, n in enumerate(nq)]).cuda()
+        slots, ks, vs = [], [], []
+        bt = db.host_tables
+        appends = [op for op in batch.script if op.kind == "append"]
+        for s, (c, n) in enumerate(zip(ctx, nq)):
+            for p in range(int(c - n), int(c)):
+                slots.append(int(bt[s, p // w.block_size]) * w.block_size + p % w.block_size)
+            ks.append(batch.append_k[s][int(c - n):])
+            vs.append(batch.append_v[s][int(c - n):])
+        assert len(appends) == w.num_seqs
+        reps.append((db, q, torch.empty_like(q), torch.tensor(slots, dtype=torch.int32, device="cuda"),
+                     to_torch(np.concatenate(ks), w.dtype).cuda(), to_torch(np.concatenate(vs), w.dtype).cuda(),
+                     torch.from_numpy(qstart).cuda()))
+    st = torch.cuda.current_stream()
+
+    def steps(n, record):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(st)
+        for k in range(n):
+            db, q, out, sl, kk, vv, qs = reps[k % len(reps)]
+            evs[k][0].record(st)
+            pa.pa_reshape_and_cache(kk, vv, db.cache.key_cache, db.cache.value_cache, sl, st)
+            evs[k][1].record(st)
+            pa.pa_multi_query(out, q, db.cache.key_cache, db.cache.value_cache, db.block_tables,
+                              db.context_lens, qs, w.scale, w.query_len, st)
+            evs[k][2].record(st)
+        t1.record(st)
+        torch.cuda.synchronize()
+        return (t0.elapsed_time(t1), [e[1].elapsed_time(e[2]) for e in evs],
+                [e[0].elapsed_time(e[1]) for e in evs])
+
+    steps(args.warmup, False)
+    total, att, pre = steps(args.steps, True)
+    ms_step = total / args.steps
+    att_ms = float(np.mean(att))
+    cpu = None
+    if not args.no_cpu:
+        # the oracle on one sequence's first 64 chunk rows' worth of work: the last 64
+        # positions of sequence 0, all heads
+        from oracle import place
+        import oracle
+        sub = W.make_batch(w, seqs=[0])
+        p = place.place(sub, poison=False)
+        p.write(p.new_key, p.new_value, p.slot_mapping, w.dtype)
+        n0 = 64
+        q0 = W.chunk_queries(w, 0, int(nq[0]))[-n0:]
+        c0 = int(ctx[0])
+        t = time.perf_counter()
+        oracle.default().multi_query(q0, p.key_cache, p.value_cache, p.block_tables, p.context_lens,
+                                     np.array([0, n0], np.int32), w.scale, w.dtype)
+        dt = time.perf_counter() - t
+        f0 = 4 * w.head_dim * w.num_q_heads * int((2 * c0 - n0 + 1) * n0 // 2)
+        cpu = {"value": round(f0 / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+               "sample": f"sequence 0's last {n0} query tokens (context {c0}, all {w.num_q_heads} heads), "
+                         f"oracle multi_query call, {dt:.2f} s on one thread"}
+    tflops = flops / (att_ms * 1e-3) / 1e12
+    return {"metric": "chunked prefill paged attention TFLOP/s (pa_multi_query)",
+            "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+            "data": "synthetic",
+            "config": {"workload": w.name, "num_seqs": w.num_seqs, "query_tokens": T,
+                       "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                       "head_dim": w.head_dim, "block_size": w.block_size,
+                       "sum_context_lens": int(ctx.sum()), "flops_per_step": flops,
+                       "kv_bytes_per_step": kv_bytes, "replicas": REPLICAS},
+            "attention_us": round(att_ms * 1e3, 2), "scatter_us": round(float(np.mean(pre)) * 1e3, 2),
+            "kv_gbs": round(kv_bytes / (att_ms * 1e-3) / 1e9, 2),
+            "roofline": {"bound": "mfma", "kernel": "multi_query_kernel", "achieved": round(tflops, 2),
+                         "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_PEAK_TFLOPS[w.dtype], 4), "flops_per_launch": flops,
+                         "traffic": measured_traffic(w.name)},
+            "cpu_baseline": cpu}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -286,6 +383,9 @@ def main():
     ab = algorithmic_bytes(w, ctx)
     if args.swap:
         print(json.dumps(swap_bench(args, w, batch)), flush=True)
+        return
+    if w.query_len:
+        print(json.dumps(mq_bench(args, w, batch)), flush=True)
         return
     log(args, f"[bench] placing {REPLICAS} replicas")
     reps = build_replicas(args, w, batch, identity=False)

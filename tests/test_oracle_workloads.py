@@ -93,7 +93,8 @@ def test_full_size_lengths_match_the_recipe():
     """The seeded draws of every workload (only the length step)."""
     sums = {n: int(W.draw_lengths(w)[0].context_lens.sum()) for n, w in W.WORKLOADS.items()}
     assert sums == {"tiny_fp32": 134, "llama7b": 46958, "llama13b_long": 95677,
-                    "prefix_sharing": 93983, "llama70b_gqa": 191507, "llama7b_fp8": 46958}
+                    "prefix_sharing": 93983, "llama70b_gqa": 191507, "llama7b_fp8": 46958,
+                    "chunked_prefill": 34069}
 
 
 def test_fp8_prefix_step_equals_attention_over_dequantised_tokens():

@@ -26,6 +26,10 @@ Workloads (shapes and length mixes of the serving examples on the pages):
   - llama7b_fp8     llama7b (same seed, lengths and numbers) with the pools held as
                     OCP E4M3 codes and one fp32 scale per (block, KV head) for K and
                     for V; query, new K/V and output stay fp16.
+  - chunked_prefill LLaMA-7B-shaped chunked prefill: 16 seqs, 32 heads MHA, d=128,
+                    B=16, fp16, 8,192 blocks; contexts uniform in [1024, 3072] whose
+                    last 512 tokens are the chunk being prefilled (512 causal query
+                    tokens per sequence over the cached prefix and the chunk).
 
 Draw recipe (numpy PCG64):
   base stream  default_rng(seed): (1) length parameters, (2) free order =
@@ -37,6 +41,8 @@ Draw recipe (numpy PCG64):
                prompt (prefix_sharing only).
   values       standard_normal(float32) rounded to the storage type with
                round-to-nearest-even; bf16 is returned as raw uint16 bits.
+  chunk query  default_rng(SeedSequence([seed, 4, s])): the query rows
+               [query_len][H_q][d] of sequence s (chunked_prefill).
   E4M3 scales  default_rng(SeedSequence([seed, 3])): K scales then V scales,
                [num_blocks][H_kv] float32, each 2^u with u uniform in [-7, -5]
                (448 * scale spans 3.5 to 14 standard deviations of the values).
@@ -73,6 +79,7 @@ class Workload:
     prefix_base: int = 0  # prefix: shared prompt = prefix_base + U{1..block_size-1}
     private_max: int = 0  # prefix: private tokens U{0..private_max}
     kv_dtype: str = ""  # pool storage type; "" = the query's type, "fp8" = E4M3 codes
+    query_len: int = 0  # > 0: that many causal query tokens per sequence (chunked prefill)
 
     @property
     def scale(self) -> float:
@@ -106,6 +113,8 @@ WORKLOADS: Dict[str, Workload] = {
                              "uniform", low=4096, high=8192),
     "llama7b_fp8": Workload("llama7b_fp8", 2, 64, 32, 32, 128, 16, 40000, "f16", 0, "lognormal",
                             kv_dtype="fp8"),
+    "chunked_prefill": Workload("chunked_prefill", 6, 16, 32, 32, 128, 16, 8192, "f16", 0, "uniform",
+                                low=1024, high=3072, query_len=512),
 }
 
 
@@ -252,6 +261,12 @@ def group_prefix_values(w: Workload, j: int, n_tokens: int):
     k = _normal(rng, (n_tokens, w.num_kv_heads, w.head_dim), w.dtype)
     v = _normal(rng, (n_tokens, w.num_kv_heads, w.head_dim), w.dtype)
     return k, v
+
+
+def chunk_queries(w: Workload, s: int, n: int) -> np.ndarray:
+    """Query rows [n][H_q][d] of sequence s's chunk (storage type)."""
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, 4, s]))
+    return _normal(rng, (n, w.num_q_heads, w.head_dim), w.dtype)
 
 
 @dataclasses.dataclass
