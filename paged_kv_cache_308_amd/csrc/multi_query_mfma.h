@@ -6,25 +6,29 @@
 // last n_s positions of its context (their K/V already cached); the token at position
 // p attends to the cached tokens t <= p.
 //
-// A workgroup takes one (KV head, sequence, tile of 16 query rows), a row being one
-// (query token, query head of the group) pair: 16 / g tokens times the g heads that
-// share the KV head.  Its four waves split the keys the tile can see ([0, last row's
-// position]) in 32-key chunks and merge through LDS at the end.  Per chunk and wave:
+// A workgroup takes one (KV head, sequence, tile of 64 query rows), a row being one
+// (query token, query head of the group) pair: 64 / g tokens times the g heads that
+// share the KV head.  Each of its four waves owns 16 rows.  The workgroup walks the
+// keys its rows can see ([0, last row's position]) in 32-key tiles; every tile is
+// loaded from HBM once, through the block table, into double-buffered LDS (K rows with
+// a padded stride, V transposed to [d][key]) while the previous tile is being used,
+// and all four waves read it there.  Per tile and wave:
 //
 //   S^T[t][r]  = sum_d K[t][d] Q[r][d]          A = K rows (16 keys x 32 d), B = Q^T
 //   O^T[d][r] += sum_t V[t][d] P[r][t]          A = V^T (16 d x 32 keys),   B = P^T
 //
-// on v_mfma_f32_16x16x32_{f16,bf16}, with the operand layouts and the staging of the
-// grouped-query decode kernel (K straight from HBM into registers, V through per-wave
-// double-buffered LDS by direct 16-byte LDS loads, the score fragment reused as the P^T
-// operand by matching the k order); the causal mask compares each key's position with
-// its row's.  Softmax is fp32 online in the exp2 domain; P enters the second product
-// rounded to the storage type and the normaliser sums the rounded weights.
+// on v_mfma_f32_16x16x32_{f16,bf16}.  Lane l supplies A[l%16][8(l/16)..+8] and
+// B[8(l/16)..+8][l%16] and receives D[4(l/16)..+4][l%16], so the score fragment holds,
+// per lane, one row's scores for keys 4q..4q+3 and 16+4q..16+4q+3: exactly a P^T
+// operand once the V^T operand uses the same k order (two 8-byte LDS reads of the
+// transposed tile).  The causal mask compares each key's position with its row's; a
+// wave skips tiles past its own last row.  Softmax is fp32 online in the exp2 domain;
+// P enters the second product rounded to the storage type and the normaliser sums the
+// rounded weights.  Rows are written by the wave that owns them (no merge).
 //
-// Tiles are numbered row tile fastest, then sequence, then KV head, and spread over the
-// XCDs in contiguous ranges, so the tiles that read the same sequence's blocks share an
-// XCD's L2 (K and V are read with cacheable loads: every row tile of a sequence reads
-// them).
+// Row tiles are numbered fastest, then sequence, then KV head, and spread over the XCDs
+// in contiguous ranges, so the row tiles that read the same sequence's blocks share an
+// XCD's L2 (K and V are read with cacheable loads).
 #include <hip/hip_runtime.h>
 
 #include "decode_mfma.h"
@@ -36,8 +40,9 @@ namespace mq {
 
 using mfma::Mma;
 using mfma::f32x4;
-constexpr int MW = 4;   // waves per workgroup
-constexpr int CT = 32;  // keys per chunk: two 16-key tiles
+constexpr int MW = 4;        // waves per workgroup, 16 query rows each
+constexpr int ROWS = 16 * MW;  // query rows per workgroup
+constexpr int KT = 32;       // keys per tile: two 16-key operands
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
@@ -46,18 +51,20 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
     int max_blocks_per_seq, int num_seqs, int num_kv_heads, int num_query_tokens, int tiles_per_seq,
     int max_query_len, int log2_block, int num_blocks, float scale_log2) {
-    constexpr int ROW = D * 2;            // bytes per token row
-    constexpr int NKK = D / 32;           // 32-wide d steps of the score product
-    constexpr int NN = D / 16;            // 16-row d fragments of the output
-    constexpr int VL = 16 * ROW / 1024;   // 1 KiB wave loads per 16-key V tile
-    constexpr int RPK = 1024 / ROW;       // token rows per KiB
-    constexpr int KSTR = 1024 + 32;       // LDS stride of one KiB group (padded)
-    constexpr int STAGE = 2 * VL * KSTR;  // LDS bytes of one chunk's V
-    constexpr int WAVE_LDS = 2 * STAGE;   // double-buffered
+    constexpr int ROW = D * 2;             // bytes per token row
+    constexpr int NKK = D / 32;            // 32-wide d steps of the score product
+    constexpr int NN = D / 16;             // 16-row d fragments of the output
+    constexpr int KROW = ROW + 16;         // LDS stride of a key row (16 lanes, 16 bytes each: no bank conflict)
+    constexpr int VTROW = KT * 2 + 8;      // LDS stride of a transposed value row (one d, KT keys)
+    constexpr int KBYTES = KT * KROW;
+    constexpr int BUF = KBYTES + D * VTROW;  // one tile: K rows, then V transposed
+    constexpr int PARTS = ROW / 16;        // 16-byte pieces of a row
+    constexpr int NCH = KT * PARTS / (MW * 64);  // pieces of K (and of V) per thread per tile
+    static_assert(NCH * MW * 64 == KT * PARTS, "tile pieces must divide over the workgroup");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n = lane & 15;  // query row of the tile / key row within a 16-key tile
+    const int n = lane & 15;  // query row of the wave / key row within a 16-key operand
     const int q = lane >> 4;  // k group
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -71,24 +78,24 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
     const int q0 = query_start[s];
     const int nq = query_start[s + 1] - q0;
     const int rows = nq * G;  // flattened (token, head) rows of the sequence
-    if (nq <= 0 || 16 * tile >= rows) return;
-    // invalid lengths: this tile's rows become NaN (no key is read)
+    if (nq <= 0 || ROWS * tile >= rows) return;
     const bool bad_len = ctx < 0 || nq > ctx || nq > max_query_len;
 
-    // this lane's row: token i, head g; its position, and the tile's last position
-    const int r = 16 * tile + n;
+    // this lane's row (token i, head g) and its position; the wave's and the
+    // workgroup's last positions bound the keys they read
+    const int r = ROWS * tile + 16 * wave + n;
     const bool row_ok = r < rows;
     const int ti = (row_ok ? r : rows - 1) / G;
     const int g = (row_ok ? r : rows - 1) % G;
-    const int pos = ctx - nq + ti;  // sees keys t <= pos
-    const int last_row = min(rows, 16 * tile + 16) - 1;
-    const int end = bad_len ? 0 : ctx - nq + last_row / G + 1;  // keys the tile reads
-    const int64_t out_row = (int64_t)q0 + ti;  // row of query / out
+    const int pos = ctx - nq + ti;
+    const int wave_last = min(rows, ROWS * tile + 16 * wave + 16) - 1;
+    const int wave_end = ROWS * tile + 16 * wave < rows ? ctx - nq + wave_last / G + 1 : 0;
+    const int wg_last = min(rows, ROWS * tile + ROWS) - 1;
+    const int end = bad_len ? 0 : ctx - nq + wg_last / G + 1;  // keys the workgroup reads
+    const int64_t out_row = (int64_t)q0 + ti;
     const bool io_ok = row_ok && out_row >= 0 && out_row < num_query_tokens;
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[MW * WAVE_LDS];
-    static_assert((2 * MW * 16 + MW * 16 * D) * 4 <= MW * WAVE_LDS, "merge area must fit the staging area");
-    uint8_t *wave_lds = lds + wave * WAVE_LDS;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
 
     const int block_size = 1 << log2_block;
     const int32_t *table = block_tables + (int64_t)s * max_blocks_per_seq;
@@ -111,63 +118,80 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
     for (int i = 0; i < NN; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     bool bad = bad_len;
 
-    const int nchunks = (end + CT - 1) / CT;
+    const int ntiles = (end + KT - 1) / KT;
 
-    // Byte offset of the first row of 16-key tile `tt` of chunk c, or -1 (past `end` or
-    // a bad entry: the loads then read block 0's first rows, masked like any key past
-    // `end`, so no branch surrounds a load).
-    auto tile_base = [&](int c, int tt) -> int64_t {
-        const int tok = c * CT + 16 * tt;
-        if (tok >= end) return -1;
-        const int lb = tok >> log2_block;
-        if (lb >= max_blocks_per_seq) {
-            bad = true;
-            return -1;
+    // Global loads of key tile t: this thread's NCH pieces of K and of V.  The tile's
+    // keys lie in at most two blocks (B >= 16); their ids are looked up once (scalar).
+    // Keys at or past `end`, and pieces of a bad block, load block 0's first row
+    // instead (inside the pool) and are stored as zeros.
+    struct Stage {
+        u32x4 k[NCH], v[NCH];
+        bool ok[NCH];
+    };
+    auto load_tile = [&](Stage &st, int t) {
+        const int k0 = t * KT;
+        const int lb0 = k0 >> log2_block;
+        const int lb1 = (k0 + KT - 1) >> log2_block;
+        int64_t base0 = -1, base1 = -1;
+        if (lb0 < max_blocks_per_seq) {
+            const int32_t pb = table[lb0];
+            if (pb >= 0 && pb < num_blocks) base0 = (int64_t)pb * block_bytes + head_off;
         }
-        const int32_t pb = table[lb];
-        if (pb < 0 || pb >= num_blocks) {
-            bad = true;
-            return -1;
+        if (lb1 == lb0) {
+            base1 = base0;
+        } else if (lb1 < max_blocks_per_seq && lb1 * block_size < end) {
+            const int32_t pb = table[lb1];
+            if (pb >= 0 && pb < num_blocks) base1 = (int64_t)pb * block_bytes + head_off;
         }
-        return (int64_t)pb * block_bytes + head_off + (int64_t)(tok & (block_size - 1)) * ROW;
-    };
-
-    struct Chunk {
-        u32x4 k[2][NKK];
-    };
-    auto issue = [&](Chunk &b, int c, int st) {
-        uint8_t *stage = wave_lds + st * STAGE;
+        if (base0 < 0 || (base1 < 0 && lb1 * block_size < end)) bad = true;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            int64_t base = tile_base(c, tt);
-            base = base < 0 ? 0 : base;
-#pragma unroll
-            for (int i = 0; i < VL; ++i)
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(value_cache + base + i * 1024 + lane * 16),
-                    (__attribute__((address_space(3))) void *)(stage + (tt * VL + i) * KSTR), 16, 0, 0);
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                b.k[tt][kk] = *(const u32x4 *)(key_cache + base + n * ROW + (32 * kk + 8 * q) * 2);
+        for (int i = 0; i < NCH; ++i) {
+            const int c = threadIdx.x + i * MW * 64;
+            const int key = c / PARTS;
+            const int part = c - key * PARTS;
+            const int kp = k0 + key;
+            const int64_t base = (kp >> log2_block) == lb0 ? base0 : base1;
+            st.ok[i] = kp < end && base >= 0;
+            const int64_t off = st.ok[i] ? base + (int64_t)(kp & (block_size - 1)) * ROW + part * 16 : 0;
+            st.k[i] = *(const u32x4 *)(key_cache + off);
+            st.v[i] = *(const u32x4 *)(value_cache + off);
         }
     };
-    auto v_at = [&](const uint8_t *stage, int rr, int col) -> const uint8_t * {
-        return stage + (rr / RPK) * KSTR + (rr % RPK) * ROW + col;
+    // K rows as they are (padded stride); V transposed: vt[d][key]
+    auto store_tile = [&](const Stage &st, uint8_t *buf) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = threadIdx.x + i * MW * 64;
+            const int key = c / PARTS;
+            const int part = c - key * PARTS;
+            const u32x4 kw = st.ok[i] ? st.k[i] : u32x4{0, 0, 0, 0};
+            const u32x4 vw = st.ok[i] ? st.v[i] : u32x4{0, 0, 0, 0};
+            *(u32x4 *)(buf + key * KROW + part * 16) = kw;
+            uint8_t *vt = buf + KBYTES + key * 2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w = vw[e];  // scalar copy before splitting
+                *(uint16_t *)(vt + (8 * part + 2 * e) * VTROW) = (uint16_t)(w & 0xffffu);
+                *(uint16_t *)(vt + (8 * part + 2 * e + 1) * VTROW) = (uint16_t)(w >> 16);
+            }
+        }
     };
-    auto consume = [&](const Chunk &b, int c, int st) {
-        const uint8_t *stage = wave_lds + st * STAGE;
-        const int tok0 = c * CT;
-        // scores S^T: lane holds keys tok0 + 16 tt + 4 q + i of row n, masked causally
+    auto compute_tile = [&](const uint8_t *buf, int t) {
+        const int k0 = t * KT;
+        // scores S^T: lane holds keys k0 + 16 tt + 4 q + i of row n, masked causally
         float sc[2][4];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) acc = Mma<T>::run(b.k[tt][kk], qb[kk], acc);
+            for (int kk = 0; kk < NKK; ++kk) {
+                const u32x4 ka = *(const u32x4 *)(buf + (16 * tt + n) * KROW + (32 * kk + 8 * q) * 2);
+                acc = Mma<T>::run(ka, qb[kk], acc);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = tok0 + 16 * tt + 4 * q + i;
-                sc[tt][i] = (key <= pos && key < end) ? acc[i] * scale_log2 : -INFINITY;
+                const int key = k0 + 16 * tt + 4 * q + i;
+                sc[tt][i] = key <= pos ? acc[i] * scale_log2 : -INFINITY;
             }
         }
         float cm = sc[0][0];
@@ -181,7 +205,7 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
         const float ms = mn == -INFINITY ? 0.f : mn;
         const float alpha = fast_exp2(m - ms);
         m = mn;
-        // P^T operand: k slot j < 4 -> key 4q + j (tile 0), j >= 4 -> key 16 + 4q + j - 4
+        // P^T operand: k slot j < 4 -> key 4q + j (operand 0), j >= 4 -> key 16 + 4q + j - 4
         uint32_t pk[4];
         float psum = 0.f;
 #pragma unroll
@@ -196,110 +220,57 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
             }
         lsum = lsum * alpha + psum;
         const u32x4 pb = u32x4{pk[0], pk[1], pk[2], pk[3]};
-#pragma unroll
-        for (int nn = 0; nn < NN; ++nn) o[nn] *= alpha;
-        // the chunk's V rows have landed in LDS (issued before its K loads, which the
-        // score product has waited for)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (tok0 + CT > end) {
-            // keys past `end` as zeros: 0 * NaN would poison the product
-            for (int rr = max(0, end - tok0); rr < CT; ++rr)
-                for (int col = lane * 4; col < ROW; col += 256)
-                    *(uint32_t *)v_at(stage, rr, col) = 0u;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
+        // V^T operand per 16-row d fragment: lane reads keys 4q..4q+3 and 16+4q..16+4q+3
+        // of d = 16 nn + n (two 8-byte reads of the transposed tile)
+        const uint8_t *vt = buf + KBYTES;
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn) {
-            uint32_t vk[4];
-#pragma unroll
-            for (int j = 0; j < 8; j += 2) {
-                const int t0 = j < 4 ? 4 * q + j : 16 + 4 * q + (j - 4);
-                const uint16_t a = *(const uint16_t *)v_at(stage, t0, (16 * nn + n) * 2);
-                const uint16_t c2 = *(const uint16_t *)v_at(stage, t0 + 1, (16 * nn + n) * 2);
-                vk[j / 2] = (uint32_t)a | ((uint32_t)c2 << 16);
-            }
-            o[nn] = Mma<T>::run(u32x4{vk[0], vk[1], vk[2], vk[3]}, pb, o[nn]);
+            o[nn] *= alpha;
+            const uint8_t *rowp = vt + (16 * nn + n) * VTROW + 8 * q;
+            const uint2 lo = *(const uint2 *)rowp;
+            const uint2 hi = *(const uint2 *)(rowp + 32);
+            o[nn] = Mma<T>::run(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, o[nn]);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    {
-        const int mine = nchunks > wave ? (nchunks - wave + MW - 1) / MW : 0;
-        Chunk A, Bf;
-        if (mine > 0) {
-            issue(A, wave, 0);
-            int j = 0;
-            for (; j + 2 < mine; j += 2) {
-                issue(Bf, wave + (j + 1) * MW, 1);
-                consume(A, wave + j * MW, 0);
-                issue(A, wave + (j + 2) * MW, 0);
-                consume(Bf, wave + (j + 1) * MW, 1);
-            }
-            if (j + 1 < mine) {
-                issue(Bf, wave + (j + 1) * MW, 1);
-                consume(A, wave + j * MW, 0);
-                consume(Bf, wave + (j + 1) * MW, 1);
-            } else {
-                consume(A, wave + j * MW, 0);
-            }
+    if (ntiles > 0) {
+        Stage st;
+        load_tile(st, 0);
+        store_tile(st, lds);
+        __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            const bool more = t + 1 < ntiles;
+            if (more) load_tile(st, t + 1);
+            if (t * KT < wave_end) compute_tile(lds + (t & 1) * BUF, t);
+            if (more) store_tile(st, lds + ((t + 1) & 1) * BUF);
+            __syncthreads();
         }
     }
 
+    // normaliser of row n over the 4 lanes of its column; every wave owns its rows
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
-
-    // merge the waves through LDS (the staging area is free now)
-    __syncthreads();
-    float *sm_m = (float *)lds;     // [MW][16]
-    float *sm_l = sm_m + MW * 16;   // [MW][16]
-    float *sm_acc = sm_l + MW * 16; // [MW][16][D]
     __shared__ int sm_bad;
     if (threadIdx.x == 0) sm_bad = 0;
     __syncthreads();
     if (bad) sm_bad = 1;
-    if (q == 0) {
-        sm_m[wave * 16 + n] = m;
-        sm_l[wave * 16 + n] = lsum;
-    }
+    __syncthreads();
+    if (!io_ok) return;
+    const bool any_bad = sm_bad != 0;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int64_t obase = (out_row * num_q_heads + kvh * G + g) * D;
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm_acc[(wave * 16 + n) * D + 16 * nn + 4 * q + i] = o[nn][i];
-    __syncthreads();
-    const bool any_bad = sm_bad != 0;
-    for (int t = threadIdx.x; t < 16 * D; t += MW * 64) {
-        const int rn = t / D;
-        const int j = t - rn * D;
-        const int rr = 16 * tile + rn;
-        if (rr >= rows) continue;
-        const int64_t orow = (int64_t)q0 + rr / G;
-        if (orow < 0 || orow >= num_query_tokens) continue;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < MW; ++w) M = fmaxf(M, sm_m[w * 16 + rn]);
-        const float Ms = M == -INFINITY ? 0.f : M;
-        float Lsum = 0.f, A = 0.f;
-#pragma unroll
-        for (int w = 0; w < MW; ++w) {
-            const float f = fast_exp2(sm_m[w * 16 + rn] - Ms);
-            Lsum += sm_l[w * 16 + rn] * f;
-            A += sm_acc[(w * 16 + rn) * D + j] * f;
+        for (int i = 0; i < 4; ++i) {
+            const float ov = any_bad ? NAN : o[nn][i] * inv;
+            store_out<T>(out, obase + 16 * nn + 4 * q + i, ov);
         }
-        float ov = Lsum > 0.f ? A / Lsum : 0.f;
-        if (any_bad) ov = NAN;
-        store_out<T>(out, (orow * num_q_heads + kvh * G + rr % G) * D + j, ov);
-    }
 }
 
 template <typename T, int D, int G>
 int launch_t(const DecodeArgs &a) {
-    const int tiles = (a.max_query_len * G + 15) / 16;
+    const int tiles = (a.max_query_len * G + ROWS - 1) / ROWS;
     const int64_t grid = (int64_t)a.num_kv_heads * a.num_seqs * tiles;
     if (grid > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "grid of %lld workgroups", (long long)grid);
     hipLaunchKernelGGL((multi_query_kernel<T, D, G>), dim3((unsigned)grid), dim3(MW * 64), 0,
