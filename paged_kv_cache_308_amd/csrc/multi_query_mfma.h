@@ -6,10 +6,11 @@
 // last n_s positions of its context (their K/V already cached); the token at position
 // p attends to the cached tokens t <= p.
 //
-// A workgroup takes one (KV head, sequence, tile of 64 query rows), a row being one
-// (query token, query head of the group) pair: 64 / g tokens times the g heads that
-// share the KV head.  Each of its four waves owns 16 rows.  The workgroup walks the
-// keys its rows can see ([0, last row's position]) in 32-key tiles; every tile is
+// A workgroup takes one (KV head, sequence, tile of 128 query rows), a row being one
+// (query token, query head of the group) pair: 128 / g tokens times the g heads that
+// share the KV head.  Each of its four waves owns 32 rows (two 16-row fragments that
+// share every operand read).  The workgroup walks the keys its rows can see ([0, last
+// row's position]) in 64-key tiles; every tile is
 // loaded from HBM once, through the block table, into double-buffered LDS (K rows with
 // a padded stride, V transposed to [d][key]) while the previous tile is being used,
 // and all four waves read it there.  Per tile and wave:
@@ -40,9 +41,16 @@ namespace mq {
 
 using mfma::Mma;
 using mfma::f32x4;
-constexpr int MW = 4;        // waves per workgroup, 16 query rows each
-constexpr int ROWS = 16 * MW;  // query rows per workgroup
-constexpr int KT = 32;       // keys per tile: two 16-key operands
+constexpr int MW = 4;  // waves per workgroup
+#ifndef PA_MQ_FRAGS
+#define PA_MQ_FRAGS 2
+#endif
+#ifndef PA_MQ_KEYS
+#define PA_MQ_KEYS 32
+#endif
+constexpr int RF = PA_MQ_FRAGS;      // 16-row query fragments per wave
+constexpr int ROWS = 16 * RF * MW;   // query rows per workgroup
+static_assert(PA_MQ_KEYS % 32 == 0 && (RF == 1 || RF == 2), "tile shape");
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
@@ -52,19 +60,22 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
     int max_blocks_per_seq, int num_seqs, int num_kv_heads, int num_query_tokens, int tiles_per_seq,
     int max_query_len, int log2_block, int num_blocks, float scale_log2) {
     constexpr int ROW = D * 2;             // bytes per token row
+    constexpr int KT = PA_MQ_KEYS * (D == 64 ? 2 : 1);  // keys per tile: the same bytes at d = 64
     constexpr int NKK = D / 32;            // 32-wide d steps of the score product
     constexpr int NN = D / 16;             // 16-row d fragments of the output
-    constexpr int KROW = ROW + 16;         // LDS stride of a key row (16 lanes, 16 bytes each: no bank conflict)
+    constexpr int NT = KT / 16;            // 16-key score operands per tile
+    constexpr int NH = KT / 32;            // 32-key value products per tile
+    constexpr int KROW = ROW + 16;         // LDS stride of a key row (16 lanes x 16 bytes: no bank conflict)
     constexpr int VTROW = KT * 2 + 8;      // LDS stride of a transposed value row (one d, KT keys)
     constexpr int KBYTES = KT * KROW;
     constexpr int BUF = KBYTES + D * VTROW;  // one tile: K rows, then V transposed
     constexpr int PARTS = ROW / 16;        // 16-byte pieces of a row
     constexpr int NCH = KT * PARTS / (MW * 64);  // pieces of K (and of V) per thread per tile
-    static_assert(NCH * MW * 64 == KT * PARTS, "tile pieces must divide over the workgroup");
+    static_assert(NCH * MW * 64 == KT * PARTS && NCH % 2 == 0, "tile pieces must divide over the workgroup");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n = lane & 15;  // query row of the wave / key row within a 16-key operand
+    const int n = lane & 15;  // query row of a fragment / key row within a 16-key operand
     const int q = lane >> 4;  // k group
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -81,19 +92,25 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
     if (nq <= 0 || ROWS * tile >= rows) return;
     const bool bad_len = ctx < 0 || nq > ctx || nq > max_query_len;
 
-    // this lane's row (token i, head g) and its position; the wave's and the
-    // workgroup's last positions bound the keys they read
-    const int r = ROWS * tile + 16 * wave + n;
-    const bool row_ok = r < rows;
-    const int ti = (row_ok ? r : rows - 1) / G;
-    const int g = (row_ok ? r : rows - 1) % G;
-    const int pos = ctx - nq + ti;
-    const int wave_last = min(rows, ROWS * tile + 16 * wave + 16) - 1;
-    const int wave_end = ROWS * tile + 16 * wave < rows ? ctx - nq + wave_last / G + 1 : 0;
+    // this lane's rows (one per fragment f: token ti, head g) and their positions; the
+    // wave's and the workgroup's last positions bound the keys they read
+    const int wrow0 = ROWS * tile + 16 * RF * wave;  // first row of the wave
+    int pos[RF], gh[RF];
+    int64_t orow[RF];
+    bool io_ok[RF];
+#pragma unroll
+    for (int f = 0; f < RF; ++f) {
+        const int r = wrow0 + 16 * f + n;
+        const bool ok = r < rows;
+        const int ti = (ok ? r : rows - 1) / G;
+        gh[f] = (ok ? r : rows - 1) % G;
+        pos[f] = ctx - nq + ti;
+        orow[f] = (int64_t)q0 + ti;
+        io_ok[f] = ok && orow[f] >= 0 && orow[f] < num_query_tokens;
+    }
+    const int wave_end = wrow0 < rows ? ctx - nq + (min(rows, wrow0 + 16 * RF) - 1) / G + 1 : 0;
     const int wg_last = min(rows, ROWS * tile + ROWS) - 1;
     const int end = bad_len ? 0 : ctx - nq + wg_last / G + 1;  // keys the workgroup reads
-    const int64_t out_row = (int64_t)q0 + ti;
-    const bool io_ok = row_ok && out_row >= 0 && out_row < num_query_tokens;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
 
@@ -102,57 +119,77 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
     const int64_t head_off = (int64_t)kvh * block_size * ROW;
     const int64_t block_bytes = (int64_t)num_kv_heads * block_size * ROW;
 
-    // Q^T operand: lane holds Q[row n][32 kk + 8 q .. +8]; rows past the sequence are zero
-    u32x4 qb[NKK];
+    // Q^T operands: lane holds Q[row n of fragment f][32 kk + 8 q .. +8]; rows past the
+    // sequence are zero
+    u32x4 qb[RF][NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        qb[kk] = u32x4{0, 0, 0, 0};
-        if (io_ok)
-            qb[kk] = *(const u32x4 *)(query + ((out_row * num_q_heads + kvh * G + g) * D + 32 * kk + 8 * q) * 2);
-    }
+    for (int f = 0; f < RF; ++f)
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            qb[f][kk] = u32x4{0, 0, 0, 0};
+            if (io_ok[f])
+                qb[f][kk] = *(const u32x4 *)(query + ((orow[f] * num_q_heads + kvh * G + gh[f]) * D + 32 * kk +
+                                                      8 * q) * 2);
+        }
 
-    float m = -INFINITY;  // running max of row n (same in the 4 lanes of a column)
-    float lsum = 0.f;     // this lane's share of the normaliser
-    f32x4 o[NN];
+    float m[RF], lsum[RF];  // running max (same in a column's 4 lanes), lane's share of the sum
+    f32x4 o[RF][NN];
 #pragma unroll
-    for (int i = 0; i < NN; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < RF; ++f) {
+        m[f] = -INFINITY;
+        lsum[f] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NN; ++i) o[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     bool bad = bad_len;
 
     const int ntiles = (end + KT - 1) / KT;
 
-    // Global loads of key tile t: this thread's NCH pieces of K and of V.  The tile's
-    // keys lie in at most two blocks (B >= 16); their ids are looked up once (scalar).
-    // Keys at or past `end`, and pieces of a bad block, load block 0's first row
-    // instead (inside the pool) and are stored as zeros.
+    // Global loads of key tile t: this thread's NCH pieces of K and of V.  Each 16-key
+    // group lies in one block (B >= 16); the NT block ids are looked up once per tile
+    // (scalar loads).  Keys at or past `end`, and pieces of a bad block, load block 0's
+    // first row instead (inside the pool) and are stored as zeros.
     struct Stage {
         u32x4 k[NCH], v[NCH];
         bool ok[NCH];
     };
+    // Pieces 2i and 2i+1 of a thread are the same 16 bytes of two neighbouring keys, so
+    // the transposed V store writes both keys of a d at once (4 bytes).
+    auto piece_key = [&](int i) -> int {
+        const int c = threadIdx.x + (i / 2) * MW * 64;  // pair index over the tile
+        return 2 * (c / PARTS) + (i & 1);
+    };
+    auto piece_part = [&](int i) -> int {
+        const int c = threadIdx.x + (i / 2) * MW * 64;
+        return c % PARTS;
+    };
     auto load_tile = [&](Stage &st, int t) {
         const int k0 = t * KT;
-        const int lb0 = k0 >> log2_block;
-        const int lb1 = (k0 + KT - 1) >> log2_block;
-        int64_t base0 = -1, base1 = -1;
-        if (lb0 < max_blocks_per_seq) {
-            const int32_t pb = table[lb0];
-            if (pb >= 0 && pb < num_blocks) base0 = (int64_t)pb * block_bytes + head_off;
+        int64_t base[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            base[j] = -1;
+            const int kj = k0 + 16 * j;
+            if (kj < end) {
+                const int lb = kj >> log2_block;
+                if (lb < max_blocks_per_seq) {
+                    const int32_t pb = table[lb];
+                    if (pb >= 0 && pb < num_blocks) base[j] = (int64_t)pb * block_bytes + head_off;
+                }
+                if (base[j] < 0) bad = true;
+            }
         }
-        if (lb1 == lb0) {
-            base1 = base0;
-        } else if (lb1 < max_blocks_per_seq && lb1 * block_size < end) {
-            const int32_t pb = table[lb1];
-            if (pb >= 0 && pb < num_blocks) base1 = (int64_t)pb * block_bytes + head_off;
-        }
-        if (base0 < 0 || (base1 < 0 && lb1 * block_size < end)) bad = true;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            const int c = threadIdx.x + i * MW * 64;
-            const int key = c / PARTS;
-            const int part = c - key * PARTS;
+            const int key = piece_key(i);
+            const int part = piece_part(i);
             const int kp = k0 + key;
-            const int64_t base = (kp >> log2_block) == lb0 ? base0 : base1;
-            st.ok[i] = kp < end && base >= 0;
-            const int64_t off = st.ok[i] ? base + (int64_t)(kp & (block_size - 1)) * ROW + part * 16 : 0;
+            int64_t b = base[0];
+#pragma unroll
+            for (int j = 1; j < NT; ++j)
+                if ((key >> 4) == j) b = base[j];
+            st.ok[i] = kp < end && b >= 0;
+            const int64_t off = st.ok[i] ? b + (int64_t)(kp & (block_size - 1)) * ROW + part * 16 : 0;
             st.k[i] = *(const u32x4 *)(key_cache + off);
             st.v[i] = *(const u32x4 *)(value_cache + off);
         }
@@ -160,76 +197,107 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
     // K rows as they are (padded stride); V transposed: vt[d][key]
     auto store_tile = [&](const Stage &st, uint8_t *buf) {
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = threadIdx.x + i * MW * 64;
-            const int key = c / PARTS;
-            const int part = c - key * PARTS;
-            const u32x4 kw = st.ok[i] ? st.k[i] : u32x4{0, 0, 0, 0};
-            const u32x4 vw = st.ok[i] ? st.v[i] : u32x4{0, 0, 0, 0};
-            *(u32x4 *)(buf + key * KROW + part * 16) = kw;
+        for (int i = 0; i < NCH; i += 2) {
+            const int key = piece_key(i);  // even; piece i + 1 holds key + 1
+            const int part = piece_part(i);
+            const u32x4 k0w = st.ok[i] ? st.k[i] : u32x4{0, 0, 0, 0};
+            const u32x4 k1w = st.ok[i + 1] ? st.k[i + 1] : u32x4{0, 0, 0, 0};
+            const u32x4 v0w = st.ok[i] ? st.v[i] : u32x4{0, 0, 0, 0};
+            const u32x4 v1w = st.ok[i + 1] ? st.v[i + 1] : u32x4{0, 0, 0, 0};
+            *(u32x4 *)(buf + key * KROW + part * 16) = k0w;
+            *(u32x4 *)(buf + (key + 1) * KROW + part * 16) = k1w;
             uint8_t *vt = buf + KBYTES + key * 2;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t w = vw[e];  // scalar copy before splitting
-                *(uint16_t *)(vt + (8 * part + 2 * e) * VTROW) = (uint16_t)(w & 0xffffu);
-                *(uint16_t *)(vt + (8 * part + 2 * e + 1) * VTROW) = (uint16_t)(w >> 16);
+                const uint32_t a = v0w[e], b = v1w[e];  // scalar copies before splitting
+                // d = 8 part + 2e: (key, key + 1) low halves; d + 1: high halves
+                *(uint32_t *)(vt + (8 * part + 2 * e) * VTROW) = (a & 0xffffu) | (b << 16);
+                *(uint32_t *)(vt + (8 * part + 2 * e + 1) * VTROW) = (a >> 16) | (b & 0xffff0000u);
             }
         }
     };
     auto compute_tile = [&](const uint8_t *buf, int t) {
         const int k0 = t * KT;
-        // scores S^T: lane holds keys k0 + 16 tt + 4 q + i of row n, masked causally
-        float sc[2][4];
+        // scores S^T: lane holds keys k0 + 16 tt + 4 q + i of row n of each fragment
+        float sc[RF][NT][4];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < NT; ++tt) {
+            f32x4 acc[RF];
+#pragma unroll
+            for (int f = 0; f < RF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 const u32x4 ka = *(const u32x4 *)(buf + (16 * tt + n) * KROW + (32 * kk + 8 * q) * 2);
-                acc = Mma<T>::run(ka, qb[kk], acc);
+#pragma unroll
+                for (int f = 0; f < RF; ++f) acc[f] = Mma<T>::run(ka, qb[f][kk], acc[f]);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = k0 + 16 * tt + 4 * q + i;
-                sc[tt][i] = key <= pos ? acc[i] * scale_log2 : -INFINITY;
-            }
+            for (int f = 0; f < RF; ++f)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = k0 + 16 * tt + 4 * q + i;
+                    sc[f][tt][i] = key <= pos[f] ? acc[f][i] * scale_log2 : -INFINITY;
+                }
         }
-        float cm = sc[0][0];
+        // P^T operands per 32-key half h: k slot j < 4 -> key 32h + 4q + j,
+        // j >= 4 -> key 32h + 16 + 4q + j - 4
+        u32x4 pb[RF][NH];
+        float alpha[RF];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int f = 0; f < RF; ++f) {
+            float cm = sc[f][0][0];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[tt][i]);
-        cm = fmaxf(cm, __shfl_xor(cm, 16));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
-        const float mn = fmaxf(m, cm);
-        const float ms = mn == -INFINITY ? 0.f : mn;
-        const float alpha = fast_exp2(m - ms);
-        m = mn;
-        // P^T operand: k slot j < 4 -> key 4q + j (operand 0), j >= 4 -> key 16 + 4q + j - 4
-        uint32_t pk[4];
-        float psum = 0.f;
+            for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+                for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[f][tt][i]);
+            cm = fmaxf(cm, __shfl_xor(cm, 16));
+            cm = fmaxf(cm, __shfl_xor(cm, 32));
+            const float mn = fmaxf(m[f], cm);
+            const float ms = mn == -INFINITY ? 0.f : mn;
+            alpha[f] = fast_exp2(m[f] - ms);
+            m[f] = mn;
+            float psum = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-                float b0, b1;
-                const uint32_t h0 = Mma<T>::round(fast_exp2(sc[tt][i] - ms), b0);
-                const uint32_t h1 = Mma<T>::round(fast_exp2(sc[tt][i + 1] - ms), b1);
-                psum += b0 + b1;
-                pk[2 * tt + i / 2] = h0 | (h1 << 16);
+            for (int h = 0; h < NH; ++h) {
+                uint32_t pk[4];
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int i = 0; i < 4; i += 2) {
+                        float b0, b1;
+                        const uint32_t h0 = Mma<T>::round(fast_exp2(sc[f][2 * h + u][i] - ms), b0);
+                        const uint32_t h1 = Mma<T>::round(fast_exp2(sc[f][2 * h + u][i + 1] - ms), b1);
+                        psum += b0 + b1;
+                        pk[2 * u + i / 2] = h0 | (h1 << 16);
+                    }
+                pb[f][h] = u32x4{pk[0], pk[1], pk[2], pk[3]};
             }
-        lsum = lsum * alpha + psum;
-        const u32x4 pb = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        // V^T operand per 16-row d fragment: lane reads keys 4q..4q+3 and 16+4q..16+4q+3
-        // of d = 16 nn + n (two 8-byte reads of the transposed tile)
+            lsum[f] = lsum[f] * alpha[f] + psum;
+        }
+        // V^T operand per 16-row d fragment and half: keys 32h + 4q..+3 and 32h + 16 + 4q..+3
+        // of d = 16 nn + n (two 8-byte reads of the transposed tile), shared by the fragments
         const uint8_t *vt = buf + KBYTES;
+        // rescale only when some row's running max moved (otherwise every alpha is 1)
+        bool moved = false;
+#pragma unroll
+        for (int f = 0; f < RF; ++f) moved |= alpha[f] != 1.f;
+        if (__any(moved)) {
+#pragma unroll
+            for (int f = 0; f < RF; ++f)
+#pragma unroll
+                for (int nn = 0; nn < NN; ++nn) o[f][nn] *= alpha[f];
+        }
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn) {
-            o[nn] *= alpha;
-            const uint8_t *rowp = vt + (16 * nn + n) * VTROW + 8 * q;
-            const uint2 lo = *(const uint2 *)rowp;
-            const uint2 hi = *(const uint2 *)(rowp + 32);
-            o[nn] = Mma<T>::run(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, o[nn]);
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                const uint8_t *rowp = vt + (16 * nn + n) * VTROW + 64 * h + 8 * q;
+                const uint2 lo = *(const uint2 *)rowp;
+                const uint2 hi = *(const uint2 *)(rowp + 32);
+                const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+                for (int f = 0; f < RF; ++f) o[f][nn] = Mma<T>::run(va, pb[f][h], o[f][nn]);
+            }
         }
     };
 
@@ -247,25 +315,29 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
         }
     }
 
-    // normaliser of row n over the 4 lanes of its column; every wave owns its rows
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
     __shared__ int sm_bad;
     if (threadIdx.x == 0) sm_bad = 0;
     __syncthreads();
     if (bad) sm_bad = 1;
     __syncthreads();
-    if (!io_ok) return;
     const bool any_bad = sm_bad != 0;
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const int64_t obase = (out_row * num_q_heads + kvh * G + g) * D;
+    // each wave writes its own rows; the normaliser of a row sums its column's 4 lanes
 #pragma unroll
-    for (int nn = 0; nn < NN; ++nn)
+    for (int f = 0; f < RF; ++f) {
+        float l = lsum[f];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (!io_ok[f]) continue;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const int64_t obase = (orow[f] * num_q_heads + kvh * G + gh[f]) * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float ov = any_bad ? NAN : o[nn][i] * inv;
-            store_out<T>(out, obase + 16 * nn + 4 * q + i, ov);
-        }
+        for (int nn = 0; nn < NN; ++nn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ov = any_bad ? NAN : o[f][nn][i] * inv;
+                store_out<T>(out, obase + 16 * nn + 4 * q + i, ov);
+            }
+    }
 }
 
 template <typename T, int D, int G>
