@@ -433,9 +433,11 @@ def main():
     gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
     achieved = ab["total_unique"] / (dec_avg * 1e-3) / 1e9
     g = w.num_q_heads // w.num_kv_heads
-    mfma = w.kv != "fp8" and (args.variant == 2 or (args.variant == 0 and g >= 2 and w.dtype != "f32"))
-    kernels = ("decode_mfma_kernel" if mfma else "decode_valu_kernel") + \
-        (" + lse_merge_kernel" if args.P else "")
+    mfma = w.kv != "fp8" and args.P >= 0 and (
+        args.variant == 2 or (args.variant == 0 and g >= 2 and w.dtype != "f32"))
+    kernels = ("decode_mfma_kernel" if mfma else
+               "decode_balanced_kernel" if args.P < 0 else "decode_valu_kernel") + \
+        (" + balanced_merge_kernel" if args.P < 0 else " + lse_merge_kernel" if args.P else "")
     line = {
         "metric": "paged decode attn: effective KV HBM GB/s (% of peak) and decode seqs/sec",
         "value": round(gbs, 2),
