@@ -369,7 +369,7 @@ def mq_bench(args, w, batch) -> dict:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(sequences, KV heads and context partitions shard without communication; "
               "run one process per GPU)", file=sys.stderr)
         sys.exit(2)
