@@ -26,9 +26,16 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-fhip-fp32-correctly-rounded-divide-sqrt"]
 
 
+# Matrix-core units: keep MFMA accumulators in ordinary VGPRs.  By default the compiler
+# places them in AGPRs and then moves them back and forth around every VALU touch
+# (the online-softmax rescale), hundreds of v_accvgpr moves per loop iteration.
+SOURCE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for src in (
+    "decode_mfma_f16.hip", "decode_mfma_bf16.hip", "multi_query_mfma_f16.hip", "multi_query_mfma_bf16.hip")}
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *DEVICE, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -67,11 +67,17 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
     constexpr int NH = KT / 32;            // 32-key value products per tile
     constexpr int KROW = ROW + 16;         // LDS stride of a key row (16 lanes x 16 bytes: no bank conflict)
     constexpr int VTROW = KT * 2 + 8;      // LDS stride of a transposed value row (one d, KT keys)
+    // The transposed V tile is kept in 8-byte groups of 4 keys; group g of row d sits at
+    // slot g ^ vswz(d) (vswz < 8 only permutes groups within each 8-group block).  With this swizzle the staging stores of a wave (16 or 8 row
+    // pieces times 4 or 8 key pairs) fall in different banks, and the operand reads (16
+    // consecutive d, one group) are unchanged in pattern.
     constexpr int KBYTES = KT * KROW;
     constexpr int BUF = KBYTES + D * VTROW;  // one tile: K rows, then V transposed
     constexpr int PARTS = ROW / 16;        // 16-byte pieces of a row
     constexpr int NCH = KT * PARTS / (MW * 64);  // pieces of K (and of V) per thread per tile
     static_assert(NCH * MW * 64 == KT * PARTS && NCH % 2 == 0, "tile pieces must divide over the workgroup");
+
+    auto vswz = [](int d) -> int { return ((d >> 5) & (PARTS / 4 - 1)) * (32 / PARTS); };
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -132,7 +138,20 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
                                                       8 * q) * 2);
         }
 
-    float m[RF], lsum[RF];  // running max (same in a column's 4 lanes), lane's share of the sum
+    // Scores stay unscaled until the exponent: exp2(s * x - m) with s = |scale * log2 e| > 0,
+    // so the running max can be taken on raw products (a negative scale flips the sign
+    // of q instead, which is exact).
+    const float sl = fabsf(scale_log2);
+    if (scale_log2 < 0.f) {
+#pragma unroll
+        for (int f = 0; f < RF; ++f)
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) qb[f][kk] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    }
+    // first key position any of the wave's rows cannot see: tiles below it need no mask
+    const int wave_first_pos = ctx - nq + min(wrow0, rows - 1) / G;
+
+    float m[RF], lsum[RF];  // running max (scaled, same in a column's 4 lanes), lane's share of the sum
     f32x4 o[RF][NN];
 #pragma unroll
     for (int f = 0; f < RF; ++f) {
@@ -152,20 +171,28 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
     struct Stage {
         u32x4 k[NCH], v[NCH];
         bool ok[NCH];
+        bool full;  // every piece of the tile is valid (uniform): no zeroing needed
     };
     // Pieces 2i and 2i+1 of a thread are the same 16 bytes of two neighbouring keys, so
-    // the transposed V store writes both keys of a d at once (4 bytes).
-    auto piece_key = [&](int i) -> int {
+    // the transposed V store writes both keys of a d at once (4 bytes).  Everything
+    // that depends only on the thread is computed once: a piece's key, its byte offset
+    // inside its 16-key group of rows, and its LDS destinations.
+    int pkey[NCH], prow[NCH], kst[NCH], vst[NCH / 2];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
         const int c = threadIdx.x + (i / 2) * MW * 64;  // pair index over the tile
-        return 2 * (c / PARTS) + (i & 1);
-    };
-    auto piece_part = [&](int i) -> int {
-        const int c = threadIdx.x + (i / 2) * MW * 64;
-        return c % PARTS;
-    };
+        const int part = c % PARTS;
+        pkey[i] = 2 * (c / PARTS) + (i & 1);
+        prow[i] = (pkey[i] & 15) * ROW + part * 16;
+        kst[i] = pkey[i] * KROW + part * 16;
+        if ((i & 1) == 0)  // d = 8 part + j (j < 8) shares the swizzle of d = 8 part
+            vst[i / 2] = 8 * part * VTROW + 8 * ((pkey[i] >> 2) ^ vswz(8 * part)) + (pkey[i] & 3) * 2;
+    }
     auto load_tile = [&](Stage &st, int t) {
         const int k0 = t * KT;
+        // byte offset of each 16-key group's first row (uniform), -1 if not valid
         int64_t base[NT];
+        bool full = k0 + KT <= end;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             base[j] = -1;
@@ -174,22 +201,22 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
                 const int lb = kj >> log2_block;
                 if (lb < max_blocks_per_seq) {
                     const int32_t pb = table[lb];
-                    if (pb >= 0 && pb < num_blocks) base[j] = (int64_t)pb * block_bytes + head_off;
+                    if (pb >= 0 && pb < num_blocks)
+                        base[j] = (int64_t)pb * block_bytes + head_off + (int64_t)(kj & (block_size - 1)) * ROW;
                 }
                 if (base[j] < 0) bad = true;
             }
+            full = full && base[j] >= 0;
         }
+        st.full = full;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            const int key = piece_key(i);
-            const int part = piece_part(i);
-            const int kp = k0 + key;
             int64_t b = base[0];
 #pragma unroll
             for (int j = 1; j < NT; ++j)
-                if ((key >> 4) == j) b = base[j];
-            st.ok[i] = kp < end && b >= 0;
-            const int64_t off = st.ok[i] ? b + (int64_t)(kp & (block_size - 1)) * ROW + part * 16 : 0;
+                if ((pkey[i] >> 4) == j) b = base[j];
+            st.ok[i] = k0 + pkey[i] < end && b >= 0;
+            const int64_t off = st.ok[i] ? b + prow[i] : 0;
             st.k[i] = *(const u32x4 *)(key_cache + off);
             st.v[i] = *(const u32x4 *)(value_cache + off);
         }
@@ -198,24 +225,28 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
     auto store_tile = [&](const Stage &st, uint8_t *buf) {
 #pragma unroll
         for (int i = 0; i < NCH; i += 2) {
-            const int key = piece_key(i);  // even; piece i + 1 holds key + 1
-            const int part = piece_part(i);
-            const u32x4 k0w = st.ok[i] ? st.k[i] : u32x4{0, 0, 0, 0};
-            const u32x4 k1w = st.ok[i + 1] ? st.k[i + 1] : u32x4{0, 0, 0, 0};
-            const u32x4 v0w = st.ok[i] ? st.v[i] : u32x4{0, 0, 0, 0};
-            const u32x4 v1w = st.ok[i + 1] ? st.v[i + 1] : u32x4{0, 0, 0, 0};
-            *(u32x4 *)(buf + key * KROW + part * 16) = k0w;
-            *(u32x4 *)(buf + (key + 1) * KROW + part * 16) = k1w;
-            uint8_t *vt = buf + KBYTES + key * 2;
+            u32x4 k0w = st.k[i], k1w = st.k[i + 1], v0w = st.v[i], v1w = st.v[i + 1];
+            if (!st.full) {
+                if (!st.ok[i]) k0w = v0w = u32x4{0, 0, 0, 0};
+                if (!st.ok[i + 1]) k1w = v1w = u32x4{0, 0, 0, 0};
+            }
+            *(u32x4 *)(buf + kst[i]) = k0w;
+            *(u32x4 *)(buf + kst[i + 1]) = k1w;
+            uint8_t *vt = buf + KBYTES + vst[i / 2];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t a = v0w[e], b = v1w[e];  // scalar copies before splitting
                 // d = 8 part + 2e: (key, key + 1) low halves; d + 1: high halves
-                *(uint32_t *)(vt + (8 * part + 2 * e) * VTROW) = (a & 0xffffu) | (b << 16);
-                *(uint32_t *)(vt + (8 * part + 2 * e + 1) * VTROW) = (a >> 16) | (b & 0xffff0000u);
+                *(uint32_t *)(vt + (2 * e) * VTROW) = (a & 0xffffu) | (b << 16);
+                *(uint32_t *)(vt + (2 * e + 1) * VTROW) = (a >> 16) | (b & 0xffff0000u);
             }
         }
     };
+    // V^T operand reads: d = 16 nn + n, keys of group g = 8h + q (+4): the swizzle of
+    // d depends on nn only, so a lane needs one base per swizzle value
+    int vrd[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vrd[c] = n * VTROW + 8 * (q ^ (2 * c));
     auto compute_tile = [&](const uint8_t *buf, int t) {
         const int k0 = t * KT;
         // scores S^T: lane holds keys k0 + 16 tt + 4 q + i of row n of each fragment
@@ -234,10 +265,16 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
 #pragma unroll
             for (int f = 0; f < RF; ++f)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = k0 + 16 * tt + 4 * q + i;
-                    sc[f][tt][i] = key <= pos[f] ? acc[f][i] * scale_log2 : -INFINITY;
-                }
+                for (int i = 0; i < 4; ++i) sc[f][tt][i] = acc[f][i];
+        }
+        if (k0 + KT - 1 > wave_first_pos) {  // a diagonal tile: mask keys past each row
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int f = 0; f < RF; ++f)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (k0 + 16 * tt + 4 * q + i > pos[f]) sc[f][tt][i] = -INFINITY;
         }
         // P^T operands per 32-key half h: k slot j < 4 -> key 32h + 4q + j,
         // j >= 4 -> key 32h + 16 + 4q + j - 4
@@ -252,7 +289,7 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
                 for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[f][tt][i]);
             cm = fmaxf(cm, __shfl_xor(cm, 16));
             cm = fmaxf(cm, __shfl_xor(cm, 32));
-            const float mn = fmaxf(m[f], cm);
+            const float mn = fmaxf(m[f], cm * sl);
             const float ms = mn == -INFINITY ? 0.f : mn;
             alpha[f] = fast_exp2(m[f] - ms);
             m[f] = mn;
@@ -265,8 +302,8 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; i += 2) {
                         float b0, b1;
-                        const uint32_t h0 = Mma<T>::round(fast_exp2(sc[f][2 * h + u][i] - ms), b0);
-                        const uint32_t h1 = Mma<T>::round(fast_exp2(sc[f][2 * h + u][i + 1] - ms), b1);
+                        const uint32_t h0 = Mma<T>::round(fast_exp2(fmaf(sc[f][2 * h + u][i], sl, -ms)), b0);
+                        const uint32_t h1 = Mma<T>::round(fast_exp2(fmaf(sc[f][2 * h + u][i + 1], sl, -ms)), b1);
                         psum += b0 + b1;
                         pk[2 * u + i / 2] = h0 | (h1 << 16);
                     }
@@ -276,7 +313,7 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
         }
         // V^T operand per 16-row d fragment and half: keys 32h + 4q..+3 and 32h + 16 + 4q..+3
         // of d = 16 nn + n (two 8-byte reads of the transposed tile), shared by the fragments
-        const uint8_t *vt = buf + KBYTES;
+        uint8_t *vt = (uint8_t *)buf + KBYTES;
         // rescale only when some row's running max moved (otherwise every alpha is 1)
         bool moved = false;
 #pragma unroll
@@ -291,9 +328,14 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
         for (int nn = 0; nn < NN; ++nn) {
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
-                const uint8_t *rowp = vt + (16 * nn + n) * VTROW + 64 * h + 8 * q;
-                const uint2 lo = *(const uint2 *)rowp;
-                const uint2 hi = *(const uint2 *)(rowp + 32);
+                // vswz(16 nn + n) = 2 c with c = (nn / 2) & (PARTS / 4 - 1) for d = 128,
+                // or 4 c' for d = 64; both are covered by vrd (q ^ 2c over c < 4)
+                const int sw = ((16 * nn) >> 5 & (PARTS / 4 - 1)) * (32 / PARTS);  // folds when unrolled
+                const uint8_t *row = vt + (16 * nn) * VTROW + 64 * h + vrd[sw / 2];
+                const uint2 lo = *(const uint2 *)row;  // group 8h + q, at slot 8h + (q ^ sw)
+                // group 8h + 4 + q sits at slot 8h + ((q ^ sw) ^ 4): 32 bytes up, or down
+                // when the swizzle already set that bit
+                const uint2 hi = *(const uint2 *)(row + ((sw & 4) ? -32 : 32));
                 const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
                 for (int f = 0; f < RF; ++f) o[f][nn] = Mma<T>::run(va, pb[f][h], o[f][nn]);
