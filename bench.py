@@ -4,9 +4,11 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b]
 
 A step is one decode step of the whole batch on the device, inputs resident in
 HBM: the copy-on-write block copies the step raised (prefix_sharing only), the
-newest tokens' K/V scattered into their slots (pa_reshape_and_cache), and decode
-attention over the block tables (pa_decode, with context partitions and their
-log-sum-exp merge when the workload uses them).  Steps rotate over R replicas of
+newest tokens' K/V stored into their slots, and decode attention over the block
+tables (with context partitions and their log-sum-exp merge when the workload uses
+them).  Where the vector kernel serves the step, the store rides in the attention
+launch (pa_decode_append / pa_decode_fp8_append); otherwise (--unfused, the matrix
+cores, the balanced split) it is its own launch (pa_reshape_and_cache).  Steps rotate over R replicas of
 the batch in separate allocations, so no step finds the previous one's K/V in the
 last-level cache.
 
@@ -84,6 +86,9 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--variant", type=int, default=0)
     ap.add_argument("--no-identity", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="store the newest tokens with their own launch even where the attention "
+                         "launch can do it")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--swap", type=int, default=0, metavar="N",
@@ -156,10 +161,14 @@ def run_steps(args, reps, n_steps: int, record: bool):
             evs[k][0].record(st)
         if src.numel():
             db.cache.copy(src, dst, st)
-        db.cache.write(db.new_key, db.new_value, db.slot_mapping, st)
+        if not args.fused:
+            db.cache.write(db.new_key, db.new_value, db.slot_mapping, st)
         if record:
             evs[k][1].record(st)
-        db.attend(args.P, args.variant, out=out, workspace=ws, stream=st)
+        if args.fused:  # the newest tokens' store rides in the attention launch
+            db.step(args.P, args.variant, out=out, workspace=ws, stream=st)
+        else:
+            db.attend(args.P, args.variant, out=out, workspace=ws, stream=st)
         if record:
             evs[k][2].record(st)
     t1.record(st)
@@ -404,6 +413,11 @@ def main():
     reps = build_replicas(args, w, batch, identity=False)
     # tokens held in the pool (a block shared by several sequences counts once)
     ab = algorithmic_bytes(w, ctx, reps[0][0].cache.alloc.stats()["stored_tokens"])
+    args.fused = not args.unfused and reps[0][0].cache.fused_step_ok(w.num_q_heads, args.P, args.variant)
+    if args.fused:  # the attention launch also stores the newest K/V into the pool
+        newest = 2 * w.num_seqs * w.num_kv_heads * w.head_dim * w.kv_elem_bytes
+        ab["total"] += newest
+        ab["total_unique"] += newest
 
     log(args, f"[bench] warmup {args.warmup}")
     run_steps(args, reps, args.warmup, record=False)
@@ -461,6 +475,7 @@ def main():
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "decode_us": round(dec_avg * 1e3, 2),
+        "fused_store": args.fused,
         "pre_decode_us": round(float(np.mean(pre_ms)) * 1e3, 2),
         "decode_kv_gbs": round(ab["kv"] / (dec_avg * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": kernels, "achieved": round(achieved, 2),

@@ -126,6 +126,26 @@ int pa_decode(void *out, const void *query, const void *key_cache, const void *v
               int variant, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The decode step in one call: each sequence's newest token, new_key[s] / new_value[s]
+ * ([num_seqs][num_kv_heads][head_dim] of `dtype`, device), is stored at position
+ * context_lens[s] - 1 of its table (block table[(ctx-1) / B], slot (ctx-1) % B) and
+ * the attention of pa_decode is computed over all ctx tokens.  The result and the
+ * pools afterwards equal pa_reshape_and_cache with those slots followed by pa_decode
+ * (up to the order of the fp32 sums).  The vector kernel does both in one launch (one
+ * pass or partitions); PA_VARIANT_MFMA and PA_PARTITION_BALANCED return
+ * PA_ERR_UNSUPPORTED.  Sequences with ctx <= 0 store nothing.  The block holding
+ * position ctx - 1 must not appear in another sequence's table (it is exclusive once the
+ * step's copy-on-write copies have run, [cpai] §6).  Other arguments and errors as
+ * pa_decode.
+ */
+int pa_decode_append(void *out, const void *query, const void *new_key, const void *new_value,
+                     void *key_cache, void *value_cache, const int32_t *block_tables,
+                     int max_blocks_per_seq, const int32_t *context_lens, int num_seqs, int num_q_heads,
+                     int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_context_len,
+                     float scale, int dtype, int partition_size, int variant, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
  * Write the newest tokens' K/V into their slots ([wmrh] "KV cache": at a decode step
  * only the newest token's K and V are computed and cached; [cpai] §5 base + offset):
  *   key_cache[slot / B][k][slot % B][:] = key[i][k][:]   (same for value)
@@ -224,6 +244,15 @@ int pa_decode_fp8(void *out, const void *query, const void *key_cache, const voi
                   int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
                   int max_context_len, float scale, int dtype, int partition_size, int variant,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* pa_decode_append over E4M3 pools: new_key / new_value are `dtype` (f16 or bf16) and are
+ * stored as the codes pa_reshape_and_cache_fp8 would write (same rounding, bit for bit). */
+int pa_decode_fp8_append(void *out, const void *query, const void *new_key, const void *new_value,
+                         void *key_cache, void *value_cache, const float *k_scales, const float *v_scales,
+                         const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                         int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                         int num_blocks, int max_context_len, float scale, int dtype, int partition_size,
+                         int variant, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Host-side checks ([cpai] §13).  PA_ERR_BOUNDS names the first offending entry in
  * pa_last_error. */

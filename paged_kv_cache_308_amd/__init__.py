@@ -28,7 +28,8 @@ PA_PARTITION_BALANCED = -1
 EXPORTS = (
     "pa_status_str", "pa_last_error", "pa_abi_version", "pa_decode_workspace_bytes", "pa_decode",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_check_tables",
-    "pa_reshape_and_cache_fp8", "pa_decode_fp8", "pa_multi_query",
+    "pa_reshape_and_cache_fp8", "pa_decode_fp8", "pa_multi_query", "pa_decode_append",
+    "pa_decode_fp8_append",
     "pa_check_copy_pairs", "pa_alloc_adopt",
     "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_set_free_order", "pa_alloc_new_seq",
     "pa_alloc_append_slot", "pa_alloc_append_slots", "pa_alloc_fork", "pa_alloc_free_seq",
@@ -76,6 +77,10 @@ def _lib():
                                 i32, f32, i32, i32, i32, vp, sz, vp]),
         "pa_multi_query": (i32, [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                  i32, f32, i32, vp]),
+        "pa_decode_append": (i32, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                   i32, f32, i32, i32, i32, vp, sz, vp]),
+        "pa_decode_fp8_append": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
+                                       i32, i32, i32, f32, i32, i32, i32, vp, sz, vp]),
         "pa_copy_blocks": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
         "pa_swap_blocks": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]),
         "pa_alloc_adopt": (i32, [vp, i32, i64p, i32p, i32]),
@@ -195,6 +200,51 @@ def pa_multi_query(out, query, key_cache, value_cache, block_tables, context_len
         _dev(query_start, "query_start", torch.int32), S, T, int(max_query_len), Hq, Hkv, d, B, nb,
         float(scale), dtype_code(query), _stream(stream))
     _check(rc, "pa_multi_query")
+    return out
+
+
+def pa_decode_append(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                     context_lens, scale: float, max_context_len: int = 0, partition_size: int = 0,
+                     variant: int = PA_VARIANT_VALU, workspace=None, stream=None, k_scales=None,
+                     v_scales=None):
+    """Store each sequence's newest token (new_key/new_value [S][H_kv][d], the query's type)
+    at position ctx - 1 and attend, in one launch.  E4M3 pools (uint8) need k_scales and
+    v_scales."""
+    torch = _torch()
+    S, Hq, d = query.shape
+    nb, Hkv, B, d2 = key_cache.shape
+    if d2 != d or value_cache.shape != key_cache.shape or out.shape != query.shape:
+        raise ValueError("shape mismatch")
+    if new_key.shape != (S, Hkv, d) or new_value.shape != new_key.shape:
+        raise ValueError("new_key / new_value must be [S][H_kv][d]")
+    for t in (new_key, new_value, out):
+        if t.dtype != query.dtype:
+            raise ValueError("query, new tokens and out must share one dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables / context_lens shape")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    common = (_dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+              _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, d, B, nb,
+              int(max_context_len), float(scale), dtype_code(query), int(partition_size), int(variant),
+              ws_ptr, ws_bytes, _stream(stream))
+    if _is_fp8(key_cache):
+        if k_scales is None or v_scales is None or k_scales.shape != (nb, Hkv) or v_scales.shape != (nb, Hkv):
+            raise ValueError("E4M3 pools need scales [num_blocks][H_kv]")
+        rc = _lib().pa_decode_fp8_append(
+            _dev(out, "out"), _dev(query, "query"), _dev(new_key, "new_key"), _dev(new_value, "new_value"),
+            _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+            _dev(k_scales, "k_scales", torch.float32), _dev(v_scales, "v_scales", torch.float32), *common)
+        _check(rc, "pa_decode_fp8_append")
+    else:
+        if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+            raise ValueError("pools must share the query's dtype")
+        rc = _lib().pa_decode_append(
+            _dev(out, "out"), _dev(query, "query"), _dev(new_key, "new_key"), _dev(new_value, "new_value"),
+            _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), *common)
+        _check(rc, "pa_decode_append")
     return out
 
 

@@ -195,6 +195,14 @@ static int decode_common(DecodeArgs &a, int max_context_len, float scale, int va
     const int kernel_choice = variant & 15;
     if (kernel_choice > PA_VARIANT_MFMA || (variant & ~(15 | PA_DECODE_SHARED_KV)))
         return fail(PA_ERR_INVALID, "variant %d", variant);
+    if (a.new_key) {
+        // the fused newest-token store lives in the vector kernel's one-pass and
+        // partitioned forms
+        if (!a.new_value || !a.key_out || !a.value_out) return fail(PA_ERR_INVALID, "NULL new token pointer");
+        if (balanced || kernel_choice == PA_VARIANT_MFMA)
+            return fail(PA_ERR_UNSUPPORTED, "the fused newest-token store runs on the vector kernel "
+                                            "(one pass or partitions)");
+    }
 
     a.max_partitions = max_partitions_for(max_context_len, partition_size);
     a.scale_log2 = scale * 1.4426950408889634f;
@@ -218,6 +226,7 @@ static int decode_common(DecodeArgs &a, int max_context_len, float scale, int va
         workspace_layout(num_seqs, num_q_heads, head_dim, a.max_partitions, workspace, &a.ws_max,
                          &a.ws_sum, &a.ws_acc);
     }
+    if (a.new_key) return launch_decode_valu(a);  // checked above: one pass or partitions
     const bool mfma_ok = !a.kv_fp8 && mfma_supported(dtype, head_dim, block_size, group);
     if (kernel_choice == PA_VARIANT_MFMA) {
         if (a.kv_fp8) return fail(PA_ERR_UNSUPPORTED, "E4M3 pools run on the vector kernel");
@@ -265,6 +274,45 @@ int pa_decode(void *out, const void *query, const void *key_cache, const void *v
     DecodeArgs a = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
                                context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                num_blocks, dtype, partition_size, stream);
+    return decode_common(a, max_context_len, scale, variant, workspace, workspace_bytes);
+}
+
+int pa_decode_append(void *out, const void *query, const void *new_key, const void *new_value,
+                     void *key_cache, void *value_cache, const int32_t *block_tables,
+                     int max_blocks_per_seq, const int32_t *context_lens, int num_seqs, int num_q_heads,
+                     int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_context_len,
+                     float scale, int dtype, int partition_size, int variant, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    clear_error();
+    if (num_seqs > 0 && (!new_key || !new_value)) return fail(PA_ERR_INVALID, "NULL new token pointer");
+    DecodeArgs a = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                               context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               num_blocks, dtype, partition_size, stream);
+    a.new_key = new_key;
+    a.new_value = new_value;
+    a.key_out = key_cache;
+    a.value_out = value_cache;
+    return decode_common(a, max_context_len, scale, variant, workspace, workspace_bytes);
+}
+
+int pa_decode_fp8_append(void *out, const void *query, const void *new_key, const void *new_value,
+                         void *key_cache, void *value_cache, const float *k_scales, const float *v_scales,
+                         const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                         int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                         int num_blocks, int max_context_len, float scale, int dtype, int partition_size,
+                         int variant, void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    if (num_seqs > 0 && (!new_key || !new_value)) return fail(PA_ERR_INVALID, "NULL new token pointer");
+    DecodeArgs a = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                               context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               num_blocks, dtype, partition_size, stream);
+    a.kv_fp8 = true;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    a.new_key = new_key;
+    a.new_value = new_value;
+    a.key_out = key_cache;
+    a.value_out = value_cache;
     return decode_common(a, max_context_len, scale, variant, workspace, workspace_bytes);
 }
 

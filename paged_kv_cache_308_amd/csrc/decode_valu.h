@@ -82,6 +82,9 @@ struct SameKV {
     __device__ static QSlice load_q(const uint8_t *p) { return {*(const u32x4 *)p}; }
     __device__ static float dot(const QSlice &q, const Word &k) { return dot16<T>(q.w, k); }
     __device__ static void values(const Word &v, float (&f)[epl]) { to_f32<T>(v, f); }
+    // this lane's slice of a token row given in the query's type (the newest token),
+    // as stored in the pool: the same bytes
+    __device__ static Word from_new(const uint8_t *p, float) { return *(const Word *)p; }
     // elements 4j .. 4j+3 of the slice
     __device__ static void values4(const Word &v, int j, float (&f)[4]) {
         float all[epl];
@@ -122,6 +125,26 @@ struct E4M3KV {
         return s;
     }
     __device__ static void values(const Word &v, float (&f)[SB]) { e4m3_to_f32<SB / 4>(v, f); }
+    // codes of P consecutive elements of a token row given in T (the newest token),
+    // packed from the low byte: each element's code of x / scale, the scatter's rounding
+    // bit for bit
+    template <int P>
+    __device__ static uint32_t encode_run(const uint8_t *p, float scale) {
+        static_assert(P == 1 || P == 2, "elements per lane");
+        uint32_t h = P == 2 ? *(const uint32_t *)p : (uint32_t) * (const uint16_t *)p;
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+            const uint32_t bits = (h >> (16 * e)) & 0xffffu;
+            float x;
+            if constexpr (std::is_same<T, F16>::value)
+                x = (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+            else
+                x = __uint_as_float(bits << 16);
+            c |= e4m3_encode(x / scale) << (8 * e);
+        }
+        return c;
+    }
     // codes 4j .. 4j+3 of the slice
     __device__ static void values4(const Word &v, int j, float (&f)[4]) {
         typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -255,7 +278,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     const float *__restrict__ v_scales, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_max, float *__restrict__ ws_sum,
     float *__restrict__ ws_acc, int max_blocks_per_seq, int num_seqs, int num_kv_heads,
-    int log2_block, int num_blocks, int partition_size, int max_partitions, float scale_log2) {
+    int log2_block, int num_blocks, int partition_size, int max_partitions, float scale_log2,
+    const uint8_t *__restrict__ new_key, const uint8_t *__restrict__ new_value, uint8_t *key_out,
+    uint8_t *value_out) {
     using T = typename KV::Q;
     constexpr int NWG = waves_per_group<KV, G>();
     constexpr int QB = T::bytes;            // query / output element bytes
@@ -312,9 +337,82 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     }
     bool bad = ctx < 0;
 
+    // Newest token given in new_key / new_value (fused scatter): this workgroup, if its
+    // range holds position ctx - 1, stores it into the pool and attends to it from the
+    // given values after the loop; the loop reads the pool up to ctx - 1 only (the pool
+    // is never read at the slot being written).
+    const bool append = new_key != nullptr && ctx >= 1 && start <= ctx - 1 && ctx - 1 < end;
+    const int end_all = end;
+    if (append) end = ctx - 1;
+
     const int ntok = ctx < 0 ? 0 : end - start;
     const int nfull = ntok / C;
     const bool has_tail = (ntok % C) != 0;
+
+    // The wave that would take the next chunk handles the newest token: before the loop
+    // it loads (and for E4M3 pools rounds) the given values and stores them into the
+    // pool, so their latency hides behind the loop; after the loop it attends to them
+    // with row 0 of its lanes (the other rows masked).
+    const bool app_here = append && wave == (nfull + (has_tail ? 1 : 0)) % NWG;
+    typename KV::Word app_k[1] = {typename KV::Word{}}, app_v[1] = {typename KV::Word{}};
+    float app_ks = 1.f, app_vs = 1.f;
+    if (app_here) {
+        const int t = ctx - 1;
+        const int lb = t >> log2_block;
+        int64_t base = -1;
+        if (lb < max_blocks_per_seq) {
+            const int32_t pb = table[lb];
+            if (pb >= 0 && pb < num_blocks) {
+                base = (int64_t)pb * block_bytes + head_off + (int64_t)(t & (block_size - 1)) * ROW_BYTES;
+                if constexpr (KV::scaled) {
+                    app_ks = k_scales[(int64_t)pb * num_kv_heads + kvh];
+                    app_vs = v_scales[(int64_t)pb * num_kv_heads + kvh];
+                }
+            }
+        }
+        if (base < 0) bad = true;
+        if constexpr (KV::scaled) {
+            // Each element costs a correctly rounded division and an encode: all 64
+            // lanes take D / 64 elements each and store their codes, and row 0 gathers
+            // its slices through LDS (in order within the wave).
+            constexpr int P = D / 64;
+            static_assert(P * 64 == D, "head_dim");
+            __shared__ __align__(16) uint8_t sm_new[2][D];
+            const int64_t src = ((int64_t)(s * num_kv_heads + kvh) * D + lane * P) * QB;
+            const uint32_t ck = KV::template encode_run<P>(new_key + src, app_ks);
+            const uint32_t cv = KV::template encode_run<P>(new_value + src, app_vs);
+            if constexpr (P == 2) {
+                *(uint16_t *)(sm_new[0] + lane * 2) = (uint16_t)ck;
+                *(uint16_t *)(sm_new[1] + lane * 2) = (uint16_t)cv;
+                if (base >= 0) {
+                    *(uint16_t *)(key_out + base + lane * 2) = (uint16_t)ck;
+                    *(uint16_t *)(value_out + base + lane * 2) = (uint16_t)cv;
+                }
+            } else {
+                sm_new[0][lane] = (uint8_t)ck;
+                sm_new[1][lane] = (uint8_t)cv;
+                if (base >= 0) {
+                    key_out[base + lane] = (uint8_t)ck;
+                    value_out[base + lane] = (uint8_t)cv;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (row == 0) {
+                app_k[0] = *(const typename KV::Word *)(sm_new[0] + col * SB);
+                app_v[0] = *(const typename KV::Word *)(sm_new[1] + col * SB);
+            }
+        } else if (row == 0) {
+            const int64_t src = ((int64_t)(s * num_kv_heads + kvh) * D + col * EPL) * QB;
+            app_k[0] = KV::from_new(new_key + src, app_ks);
+            app_v[0] = KV::from_new(new_value + src, app_vs);
+            if (base >= 0) {
+                *(typename KV::Word *)(key_out + base + col * SB) = app_k[0];
+                *(typename KV::Word *)(value_out + base + col * SB) = app_v[0];
+            }
+        }
+    }
 
     // Byte offset of the first row of wave load i of chunk c (uniform), or -1 when the
     // load lies past `end` or its table entry is outside the pool.  The last block
@@ -404,6 +502,13 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
             consume(A, nfull, true);
         }
     }
+
+    if (app_here) {
+        const float ksl1[1] = {KV::scaled ? scale_log2 * app_ks : scale_log2};
+        const float vsc1[1] = {app_vs};
+        chunk_update<KV, G, 1, LPT, TPW>(qv, app_k, app_v, ksl1, vsc1, row, 1, true, m, l, acc);
+    }
+    end = end_all;
 
     merge_rows<G, EPL, LPT>(m, l, acc);
 
@@ -828,7 +933,8 @@ int launch_t(const DecodeArgs &a) {
                            (const uint8_t *)a.value_cache, a.k_scales, a.v_scales, a.block_tables,
                            a.context_lens, a.ws_max, a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs,
                            a.num_kv_heads, log2b, a.num_blocks, a.partition_size, a.max_partitions,
-                           a.scale_log2);
+                           a.scale_log2, (const uint8_t *)a.new_key, (const uint8_t *)a.new_value,
+                           (uint8_t *)a.key_out, (uint8_t *)a.value_out);
         const int rc = check_launch("decode_valu (partitions)");
         if (rc != PA_OK) return rc;
         return launch_lse_merge(a);
@@ -838,7 +944,8 @@ int launch_t(const DecodeArgs &a) {
                        a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
                        (const uint8_t *)a.value_cache, a.k_scales, a.v_scales, a.block_tables,
                        a.context_lens, nullptr, nullptr, nullptr, a.max_blocks_per_seq, a.num_seqs,
-                       a.num_kv_heads, log2b, a.num_blocks, 0, 1, a.scale_log2);
+                       a.num_kv_heads, log2b, a.num_blocks, 0, 1, a.scale_log2, (const uint8_t *)a.new_key,
+                       (const uint8_t *)a.new_value, (uint8_t *)a.key_out, (uint8_t *)a.value_out);
     return check_launch("decode_valu");
 }
 

@@ -41,6 +41,12 @@ struct DecodeArgs {
     bool cached_kv;      // K/V through cacheable loads (blocks shared between sequences)
     int dtype;           // query / output type
     bool kv_fp8;         // pools hold E4M3 codes (k_scales / v_scales set)
+    // newest tokens to store and attend to in the same launch (pa_decode_append): [S][H_kv][d]
+    // of the query's type; key_out / value_out are the pools, written at position ctx - 1
+    const void *new_key;
+    const void *new_value;
+    void *key_out;
+    void *value_out;
     // several query tokens per sequence (pa_multi_query)
     const int32_t *query_start;  // [S + 1]: the sequence's rows of query / out
     int num_query_tokens;        // rows of query / out

@@ -19,9 +19,9 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (PA_VARIANT_AUTO, Allocator, pa_copy_blocks, pa_decode, pa_decode_fp8,
-               pa_decode_workspace_bytes, pa_reshape_and_cache, pa_reshape_and_cache_fp8,
-               pa_swap_blocks)
+from . import (PA_VARIANT_AUTO, PA_VARIANT_MFMA, PA_VARIANT_VALU, Allocator, pa_copy_blocks,
+               pa_decode, pa_decode_append, pa_decode_fp8, pa_decode_workspace_bytes,
+               pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_swap_blocks)
 
 FP8_NAN_CODE = 0x7F
 
@@ -122,6 +122,42 @@ class PagedKVCache:
             pa_decode(out, query, self.key_cache, self.value_cache, block_tables, context_lens,
                       scale, max_context_len=max_context_len, partition_size=partition_size,
                       variant=variant, workspace=workspace, stream=stream)
+        return out
+
+
+    def fused_step_ok(self, num_q_heads: int, partition_size: int, variant: int) -> bool:
+        """Whether the newest-token store can ride in the attention launch: the vector
+        kernel, one pass or partitions (AUTO keeps the matrix cores for grouped heads at
+        16 bits, whose launch does not store)."""
+        choice = variant & 15
+        if partition_size < 0 or choice == PA_VARIANT_MFMA:
+            return False
+        if choice == PA_VARIANT_AUTO and not self.fp8 and num_q_heads > self.num_kv_heads \
+                and self.dtype != torch.float32:
+            return False
+        return True
+
+    def step(self, query, new_key, new_value, slots, block_tables, context_lens, scale: float,
+             out=None, partition_size: int = 0, max_context_len: int = 0,
+             variant: int = PA_VARIANT_AUTO, workspace=None, stream=None) -> torch.Tensor:
+        """The decode step: the newest K/V into their slots (position ctx - 1 of each
+        table, `slots` as int32), then attention over the tables.  One launch when the
+        vector kernel serves the step (pa_decode_append), else the scatter and the
+        attention launch."""
+        if not self.fused_step_ok(query.shape[1], partition_size, variant):
+            self.write(new_key, new_value, slots, stream)
+            return self.attend(query, block_tables, context_lens, scale, out=out,
+                               partition_size=partition_size, max_context_len=max_context_len,
+                               variant=variant, workspace=workspace, stream=stream)
+        out = torch.empty_like(query) if out is None else out
+        if partition_size and workspace is None:
+            workspace = self.workspace(query.shape[0], query.shape[1], max_context_len,
+                                       partition_size)
+        v = variant if (variant & 15) != PA_VARIANT_AUTO else (variant | PA_VARIANT_VALU)
+        pa_decode_append(out, query, new_key, new_value, self.key_cache, self.value_cache,
+                         block_tables, context_lens, scale, max_context_len=max_context_len,
+                         partition_size=partition_size, variant=v, workspace=workspace,
+                         stream=stream, k_scales=self.k_scales, v_scales=self.v_scales)
         return out
 
 

@@ -37,10 +37,19 @@ class DeviceBatch:
     seq_ids: Optional[List[int]] = None  # allocator id of each batch sequence
 
     def step(self, partition_size: int = 0, variant: int = PA_VARIANT_AUTO, out=None,
-             workspace=None, stream=None) -> torch.Tensor:
-        """The decode step: newest K/V into their slots, then attention."""
+             workspace=None, stream=None, fused: bool = True) -> torch.Tensor:
+        """The decode step: newest K/V into their slots, then attention (one launch when
+        the vector kernel serves it and `fused`)."""
+        if self.shared:
+            variant |= PA_DECODE_SHARED_KV
+        if fused:
+            return self.cache.step(self.query, self.new_key, self.new_value, self.slot_mapping,
+                                   self.block_tables, self.context_lens, self.scale, out=out,
+                                   partition_size=partition_size,
+                                   max_context_len=self.max_context_len, variant=variant,
+                                   workspace=workspace, stream=stream)
         self.cache.write(self.new_key, self.new_value, self.slot_mapping, stream)
-        return self.attend(partition_size, variant, out, workspace, stream)
+        return self.attend(partition_size, variant & ~PA_DECODE_SHARED_KV, out, workspace, stream)
 
     def attend(self, partition_size: int = 0, variant: int = PA_VARIANT_AUTO, out=None,
                workspace=None, stream=None) -> torch.Tensor:

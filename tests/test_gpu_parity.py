@@ -134,6 +134,58 @@ def test_small_workload(name, oracle_steps):
                 assert bits(db.cache.v_scales) == np_bits(placed.v_scales)
 
 
+@pytest.mark.parametrize("name", ["mha_f16", "long_bf16", "prefix_f16", "tiny_fp32", "gqa_f16_b16",
+                                  "fp8_mha_f16", "fp8_gqa4_bf16", "fp8_d64_g8_f16"])
+def test_fused_step_matches_scatter_then_decode(name, oracle_steps):
+    """The newest-token store inside the attention launch: the pools afterwards are
+    bit-identical to the separate scatter's, the output matches the oracle."""
+    w = SMALL[name]
+    batch, want, placed = oracle_steps(name)
+    for P in sorted({0, w.partition_size}):
+        say(f"[gpu] fused step {name} P={P}")
+        db = replay(batch)
+        got = db.step(partition_size=P, variant=VALU, fused=True)
+        torch.cuda.synchronize()
+        assert np.max(np.abs(f64(got) - want)) <= TOL[w.dtype], (name, P)
+        assert bits(db.cache.key_cache) == np_bits(placed.key_cache)
+        assert bits(db.cache.value_cache) == np_bits(placed.value_cache)
+        ref = replay(batch)
+        two = ref.step(partition_size=P, variant=VALU, fused=False)
+        torch.cuda.synchronize()
+        assert np.max(np.abs(f64(got) - f64(two))) <= TOL[w.dtype]
+
+
+def test_fused_step_edge_lengths():
+    """Contexts of 1 (the newest token alone), partition starts and ends, block edges."""
+    rng = np.random.default_rng(31)
+    lens = [1, 2, 16, 17, 64, 65, 128, 129, 511, 512, 513]
+    c = Case(rng, lens, 4, 4, 128, 16, "f16")
+    want = c.run(oracle.default())
+    q, kc, vc, bt, cl = _upload_case(c)
+    # the newest token of each sequence, taken from the placed pools, then poisoned there
+    S = len(lens)
+    nk = torch.empty((S, c.Hkv, c.d), dtype=kc.dtype, device="cuda")
+    nv = torch.empty_like(nk)
+    for s_, n in enumerate(lens):
+        b, o = int(c.tables[s_, (n - 1) // c.B]), (n - 1) % c.B
+        nk[s_] = kc[b, :, o, :]
+        nv[s_] = vc[b, :, o, :]
+        kc[b, :, o, :] = float("nan")
+        vc[b, :, o, :] = float("nan")
+    for P in (0, 64):
+        out = torch.empty_like(q)
+        ws = None
+        if P:
+            ws = torch.empty(pa.pa_decode_workspace_bytes(S, 4, 4, 128, max(lens), P), dtype=torch.uint8,
+                             device="cuda")
+        say(f"[gpu] fused edge P={P}")
+        pa.pa_decode_append(out, q, nk, nv, kc, vc, bt, cl, c.scale, max_context_len=max(lens),
+                            partition_size=P, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.max(np.abs(f64(out) - want)) <= TOL["f16"], P
+        assert bits(kc) == np_bits(c.kc) and bits(vc) == np_bits(c.vc)
+
+
 # ----------------------------------------------------------------- edge cases
 
 
@@ -300,7 +352,7 @@ def test_swap_out_and_in_round_trip():
     w = SMALL["prefix_f16"]
     batch = W.make_batch(w)
     db = replay(batch)
-    before = bits(db.step(partition_size=0, variant=VALU))
+    before = bits(db.step(partition_size=0, variant=VALU, fused=False))
     cache = db.cache
     host = HostKVPool(300, w.num_kv_heads, w.head_dim, w.block_size, TORCH_DTYPE[w.dtype])
     host.key_cache.fill_(0.0)
@@ -498,7 +550,7 @@ def test_fp8_swap_out_and_in_round_trip():
     w = SMALL["fp8_prefix_bf16"]
     batch = W.make_batch(w)
     db = replay(batch)
-    before = bits(db.step(partition_size=0, variant=VALU))
+    before = bits(db.step(partition_size=0, variant=VALU, fused=False))
     cache = db.cache
     host = HostKVPool(300, w.num_kv_heads, w.head_dim, w.block_size, torch.uint8)
     moved = [0, 4, 7]

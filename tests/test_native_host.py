@@ -227,6 +227,20 @@ def test_empty_batch_is_a_no_op():
     assert _decode(S=0) == pa.PA_OK
 
 
+def test_decode_append_rejects_before_launch():
+    L = pa._lib()
+    args = lambda P=0, variant=0, nk=FAKE: (FAKE, FAKE, nk, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 8, 8, 128,
+                                            16, 10, 64, 0.1, pa.PA_F16, P, variant, None, 0, None)
+    assert L.pa_decode_append(*args(variant=pa.PA_VARIANT_MFMA)) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_decode_append(*args(P=pa.PA_PARTITION_BALANCED, variant=pa.PA_VARIANT_VALU)) == \
+        pa.PA_ERR_UNSUPPORTED
+    assert L.pa_decode_append(*args(nk=None)) == pa.PA_ERR_INVALID
+    assert L.pa_decode_fp8_append(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 8, 8,
+                                  128, 16, 10, 64, 0.1, pa.PA_F16, 0, 0, None, 0, None) == pa.PA_ERR_INVALID
+    assert L.pa_decode_fp8_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 8, 8,
+                                  128, 16, 10, 64, 0.1, pa.PA_F32, 0, 0, None, 0, None) == pa.PA_ERR_UNSUPPORTED
+
+
 def _mq(**kw):
     a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, maxb=4, cl=FAKE, qs=FAKE, S=2, T=10, mql=8,
              Hq=8, Hkv=8, d=128, B=16, nb=10, scale=0.1, dtype=pa.PA_F16, stream=None)
