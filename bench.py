@@ -42,12 +42,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # Sources the vector decode kernels are built from (their counters go stale when these change).
 DECODE_SOURCES = {
-    "f16": ["decode_valu.h", "kernel_common.h", "internal.h", "decode_valu_f16.hip"],
-    "bf16": ["decode_valu.h", "kernel_common.h", "internal.h", "decode_valu_bf16.hip"],
-    "f32": ["decode_valu.h", "kernel_common.h", "internal.h", "decode_valu_f32.hip"],
-    "fp8": ["decode_valu.h", "kernel_common.h", "internal.h", "decode_valu_fp8_f16.hip",
+    "f16": ["decode_valu.h", "balanced.h", "kernel_common.h", "internal.h", "decode_valu_f16.hip"],
+    "bf16": ["decode_valu.h", "balanced.h", "kernel_common.h", "internal.h", "decode_valu_bf16.hip"],
+    "f32": ["decode_valu.h", "balanced.h", "kernel_common.h", "internal.h", "decode_valu_f32.hip"],
+    "fp8": ["decode_valu.h", "balanced.h", "kernel_common.h", "internal.h", "decode_valu_fp8_f16.hip",
             "decode_valu_fp8_bf16.hip"],
-    "mfma": ["decode_mfma.h", "kernel_common.h", "internal.h", "decode_mfma_f16.hip",
+    "mfma": ["decode_mfma.h", "balanced.h", "kernel_common.h", "internal.h", "decode_mfma_f16.hip",
              "decode_mfma_bf16.hip"],
 }
 
@@ -447,11 +447,11 @@ def main():
     gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
     achieved = ab["total_unique"] / (dec_avg * 1e-3) / 1e9
     g = w.num_q_heads // w.num_kv_heads
-    mfma = w.kv != "fp8" and args.P >= 0 and (
-        args.variant == 2 or (args.variant == 0 and g >= 2 and w.dtype != "f32"))
-    kernels = ("decode_mfma_kernel" if mfma else
-               "decode_balanced_kernel" if args.P < 0 else "decode_valu_kernel") + \
-        (" + balanced_merge_kernel" if args.P < 0 else " + lse_merge_kernel" if args.P else "")
+    mfma = w.kv != "fp8" and (args.variant == 2 or (args.variant == 0 and g >= 2 and w.dtype != "f32"))
+    if args.P < 0:
+        kernels = ("decode_mfma_balanced_kernel" if mfma else "decode_balanced_kernel") + " + balanced_merge_kernel"
+    else:
+        kernels = ("decode_mfma_kernel" if mfma else "decode_valu_kernel") + (" + lse_merge_kernel" if args.P else "")
     line = {
         "metric": "paged decode attn: effective KV HBM GB/s (% of peak) and decode seqs/sec",
         "value": round(gbs, 2),

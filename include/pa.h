@@ -111,8 +111,8 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
  * partition_size == 0: one pass per (sequence, KV head).  A multiple of block_size
  * (and of 16): each partition of that many tokens is reduced on its own and a second
  * kernel merges the partials with log-sum-exp weights; max_context_len must bound
- * every context_lens[s].  PA_PARTITION_BALANCED (vector kernel, at most 4096
- * sequences): the batch's work, as one list of 16-token chunks over KV heads and
+ * every context_lens[s].  PA_PARTITION_BALANCED (at most 4096 sequences; either
+ * kernel): the batch's work, as one list of fixed-size chunks over KV heads and
  * sequences, is cut into equal ranges for all the waves the device holds at once,
  * whatever the length mix; each wave writes a partial per (sequence, KV head) it
  * touches and a second kernel merges them.  With partitions `workspace` must hold

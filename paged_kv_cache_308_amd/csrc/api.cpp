@@ -230,13 +230,12 @@ static int decode_common(DecodeArgs &a, int max_context_len, float scale, int va
     const bool mfma_ok = !a.kv_fp8 && mfma_supported(dtype, head_dim, block_size, group);
     if (kernel_choice == PA_VARIANT_MFMA) {
         if (a.kv_fp8) return fail(PA_ERR_UNSUPPORTED, "E4M3 pools run on the vector kernel");
-        if (balanced) return fail(PA_ERR_UNSUPPORTED, "balanced split runs on the vector kernel");
         if (!mfma_ok)
             return fail(PA_ERR_UNSUPPORTED, "MFMA kernel needs 16-bit dtype and group >= 2 (group %d)",
                         group);
         return launch_decode_mfma(a);
     }
-    if (kernel_choice == PA_VARIANT_AUTO && mfma_ok && group >= 2 && !balanced) return launch_decode_mfma(a);
+    if (kernel_choice == PA_VARIANT_AUTO && mfma_ok && group >= 2) return launch_decode_mfma(a);
     return launch_decode_valu(a);
 }
 

@@ -31,6 +31,7 @@
 // vector kernel, so the same log-sum-exp merge kernel finishes a partitioned run.
 #include <hip/hip_runtime.h>
 
+#include "balanced.h"
 #include "internal.h"
 #include "kernel_common.h"
 
@@ -39,6 +40,9 @@ namespace mfma {
 
 #ifndef PA_MFMA_WAVES
 #define PA_MFMA_WAVES 4
+#endif
+#ifndef PA_MFMA_BAL_PER_CU
+#define PA_MFMA_BAL_PER_CU 0  // balanced split: workgroups per CU (0: as many as fit)
 #endif
 constexpr int MW = PA_MFMA_WAVES;  // waves per workgroup
 constexpr int CT = 32;             // tokens per chunk: two 16-token tiles
@@ -77,6 +81,303 @@ struct Mma<BF16> {
     }
 };
 
+// Tile geometry of head dimension D (16-bit elements).
+template <int D>
+struct Geom {
+    static constexpr int ROW = D * 2;            // bytes per token row
+    static constexpr int NKK = D / 32;           // 32-wide d steps of the score product
+    static constexpr int NN = D / 16;            // 16-row d fragments of the output
+    static constexpr int VL = 16 * ROW / 1024;   // 1 KiB wave loads per 16-token V tile
+    static constexpr int RPK = 1024 / ROW;       // token rows per KiB
+    static constexpr int KSTR = 1024 + 32;       // LDS stride of one KiB group (padded)
+    static constexpr int STAGE = 2 * VL * KSTR;  // LDS bytes of one chunk's V
+    static constexpr int WAVE_LDS = 2 * STAGE;   // double-buffered
+};
+
+// LDS address of V[row r of the chunk][byte col] in a stage
+template <int D>
+__device__ inline uint8_t *v_at(uint8_t *stage, int r, int col) {
+    using Gm = Geom<D>;
+    return stage + (r / Gm::RPK) * Gm::KSTR + (r % Gm::RPK) * Gm::ROW + col;
+}
+
+// Loads of one chunk: tile tt's 16 rows start at byte base[tt] of the pools.  Its V
+// rows go to LDS stage `stage` (direct loads), its K operands to k.
+template <int D, bool NT>
+__device__ __forceinline__ void issue_chunk(u32x4 (&k)[2][Geom<D>::NKK], uint8_t *stage, const int64_t (&base)[2],
+                                            const uint8_t *key_cache, const uint8_t *value_cache, int lane,
+                                            int n, int q) {
+    using Gm = Geom<D>;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int i = 0; i < Gm::VL; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(value_cache + base[tt] + i * 1024 + lane * 16),
+                (__attribute__((address_space(3))) void *)(stage + (tt * Gm::VL + i) * Gm::KSTR), 16, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < Gm::NKK; ++kk)
+            k[tt][kk] = kv_load<NT>((const u32x4 *)(key_cache + base[tt] + n * Gm::ROW + (32 * kk + 8 * q) * 2));
+    }
+}
+
+// One chunk of CT tokens starting at position tok0 (rows at or past `end` masked)
+// folded into a wave's online-softmax state: m (running max of head n), lsum (this
+// lane's share of the normaliser) and o (O^T fragments).
+template <typename T, int D>
+__device__ __forceinline__ void consume_chunk(const u32x4 (&k)[2][Geom<D>::NKK], const u32x4 (&qb)[Geom<D>::NKK],
+                                              uint8_t *stage, int tok0, int end, float scale_log2, int lane,
+                                              int n, int q, float &m, float &lsum, f32x4 (&o)[Geom<D>::NN]) {
+    using Gm = Geom<D>;
+    const bool tail = tok0 + CT > end;
+    // scores S^T: lane holds tokens 16 tt + 4 q + i of head n
+    float sc[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < Gm::NKK; ++kk) acc = Mma<T>::run(k[tt][kk], qb[kk], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = !tail || (tok0 + 16 * tt + 4 * q + i < end);
+            sc[tt][i] = ok ? acc[i] * scale_log2 : -INFINITY;
+        }
+    }
+    float cm = sc[0][0];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[tt][i]);
+    cm = fmaxf(cm, __shfl_xor(cm, 16));
+    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    const float mn = fmaxf(m, cm);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(m - ms);
+    m = mn;
+    // P^T operand: k slot j < 4 -> token 4q + j (tile 0), j >= 4 -> token 16 + 4q + j - 4
+    uint32_t pk[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            float b0, b1;
+            const uint32_t h0 = Mma<T>::round(fast_exp2(sc[tt][i] - ms), b0);
+            const uint32_t h1 = Mma<T>::round(fast_exp2(sc[tt][i + 1] - ms), b1);
+            psum += b0 + b1;
+            pk[2 * tt + i / 2] = h0 | (h1 << 16);
+        }
+    lsum = lsum * alpha + psum;
+    const u32x4 pb = u32x4{pk[0], pk[1], pk[2], pk[3]};
+#pragma unroll
+    for (int nn = 0; nn < Gm::NN; ++nn) o[nn] *= alpha;
+    // this chunk's V rows have landed in LDS: its V loads were issued before its K
+    // loads, which the score product above already waited for
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (tail) {
+        // rows past `end` as zeros: 0 * NaN would poison the product
+        for (int r = max(0, end - tok0); r < CT; ++r)
+            for (int col = lane * 4; col < Gm::ROW; col += 256) *(uint32_t *)v_at<D>(stage, r, col) = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // V^T operand per 16-row d fragment: lane reads V[t(q, j)][16 nn + n]
+#pragma unroll
+    for (int nn = 0; nn < Gm::NN; ++nn) {
+        uint32_t vk[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            const int t0 = j < 4 ? 4 * q + j : 16 + 4 * q + (j - 4);
+            const uint16_t a = *(const uint16_t *)v_at<D>(stage, t0, (16 * nn + n) * 2);
+            const uint16_t c2 = *(const uint16_t *)v_at<D>(stage, t0 + 1, (16 * nn + n) * 2);
+            vk[j / 2] = (uint32_t)a | ((uint32_t)c2 << 16);
+        }
+        o[nn] = Mma<T>::run(u32x4{vk[0], vk[1], vk[2], vk[3]}, pb, o[nn]);
+    }
+    // the stage is rewritten by a later chunk's loads: finish reading it first
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Q^T operand of (sequence s, KV head kvh): lane holds Q[head n][32 kk + 8 q .. +8];
+// heads past the group are zero
+template <int D, int G>
+__device__ __forceinline__ void load_q(u32x4 (&qb)[Geom<D>::NKK], const uint8_t *query, int s, int kvh,
+                                       int num_q_heads, int n, int q) {
+#pragma unroll
+    for (int kk = 0; kk < Geom<D>::NKK; ++kk) {
+        qb[kk] = u32x4{0, 0, 0, 0};
+        if (n < G)
+            qb[kk] = *(const u32x4 *)(query + ((int64_t)(s * num_q_heads + kvh * G + n) * D + 32 * kk + 8 * q) * 2);
+    }
+}
+
+// Per-wave online-softmax state of one range: m (running max of head n, same in the 4
+// lanes of a column), lsum (this lane's share of the normaliser), o (O^T fragments).
+template <int D>
+struct WaveState {
+    float m, lsum;
+    f32x4 o[Geom<D>::NN];
+    bool bad;
+};
+
+// The workgroup's MW waves over tokens [start, end) of (sequence s, KV head kvh):
+// wave w takes the CT-token chunks w, w + MW, ... of the range through a double-
+// buffered pipeline (K operands in registers, V rows in its LDS stages).
+template <typename T, int D, int G, bool NT>
+__device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds, const uint8_t *query,
+                                             const uint8_t *key_cache, const uint8_t *value_cache,
+                                             const int32_t *table, int max_blocks_per_seq, int s, int kvh,
+                                             int num_kv_heads, int log2_block, int num_blocks, int start,
+                                             int end, float scale_log2, int wave, int lane) {
+    using Gm = Geom<D>;
+    constexpr int ROW = Gm::ROW;
+    constexpr int NKK = Gm::NKK;
+    const int n = lane & 15;  // head column / token row within a tile
+    const int q = lane >> 4;  // k group
+    const int num_q_heads = num_kv_heads * G;
+    const int block_size = 1 << log2_block;
+    const int64_t head_off = (int64_t)kvh * block_size * ROW;
+    const int64_t block_bytes = (int64_t)num_kv_heads * block_size * ROW;
+
+    u32x4 qb[NKK];
+    load_q<D, G>(qb, query, s, kvh, num_q_heads, n, q);
+
+    st.m = -INFINITY;
+    st.lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < Gm::NN; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int ntok = end > start ? end - start : 0;
+    const int nchunks = (ntok + CT - 1) / CT;
+
+    // Byte offset of the first row of 16-token tile `tt` of chunk c, or -1.  A tile with
+    // no data (past `end`, or a bad entry) reads block 0's first rows instead (inside
+    // the pool; masked like any row past `end`): no branch around a load, because one
+    // makes the compiler wait for every outstanding load.
+    auto tile_base = [&](int c, int tt) -> int64_t {
+        const int tok = start + c * CT + 16 * tt;
+        if (tok >= end) return -1;
+        const int lb = tok >> log2_block;
+        if (lb >= max_blocks_per_seq) {
+            st.bad = true;
+            return -1;
+        }
+        const int32_t pb = table[lb];
+        if (pb < 0 || pb >= num_blocks) {
+            st.bad = true;
+            return -1;
+        }
+        return (int64_t)pb * block_bytes + head_off + (int64_t)(tok & (block_size - 1)) * ROW;
+    };
+    struct Chunk {
+        u32x4 k[2][NKK];
+    };
+    auto issue = [&](Chunk &b, int c, int stage) {
+        int64_t base[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            base[tt] = tile_base(c, tt);
+            base[tt] = base[tt] < 0 ? 0 : base[tt];
+        }
+        issue_chunk<D, NT>(b.k, wave_lds + stage * Gm::STAGE, base, key_cache, value_cache, lane, n, q);
+    };
+    auto consume = [&](const Chunk &b, int c, int stage) {
+        consume_chunk<T, D>(b.k, qb, wave_lds + stage * Gm::STAGE, start + c * CT, end, scale_log2, lane, n, q,
+                            st.m, st.lsum, st.o);
+    };
+
+    // this wave's chunks are wave, wave + MW, ...; the steady-state loop always has a
+    // next chunk to prefetch (see tile_base), the last one or two run after it
+    const int mine = nchunks > wave ? (nchunks - wave + MW - 1) / MW : 0;
+    Chunk A, Bf;
+    if (mine > 0) {
+        issue(A, wave, 0);
+        int j = 0;
+        for (; j + 2 < mine; j += 2) {
+            issue(Bf, wave + (j + 1) * MW, 1);
+            consume(A, wave + j * MW, 0);
+            issue(A, wave + (j + 2) * MW, 0);
+            consume(Bf, wave + (j + 1) * MW, 1);
+        }
+        if (j + 1 < mine) {
+            issue(Bf, wave + (j + 1) * MW, 1);
+            consume(A, wave + j * MW, 0);
+            consume(Bf, wave + (j + 1) * MW, 1);
+        } else {
+            consume(A, wave + j * MW, 0);
+        }
+    }
+    // normaliser of head n over the 4 lanes of its column
+    st.lsum += __shfl_xor(st.lsum, 16);
+    st.lsum += __shfl_xor(st.lsum, 32);
+}
+
+// Merge the waves' states through LDS (the staging area; every wave's loads of the range
+// are complete) and write, per query head g of the group, either the normalised output
+// row out_row0 + g (ws_max == nullptr) or the partial (max, sum, weighted value sums)
+// at index idx0 + g * idx_stride of the workspace arrays.  Called by every thread;
+// leaves LDS free for the next range.
+template <typename T, int D, int G>
+__device__ __forceinline__ void finish(const WaveState<D> &st, uint8_t *lds, int *sm_bad, int wave, int lane,
+                                       void *out, int64_t out_row0, float *ws_max, float *ws_sum, float *ws_acc,
+                                       int64_t idx0, int64_t idx_stride) {
+    constexpr int NN = Geom<D>::NN;
+    const int n = lane & 15;
+    const int q = lane >> 4;
+    __syncthreads();
+    float *sm_m = (float *)lds;     // [MW][G]
+    float *sm_l = sm_m + MW * G;    // [MW][G]
+    float *sm_acc = sm_l + MW * G;  // [MW][G][D]
+    if (threadIdx.x == 0) *sm_bad = 0;
+    __syncthreads();
+    if (st.bad) *sm_bad = 1;
+    if (n < G) {
+        if (q == 0) {
+            sm_m[wave * G + n] = st.m;
+            sm_l[wave * G + n] = st.lsum;
+        }
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm_acc[(wave * G + n) * D + 16 * nn + 4 * q + i] = st.o[nn][i];
+    }
+    __syncthreads();
+    const bool any_bad = *sm_bad != 0;
+    for (int t = threadIdx.x; t < G * D; t += MW * 64) {
+        const int g = t / D;
+        const int j = t - g * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < MW; ++w) M = fmaxf(M, sm_m[w * G + g]);
+        const float Ms = M == -INFINITY ? 0.f : M;
+        float Lsum = 0.f, A = 0.f;
+#pragma unroll
+        for (int w = 0; w < MW; ++w) {
+            const float f = fast_exp2(sm_m[w * G + g] - Ms);
+            Lsum += sm_l[w * G + g] * f;
+            A += sm_acc[(w * G + g) * D + j] * f;
+        }
+        if (ws_max) {
+            const int64_t pi = idx0 + g * idx_stride;
+            if (j == 0) {
+                ws_max[pi] = any_bad ? NAN : M;
+                ws_sum[pi] = Lsum;
+            }
+            ws_acc[pi * D + j] = A;
+        } else {
+            float ov = Lsum > 0.f ? A / Lsum : 0.f;
+            if (any_bad) ov = NAN;
+            store_out<T>(out, (out_row0 + g) * D + j, ov);
+        }
+    }
+    __syncthreads();
+}
+
 template <typename T, int D, int G, bool SPLIT, bool NT>
 __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
     void *__restrict__ out, const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
@@ -84,19 +385,8 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_max, float *__restrict__ ws_sum,
     float *__restrict__ ws_acc, int max_blocks_per_seq, int num_seqs, int num_kv_heads,
     int log2_block, int num_blocks, int partition_size, int max_partitions, float scale_log2) {
-    constexpr int ROW = D * 2;            // bytes per token row
-    constexpr int NKK = D / 32;           // 32-wide d steps of the score product
-    constexpr int NN = D / 16;            // 16-row d fragments of the output
-    constexpr int VL = 16 * ROW / 1024;   // 1 KiB wave loads per 16-token V tile
-    constexpr int RPK = 1024 / ROW;       // token rows per KiB
-    constexpr int KSTR = 1024 + 32;       // LDS stride of one KiB group (padded)
-    constexpr int STAGE = 2 * VL * KSTR;  // LDS bytes of one chunk's V
-    constexpr int WAVE_LDS = 2 * STAGE;   // double-buffered
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n = lane & 15;  // head column / token row within a tile
-    const int q = lane >> 4;  // k group
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int part = L % max_partitions;
@@ -113,238 +403,154 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
         end = min(ctx, start + partition_size);
     }
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[MW * WAVE_LDS];
-    static_assert((2 * MW * G + MW * G * D) * 4 <= MW * WAVE_LDS, "merge area must fit the staging area");
-    uint8_t *wave_lds = lds + wave * WAVE_LDS;
-
-    const int block_size = 1 << log2_block;
-    const int32_t *table = block_tables + (int64_t)s * max_blocks_per_seq;
-    const int64_t head_off = (int64_t)kvh * block_size * ROW;
-    const int64_t block_bytes = (int64_t)num_kv_heads * block_size * ROW;
-
-    // Q^T operand: lane holds Q[head n][32 kk + 8 q .. +8]; heads past the group are zero
-    u32x4 qb[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        qb[kk] = u32x4{0, 0, 0, 0};
-        if (n < G)
-            qb[kk] = *(const u32x4 *)(query + ((int64_t)(s * num_q_heads + kvh * G + n) * D + 32 * kk + 8 * q) * 2);
-    }
-
-    float m = -INFINITY;  // running max of head n (same in the 4 lanes of a column)
-    float lsum = 0.f;     // this lane's share of the normaliser
-    f32x4 o[NN];
-#pragma unroll
-    for (int i = 0; i < NN; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool bad = ctx < 0;
-
-    const int ntok = ctx < 0 ? 0 : end - start;
-    const int nchunks = (ntok + CT - 1) / CT;
-
-    // Byte offset of the first row of 16-token tile `tt` of chunk c, or -1.  A tile with
-    // no data (past `end`, or a bad entry) reads block 0's first rows instead (inside
-    // the pool; masked like any row past `end`): no branch around a load, because one
-    // makes the compiler wait for every outstanding load.
-    auto tile_base = [&](int c, int tt) -> int64_t {
-        const int tok = start + c * CT + 16 * tt;
-        if (tok >= end) return -1;
-        const int lb = tok >> log2_block;
-        if (lb >= max_blocks_per_seq) {
-            bad = true;
-            return -1;
-        }
-        const int32_t pb = table[lb];
-        if (pb < 0 || pb >= num_blocks) {
-            bad = true;
-            return -1;
-        }
-        return (int64_t)pb * block_bytes + head_off + (int64_t)(tok & (block_size - 1)) * ROW;
-    };
-
-    // a chunk's K operands live in registers; its V rows go to LDS stage `st`
-    struct Chunk {
-        u32x4 k[2][NKK];
-    };
-    auto issue = [&](Chunk &b, int c, int st) {
-        uint8_t *stage = wave_lds + st * STAGE;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            int64_t base = tile_base(c, tt);
-            base = base < 0 ? 0 : base;
-#pragma unroll
-            for (int i = 0; i < VL; ++i)
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(value_cache + base + i * 1024 + lane * 16),
-                    (__attribute__((address_space(3))) void *)(stage + (tt * VL + i) * KSTR), 16, 0, 0);
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                b.k[tt][kk] = kv_load<NT>(
-                    (const u32x4 *)(key_cache + base + n * ROW + (32 * kk + 8 * q) * 2));
-        }
-    };
-    // LDS address of V[row r of the chunk][byte col]
-    auto v_at = [&](const uint8_t *stage, int r, int col) -> const uint8_t * {
-        return stage + (r / RPK) * KSTR + (r % RPK) * ROW + col;
-    };
-    auto consume = [&](const Chunk &b, int c, int st) {
-        const uint8_t *stage = wave_lds + st * STAGE;
-        const int tok0 = start + c * CT;
-        const bool tail = tok0 + CT > end;
-        // scores S^T: lane holds tokens 16 tt + 4 q + i of head n
-        float sc[2][4];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) acc = Mma<T>::run(b.k[tt][kk], qb[kk], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = !tail || (tok0 + 16 * tt + 4 * q + i < end);
-                sc[tt][i] = ok ? acc[i] * scale_log2 : -INFINITY;
-            }
-        }
-        float cm = sc[0][0];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[tt][i]);
-        cm = fmaxf(cm, __shfl_xor(cm, 16));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
-        const float mn = fmaxf(m, cm);
-        const float ms = mn == -INFINITY ? 0.f : mn;
-        const float alpha = fast_exp2(m - ms);
-        m = mn;
-        // P^T operand: k slot j < 4 -> token 4q + j (tile 0), j >= 4 -> token 16 + 4q + j - 4
-        uint32_t pk[4];
-        float psum = 0.f;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-                float b0, b1;
-                const uint32_t h0 = Mma<T>::round(fast_exp2(sc[tt][i] - ms), b0);
-                const uint32_t h1 = Mma<T>::round(fast_exp2(sc[tt][i + 1] - ms), b1);
-                psum += b0 + b1;
-                pk[2 * tt + i / 2] = h0 | (h1 << 16);
-            }
-        lsum = lsum * alpha + psum;
-        const u32x4 pb = u32x4{pk[0], pk[1], pk[2], pk[3]};
-#pragma unroll
-        for (int nn = 0; nn < NN; ++nn) o[nn] *= alpha;
-        // this chunk's V rows have landed in LDS: its V loads were issued before its K
-        // loads, which the score product above already waited for
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (tail) {
-            // rows past `end` as zeros: 0 * NaN would poison the product
-            for (int r = max(0, end - tok0); r < CT; ++r)
-                for (int col = lane * 4; col < ROW; col += 256)
-                    *(uint32_t *)v_at(stage, r, col) = 0u;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-        // V^T operand per 16-row d fragment: lane reads V[t(q, j)][16 nn + n]
-#pragma unroll
-        for (int nn = 0; nn < NN; ++nn) {
-            uint32_t vk[4];
-#pragma unroll
-            for (int j = 0; j < 8; j += 2) {
-                const int t0 = j < 4 ? 4 * q + j : 16 + 4 * q + (j - 4);
-                const uint16_t a = *(const uint16_t *)v_at(stage, t0, (16 * nn + n) * 2);
-                const uint16_t c2 = *(const uint16_t *)v_at(stage, t0 + 1, (16 * nn + n) * 2);
-                vk[j / 2] = (uint32_t)a | ((uint32_t)c2 << 16);
-            }
-            o[nn] = Mma<T>::run(u32x4{vk[0], vk[1], vk[2], vk[3]}, pb, o[nn]);
-        }
-        // the stage is rewritten by a later chunk's loads: finish reading it first
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-
-    {
-        // this wave's chunks are wave, wave + MW, ...; the steady-state loop always has
-        // a next chunk to prefetch (see tile_base), the last one or two run after it
-        const int mine = nchunks > wave ? (nchunks - wave + MW - 1) / MW : 0;
-        Chunk A, Bf;
-        if (mine > 0) {
-            issue(A, wave, 0);
-            int j = 0;
-            for (; j + 2 < mine; j += 2) {
-                issue(Bf, wave + (j + 1) * MW, 1);
-                consume(A, wave + j * MW, 0);
-                issue(A, wave + (j + 2) * MW, 0);
-                consume(Bf, wave + (j + 1) * MW, 1);
-            }
-            if (j + 1 < mine) {
-                issue(Bf, wave + (j + 1) * MW, 1);
-                consume(A, wave + j * MW, 0);
-                consume(Bf, wave + (j + 1) * MW, 1);
-            } else {
-                consume(A, wave + j * MW, 0);
-            }
-        }
-    }
-
-    // normaliser of head n over the 4 lanes of its column
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-
-    // merge the waves through LDS (the staging area is free now)
-    __syncthreads();
-    float *sm_m = (float *)lds;          // [MW][G]
-    float *sm_l = sm_m + MW * G;         // [MW][G]
-    float *sm_acc = sm_l + MW * G;       // [MW][G][D]
+    __shared__ __attribute__((aligned(16))) uint8_t lds[MW * Geom<D>::WAVE_LDS];
+    static_assert((2 * MW * G + MW * G * D) * 4 <= MW * Geom<D>::WAVE_LDS, "merge area must fit the staging area");
     __shared__ int sm_bad;
-    if (threadIdx.x == 0) sm_bad = 0;
-    __syncthreads();
-    if (bad) sm_bad = 1;
-    if (n < G) {
-        if (q == 0) {
-            sm_m[wave * G + n] = m;
-            sm_l[wave * G + n] = lsum;
+
+    WaveState<D> st;
+    st.bad = ctx < 0;
+    attend_range<T, D, G, NT>(st, lds + wave * Geom<D>::WAVE_LDS, query, key_cache, value_cache,
+                              block_tables + (int64_t)s * max_blocks_per_seq, max_blocks_per_seq, s, kvh,
+                              num_kv_heads, log2_block, num_blocks, start, end, scale_log2, wave, lane);
+    const int64_t row0 = (int64_t)s * num_q_heads + kvh * G;
+    if (SPLIT)
+        finish<T, D, G>(st, lds, &sm_bad, wave, lane, nullptr, 0, ws_max, ws_sum, ws_acc,
+                        row0 * max_partitions + part, max_partitions);
+    else
+        finish<T, D, G>(st, lds, &sm_bad, wave, lane, out, row0, nullptr, nullptr, nullptr, 0, 0);
+}
+
+// Balanced split on the matrix cores (balanced.h): CT-token chunks, one worker per
+// workgroup.  The workgroup walks its range item by item; within an item its waves
+// take the range's chunks in turn, as the one-pass kernel does for a whole context,
+// and at the item's end they merge and write the item's partial.
+template <typename T, int D, int G, bool NT>
+__global__ __launch_bounds__(MW * 64) void decode_mfma_balanced_kernel(
+    const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
+    const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, int32_t *__restrict__ ws_hdr, float *__restrict__ ws_max,
+    float *__restrict__ ws_sum, float *__restrict__ ws_acc, int max_blocks_per_seq, int num_seqs,
+    int num_kv_heads, int log2_block, int num_blocks, float scale_log2) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = num_seqs;
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds[MW * Geom<D>::WAVE_LDS];
+    static_assert((BAL_MAX_SEQS + 1) * 4 <= MW * Geom<D>::WAVE_LDS, "chunk prefix must fit the staging area");
+    static_assert((2 * MW * G + MW * G * D) * 4 <= MW * Geom<D>::WAVE_LDS, "merge area must fit the staging area");
+    __shared__ int sm_bad;
+
+    // chunks per sequence and their prefix, in the staging area until the range is
+    // located (wave 0 scans 64 sequences a step)
+    int *sm_pre = (int *)lds;
+    if (wave == 0) {
+        int carry = 0;
+        for (int base = 0; base < S; base += 64) {
+            const int s = base + lane;
+            const int c = s < S ? context_lens[s] : 0;
+            int v = c > 0 ? (c + CT - 1) / CT : 0;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(v, o);
+                if (lane >= o) v += t;
+            }
+            if (s < S) sm_pre[s + 1] = carry + v;
+            carry += __shfl(v, 63);
         }
-#pragma unroll
-        for (int nn = 0; nn < NN; ++nn)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm_acc[(wave * G + n) * D + 16 * nn + 4 * q + i] = o[nn][i];
+        if (lane == 0) sm_pre[0] = 0;
     }
     __syncthreads();
-    const bool any_bad = sm_bad != 0;
-    for (int t = threadIdx.x; t < G * D; t += MW * 64) {
-        const int g = t / D;
-        const int j = t - g * D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < MW; ++w) M = fmaxf(M, sm_m[w * G + g]);
-        const float Ms = M == -INFINITY ? 0.f : M;
-        float Lsum = 0.f, A = 0.f;
-#pragma unroll
-        for (int w = 0; w < MW; ++w) {
-            const float f = fast_exp2(sm_m[w * G + g] - Ms);
-            Lsum += sm_l[w * G + g] * f;
-            A += sm_acc[(w * G + g) * D + j] * f;
+    auto pre = [&](int s) -> int { return __builtin_amdgcn_readfirstlane(sm_pre[s]); };
+
+    const int per_head = pre(S);
+    const int total = per_head * num_kv_heads;
+    const int W = gridDim.x;
+    const int per = (total + W - 1) / W;
+    if (blockIdx.x == 0) {
+        if (threadIdx.x == 0) {
+            ws_hdr[0] = per_head;
+            ws_hdr[1] = per;
+            ws_hdr[2] = W;
+            ws_hdr[3] = 0;
         }
-        const int h = kvh * G + g;
-        if (SPLIT) {
-            const int64_t pi = ((int64_t)s * num_q_heads + h) * max_partitions + part;
-            if (j == 0) {
-                ws_max[pi] = any_bad ? NAN : M;
-                ws_sum[pi] = Lsum;
-            }
-            ws_acc[pi * D + j] = A;
-        } else {
-            float ov = Lsum > 0.f ? A / Lsum : 0.f;
-            if (any_bad) ov = NAN;
-            store_out<T>(out, ((int64_t)s * num_q_heads + h) * D + j, ov);
+        for (int t = threadIdx.x; t <= S; t += MW * 64) ws_hdr[BAL_HDR + t] = sm_pre[t];
+    }
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int g_begin = w * per;
+    const int g_end = min(total, g_begin + per);
+
+    // first item of the range: KV head, sequence, chunk within the sequence
+    int kvh = num_kv_heads, s = 0, c = 0;
+    if (per > 0 && g_begin < total) {
+        kvh = g_begin / per_head;
+        const int r = g_begin - kvh * per_head;
+        int lo = 0, hi = S - 1;  // smallest s with pre(s + 1) > r
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (pre(mid + 1) > r)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        s = lo;
+        c = r - pre(lo);
+    }
+    __syncthreads();  // the prefix is dead: the staging area is the waves' from here
+    if (per == 0 || g_begin >= total) return;  // the whole workgroup
+
+    for (int g = g_begin; g < g_end;) {
+        const int ctx = __builtin_amdgcn_readfirstlane(context_lens[s]);
+        const int nc = (ctx + CT - 1) / CT;  // > 0: the list holds only non-empty items
+        const int take = min(nc - c, g_end - g);
+        WaveState<D> st;
+        st.bad = false;
+        attend_range<T, D, G, NT>(st, lds + wave * Geom<D>::WAVE_LDS, query, key_cache, value_cache,
+                                  block_tables + (int64_t)s * max_blocks_per_seq, max_blocks_per_seq, s, kvh,
+                                  num_kv_heads, log2_block, num_blocks, c * CT, min(ctx, (c + take) * CT),
+                                  scale_log2, wave, lane);
+        const int64_t slot = (int64_t)w + (int64_t)kvh * S + s;
+        finish<T, D, G>(st, lds, &sm_bad, wave, lane, nullptr, 0, ws_max, ws_sum, ws_acc, slot * G, 1);
+        g += take;
+        // next non-empty item
+        c = 0;
+        if (g < g_end) {
+            do {
+                if (++s == S) {
+                    s = 0;
+                    ++kvh;
+                }
+            } while (__builtin_amdgcn_readfirstlane(context_lens[s]) <= 0);
         }
     }
 }
 
 template <typename T, int D, int G, bool NT>
+int launch_balanced(const DecodeArgs &a) {
+    auto kernel = decode_mfma_balanced_kernel<T, D, G, NT>;
+    static int resident = 0;  // workgroups the device holds at once (per instantiation)
+    if (resident == 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)kernel, MW * 64, 0) == hipSuccess)
+            resident = cus * (PA_MFMA_BAL_PER_CU > 0 && per_cu > PA_MFMA_BAL_PER_CU ? PA_MFMA_BAL_PER_CU
+                              : per_cu > 0 ? per_cu : 1);
+    }
+    if (resident <= 0) return fail(PA_ERR_HIP, "occupancy query failed");
+    const int workers = resident > a.max_workers ? a.max_workers : resident;  // workgroups
+    const int log2b = __builtin_ctz(a.block_size);
+    hipLaunchKernelGGL(kernel, dim3(workers), dim3(MW * 64), 0, (hipStream_t)a.stream,
+                       (const uint8_t *)a.query, (const uint8_t *)a.key_cache, (const uint8_t *)a.value_cache,
+                       a.block_tables, a.context_lens, a.ws_hdr, a.ws_max, a.ws_sum, a.ws_acc,
+                       a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads, log2b, a.num_blocks, a.scale_log2);
+    const int rc = check_launch("decode_mfma_balanced");
+    if (rc != PA_OK) return rc;
+    return launch_balanced_merge<T, D, G>(a);
+}
+
+template <typename T, int D, int G, bool NT>
 int launch_t(const DecodeArgs &a) {
+    if (a.partition_size < 0) return launch_balanced<T, D, G, NT>(a);
     const int log2b = __builtin_ctz(a.block_size);
     const bool split = a.partition_size > 0;
     const unsigned grid = (unsigned)a.num_seqs * a.num_kv_heads * (split ? a.max_partitions : 1);

@@ -32,6 +32,7 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "balanced.h"
 #include "kernel_common.h"
 
 namespace pa {
@@ -125,13 +126,12 @@ struct E4M3KV {
         return s;
     }
     __device__ static void values(const Word &v, float (&f)[SB]) { e4m3_to_f32<SB / 4>(v, f); }
-    // codes of P consecutive elements of a token row given in T (the newest token),
-    // packed from the low byte: each element's code of x / scale, the scatter's rounding
-    // bit for bit
+    // codes of P consecutive elements of a token row given in T (the newest token; their
+    // bits packed from the low half in h), packed from the low byte: each element's
+    // code of x / scale, the scatter's rounding bit for bit
     template <int P>
-    __device__ static uint32_t encode_run(const uint8_t *p, float scale) {
+    __device__ static uint32_t encode_run(uint32_t h, float scale) {
         static_assert(P == 1 || P == 2, "elements per lane");
-        uint32_t h = P == 2 ? *(const uint32_t *)p : (uint32_t) * (const uint16_t *)p;
         uint32_t c = 0;
 #pragma unroll
         for (int e = 0; e < P; ++e) {
@@ -257,6 +257,9 @@ __device__ inline void merge_rows(float (&m)[G], float (&l)[G], float (&acc)[G][
 #ifndef PA_FP8_WAVES
 #define PA_FP8_WAVES 8
 #endif
+#ifndef PA_VALU_WAVES_PER_EU
+#define PA_VALU_WAVES_PER_EU 1
+#endif
 #ifndef PA_FP8_WAVES_PER_EU
 #define PA_FP8_WAVES_PER_EU 1
 #endif
@@ -267,7 +270,7 @@ constexpr int waves_per_group() {
 // Waves per SIMD the register allocation must allow (1 = no constraint).
 template <typename KV, int G>
 constexpr int min_waves_per_eu() {
-    return KV::scaled ? PA_FP8_WAVES_PER_EU : 1;
+    return KV::scaled ? PA_FP8_WAVES_PER_EU : PA_VALU_WAVES_PER_EU;
 }
 
 template <typename KV, int D, int G, bool SPLIT, bool NT>
@@ -320,6 +323,10 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     const int32_t *table = block_tables + (int64_t)s * max_blocks_per_seq;
     const int64_t head_off = (int64_t)kvh * block_size * ROW_BYTES;
     const int64_t block_bytes = (int64_t)num_kv_heads * block_size * ROW_BYTES;
+    // This wave's first table entry, read beside the context length instead of after it
+    // (the first chunk's position does not depend on the length).
+    const int lb0 = (start + wave * C) >> log2_block;
+    const int32_t pb0 = lb0 < max_blocks_per_seq ? table[lb0] : -1;
 
     // this lane's slice of every query head of the group
     typename KV::QSlice qv[G];
@@ -349,68 +356,45 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     const int nfull = ntok / C;
     const bool has_tail = (ntok % C) != 0;
 
-    // The wave that would take the next chunk handles the newest token: before the loop
-    // it loads (and for E4M3 pools rounds) the given values and stores them into the
-    // pool, so their latency hides behind the loop; after the loop it attends to them
-    // with row 0 of its lanes (the other rows masked).
+    // The wave that would take the next chunk handles the newest token.  Before the loop
+    // it looks up the token's slot and loads the given values (their latency hides
+    // behind the loop); after the loop it stores them into the pool (E4M3: rounded by
+    // all 64 lanes, D / 64 elements each) and attends to them with row 0 of its lanes
+    // (the other rows masked).  The loop never reads that slot.
     const bool app_here = append && wave == (nfull + (has_tail ? 1 : 0)) % NWG;
+    constexpr int AP = D / 64;  // E4M3: elements of the newest row per lane
+    static_assert(AP * 64 == D, "head_dim");
     typename KV::Word app_k[1] = {typename KV::Word{}}, app_v[1] = {typename KV::Word{}};
+    uint32_t app_rk = 0, app_rv = 0;  // E4M3: this lane's AP raw elements of T
+    int64_t app_base = -1;
     float app_ks = 1.f, app_vs = 1.f;
     if (app_here) {
         const int t = ctx - 1;
         const int lb = t >> log2_block;
-        int64_t base = -1;
         if (lb < max_blocks_per_seq) {
             const int32_t pb = table[lb];
             if (pb >= 0 && pb < num_blocks) {
-                base = (int64_t)pb * block_bytes + head_off + (int64_t)(t & (block_size - 1)) * ROW_BYTES;
+                app_base = (int64_t)pb * block_bytes + head_off + (int64_t)(t & (block_size - 1)) * ROW_BYTES;
                 if constexpr (KV::scaled) {
                     app_ks = k_scales[(int64_t)pb * num_kv_heads + kvh];
                     app_vs = v_scales[(int64_t)pb * num_kv_heads + kvh];
                 }
             }
         }
-        if (base < 0) bad = true;
+        if (app_base < 0) bad = true;
         if constexpr (KV::scaled) {
-            // Each element costs a correctly rounded division and an encode: all 64
-            // lanes take D / 64 elements each and store their codes, and row 0 gathers
-            // its slices through LDS (in order within the wave).
-            constexpr int P = D / 64;
-            static_assert(P * 64 == D, "head_dim");
-            __shared__ __align__(16) uint8_t sm_new[2][D];
-            const int64_t src = ((int64_t)(s * num_kv_heads + kvh) * D + lane * P) * QB;
-            const uint32_t ck = KV::template encode_run<P>(new_key + src, app_ks);
-            const uint32_t cv = KV::template encode_run<P>(new_value + src, app_vs);
-            if constexpr (P == 2) {
-                *(uint16_t *)(sm_new[0] + lane * 2) = (uint16_t)ck;
-                *(uint16_t *)(sm_new[1] + lane * 2) = (uint16_t)cv;
-                if (base >= 0) {
-                    *(uint16_t *)(key_out + base + lane * 2) = (uint16_t)ck;
-                    *(uint16_t *)(value_out + base + lane * 2) = (uint16_t)cv;
-                }
+            const int64_t src = ((int64_t)(s * num_kv_heads + kvh) * D + lane * AP) * QB;
+            if constexpr (AP == 2) {
+                app_rk = *(const uint32_t *)(new_key + src);
+                app_rv = *(const uint32_t *)(new_value + src);
             } else {
-                sm_new[0][lane] = (uint8_t)ck;
-                sm_new[1][lane] = (uint8_t)cv;
-                if (base >= 0) {
-                    key_out[base + lane] = (uint8_t)ck;
-                    value_out[base + lane] = (uint8_t)cv;
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (row == 0) {
-                app_k[0] = *(const typename KV::Word *)(sm_new[0] + col * SB);
-                app_v[0] = *(const typename KV::Word *)(sm_new[1] + col * SB);
+                app_rk = *(const uint16_t *)(new_key + src);
+                app_rv = *(const uint16_t *)(new_value + src);
             }
         } else if (row == 0) {
             const int64_t src = ((int64_t)(s * num_kv_heads + kvh) * D + col * EPL) * QB;
             app_k[0] = KV::from_new(new_key + src, app_ks);
             app_v[0] = KV::from_new(new_value + src, app_vs);
-            if (base >= 0) {
-                *(typename KV::Word *)(key_out + base + col * SB) = app_k[0];
-                *(typename KV::Word *)(value_out + base + col * SB) = app_v[0];
-            }
         }
     }
 
@@ -434,7 +418,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
             if (lb >= max_blocks_per_seq) {  // context longer than the table row
                 bad = true;
             } else {
-                const int32_t pb = table[lb];
+                const int32_t pb = lb == lb0 ? pb0 : table[lb];
                 if (pb < 0 || pb >= num_blocks) {
                     bad = true;
                 } else {
@@ -504,6 +488,37 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     }
 
     if (app_here) {
+        if constexpr (KV::scaled) {
+            __shared__ __align__(16) uint8_t sm_new[2][D];
+            const uint32_t ck = KV::template encode_run<AP>(app_rk, app_ks);
+            const uint32_t cv = KV::template encode_run<AP>(app_rv, app_vs);
+            if constexpr (AP == 2) {
+                *(uint16_t *)(sm_new[0] + lane * 2) = (uint16_t)ck;
+                *(uint16_t *)(sm_new[1] + lane * 2) = (uint16_t)cv;
+                if (app_base >= 0) {
+                    *(uint16_t *)(key_out + app_base + lane * 2) = (uint16_t)ck;
+                    *(uint16_t *)(value_out + app_base + lane * 2) = (uint16_t)cv;
+                }
+            } else {
+                sm_new[0][lane] = (uint8_t)ck;
+                sm_new[1][lane] = (uint8_t)cv;
+                if (app_base >= 0) {
+                    key_out[app_base + lane] = (uint8_t)ck;
+                    value_out[app_base + lane] = (uint8_t)cv;
+                }
+            }
+            // row 0 gathers its slices (LDS operations of one wave complete in order)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (row == 0) {
+                app_k[0] = *(const typename KV::Word *)(sm_new[0] + col * SB);
+                app_v[0] = *(const typename KV::Word *)(sm_new[1] + col * SB);
+            }
+        } else if (row == 0 && app_base >= 0) {
+            *(typename KV::Word *)(key_out + app_base + col * SB) = app_k[0];
+            *(typename KV::Word *)(value_out + app_base + col * SB) = app_v[0];
+        }
         const float ksl1[1] = {KV::scaled ? scale_log2 * app_ks : scale_log2};
         const float vsc1[1] = {app_vs};
         chunk_update<KV, G, 1, LPT, TPW>(qv, app_k, app_v, ksl1, vsc1, row, 1, true, m, l, acc);
@@ -601,22 +616,12 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(
 
 // ------------------------------------------------------------------ balanced split
 //
-// All work of the batch is one ordered list of chunks (KV head, then sequence, then
-// C-token chunk).  Each of the W resident waves takes an equal contiguous range of it
-// and streams it with the same double-buffered pipeline, so no wave waits for a long
-// sequence and no sequence waits for a free wave.  When a wave finishes the part of a
-// (sequence, KV head) item that lies in its range it writes that item's partial
-// (running max, sum, weighted value sums per query head) to slot `wave + item`: ranges
-// and items are both ordered, so two (wave, item) pairs that share a slot would need
-// a later wave on an earlier item, which cannot happen.  balanced_merge_kernel then
-// combines each item's partials with log-sum-exp weights.
-//
-// Workspace header (int32), written by workgroup 0: [0] chunks per KV head, [1] chunks
-// per wave, [2] waves, [4 + s] chunks of the sequences before s (s = 0..S).
+// The list, ranges, partial slots and header are those of balanced.h, with C-token
+// chunks and one worker per wave: each of the W resident waves streams its range with
+// the same double-buffered pipeline, so no wave waits for a long sequence and no
+// sequence waits for a free wave.
 
-constexpr int NWB = 4;               // waves per workgroup of the balanced kernel
-constexpr int BAL_MAX_SEQS = 4096;   // sequences per batch in balanced mode
-constexpr int BAL_HDR = 4;           // header ints before the prefix
+constexpr int NWB = 4;  // waves per workgroup of the balanced kernel
 
 template <typename KV, int D, int G, bool NT>
 __global__ __launch_bounds__(NWB * 64) void decode_balanced_kernel(
@@ -841,52 +846,6 @@ __global__ __launch_bounds__(NWB * 64) void decode_balanced_kernel(
     }
 }
 
-// Combine the partials of one (sequence, query head) written by the waves whose
-// ranges cover it: out = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w.
-template <typename T, int D, int G>
-__global__ __launch_bounds__(64) void balanced_merge_kernel(
-    void *__restrict__ out, const int32_t *__restrict__ ws_hdr, const float *__restrict__ ws_max,
-    const float *__restrict__ ws_sum, const float *__restrict__ ws_acc,
-    const int32_t *__restrict__ context_lens, int num_seqs, int num_kv_heads) {
-    const int num_q_heads = num_kv_heads * G;
-    const int sh = blockIdx.x;
-    const int s = sh / num_q_heads;
-    const int h = sh - s * num_q_heads;
-    const int kvh = h / G;
-    const int gg = h - kvh * G;
-    const int64_t obase = (int64_t)sh * D;
-    const int ctx = context_lens[s];
-    const int per_head = ws_hdr[0];
-    const int per = ws_hdr[1];
-    const int first = ws_hdr[BAL_HDR + s];
-    const int n = ws_hdr[BAL_HDR + s + 1] - first;
-    if (ctx < 0 || n == 0) {
-        for (int j = threadIdx.x; j < D; j += 64) store_out<T>(out, obase + j, ctx < 0 ? NAN : 0.f);
-        return;
-    }
-    const int g0 = kvh * per_head + first;
-    const int w0 = g0 / per, w1 = (g0 + n - 1) / per;
-    const int64_t item = (int64_t)kvh * num_seqs + s;
-    float M = -INFINITY;
-    bool bad = false;
-    for (int w = w0; w <= w1; ++w) {
-        const float x = ws_max[(w + item) * G + gg];
-        bad |= x != x;
-        M = fmaxf(M, x);
-    }
-    const float Ms = M == -INFINITY ? 0.f : M;
-    float Lsum = 0.f;
-    for (int w = w0; w <= w1; ++w) Lsum += ws_sum[(w + item) * G + gg] * fast_exp2(ws_max[(w + item) * G + gg] - Ms);
-    for (int j = threadIdx.x; j < D; j += 64) {
-        float A = 0.f;
-        for (int w = w0; w <= w1; ++w)
-            A += fast_exp2(ws_max[(w + item) * G + gg] - Ms) * ws_acc[((w + item) * G + gg) * D + j];
-        float o = Lsum > 0.f ? A / Lsum : 0.f;
-        if (bad) o = NAN;
-        store_out<T>(out, obase + j, o);
-    }
-}
-
 // Waves of one balanced launch: as many as can be resident at once on this device.
 template <typename K>
 int balanced_workers(K kernel) {
@@ -913,10 +872,7 @@ int launch_balanced(const DecodeArgs &a) {
                        a.num_blocks, a.scale_log2);
     int rc = check_launch("decode_balanced");
     if (rc != PA_OK) return rc;
-    hipLaunchKernelGGL((balanced_merge_kernel<typename KV::Q, D, G>), dim3(a.num_seqs * a.num_q_heads),
-                       dim3(64), 0, st, a.out, a.ws_hdr, a.ws_max, a.ws_sum, a.ws_acc, a.context_lens,
-                       a.num_seqs, a.num_kv_heads);
-    return check_launch("balanced_merge");
+    return launch_balanced_merge<typename KV::Q, D, G>(a);
 }
 
 template <typename KV, int D, int G, bool NT>

@@ -46,7 +46,7 @@ HAVE_MFMA = True
 
 def variants(Hq, Hkv, dtype, P=0):
     vs = [VALU]
-    if HAVE_MFMA and Hq // Hkv >= 2 and dtype != "f32" and P != BAL:
+    if HAVE_MFMA and Hq // Hkv >= 2 and dtype != "f32":
         vs.append(MFMA)
     return vs
 
@@ -283,15 +283,17 @@ def test_shared_kv_hint_changes_nothing_but_the_cache_policy():
 
 
 @pytest.mark.parametrize("P", [0, 64, BAL])
-def test_bad_table_entry_gives_nan_for_that_sequence_only(P):
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_bad_table_entry_gives_nan_for_that_sequence_only(P, kernel):
     rng = np.random.default_rng(12)
-    c = Case(rng, [40, 50, 60], 4, 4, 128, 16, "f16")
-    clean = _run_case(c, P, VALU)
+    Hq, Hkv, v = (4, 4, VALU) if kernel == "valu" else (8, 2, MFMA)
+    c = Case(rng, [40, 50, 60], Hq, Hkv, 128, 16, "f16")
+    clean = _run_case(c, P, v)
     for bad in (-1, c.num_blocks, 1 << 30):
         t = c.tables.copy()
         t[1, 2] = bad
-        say(f"[gpu] bad entry {bad} P={P}")
-        got = _run_case(c, P, VALU, tables=t)
+        say(f"[gpu] bad entry {bad} P={P} {kernel}")
+        got = _run_case(c, P, v, tables=t)
         assert torch.isnan(got[1]).all()
         assert bits(got[0]) == bits(clean[0]) and bits(got[2]) == bits(clean[2])
 
@@ -625,19 +627,23 @@ def _sub_batch_scales(w, batch, sub, seqs):
     return ks, vs
 
 
-@pytest.mark.parametrize("name", ["llama7b", "llama13b_long", "llama70b_gqa", "prefix_sharing",
-                                  "llama7b_fp8"])
-def test_full_size_sampled(name):
-    """Whole batch on the GPU in the benchmark's launch setup; oracle on a sample of
-    sequences (attention does not depend on where blocks sit, so the oracle may
-    place its sub-batch in its own pool)."""
+FULL_SIZE = [("llama7b", None), ("llama13b_long", None), ("llama70b_gqa", None),
+             ("llama70b_gqa", 0), ("prefix_sharing", None), ("llama7b_fp8", None)]
+
+
+@pytest.mark.parametrize("name,P", FULL_SIZE, ids=lambda x: str(x))
+def test_full_size_sampled(name, P):
+    """Whole batch on the GPU in the benchmark's launch setup (P None: the workload's
+    partition setting); oracle on a sample of sequences (attention does not depend on
+    where blocks sit, so the oracle may place its sub-batch in its own pool)."""
     w = W.WORKLOADS[name]
+    P = w.partition_size if P is None else P
     say(f"[gpu] full-size {name}: generating")
     batch = W.make_batch(w)
     db = replay(batch)
     variant = AUTO
-    say(f"[gpu] full-size {name}: step P={w.partition_size}")
-    got = f64(db.step(partition_size=w.partition_size, variant=variant))
+    say(f"[gpu] full-size {name}: step P={P}")
+    got = f64(db.step(partition_size=P, variant=variant))
     torch.cuda.synchronize()
     assert np.all(np.isfinite(got))
     if w.lengths == "prefix":

@@ -21,8 +21,8 @@ Workloads (shapes and length mixes of the serving examples on the pages):
                     (the last prompt block partly filled), then 0..256 private tokens
                     and the current one; 32 heads, d=128, B=16, fp16, 8,192 blocks.
   - llama70b_gqa    70B-shaped GQA: 32 seqs, 64 query / 8 KV heads, d=128, B=128,
-                    bf16, 4,096 blocks, lengths uniform in [4096, 8192], 512-token
-                    partitions.
+                    bf16, 4,096 blocks, lengths uniform in [4096, 8192], balanced split
+                    (partition_size -1).
   - llama7b_fp8     llama7b (same seed, lengths and numbers) with the pools held as
                     OCP E4M3 codes and one fp32 scale per (block, KV head) for K and
                     for V; query, new K/V and output stay fp16.
@@ -69,7 +69,7 @@ class Workload:
     block_size: int
     num_blocks: int
     dtype: str
-    partition_size: int  # 0: one pass over the whole context
+    partition_size: int  # 0: one pass over the whole context; -1: balanced split
     lengths: str  # "fixed" | "lognormal" | "uniform" | "prefix"
     fixed_lengths: Tuple[int, ...] = ()
     low: int = 0  # uniform: inclusive bounds
@@ -109,7 +109,7 @@ WORKLOADS: Dict[str, Workload] = {
     "prefix_sharing": Workload("prefix_sharing", 4, 80, 32, 32, 128, 16, 8192, "f16", 512,
                                "prefix", groups=16, samples=5, prefix_base=1024,
                                private_max=256),
-    "llama70b_gqa": Workload("llama70b_gqa", 5, 32, 64, 8, 128, 128, 4096, "bf16", 0,
+    "llama70b_gqa": Workload("llama70b_gqa", 5, 32, 64, 8, 128, 128, 4096, "bf16", -1,
                              "uniform", low=4096, high=8192),
     "llama7b_fp8": Workload("llama7b_fp8", 2, 64, 32, 32, 128, 16, 40000, "f16", 0, "lognormal",
                             kv_dtype="fp8"),
