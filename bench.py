@@ -90,6 +90,8 @@ def parse():
                     help="store the newest tokens with their own launch even where the attention "
                          "launch can do it")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-stream", action="store_true",
+                    help="skip the read-bandwidth probe (pa_stream_read over 4 GiB)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--swap", type=int, default=0, metavar="N",
                     help="instead of decode: move N sequences' blocks to pinned host memory and "
@@ -229,7 +231,62 @@ def cpu_baseline(args, w, batch, kv_bytes: int) -> dict:
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole {w.name} decode step ({w.num_seqs} sequences, all heads), "
                       f"oracle decode call only, {dt:.2f} s on one thread of {cpu}",
-            "seconds": round(dt, 3), "seqs_per_s": round(w.num_seqs / dt, 3)}
+            "seconds": round(dt, 3), "seqs_per_s": round(w.num_seqs / dt, 3),
+            "threads": cpu_baseline_threads(w, batch, p, o, kv_bytes)}
+
+
+def cpu_baseline_threads(w, batch, p, o, kv_bytes: int) -> dict:
+    """The same oracle call split over sequences on the host's cores (threads: the oracle
+    is C behind ctypes, which releases the GIL; its decode keeps no shared state).
+    Contiguous sequence ranges of about equal token counts, one per thread."""
+    import concurrent.futures as cf
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    n = max(1, min(n, 16, w.num_seqs))
+    ctx = np.maximum(np.asarray(p.context_lens, np.int64), 1)
+    cuts = np.searchsorted(np.cumsum(ctx), np.arange(1, n) * ctx.sum() / n)
+    bounds = [0, *[int(c) + 1 for c in cuts], w.num_seqs]
+    ranges = [(a, b) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+
+    def run(r):
+        a, b = r
+        if w.kv == "fp8":
+            o.decode_fp8(batch.q[a:b], p.key_cache, p.value_cache, p.k_scales, p.v_scales,
+                         p.block_tables[a:b], p.context_lens[a:b], w.scale, w.dtype)
+        else:
+            o.decode(batch.q[a:b], p.key_cache, p.value_cache, p.block_tables[a:b],
+                     p.context_lens[a:b], w.scale, w.dtype)
+
+    with cf.ThreadPoolExecutor(len(ranges)) as ex:
+        t = time.perf_counter()
+        list(ex.map(run, ranges))
+        dt = time.perf_counter() - t
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": len(ranges),
+            "seconds": round(dt, 3)}
+
+
+def stream_read_gbs(nbytes: int = 4 << 30, reps: int = 5) -> float:
+    """Achievable HBM read bandwidth: pa_stream_read over a buffer far beyond the caches,
+    timed with events on the launch stream."""
+    import torch
+    from paged_kv_cache_308_amd import pa_stream_read
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    for _ in range(2):
+        pa_stream_read(buf, sink, st)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for _ in range(reps):
+        pa_stream_read(buf, sink, st)
+    b.record(st)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del buf, sink
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def swap_bench(args, w, batch) -> dict:
@@ -442,6 +499,7 @@ def main():
         log(args, f"[bench] identity layout decode {ident * 1e3:.1f} us")
 
     alloc_us = host_alloc_cost(w, batch)
+    stream = None if args.no_stream else stream_read_gbs()
     cpu = None if args.no_cpu else cpu_baseline(args, w, batch, ab["kv"])
 
     gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
@@ -475,6 +533,11 @@ def main():
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "decode_us": round(dec_avg * 1e3, 2),
+        "decode_us_p10_median_p90": [round(float(np.percentile(dec_ms, x)) * 1e3, 2) for x in (10, 50, 90)],
+        "stream_read_gbs": None if stream is None else round(stream, 1),
+        "pct_of_stream_read": None if stream is None else round(100 * gbs / stream, 2),
+        "mfma_util": round(4.0 * float(ctx.sum()) * w.num_q_heads * w.head_dim / (dec_avg * 1e-3) / 1e12 /
+                           MFMA_PEAK_TFLOPS[w.dtype], 4) if mfma else None,
         "fused_store": args.fused,
         "pre_decode_us": round(float(np.mean(pre_ms)) * 1e3, 2),
         "decode_kv_gbs": round(ab["kv"] / (dec_avg * 1e-3) / 1e9, 2),

@@ -254,6 +254,16 @@ int pa_decode_fp8_append(void *out, const void *query, const void *new_key, cons
                          int num_blocks, int max_context_len, float scale, int dtype, int partition_size,
                          int variant, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Measurement helper, not part of the attention path: reads `bytes` bytes of device
+ * memory at buf once (16-byte non-temporal loads spread over the whole device) and
+ * folds them into a value that is stored to *sink (device, 4 bytes) only when it
+ * equals a fixed constant, so the reads cannot be elided.  The achievable read
+ * bandwidth that the decode kernels' HBM roofline is compared against.  buf 16-byte
+ * aligned, bytes a positive multiple of 16; PA_ERR_INVALID otherwise.
+ */
+int pa_stream_read(const void *buf, size_t bytes, void *sink, void *stream);
+
 /* Host-side checks ([cpai] §13).  PA_ERR_BOUNDS names the first offending entry in
  * pa_last_error. */
 int pa_check_tables(const int32_t *block_tables, const int32_t *context_lens, int num_seqs,

@@ -29,7 +29,7 @@ EXPORTS = (
     "pa_status_str", "pa_last_error", "pa_abi_version", "pa_decode_workspace_bytes", "pa_decode",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_check_tables",
     "pa_reshape_and_cache_fp8", "pa_decode_fp8", "pa_multi_query", "pa_decode_append",
-    "pa_decode_fp8_append",
+    "pa_decode_fp8_append", "pa_stream_read",
     "pa_check_copy_pairs", "pa_alloc_adopt",
     "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_set_free_order", "pa_alloc_new_seq",
     "pa_alloc_append_slot", "pa_alloc_append_slots", "pa_alloc_fork", "pa_alloc_free_seq",
@@ -83,6 +83,7 @@ def _lib():
                                        i32, i32, i32, f32, i32, i32, i32, vp, sz, vp]),
         "pa_copy_blocks": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
         "pa_swap_blocks": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]),
+        "pa_stream_read": (i32, [vp, sz, vp, vp]),
         "pa_alloc_adopt": (i32, [vp, i32, i64p, i32p, i32]),
         "pa_check_tables": (i32, [i32p, i32p, i32, i32, i32, i32]),
         "pa_check_copy_pairs": (i32, [i32p, i32p, i32, i32]),
@@ -363,6 +364,16 @@ def pa_swap_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cach
         _any_ptr(src, "src"), _any_ptr(dst, "dst"), src.shape[0], Hkv, d, B, ns, nd,
         dtype_code(src_key_cache), _stream(stream))
     _check(rc, "pa_swap_blocks")
+
+
+def pa_stream_read(buf, sink, stream=None):
+    """Read every byte of the device tensor `buf` once (read-bandwidth probe); `sink` is a
+    device tensor of at least 4 bytes."""
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_contiguous() or sink.numel() * sink.element_size() < 4:
+        raise ValueError("contiguous buffer and a 4-byte sink required")
+    rc = _lib().pa_stream_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink"), _stream(stream))
+    _check(rc, "pa_stream_read")
 
 
 # ------------------------------------------------------------------ host checks

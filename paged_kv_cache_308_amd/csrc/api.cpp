@@ -418,6 +418,13 @@ int pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *src, const
                               num_kv_heads, head_dim, block_size, num_blocks, num_blocks, eb, stream);
 }
 
+int pa_stream_read(const void *buf, size_t bytes, void *sink, void *stream) {
+    clear_error();
+    if (!buf || !sink) return fail(PA_ERR_INVALID, "NULL device pointer");
+    if (bytes == 0 || bytes % 16 || ((uintptr_t)buf & 15)) return fail(PA_ERR_INVALID, "buffer of %zu bytes", bytes);
+    return launch_stream_read(buf, bytes, sink, stream);
+}
+
 int pa_swap_blocks(const void *src_key_cache, const void *src_value_cache, void *dst_key_cache,
                    void *dst_value_cache, const int32_t *src, const int32_t *dst, int num_pairs,
                    int num_kv_heads, int head_dim, int block_size, int src_num_blocks,

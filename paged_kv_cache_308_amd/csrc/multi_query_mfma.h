@@ -50,7 +50,7 @@ constexpr int MW = 4;  // waves per workgroup
 #endif
 constexpr int RF = PA_MQ_FRAGS;      // 16-row query fragments per wave
 constexpr int ROWS = 16 * RF * MW;   // query rows per workgroup
-static_assert(PA_MQ_KEYS % 32 == 0 && (RF == 1 || RF == 2), "tile shape");
+static_assert(PA_MQ_KEYS % 32 == 0 && (RF == 1 || RF == 2 || RF == 4), "tile shape");
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(MW * 64) void multi_query_kernel(

@@ -658,3 +658,18 @@ def test_full_size_sampled(name, P):
         err = np.max(np.abs(got[seqs] - want))
     say(f"[gpu] full-size {name}: max abs err {err:.3e}")
     assert err <= TOL[w.dtype]
+
+
+def test_stream_read_probe_reads_without_writing():
+    """pa_stream_read (the read-bandwidth probe) runs over a buffer and leaves the sink
+    alone unless the folded value hits its constant (an all-zero buffer folds to 0)."""
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    say("[gpu] stream read 1 MiB")
+    pa.pa_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert sink.tolist() == [7, 7, 7, 7]
+    small = torch.zeros(48, dtype=torch.uint8, device="cuda")  # fewer words than one workgroup
+    pa.pa_stream_read(small, sink)
+    torch.cuda.synchronize()
+    assert sink.tolist() == [7, 7, 7, 7]

@@ -339,3 +339,12 @@ def test_block_ops_reject_before_launch():
                                       pa.PA_F16, None) == pa.PA_ERR_INVALID
     assert L.pa_reshape_and_cache_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 10,
                                       pa.PA_F16, None) == pa.PA_OK
+
+
+def test_stream_read_rejects_bad_arguments_before_launch():
+    L = pa._lib()
+    assert L.pa_stream_read(None, 1024, FAKE, None) == pa.PA_ERR_INVALID
+    assert L.pa_stream_read(FAKE, 1024, None, None) == pa.PA_ERR_INVALID
+    assert L.pa_stream_read(FAKE, 0, FAKE, None) == pa.PA_ERR_INVALID
+    assert L.pa_stream_read(FAKE, 1000, FAKE, None) == pa.PA_ERR_INVALID  # not a multiple of 16
+    assert L.pa_stream_read(ctypes.c_void_p(0x1008), 1024, FAKE, None) == pa.PA_ERR_INVALID  # misaligned
