@@ -48,7 +48,9 @@ constexpr int MW = 4;  // waves per workgroup
 #ifndef PA_MQ_KEYS
 #define PA_MQ_KEYS 32
 #endif
-constexpr int RF = PA_MQ_FRAGS;      // 16-row query fragments per wave
+// 16-row query fragments per wave.  Four halve the LDS reads per product but need more
+// than 256 registers (one wave per SIMD), which measured 1.4x slower than two.
+constexpr int RF = PA_MQ_FRAGS;
 constexpr int ROWS = 16 * RF * MW;   // query rows per workgroup
 static_assert(PA_MQ_KEYS % 32 == 0 && (RF == 1 || RF == 2 || RF == 4), "tile shape");
 
