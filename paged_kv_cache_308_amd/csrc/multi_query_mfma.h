@@ -12,7 +12,8 @@
 // share every operand read).  The workgroup walks the keys its rows can see ([0, last
 // row's position]) in 64-key tiles; every tile is
 // loaded from HBM once, through the block table, into double-buffered LDS (K rows with
-// a padded stride, V transposed to [d][key]) while the previous tile is being used,
+// a padded stride, V transposed to [d][key]) while the previous tile is being used
+// (with the tile after it already on its way in registers),
 // and all four waves read it there.  Per tile and wave:
 //
 //   S^T[t][r]  = sum_d K[t][d] Q[r][d]          A = K rows (16 keys x 32 d), B = Q^T
@@ -345,17 +346,25 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
         }
     };
 
+    // Two tiles in flight: while tile t is used from LDS, tile t + 1 waits in registers
+    // and tile t + 2 is being loaded.  Loads past the last tile read block 0's first row
+    // (all masked) instead of being skipped, so the compiler's waits stay exact.
     if (ntiles > 0) {
-        Stage st;
-        load_tile(st, 0);
-        store_tile(st, lds);
+        Stage sa, sb;
+        load_tile(sa, 0);
+        load_tile(sb, 1);
+        store_tile(sa, lds);
         __syncthreads();
-        for (int t = 0; t < ntiles; ++t) {
-            const bool more = t + 1 < ntiles;
-            if (more) load_tile(st, t + 1);
+        // next: the stage holding tile t + 1; spare: free, receives tile t + 2
+        auto step = [&](Stage &next, Stage &spare, int t) {
+            load_tile(spare, t + 2);
             if (t * KT < wave_end) compute_tile(lds + (t & 1) * BUF, t);
-            if (more) store_tile(st, lds + ((t + 1) & 1) * BUF);
+            if (t + 1 < ntiles) store_tile(next, lds + ((t + 1) & 1) * BUF);
             __syncthreads();
+        };
+        for (int t = 0; t < ntiles; t += 2) {
+            step(sb, sa, t);
+            if (t + 1 < ntiles) step(sa, sb, t + 1);
         }
     }
 
