@@ -10,7 +10,7 @@
 // (query token, query head of the group) pair: 128 / g tokens times the g heads that
 // share the KV head.  Each of its four waves owns 32 rows (two 16-row fragments that
 // share every operand read).  The workgroup walks the keys its rows can see ([0, last
-// row's position]) in 64-key tiles; every tile is
+// row's position]) in tiles of 32 keys (64 at d = 64, the same bytes); every tile is
 // loaded from HBM once, through the block table, into double-buffered LDS (K rows with
 // a padded stride, V transposed to [d][key]) while the previous tile is being used
 // (with the tile after it already on its way in registers),
