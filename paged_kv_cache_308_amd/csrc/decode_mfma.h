@@ -148,8 +148,7 @@ __device__ __forceinline__ void consume_chunk(const u32x4 (&k)[2][Geom<D>::NKK],
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[tt][i]);
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    cm = max_over_column(cm);
     const float mn = fmaxf(m, cm);
     const float ms = mn == -INFINITY ? 0.f : mn;
     const float alpha = fast_exp2(m - ms);
@@ -313,8 +312,7 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
         }
     }
     // normaliser of head n over the 4 lanes of its column
-    st.lsum += __shfl_xor(st.lsum, 16);
-    st.lsum += __shfl_xor(st.lsum, 32);
+    st.lsum = sum_over_column(st.lsum);
 }
 
 // Merge the waves' states through LDS (the staging area; every wave's loads of the range

@@ -167,6 +167,23 @@ __device__ inline uint32_t e4m3_encode(float y) {
     return sign | (e << 3) | ((r >> 20) & 7u);
 }
 
+// Max and sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 of a wave (the 4 lanes of a
+// matrix-core fragment column), every lane receiving the same value.  gfx950's
+// v_permlane32_swap pairs each lane with lane ^ 32 and v_permlane16_swap with lane ^ 16,
+// on the vector unit (no LDS round trip).
+__device__ inline float max_over_column(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float sum_over_column(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // 2^x on the hardware transcendental unit (exact 1 at 0, 0 at -inf).
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

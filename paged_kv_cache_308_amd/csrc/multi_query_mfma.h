@@ -26,7 +26,8 @@
 // transposed tile).  The causal mask compares each key's position with its row's; a
 // wave skips tiles past its own last row.  Softmax is fp32 online in the exp2 domain;
 // P enters the second product rounded to the storage type and the normaliser sums the
-// rounded weights.  Rows are written by the wave that owns them (no merge).
+// rounded weights (on the matrix cores, P against a ones operand).  Rows are written by
+// the wave that owns them (no merge).
 //
 // Row tiles are numbered fastest, then sequence, then KV head, and spread over the XCDs
 // in contiguous ranges, so the row tiles that read the same sequence's blocks share an
@@ -54,6 +55,23 @@ constexpr int MW = 4;  // waves per workgroup
 constexpr int RF = PA_MQ_FRAGS;
 constexpr int ROWS = 16 * RF * MW;   // query rows per workgroup
 static_assert(PA_MQ_KEYS % 32 == 0 && (RF == 1 || RF == 2 || RF == 4), "tile shape");
+
+// Two fp32 weights rounded to T (to nearest even) and packed, the first in the low half
+// (one v_cvt_pk_{f16,bf16}_f32 on gfx950).
+template <typename T>
+__device__ inline uint32_t round2(float a, float b);
+template <>
+__device__ inline uint32_t round2<F16>(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), h2));
+}
+template <>
+__device__ inline uint32_t round2<BF16>(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), b2));
+}
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
@@ -154,12 +172,21 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
     // first key position any of the wave's rows cannot see: tiles below it need no mask
     const int wave_first_pos = ctx - nq + min(wrow0, rows - 1) / G;
 
-    float m[RF], lsum[RF];  // running max (scaled, same in a column's 4 lanes), lane's share of the sum
-    f32x4 o[RF][NN];
+    // Per row: m, the reference max the weights are taken against (scaled; the same in a
+    // column's 4 lanes); o, the weighted value sums; osum, the sum of the rounded weights,
+    // formed on the matrix cores as the product of P with a ones operand (every element
+    // of a lane's fragment holds its row's sum).  The reference only moves, and o and
+    // osum are only rescaled, when a row's max exceeds it by more than 2^RESCALE_LOG2,
+    // so the weights stay in (0, 2^RESCALE_LOG2]: the result is the same up to rounding.
+    constexpr float RESCALE_LOG2 = 8.f;
+    const uint32_t one2 = std::is_same<T, F16>::value ? 0x3C003C00u : 0x3F803F80u;  // two 1.0s
+    const u32x4 ones = u32x4{one2, one2, one2, one2};
+    float m[RF];
+    f32x4 o[RF][NN], osum[RF];
 #pragma unroll
     for (int f = 0; f < RF; ++f) {
         m[f] = -INFINITY;
-        lsum[f] = 0.f;
+        osum[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NN; ++i) o[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -283,6 +310,7 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
         // j >= 4 -> key 32h + 16 + 4q + j - 4
         u32x4 pb[RF][NH];
         float alpha[RF];
+        bool grow = false;
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
             float cm = sc[f][0][0];
@@ -290,43 +318,41 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[f][tt][i]);
-            cm = fmaxf(cm, __shfl_xor(cm, 16));
-            cm = fmaxf(cm, __shfl_xor(cm, 32));
-            const float mn = fmaxf(m[f], cm * sl);
-            const float ms = mn == -INFINITY ? 0.f : mn;
-            alpha[f] = fast_exp2(m[f] - ms);
-            m[f] = mn;
-            float psum = 0.f;
+            cm = max_over_column(cm);
+            const float mt = cm * sl;  // this tile's max of the row (-inf: nothing visible)
+            const bool g = mt > m[f] + RESCALE_LOG2;
+            alpha[f] = g ? fast_exp2(m[f] - mt) : 1.f;
+            m[f] = g ? mt : m[f];
+            grow |= g;
+            const float ms = m[f] == -INFINITY ? 0.f : m[f];
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
                 uint32_t pk[4];
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
-                    for (int i = 0; i < 4; i += 2) {
-                        float b0, b1;
-                        const uint32_t h0 = Mma<T>::round(fast_exp2(fmaf(sc[f][2 * h + u][i], sl, -ms)), b0);
-                        const uint32_t h1 = Mma<T>::round(fast_exp2(fmaf(sc[f][2 * h + u][i + 1], sl, -ms)), b1);
-                        psum += b0 + b1;
-                        pk[2 * u + i / 2] = h0 | (h1 << 16);
-                    }
+                    for (int i = 0; i < 4; i += 2)
+                        pk[2 * u + i / 2] = round2<T>(fast_exp2(fmaf(sc[f][2 * h + u][i], sl, -ms)),
+                                                      fast_exp2(fmaf(sc[f][2 * h + u][i + 1], sl, -ms)));
                 pb[f][h] = u32x4{pk[0], pk[1], pk[2], pk[3]};
             }
-            lsum[f] = lsum[f] * alpha[f] + psum;
         }
         // V^T operand per 16-row d fragment and half: keys 32h + 4q..+3 and 32h + 16 + 4q..+3
         // of d = 16 nn + n (two 8-byte reads of the transposed tile), shared by the fragments
         uint8_t *vt = (uint8_t *)buf + KBYTES;
-        // rescale only when some row's running max moved (otherwise every alpha is 1)
-        bool moved = false;
+        // rescale only when some row's reference moved (otherwise every alpha is 1)
+        if (__any(grow)) {
 #pragma unroll
-        for (int f = 0; f < RF; ++f) moved |= alpha[f] != 1.f;
-        if (__any(moved)) {
-#pragma unroll
-            for (int f = 0; f < RF; ++f)
+            for (int f = 0; f < RF; ++f) {
+                osum[f] *= alpha[f];
 #pragma unroll
                 for (int nn = 0; nn < NN; ++nn) o[f][nn] *= alpha[f];
+            }
         }
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int f = 0; f < RF; ++f) osum[f] = Mma<T>::run(ones, pb[f][h], osum[f]);
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn) {
 #pragma unroll
@@ -377,9 +403,7 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
     // each wave writes its own rows; the normaliser of a row sums its column's 4 lanes
 #pragma unroll
     for (int f = 0; f < RF; ++f) {
-        float l = lsum[f];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = osum[f][0];
         if (!io_ok[f]) continue;
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const int64_t obase = (orow[f] * num_q_heads + kvh * G + gh[f]) * D;
