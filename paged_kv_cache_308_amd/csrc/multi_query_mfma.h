@@ -12,8 +12,7 @@
 // share every operand read).  The workgroup walks the keys its rows can see ([0, last
 // row's position]) in tiles of 32 keys (64 at d = 64, the same bytes); every tile is
 // loaded from HBM once, through the block table, into double-buffered LDS (K rows with
-// a padded stride, V transposed to [d][key]) while the previous tile is being used
-// (with the tile after it already on its way in registers),
+// a padded stride, V transposed to [d][key]) while the previous tile is being used,
 // and all four waves read it there.  Per tile and wave:
 //
 //   S^T[t][r]  = sum_d K[t][d] Q[r][d]          A = K rows (16 keys x 32 d), B = Q^T
@@ -50,6 +49,16 @@ constexpr int MW = 4;  // waves per workgroup
 #ifndef PA_MQ_KEYS
 #define PA_MQ_KEYS 32
 #endif
+// The loop is latency-bound (each wave's chain of LDS reads, score products, max,
+// exponentials and value products), so occupancy wins over prefetch depth: one key tile
+// in flight and registers held to 168 so that 3 waves share each SIMD (388 us against
+// 455 us with two tiles in flight at 2 waves; a few bytes of spill at d = 128).
+#ifndef PA_MQ_DEPTH
+#define PA_MQ_DEPTH 1  // key tiles in flight beyond the one in use (1 or 2)
+#endif
+#ifndef PA_MQ_WAVES_PER_EU
+#define PA_MQ_WAVES_PER_EU 3  // waves per SIMD the register allocation must allow
+#endif
 // 16-row query fragments per wave.  Four halve the LDS reads per product but need more
 // than 256 registers (one wave per SIMD), which measured 1.4x slower than two.
 constexpr int RF = PA_MQ_FRAGS;
@@ -74,7 +83,7 @@ __device__ inline uint32_t round2<BF16>(float a, float b) {
 }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(MW * 64) void multi_query_kernel(
+__global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_WAVES_PER_EU))) void multi_query_kernel(
     void *__restrict__ out, const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
     const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
@@ -372,10 +381,21 @@ __global__ __launch_bounds__(MW * 64) void multi_query_kernel(
         }
     };
 
-    // Two tiles in flight: while tile t is used from LDS, tile t + 1 waits in registers
-    // and tile t + 2 is being loaded.  Loads past the last tile read block 0's first row
-    // (all masked) instead of being skipped, so the compiler's waits stay exact.
-    if (ntiles > 0) {
+    // While tile t is used from LDS, tile t + 1 is being loaded into registers (and with
+    // PA_MQ_DEPTH 2, tile t + 2 as well).  Loads past the last tile read block 0's first
+    // row (all masked) instead of being skipped, so the compiler's waits stay exact.
+    if (PA_MQ_DEPTH == 1 && ntiles > 0) {
+        Stage st;
+        load_tile(st, 0);
+        store_tile(st, lds);
+        __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            load_tile(st, t + 1);
+            if (t * KT < wave_end) compute_tile(lds + (t & 1) * BUF, t);
+            if (t + 1 < ntiles) store_tile(st, lds + ((t + 1) & 1) * BUF);
+            __syncthreads();
+        }
+    } else if (ntiles > 0) {
         Stage sa, sb;
         load_tile(sa, 0);
         load_tile(sb, 1);
