@@ -63,6 +63,22 @@ def test_multi_query_matches_oracle(shape):
             assert torch.equal(row0, v0)
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_multi_query_rescales_when_a_row_max_grows(dt):
+    """Scores with a wide spread (scale 8 / sqrt(d)): a row's running max keeps growing
+    past the 2^8 margin of the kernel's reference max over later key tiles, so the
+    rescaling of the accumulators runs mid-sequence, not only on the first tile."""
+    lens, qlens = [1000, 700, 130], [300, 64, 130]
+    c = MQCase(np.random.default_rng(45), lens, qlens, 8, 2, 128, 16, dt)
+    c.scale = 8.0 / np.sqrt(128)
+    want = c.run_mq(oracle.default())
+    say(f"[gpu] multi_query wide scores {dt}")
+    got = run_mq(c).float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got - want)))
+    assert err <= TOL, err
+
+
 def test_multi_query_with_one_token_per_sequence_is_decode():
     """n_s = 1 is a decode step: same result as pa_decode within the bar of each."""
     lens = [40, 513, 17, 1]
