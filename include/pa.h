@@ -131,9 +131,10 @@ int pa_decode(void *out, const void *query, const void *key_cache, const void *v
  * context_lens[s] - 1 of its table (block table[(ctx-1) / B], slot (ctx-1) % B) and
  * the attention of pa_decode is computed over all ctx tokens.  The result and the
  * pools afterwards equal pa_reshape_and_cache with those slots followed by pa_decode
- * (up to the order of the fp32 sums).  The vector kernel does both in one launch (one
- * pass or partitions); PA_VARIANT_MFMA and PA_PARTITION_BALANCED return
- * PA_ERR_UNSUPPORTED.  Sequences with ctx <= 0 store nothing.  The block holding
+ * (up to the order of the fp32 sums).  One launch (plus the merge when partitioned or
+ * balanced) on either kernel; the vector kernel's balanced split (PA_PARTITION_BALANCED
+ * with the vector kernel chosen) returns PA_ERR_UNSUPPORTED.  Sequences with ctx <= 0
+ * store nothing.  The block holding
  * position ctx - 1 must not appear in another sequence's table (it is exclusive once the
  * step's copy-on-write copies have run, [cpai] §6).  Other arguments and errors as
  * pa_decode.

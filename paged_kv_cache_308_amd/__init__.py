@@ -206,7 +206,7 @@ def pa_multi_query(out, query, key_cache, value_cache, block_tables, context_len
 
 def pa_decode_append(out, query, new_key, new_value, key_cache, value_cache, block_tables,
                      context_lens, scale: float, max_context_len: int = 0, partition_size: int = 0,
-                     variant: int = PA_VARIANT_VALU, workspace=None, stream=None, k_scales=None,
+                     variant: int = PA_VARIANT_AUTO, workspace=None, stream=None, k_scales=None,
                      v_scales=None):
     """Store each sequence's newest token (new_key/new_value [S][H_kv][d], the query's type)
     at position ctx - 1 and attend, in one launch.  E4M3 pools (uint8) need k_scales and

@@ -195,13 +195,16 @@ static int decode_common(DecodeArgs &a, int max_context_len, float scale, int va
     const int kernel_choice = variant & 15;
     if (kernel_choice > PA_VARIANT_MFMA || (variant & ~(15 | PA_DECODE_SHARED_KV)))
         return fail(PA_ERR_INVALID, "variant %d", variant);
+    const bool mfma_ok = !a.kv_fp8 && mfma_supported(dtype, head_dim, block_size, group);
+    const bool on_mfma = mfma_ok && (kernel_choice == PA_VARIANT_MFMA ||
+                                     (kernel_choice == PA_VARIANT_AUTO && group >= 2));
     if (a.new_key) {
-        // the fused newest-token store lives in the vector kernel's one-pass and
-        // partitioned forms
+        // the fused newest-token store lives in every form but the vector kernel's
+        // balanced split
         if (!a.new_value || !a.key_out || !a.value_out) return fail(PA_ERR_INVALID, "NULL new token pointer");
-        if (balanced || kernel_choice == PA_VARIANT_MFMA)
-            return fail(PA_ERR_UNSUPPORTED, "the fused newest-token store runs on the vector kernel "
-                                            "(one pass or partitions)");
+        if (balanced && !on_mfma)
+            return fail(PA_ERR_UNSUPPORTED, "the fused newest-token store does not run on the vector "
+                                            "kernel's balanced split");
     }
 
     a.max_partitions = max_partitions_for(max_context_len, partition_size);
@@ -226,8 +229,6 @@ static int decode_common(DecodeArgs &a, int max_context_len, float scale, int va
         workspace_layout(num_seqs, num_q_heads, head_dim, a.max_partitions, workspace, &a.ws_max,
                          &a.ws_sum, &a.ws_acc);
     }
-    if (a.new_key) return launch_decode_valu(a);  // checked above: one pass or partitions
-    const bool mfma_ok = !a.kv_fp8 && mfma_supported(dtype, head_dim, block_size, group);
     if (kernel_choice == PA_VARIANT_MFMA) {
         if (a.kv_fp8) return fail(PA_ERR_UNSUPPORTED, "E4M3 pools run on the vector kernel");
         if (!mfma_ok)

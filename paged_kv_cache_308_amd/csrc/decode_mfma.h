@@ -227,12 +227,22 @@ struct WaveState {
 // The workgroup's MW waves over tokens [start, end) of (sequence s, KV head kvh):
 // wave w takes the CT-token chunks w, w + MW, ... of the range through a double-
 // buffered pipeline (K operands in registers, V rows in its LDS stages).
+//
+// Newest token given (new_k non-null; the range ends at the context's end): the chunks
+// stop before position end - 1, and the wave that would take the next chunk then stores
+// the given K/V row (new_k, new_v: D elements each) into the pools at that position's
+// slot and folds it into its state from registers: the score by vector dot products
+// over the 4 lanes of each head's column, the weight rounded to T as the matrix-core
+// path rounds it.  A wave whose 16-row tile holds that slot treats the row as past the
+// end (score -inf, V row zeroed in LDS), whichever value it read.
 template <typename T, int D, int G, bool NT>
 __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds, const uint8_t *query,
                                              const uint8_t *key_cache, const uint8_t *value_cache,
                                              const int32_t *table, int max_blocks_per_seq, int s, int kvh,
                                              int num_kv_heads, int log2_block, int num_blocks, int start,
-                                             int end, float scale_log2, int wave, int lane) {
+                                             int end, float scale_log2, int wave, int lane,
+                                             const uint8_t *new_k = nullptr, const uint8_t *new_v = nullptr,
+                                             uint8_t *key_out = nullptr, uint8_t *value_out = nullptr) {
     using Gm = Geom<D>;
     constexpr int ROW = Gm::ROW;
     constexpr int NKK = Gm::NKK;
@@ -251,6 +261,9 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
 #pragma unroll
     for (int i = 0; i < Gm::NN; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    const bool append = new_k != nullptr && end > start;
+    const int tnew = end - 1;  // position of the newest token when appending
+    if (append) end = tnew;
     const int ntok = end > start ? end - start : 0;
     const int nchunks = (ntok + CT - 1) / CT;
 
@@ -309,6 +322,54 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
             consume(Bf, wave + (j + 1) * MW, 1);
         } else {
             consume(A, wave + j * MW, 0);
+        }
+    }
+    if (append && wave == nchunks % MW) {
+        const int lb = tnew >> log2_block;
+        int64_t base = -1;
+        if (lb < max_blocks_per_seq) {
+            const int32_t pb = table[lb];
+            if (pb >= 0 && pb < num_blocks)
+                base = (int64_t)pb * block_bytes + head_off + (int64_t)(tnew & (block_size - 1)) * ROW;
+        }
+        if (base < 0) st.bad = true;
+        // the store: lanes 0.. carry K, lanes 32.. carry V, 16 bytes each
+        const int w16 = lane & 31;
+        if (w16 < ROW / 16 && base >= 0) {
+            const uint8_t *src = lane < 32 ? new_k : new_v;
+            uint8_t *dst = lane < 32 ? key_out : value_out;
+            *(u32x4 *)(dst + base + w16 * 16) = *(const u32x4 *)(src + w16 * 16);
+        }
+        // score of head n: lane (n, q) holds the products over d = 32 kk + 8 q .. +8
+        float part = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) part += dot16<T>(qb[kk], *(const u32x4 *)(new_k + (32 * kk + 8 * q) * 2));
+        const float sc = sum_over_column(part) * scale_log2;
+        const float mn = fmaxf(st.m, sc);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        const float alpha = fast_exp2(st.m - ms);
+        st.m = mn;
+        float pr;
+        (void)Mma<T>::round(fast_exp2(sc - ms), pr);
+        st.lsum = st.lsum * alpha + (q == 0 ? pr : 0.f);
+        // O^T fragment nn of lane (n, q): d = 16 nn + 4 q + i
+#pragma unroll
+        for (int nn = 0; nn < Gm::NN; ++nn) {
+            const uint2 vw = *(const uint2 *)(new_v + (16 * nn + 4 * q) * 2);
+            float v4[4];
+            if constexpr (std::is_same<T, F16>::value) {
+                v4[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(vw.x & 0xffffu));
+                v4[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(vw.x >> 16));
+                v4[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(vw.y & 0xffffu));
+                v4[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(vw.y >> 16));
+            } else {
+                v4[0] = __uint_as_float(vw.x << 16);
+                v4[1] = __uint_as_float(vw.x & 0xffff0000u);
+                v4[2] = __uint_as_float(vw.y << 16);
+                v4[3] = __uint_as_float(vw.y & 0xffff0000u);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.o[nn][i] = st.o[nn][i] * alpha + pr * v4[i];
         }
     }
     // normaliser of head n over the 4 lanes of its column
@@ -382,7 +443,9 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
     const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_max, float *__restrict__ ws_sum,
     float *__restrict__ ws_acc, int max_blocks_per_seq, int num_seqs, int num_kv_heads,
-    int log2_block, int num_blocks, int partition_size, int max_partitions, float scale_log2) {
+    int log2_block, int num_blocks, int partition_size, int max_partitions, float scale_log2,
+    const uint8_t *__restrict__ new_key, const uint8_t *__restrict__ new_value, uint8_t *key_out,
+    uint8_t *value_out) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -407,9 +470,14 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
 
     WaveState<D> st;
     st.bad = ctx < 0;
+    // the newest token (given in new_key / new_value) belongs to the range holding ctx - 1
+    const bool app = new_key != nullptr && ctx >= 1 && end == ctx;
+    const int64_t nrow = (int64_t)(s * num_kv_heads + kvh) * Geom<D>::ROW;
     attend_range<T, D, G, NT>(st, lds + wave * Geom<D>::WAVE_LDS, query, key_cache, value_cache,
                               block_tables + (int64_t)s * max_blocks_per_seq, max_blocks_per_seq, s, kvh,
-                              num_kv_heads, log2_block, num_blocks, start, end, scale_log2, wave, lane);
+                              num_kv_heads, log2_block, num_blocks, start, end, scale_log2, wave, lane,
+                              app ? new_key + nrow : nullptr, app ? new_value + nrow : nullptr, key_out,
+                              value_out);
     const int64_t row0 = (int64_t)s * num_q_heads + kvh * G;
     if (SPLIT)
         finish<T, D, G>(st, lds, &sm_bad, wave, lane, nullptr, 0, ws_max, ws_sum, ws_acc,
@@ -428,7 +496,8 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_balanced_kernel(
     const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int32_t *__restrict__ ws_hdr, float *__restrict__ ws_max,
     float *__restrict__ ws_sum, float *__restrict__ ws_acc, int max_blocks_per_seq, int num_seqs,
-    int num_kv_heads, int log2_block, int num_blocks, float scale_log2) {
+    int num_kv_heads, int log2_block, int num_blocks, float scale_log2, const uint8_t *__restrict__ new_key,
+    const uint8_t *__restrict__ new_value, uint8_t *key_out, uint8_t *value_out) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = num_seqs;
@@ -502,10 +571,15 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_balanced_kernel(
         const int take = min(nc - c, g_end - g);
         WaveState<D> st;
         st.bad = false;
+        const int seg_end = min(ctx, (c + take) * CT);
+        // the item's last segment holds the newest token
+        const bool app = new_key != nullptr && seg_end == ctx;
+        const int64_t nrow = (int64_t)(s * num_kv_heads + kvh) * Geom<D>::ROW;
         attend_range<T, D, G, NT>(st, lds + wave * Geom<D>::WAVE_LDS, query, key_cache, value_cache,
                                   block_tables + (int64_t)s * max_blocks_per_seq, max_blocks_per_seq, s, kvh,
-                                  num_kv_heads, log2_block, num_blocks, c * CT, min(ctx, (c + take) * CT),
-                                  scale_log2, wave, lane);
+                                  num_kv_heads, log2_block, num_blocks, c * CT, seg_end, scale_log2, wave, lane,
+                                  app ? new_key + nrow : nullptr, app ? new_value + nrow : nullptr, key_out,
+                                  value_out);
         const int64_t slot = (int64_t)w + (int64_t)kvh * S + s;
         finish<T, D, G>(st, lds, &sm_bad, wave, lane, nullptr, 0, ws_max, ws_sum, ws_acc, slot * G, 1);
         g += take;
@@ -540,7 +614,9 @@ int launch_balanced(const DecodeArgs &a) {
     hipLaunchKernelGGL(kernel, dim3(workers), dim3(MW * 64), 0, (hipStream_t)a.stream,
                        (const uint8_t *)a.query, (const uint8_t *)a.key_cache, (const uint8_t *)a.value_cache,
                        a.block_tables, a.context_lens, a.ws_hdr, a.ws_max, a.ws_sum, a.ws_acc,
-                       a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads, log2b, a.num_blocks, a.scale_log2);
+                       a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads, log2b, a.num_blocks, a.scale_log2,
+                       (const uint8_t *)a.new_key, (const uint8_t *)a.new_value, (uint8_t *)a.key_out,
+                       (uint8_t *)a.value_out);
     const int rc = check_launch("decode_mfma_balanced");
     if (rc != PA_OK) return rc;
     return launch_balanced_merge<T, D, G>(a);
@@ -558,7 +634,9 @@ int launch_t(const DecodeArgs &a) {
                            a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
                            (const uint8_t *)a.value_cache, a.block_tables, a.context_lens, a.ws_max,
                            a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads,
-                           log2b, a.num_blocks, a.partition_size, a.max_partitions, a.scale_log2);
+                           log2b, a.num_blocks, a.partition_size, a.max_partitions, a.scale_log2,
+                           (const uint8_t *)a.new_key, (const uint8_t *)a.new_value, (uint8_t *)a.key_out,
+                           (uint8_t *)a.value_out);
         const int rc = check_launch("decode_mfma (partitions)");
         if (rc != PA_OK) return rc;
         return launch_lse_merge(a);
@@ -567,7 +645,8 @@ int launch_t(const DecodeArgs &a) {
                        a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
                        (const uint8_t *)a.value_cache, a.block_tables, a.context_lens, nullptr,
                        nullptr, nullptr, a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads, log2b,
-                       a.num_blocks, 0, 1, a.scale_log2);
+                       a.num_blocks, 0, 1, a.scale_log2, (const uint8_t *)a.new_key,
+                       (const uint8_t *)a.new_value, (uint8_t *)a.key_out, (uint8_t *)a.value_out);
     return check_launch("decode_mfma");
 }
 

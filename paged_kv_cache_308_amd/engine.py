@@ -126,24 +126,22 @@ class PagedKVCache:
 
 
     def fused_step_ok(self, num_q_heads: int, partition_size: int, variant: int) -> bool:
-        """Whether the newest-token store can ride in the attention launch: the vector
-        kernel, one pass or partitions (AUTO keeps the matrix cores for grouped heads at
-        16 bits, whose launch does not store)."""
+        """Whether the newest-token store can ride in the attention launch: every kernel
+        form but the vector kernel's balanced split (the matrix-core kernels serve 16-bit
+        grouped heads under AUTO, or PA_VARIANT_MFMA)."""
         choice = variant & 15
-        if partition_size < 0 or choice == PA_VARIANT_MFMA:
-            return False
-        if choice == PA_VARIANT_AUTO and not self.fp8 and num_q_heads > self.num_kv_heads \
-                and self.dtype != torch.float32:
-            return False
-        return True
+        mfma = choice == PA_VARIANT_MFMA or (
+            choice == PA_VARIANT_AUTO and not self.fp8 and self.dtype != torch.float32
+            and num_q_heads > self.num_kv_heads)
+        return partition_size >= 0 or mfma
 
     def step(self, query, new_key, new_value, slots, block_tables, context_lens, scale: float,
              out=None, partition_size: int = 0, max_context_len: int = 0,
              variant: int = PA_VARIANT_AUTO, workspace=None, stream=None) -> torch.Tensor:
         """The decode step: the newest K/V into their slots (position ctx - 1 of each
-        table, `slots` as int32), then attention over the tables.  One launch when the
-        vector kernel serves the step (pa_decode_append), else the scatter and the
-        attention launch."""
+        table, `slots` as int32), then attention over the tables.  One launch
+        (pa_decode_append) unless the vector kernel's balanced split serves the step; then
+        the scatter and the attention launch."""
         if not self.fused_step_ok(query.shape[1], partition_size, variant):
             self.write(new_key, new_value, slots, stream)
             return self.attend(query, block_tables, context_lens, scale, out=out,
@@ -153,10 +151,9 @@ class PagedKVCache:
         if partition_size and workspace is None:
             workspace = self.workspace(query.shape[0], query.shape[1], max_context_len,
                                        partition_size)
-        v = variant if (variant & 15) != PA_VARIANT_AUTO else (variant | PA_VARIANT_VALU)
         pa_decode_append(out, query, new_key, new_value, self.key_cache, self.value_cache,
                          block_tables, context_lens, scale, max_context_len=max_context_len,
-                         partition_size=partition_size, variant=v, workspace=workspace,
+                         partition_size=partition_size, variant=variant, workspace=workspace,
                          stream=stream, k_scales=self.k_scales, v_scales=self.v_scales)
         return out
 

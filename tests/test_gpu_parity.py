@@ -135,31 +135,38 @@ def test_small_workload(name, oracle_steps):
 
 
 @pytest.mark.parametrize("name", ["mha_f16", "long_bf16", "prefix_f16", "tiny_fp32", "gqa_f16_b16",
-                                  "fp8_mha_f16", "fp8_gqa4_bf16", "fp8_d64_g8_f16"])
+                                  "gqa_bf16", "bf16_d64_b128_g16", "fp8_mha_f16", "fp8_gqa4_bf16",
+                                  "fp8_d64_g8_f16"])
 def test_fused_step_matches_scatter_then_decode(name, oracle_steps):
     """The newest-token store inside the attention launch: the pools afterwards are
     bit-identical to the separate scatter's, the output matches the oracle."""
     w = SMALL[name]
     batch, want, placed = oracle_steps(name)
-    for P in sorted({0, w.partition_size}):
-        say(f"[gpu] fused step {name} P={P}")
+    mfma = w.kv != "fp8" and w.dtype != "f32" and w.num_q_heads > w.num_kv_heads
+    runs = [(P, VALU) for P in sorted({0, w.partition_size})]
+    if mfma:  # the matrix-core kernels: one pass, partitions, balanced split
+        runs += [(P, MFMA) for P in sorted({0, w.partition_size, BAL})]
+    for P, v in runs:
+        say(f"[gpu] fused step {name} P={P} variant={v}")
         db = replay(batch)
-        got = db.step(partition_size=P, variant=VALU, fused=True)
+        got = db.step(partition_size=P, variant=v, fused=True)
         torch.cuda.synchronize()
-        assert np.max(np.abs(f64(got) - want)) <= TOL[w.dtype], (name, P)
+        assert np.max(np.abs(f64(got) - want)) <= TOL[w.dtype], (name, P, v)
         assert bits(db.cache.key_cache) == np_bits(placed.key_cache)
         assert bits(db.cache.value_cache) == np_bits(placed.value_cache)
         ref = replay(batch)
-        two = ref.step(partition_size=P, variant=VALU, fused=False)
+        two = ref.step(partition_size=P, variant=v, fused=False)
         torch.cuda.synchronize()
         assert np.max(np.abs(f64(got) - f64(two))) <= TOL[w.dtype]
 
 
-def test_fused_step_edge_lengths():
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_fused_step_edge_lengths(kernel):
     """Contexts of 1 (the newest token alone), partition starts and ends, block edges."""
     rng = np.random.default_rng(31)
-    lens = [1, 2, 16, 17, 64, 65, 128, 129, 511, 512, 513]
-    c = Case(rng, lens, 4, 4, 128, 16, "f16")
+    lens = [1, 2, 16, 17, 31, 32, 33, 64, 65, 128, 129, 511, 512, 513]
+    Hq, Hkv, v, Ps = (4, 4, VALU, (0, 64)) if kernel == "valu" else (8, 2, MFMA, (0, 64, BAL))
+    c = Case(rng, lens, Hq, Hkv, 128, 16, "f16")
     want = c.run(oracle.default())
     q, kc, vc, bt, cl = _upload_case(c)
     # the newest token of each sequence, taken from the placed pools, then poisoned there
@@ -172,18 +179,21 @@ def test_fused_step_edge_lengths():
         nv[s_] = vc[b, :, o, :]
         kc[b, :, o, :] = float("nan")
         vc[b, :, o, :] = float("nan")
-    for P in (0, 64):
+    for P in Ps:
         out = torch.empty_like(q)
         ws = None
         if P:
-            ws = torch.empty(pa.pa_decode_workspace_bytes(S, 4, 4, 128, max(lens), P), dtype=torch.uint8,
+            ws = torch.empty(pa.pa_decode_workspace_bytes(S, Hq, Hkv, 128, max(lens), P), dtype=torch.uint8,
                              device="cuda")
-        say(f"[gpu] fused edge P={P}")
+        say(f"[gpu] fused edge {kernel} P={P}")
         pa.pa_decode_append(out, q, nk, nv, kc, vc, bt, cl, c.scale, max_context_len=max(lens),
-                            partition_size=P, workspace=ws)
+                            partition_size=P, variant=v, workspace=ws)
         torch.cuda.synchronize()
         assert np.max(np.abs(f64(out) - want)) <= TOL["f16"], P
         assert bits(kc) == np_bits(c.kc) and bits(vc) == np_bits(c.vc)
+        # one token: exactly its V
+        g = Hq // Hkv
+        assert bits(out[0]) == bits(nv[0].repeat_interleave(g, dim=0))
 
 
 # ----------------------------------------------------------------- edge cases
