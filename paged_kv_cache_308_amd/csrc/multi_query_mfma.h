@@ -11,8 +11,8 @@
 // share the KV head.  Each of its four waves owns 32 rows (two 16-row fragments that
 // share every operand read).  The workgroup walks the keys its rows can see ([0, last
 // row's position]) in tiles of 32 keys (64 at d = 64, the same bytes); every tile is
-// loaded from HBM once, through the block table, into double-buffered LDS (K rows with
-// a padded stride, V transposed to [d][key]) while the previous tile is being used,
+// loaded from HBM once, through the block table, into double-buffered LDS (K and V rows
+// on padded strides) while the previous tile is being used,
 // and all four waves read it there.  Per tile and wave:
 //
 //   S^T[t][r]  = sum_d K[t][d] Q[r][d]          A = K rows (16 keys x 32 d), B = Q^T
@@ -21,8 +21,8 @@
 // on v_mfma_f32_16x16x32_{f16,bf16}.  Lane l supplies A[l%16][8(l/16)..+8] and
 // B[8(l/16)..+8][l%16] and receives D[4(l/16)..+4][l%16], so the score fragment holds,
 // per lane, one row's scores for keys 4q..4q+3 and 16+4q..16+4q+3: exactly a P^T
-// operand once the V^T operand uses the same k order (two 8-byte LDS reads of the
-// transposed tile).  The causal mask compares each key's position with its row's; a
+// operand once the V^T operand uses the same k order (two LDS transpose reads,
+// ds_read_b64_tr_b16, of the V rows).  The causal mask compares each key's position with its row's; a
 // wave skips tiles past its own last row.  Softmax is fp32 online in the exp2 domain;
 // P enters the second product rounded to the storage type and the normaliser sums the
 // rounded weights (on the matrix cores, P against a ones operand).  Rows are written by
@@ -96,18 +96,14 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
     constexpr int NT = KT / 16;            // 16-key score operands per tile
     constexpr int NH = KT / 32;            // 32-key value products per tile
     constexpr int KROW = ROW + 16;         // LDS stride of a key row (16 lanes x 16 bytes: no bank conflict)
-    constexpr int VTROW = KT * 2 + 8;      // LDS stride of a transposed value row (one d, KT keys)
-    // The transposed V tile is kept in 8-byte groups of 4 keys; group g of row d sits at
-    // slot g ^ vswz(d) (vswz < 8 only permutes groups within each 8-group block).  With this swizzle the staging stores of a wave (16 or 8 row
-    // pieces times 4 or 8 key pairs) fall in different banks, and the operand reads (16
-    // consecutive d, one group) are unchanged in pattern.
     constexpr int KBYTES = KT * KROW;
-    constexpr int BUF = KBYTES + D * VTROW;  // one tile: K rows, then V transposed
+    // V rows as they are, read transposed by ds_read_b64_tr_b16; a 32-byte pad keeps the
+    // 16 rows one operand read touches in different banks
+    constexpr int VROW = ROW + 32;
+    constexpr int BUF = KBYTES + KT * VROW;  // one tile: K rows, then V rows
     constexpr int PARTS = ROW / 16;        // 16-byte pieces of a row
     constexpr int NCH = KT * PARTS / (MW * 64);  // pieces of K (and of V) per thread per tile
     static_assert(NCH * MW * 64 == KT * PARTS && NCH % 2 == 0, "tile pieces must divide over the workgroup");
-
-    auto vswz = [](int d) -> int { return ((d >> 5) & (PARTS / 4 - 1)) * (32 / PARTS); };
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -212,10 +208,9 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
         bool ok[NCH];
         bool full;  // every piece of the tile is valid (uniform): no zeroing needed
     };
-    // Pieces 2i and 2i+1 of a thread are the same 16 bytes of two neighbouring keys, so
-    // the transposed V store writes both keys of a d at once (4 bytes).  Everything
-    // that depends only on the thread is computed once: a piece's key, its byte offset
-    // inside its 16-key group of rows, and its LDS destinations.
+    // Pieces 2i and 2i+1 of a thread are the same 16 bytes of two neighbouring keys.
+    // Everything that depends only on the thread is computed once: a piece's key, its
+    // byte offset inside its 16-key group of rows, and its LDS destinations.
     int pkey[NCH], prow[NCH], kst[NCH], vst[NCH / 2];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -224,8 +219,7 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
         pkey[i] = 2 * (c / PARTS) + (i & 1);
         prow[i] = (pkey[i] & 15) * ROW + part * 16;
         kst[i] = pkey[i] * KROW + part * 16;
-        if ((i & 1) == 0)  // d = 8 part + j (j < 8) shares the swizzle of d = 8 part
-            vst[i / 2] = 8 * part * VTROW + 8 * ((pkey[i] >> 2) ^ vswz(8 * part)) + (pkey[i] & 3) * 2;
+        if ((i & 1) == 0) vst[i / 2] = pkey[i] * VROW + part * 16;  // the pair's second key: + VROW
     }
     auto load_tile = [&](Stage &st, int t) {
         const int k0 = t * KT;
@@ -260,7 +254,7 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
             st.v[i] = *(const u32x4 *)(value_cache + off);
         }
     };
-    // K rows as they are (padded stride); V transposed: vt[d][key]
+    // K and V rows as they are (padded strides)
     auto store_tile = [&](const Stage &st, uint8_t *buf) {
 #pragma unroll
         for (int i = 0; i < NCH; i += 2) {
@@ -272,20 +266,18 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
             *(u32x4 *)(buf + kst[i]) = k0w;
             *(u32x4 *)(buf + kst[i + 1]) = k1w;
             uint8_t *vt = buf + KBYTES + vst[i / 2];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t a = v0w[e], b = v1w[e];  // scalar copies before splitting
-                // d = 8 part + 2e: (key, key + 1) low halves; d + 1: high halves
-                *(uint32_t *)(vt + (2 * e) * VTROW) = (a & 0xffffu) | (b << 16);
-                *(uint32_t *)(vt + (2 * e + 1) * VTROW) = (a >> 16) | (b & 0xffff0000u);
-            }
+            *(u32x4 *)vt = v0w;
+            *(u32x4 *)(vt + VROW) = v1w;
         }
     };
     // V^T operand reads: d = 16 nn + n, keys of group g = 8h + q (+4): the swizzle of
     // d depends on nn only, so a lane needs one base per swizzle value
-    int vrd[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) vrd[c] = n * VTROW + 8 * (q ^ (2 * c));
+    // ds_read_b64_tr_b16 (checked on gfx950): within each 16-lane group, lane j receives
+    // element j % 4 of the 8-byte reads of lanes 4k + j / 4, k = 0..3.  Lane (n, q) reads
+    // row 4q + n / 4, columns 16 nn + 4 (n % 4) .. +3, so lane (n, q) receives
+    // V[keys 4q .. 4q + 3][d = 16 nn + n]: the V^T operand's k order.
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int vrd0 = (4 * q + (n >> 2)) * VROW + 8 * (n & 3);
     auto compute_tile = [&](const uint8_t *buf, int t) {
         const int k0 = t * KT;
         // scores S^T: lane holds keys k0 + 16 tt + 4 q + i of row n of each fragment
@@ -347,7 +339,7 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
             }
         }
         // V^T operand per 16-row d fragment and half: keys 32h + 4q..+3 and 32h + 16 + 4q..+3
-        // of d = 16 nn + n (two 8-byte reads of the transposed tile), shared by the fragments
+        // of d = 16 nn + n (two transpose reads of the V rows), shared by the fragments
         uint8_t *vt = (uint8_t *)buf + KBYTES;
         // rescale only when some row's reference moved (otherwise every alpha is 1)
         if (__any(grow)) {
@@ -366,15 +358,14 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
         for (int nn = 0; nn < NN; ++nn) {
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
-                // vswz(16 nn + n) = 2 c with c = (nn / 2) & (PARTS / 4 - 1) for d = 128,
-                // or 4 c' for d = 64; both are covered by vrd (q ^ 2c over c < 4)
-                const int sw = ((16 * nn) >> 5 & (PARTS / 4 - 1)) * (32 / PARTS);  // folds when unrolled
-                const uint8_t *row = vt + (16 * nn) * VTROW + 64 * h + vrd[sw / 2];
-                const uint2 lo = *(const uint2 *)row;  // group 8h + q, at slot 8h + (q ^ sw)
-                // group 8h + 4 + q sits at slot 8h + ((q ^ sw) ^ 4): 32 bytes up, or down
-                // when the swizzle already set that bit
-                const uint2 hi = *(const uint2 *)(row + ((sw & 4) ? -32 : 32));
-                const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
+                // keys 32h + 4q .. +3, then 32h + 16 + 4q .. +3, of d = 16 nn + n
+                const uint8_t *r0 = vt + vrd0 + (32 * h) * VROW + 32 * nn;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(r0));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(r0 + 16 * VROW));
+                const uint2 lw = __builtin_bit_cast(uint2, lo), hw = __builtin_bit_cast(uint2, hi);
+                const u32x4 va = u32x4{lw.x, lw.y, hw.x, hw.y};
 #pragma unroll
                 for (int f = 0; f < RF; ++f) o[f][nn] = Mma<T>::run(va, pb[f][h], o[f][nn]);
             }
