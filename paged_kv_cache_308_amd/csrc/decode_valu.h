@@ -23,10 +23,13 @@
 //    loads are in flight while the current one is reduced);
 //  * at the end the rows of a wave, then the waves of the workgroup (through LDS),
 //    are merged with log-sum-exp weights;
-//  * workgroup ids are remapped so that each XCD runs a contiguous range of work
-//    items (partition fastest, then sequence, then KV head): the XCDs get equal
-//    shares, and consecutive sequences of one KV head share an XCD's L2 when their
-//    tables point at the same blocks (shared prefixes).
+//  * one pass: work items run longest sequence first (every workgroup sorts the
+//    batch's context lengths, a few hundred instructions), KV head fastest, so no
+//    long sequence starts in the last round; partitions: workgroup ids are remapped
+//    so that each XCD runs a contiguous range of work items (partition fastest, then
+//    sequence, then KV head).  Either way the XCDs get equal shares, and the
+//    sequences of one KV head share an XCD's L2 when their tables point at the same
+//    blocks (shared prefixes).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -301,14 +304,27 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     const int row = lane / LPT;
     const int col = lane % LPT;
 
-    // work item order: partition fastest, then sequence, then KV head, so every XCD's
-    // contiguous range holds whole sequences (balanced) and a head's sequences are
-    // neighbours (shared-prefix siblings land on one XCD)
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int part = L % max_partitions;
-    const int rest = L / max_partitions;
-    const int s = rest % num_seqs;
-    const int kvh = rest / num_seqs;
+    int part = 0, s, kvh;
+    if constexpr (SPLIT) {
+        // work item order: partition fastest, then sequence, then KV head, so every
+        // XCD's contiguous range holds whole sequences (balanced) and a head's sequences
+        // are neighbours (shared-prefix siblings land on one XCD)
+        const int L = xcd_remap(blockIdx.x, gridDim.x);
+        part = L % max_partitions;
+        const int rest = L / max_partitions;
+        s = rest % num_seqs;
+        kvh = rest / num_seqs;
+    } else {
+        // One pass: workgroups are dispatched in index order, KV head fastest, sequences
+        // longest first, so the longest items start in the first round and the last
+        // rounds hold short ones (no tail of one long sequence).  Workgroup w runs on
+        // XCD w % 8: with a multiple of 8 KV heads, one head's sequences share an XCD.
+        kvh = blockIdx.x % num_kv_heads;
+        const int rank = blockIdx.x / num_kv_heads;
+        __shared__ uint32_t sm_order[NWG * 64];
+        s = num_seqs <= NWG * 64 ? longest_first<NWG * 64>(context_lens, num_seqs, rank, sm_order) : rank;
+        s = __builtin_amdgcn_readfirstlane(s);
+    }
     const int num_q_heads = num_kv_heads * G;
 
     const int ctx = context_lens[s];

@@ -196,6 +196,55 @@ __device__ inline int xcd_remap(int w, int n) {
     return x * q + (x < r ? x : r) + k;
 }
 
+// Longest-first order of a batch: the index of the sequence whose context is the
+// rank-th longest (ties: lower index first; negative lengths count as 0), for batches
+// of at most NTH sequences (NTH = threads of the calling workgroup, a power of two).
+// Every workgroup computes the same order: a bitonic sort of (length, index) keys,
+// one key per lane; a batch that fits one wave is sorted by every wave on its own
+// with lane exchanges only, a larger one by the whole workgroup, the exchanges
+// between waves going through LDS (`sm`, NTH words).  The caller guarantees
+// num_seqs <= NTH and rank < num_seqs; uniform control flow (the barriers).
+template <int NTH>
+__device__ inline int longest_first(const int32_t *__restrict__ context_lens, int num_seqs, int rank,
+                                    uint32_t *sm) {
+    static_assert(NTH <= 1024 && (NTH & (NTH - 1)) == 0, "one key per thread, 10 index bits");
+    constexpr uint32_t LEN_MAX = (1u << 22) - 1;  // 22 length bits above 10 index bits
+    const int ns = num_seqs <= 1 ? 1 : 1 << (32 - __builtin_clz(num_seqs - 1));  // power of two >= S
+    const bool wide = ns > 64;
+    const int t = wide ? (int)threadIdx.x : (int)(threadIdx.x & 63);
+    uint32_t key = 0;  // slots past the batch sort last
+    if (t < num_seqs) {
+        const int c = context_lens[t];
+        const uint32_t len = c <= 0 ? 0u : ((uint32_t)c > LEN_MAX ? LEN_MAX : (uint32_t)c);
+        key = (len << 10) | (1023u - (uint32_t)t);
+    }
+    for (int k = 2; k <= ns; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            uint32_t other;
+            if (j >= 64) {
+                sm[t] = key;
+                __syncthreads();
+                other = sm[t ^ j];
+                __syncthreads();
+            } else {
+                other = (uint32_t)__shfl_xor((int)key, j);
+            }
+            // blocks of k alternate direction; the last (k = ns) runs descending
+            const bool keep_max = ((t & j) == 0) == ((t & k) == 0);
+            key = keep_max ? (key > other ? key : other) : (key < other ? key : other);
+        }
+    }
+    uint32_t kr;
+    if (wide) {
+        sm[t] = key;
+        __syncthreads();
+        kr = sm[rank];
+    } else {
+        kr = (uint32_t)__shfl((int)key, rank);
+    }
+    return 1023 - (int)(kr & 1023u);
+}
+
 // Round fp32 to the output type (round to nearest even) and store element i.
 template <typename T>
 __device__ inline void store_out(void *out, int64_t i, float v);

@@ -308,6 +308,36 @@ def test_bad_table_entry_gives_nan_for_that_sequence_only(P, kernel):
         assert bits(got[0]) == bits(clean[0]) and bits(got[2]) == bits(clean[2])
 
 
+@pytest.mark.parametrize("S", [1, 2, 63, 64, 65, 300, 512, 513, 700])
+def test_one_pass_batch_sizes_and_longest_first_order(S):
+    """The one-pass vector kernel runs sequences longest first (a sort of the lengths
+    inside every workgroup: one wave up to 64 sequences, the whole workgroup up to 512,
+    index order beyond).  Outputs must not depend on it: every row against the oracle,
+    many equal lengths (ties), and a negative length (NaN for that sequence only)."""
+    rng = np.random.default_rng(100 + S)
+    lens = rng.integers(0, 49, S)
+    lens[rng.integers(0, S)] = 48
+    for dt, v in (("f16", VALU), ("f32", VALU)):
+        c = Case(rng, lens, 2, 2, 64, 16, dt)
+        want = c.run(oracle.default())
+        say(f"[gpu] one pass S={S} {dt}")
+        got = _run_case(c, 0, v)
+        err = np.max(np.abs(f64(got) - want))
+        assert err <= TOL[dt], (S, dt, err)
+        assert torch.all(got[torch.from_numpy(lens == 0).cuda()] == 0)
+        if S >= 2:
+            bad = int(rng.integers(0, S))
+            q, kc, vc, bt, cl = _upload_case(c)
+            cl[bad] = -1
+            out = torch.empty_like(q)
+            pa.pa_decode(out, q, kc, vc, bt, cl, c.scale, max_context_len=int(c.ctx.max()),
+                         partition_size=0, variant=v)
+            torch.cuda.synchronize()
+            assert torch.isnan(out[bad]).all()
+            keep = torch.arange(S, device="cuda") != bad
+            assert bits(out[keep]) == bits(got[keep])
+
+
 def test_context_longer_than_max_context_len_gives_nan():
     rng = np.random.default_rng(13)
     c = Case(rng, [100, 300], 4, 4, 128, 16, "bf16")
