@@ -501,6 +501,23 @@ def test_fp8_bad_table_entry_gives_nan_for_that_sequence_only(P):
     assert bits(got[0]) == bits(clean[0]) and bits(got[2]) == bits(clean[2])
 
 
+@pytest.mark.parametrize("S", [1, 64, 65, 256, 257, 300])
+def test_fp8_one_pass_batch_sizes_and_longest_first_order(S):
+    """The E4M3 one-pass kernel (4-wave workgroups) sorts up to 256 sequences longest
+    first and keeps index order beyond; outputs against the oracle either way, ties
+    included."""
+    rng = np.random.default_rng(200 + S)
+    lens = rng.integers(0, 40, S)
+    lens[rng.integers(0, S)] = 40
+    c = Fp8Case(rng, lens, 2, 2, 128, 16, "f16")
+    want = c.run(oracle.default())
+    say(f"[gpu] E4M3 one pass S={S}")
+    got = _run_fp8_case(c, 0)
+    err = np.max(np.abs(f64(got) - want))
+    assert err <= TOL["f16"], (S, err)
+    assert torch.all(got[torch.from_numpy(lens == 0).cuda()] == 0)
+
+
 def _fp8_special_values(rng, n):
     """Every E4M3 value and every midpoint between neighbours (ties), both signs, the
     saturation edge, zeros, infinities, NaN, then random numbers over many magnitudes."""
