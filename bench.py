@@ -91,7 +91,7 @@ def parse():
                          "launch can do it")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-stream", action="store_true",
-                    help="skip the read-bandwidth probe (pa_stream_read over 4 GiB)")
+                    help="skip the read-bandwidth probes (pa_stream_read over 4 GiB, pa_gather_read over the step's tiles)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--swap", type=int, default=0, metavar="N",
                     help="instead of decode: move N sequences' blocks to pinned host memory and "
@@ -292,6 +292,46 @@ def stream_read_gbs(nbytes: int = 4 << 30, reps: int = 5) -> float:
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def gather_read_gbs(w, reps, n_runs: int = 5) -> dict:
+    """Achievable read rate for the step's own access pattern: pa_gather_read over the
+    (physical block, KV head) tiles of both pools that each replica's tables reach (a
+    block shared by several sequences once; tiles above 4 KiB as 4 KiB pieces), the
+    replicas in turn as the decode steps take them, timed with events on the launch
+    stream."""
+    import torch
+    from paged_kv_cache_308_amd import pa_gather_read
+    tile = w.block_size * w.head_dim * w.kv_elem_bytes
+    piece = min(tile, 4096)
+    lists, nbytes = [], []
+    for db, *_ in reps:
+        ctx = db.host_context_lens.astype(np.int64)
+        used = [db.host_tables[s, :(int(c) + w.block_size - 1) // w.block_size] for s, c in enumerate(ctx)]
+        ids = np.concatenate(used) if used else np.zeros(0, np.int32)
+        _, first = np.unique(ids, return_index=True)
+        blocks = ids[np.sort(first)].astype(np.int64)
+        kc, vc = db.cache.key_cache, db.cache.value_cache
+        off = ((blocks[:, None] * w.num_kv_heads + np.arange(w.num_kv_heads)[None, :]) * tile).reshape(-1)
+        off = (off[:, None] + np.arange(0, tile, piece)[None, :]).reshape(-1)
+        addrs = np.stack([kc.data_ptr() + off, vc.data_ptr() + off], axis=1).reshape(-1)
+        assert off.max() + piece <= kc.numel() * kc.element_size()
+        lists.append(torch.from_numpy(addrs.astype(np.int64)).cuda())
+        nbytes.append(len(addrs) * piece)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    for i in range(2 * len(lists)):
+        pa_gather_read(lists[i % len(lists)], piece, sink, st)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(st)
+    for i in range(n_runs * len(lists)):
+        pa_gather_read(lists[i % len(lists)], piece, sink, st)
+    b.record(st)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / (n_runs * len(lists))
+    return {"gbs": float(np.mean(nbytes)) / (ms * 1e-3) / 1e9, "bytes": int(np.mean(nbytes)), "piece": piece,
+            "us": ms * 1e3}
+
+
 def swap_bench(args, w, batch) -> dict:
     """Block swap (preemption data mover): N sequences out to pinned host memory and back."""
     import torch
@@ -488,6 +528,7 @@ def main():
     ms_step = total_ms / args.steps
     dec_avg = float(np.mean(dec_ms))
     log(args, f"[bench] {ms_step * 1e3:.1f} us/step, decode {dec_avg * 1e3:.1f} us")
+    gather = None if args.no_stream else gather_read_gbs(w, reps)
 
     ident = None
     if not args.no_identity:
@@ -539,6 +580,11 @@ def main():
         "decode_us_p10_median_p90": [round(float(np.percentile(dec_ms, x)) * 1e3, 2) for x in (10, 50, 90)],
         "stream_read_gbs": None if stream is None else round(stream, 1),
         "pct_of_stream_read": None if stream is None else round(100 * gbs / stream, 2),
+        "gather_read_gbs": None if gather is None else round(gather["gbs"], 1),
+        "gather_read": None if gather is None else {
+            "bytes": gather["bytes"], "piece_bytes": gather["piece"], "us": round(gather["us"], 2),
+            "what": "pa_gather_read over the (block, KV head) tiles of both pools the step's tables reach"},
+        "pct_of_gather_read": None if gather is None else round(100 * achieved / gather["gbs"], 2),
         "mfma_util": round(4.0 * float(ctx.sum()) * w.num_q_heads * w.head_dim / (dec_avg * 1e-3) / 1e12 /
                            MFMA_PEAK_TFLOPS[w.dtype], 4) if mfma else None,
         "fused_store": args.fused,

@@ -265,6 +265,22 @@ int pa_decode_fp8_append(void *out, const void *query, const void *new_key, cons
  */
 int pa_stream_read(const void *buf, size_t bytes, void *sink, void *stream);
 
+/*
+ * Measurement helper, not part of the attention path: the achievable read rate for
+ * the decode kernels' own access pattern.  Reads num_tiles tiles of tile_bytes bytes
+ * once, tile i at device address tile_addrs[i] (a device array of num_tiles addresses,
+ * each 16-byte aligned), with 16-byte non-temporal loads, one wave per tile and two
+ * tiles in flight per wave, spread over the whole device; the folded value is stored to
+ * *sink (device, 4 bytes) only when it equals a fixed constant.  A decode step's tiles
+ * are the (physical block, KV head) tiles of both pools its tables reach
+ * ("PagedAttention" concept report (compassingai.com) §5: a block's tokens sit at
+ * consecutive offsets).  tile_bytes is 1024, 2048, 4096 or 8192 (a larger tile is
+ * passed as consecutive pieces); num_tiles >= 0 (0: nothing is launched).  The
+ * addresses are the caller's: each must point at tile_bytes readable device bytes,
+ * which the library cannot check.  PA_ERR_INVALID for the checkable errors.
+ */
+int pa_gather_read(const uint64_t *tile_addrs, int num_tiles, int tile_bytes, void *sink, void *stream);
+
 /* Host-side checks ([cpai] §13).  PA_ERR_BOUNDS names the first offending entry in
  * pa_last_error. */
 int pa_check_tables(const int32_t *block_tables, const int32_t *context_lens, int num_seqs,

@@ -29,7 +29,7 @@ EXPORTS = (
     "pa_status_str", "pa_last_error", "pa_abi_version", "pa_decode_workspace_bytes", "pa_decode",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_check_tables",
     "pa_reshape_and_cache_fp8", "pa_decode_fp8", "pa_multi_query", "pa_decode_append",
-    "pa_decode_fp8_append", "pa_stream_read",
+    "pa_decode_fp8_append", "pa_stream_read", "pa_gather_read",
     "pa_check_copy_pairs", "pa_alloc_adopt",
     "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_set_free_order", "pa_alloc_new_seq",
     "pa_alloc_append_slot", "pa_alloc_append_slots", "pa_alloc_fork", "pa_alloc_free_seq",
@@ -84,6 +84,7 @@ def _lib():
         "pa_copy_blocks": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
         "pa_swap_blocks": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]),
         "pa_stream_read": (i32, [vp, sz, vp, vp]),
+        "pa_gather_read": (i32, [vp, i32, i32, vp, vp]),
         "pa_alloc_adopt": (i32, [vp, i32, i64p, i32p, i32]),
         "pa_check_tables": (i32, [i32p, i32p, i32, i32, i32, i32]),
         "pa_check_copy_pairs": (i32, [i32p, i32p, i32, i32]),
@@ -374,6 +375,18 @@ def pa_stream_read(buf, sink, stream=None):
         raise ValueError("contiguous buffer and a 4-byte sink required")
     rc = _lib().pa_stream_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink"), _stream(stream))
     _check(rc, "pa_stream_read")
+
+
+def pa_gather_read(tile_addrs, tile_bytes: int, sink, stream=None):
+    """Read tile_bytes bytes at each device address in the int64 device tensor
+    `tile_addrs` once (read-rate probe for a paged access pattern); `sink` is a device
+    tensor of at least 4 bytes.  Every address must point at readable device memory."""
+    torch = _torch()
+    if tile_addrs.dim() != 1 or sink.numel() * sink.element_size() < 4:
+        raise ValueError("1-D address tensor and a 4-byte sink required")
+    rc = _lib().pa_gather_read(_dev(tile_addrs, "tile_addrs", torch.int64), tile_addrs.numel(), int(tile_bytes),
+                               _dev(sink, "sink"), _stream(stream))
+    _check(rc, "pa_gather_read")
 
 
 # ------------------------------------------------------------------ host checks

@@ -426,6 +426,16 @@ int pa_stream_read(const void *buf, size_t bytes, void *sink, void *stream) {
     return launch_stream_read(buf, bytes, sink, stream);
 }
 
+int pa_gather_read(const uint64_t *tile_addrs, int num_tiles, int tile_bytes, void *sink, void *stream) {
+    clear_error();
+    if (num_tiles < 0) return fail(PA_ERR_INVALID, "num_tiles %d", num_tiles);
+    if (tile_bytes != 1024 && tile_bytes != 2048 && tile_bytes != 4096 && tile_bytes != 8192)
+        return fail(PA_ERR_INVALID, "tile of %d bytes (1024, 2048, 4096 or 8192)", tile_bytes);
+    if (num_tiles == 0) return PA_OK;
+    if (!tile_addrs || !sink) return fail(PA_ERR_INVALID, "NULL device pointer");
+    return launch_gather_read(tile_addrs, num_tiles, tile_bytes, sink, stream);
+}
+
 int pa_swap_blocks(const void *src_key_cache, const void *src_value_cache, void *dst_key_cache,
                    void *dst_value_cache, const int32_t *src, const int32_t *dst, int num_pairs,
                    int num_kv_heads, int head_dim, int block_size, int src_num_blocks,

@@ -245,4 +245,50 @@ int launch_stream_read(const void *buf, size_t bytes, void *sink, void *stream) 
     return check_launch("stream_read");
 }
 
+// Tile-gather read probe: wave w of the grid reads tiles w, w + W, w + 2W, ... (W waves
+// in all), two tiles in flight (tile t and t + W loaded before either is folded); each
+// tile is TB / 1024 wave loads of 1 KiB, 16 bytes per lane.
+template <int TB>
+__global__ __launch_bounds__(256) void gather_read_kernel(const uint64_t *__restrict__ tile_addrs, int num_tiles,
+                                                          uint32_t *__restrict__ sink) {
+    constexpr int LOADS = TB / 1024;
+    const int lane = threadIdx.x & 63;
+    const int nw = gridDim.x * 4;
+    uint32_t x = 0;
+    for (int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6); t < num_tiles; t += 2 * nw) {
+        const uint8_t *a = (const uint8_t *)tile_addrs[t];
+        const int t1 = t + nw;
+        const uint8_t *b = t1 < num_tiles ? (const uint8_t *)tile_addrs[t1] : a;
+        u32x4 v[2 * LOADS];
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            v[i] = __builtin_nontemporal_load((const u32x4 *)(a + i * 1024 + lane * 16));
+            v[LOADS + i] = __builtin_nontemporal_load((const u32x4 *)(b + i * 1024 + lane * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * LOADS; ++i) x ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
+    }
+    if (x == 0x9e3779b9u) *sink = x;
+}
+
+int launch_gather_read(const uint64_t *tile_addrs, int num_tiles, int tile_bytes, void *sink, void *stream) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return fail(PA_ERR_HIP, "device properties unavailable");
+    int64_t grid = (int64_t)cus * 8;
+    const int64_t need = ((int64_t)num_tiles + 3) / 4;
+    if (grid > need) grid = need;
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t *sk = (uint32_t *)sink;
+    switch (tile_bytes) {
+        case 1024: hipLaunchKernelGGL(gather_read_kernel<1024>, dim3((unsigned)grid), dim3(256), 0, st, tile_addrs, num_tiles, sk); break;
+        case 2048: hipLaunchKernelGGL(gather_read_kernel<2048>, dim3((unsigned)grid), dim3(256), 0, st, tile_addrs, num_tiles, sk); break;
+        case 4096: hipLaunchKernelGGL(gather_read_kernel<4096>, dim3((unsigned)grid), dim3(256), 0, st, tile_addrs, num_tiles, sk); break;
+        case 8192: hipLaunchKernelGGL(gather_read_kernel<8192>, dim3((unsigned)grid), dim3(256), 0, st, tile_addrs, num_tiles, sk); break;
+        default: return fail(PA_ERR_INVALID, "tile of %d bytes", tile_bytes);
+    }
+    return check_launch("gather_read");
+}
+
 }  // namespace pa

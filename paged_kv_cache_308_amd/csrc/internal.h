@@ -82,6 +82,7 @@ int launch_reshape_and_cache_fp8(const void *key, const void *value, void *key_c
                                  int head_dim, int block_size, int num_blocks, int src_dtype,
                                  void *stream);
 int launch_stream_read(const void *buf, size_t bytes, void *sink, void *stream);
+int launch_gather_read(const uint64_t *tile_addrs, int num_tiles, int tile_bytes, void *sink, void *stream);
 int launch_move_blocks(const void *src_key, const void *src_value, void *dst_key, void *dst_value,
                        const int32_t *src, const int32_t *dst, int num_pairs, int num_kv_heads,
                        int head_dim, int block_size, int src_blocks, int dst_blocks, int elem_bytes,

@@ -717,6 +717,22 @@ def test_full_size_sampled(name, P):
     assert err <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("tile", [1024, 2048, 4096, 8192])
+def test_gather_read_probe_reads_without_writing(tile):
+    """pa_gather_read reads the listed tiles (addresses inside one zero buffer, in random
+    order, an odd count) and leaves the sink alone (all-zero data folds to 0)."""
+    ntiles = 37
+    buf = torch.zeros(ntiles * tile, dtype=torch.uint8, device="cuda")
+    sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    order = np.random.default_rng(tile).permutation(ntiles).astype(np.int64)
+    addrs = torch.from_numpy(buf.data_ptr() + order * tile).cuda()
+    say(f"[gpu] gather read {ntiles} tiles of {tile} bytes")
+    pa.pa_gather_read(addrs, tile, sink)
+    pa.pa_gather_read(addrs[:1], tile, sink)
+    torch.cuda.synchronize()
+    assert sink.tolist() == [7, 7, 7, 7]
+
+
 def test_stream_read_probe_reads_without_writing():
     """pa_stream_read (the read-bandwidth probe) runs over a buffer and leaves the sink
     alone unless the folded value hits its constant (an all-zero buffer folds to 0)."""

@@ -348,3 +348,13 @@ def test_stream_read_rejects_bad_arguments_before_launch():
     assert L.pa_stream_read(FAKE, 0, FAKE, None) == pa.PA_ERR_INVALID
     assert L.pa_stream_read(FAKE, 1000, FAKE, None) == pa.PA_ERR_INVALID  # not a multiple of 16
     assert L.pa_stream_read(ctypes.c_void_p(0x1008), 1024, FAKE, None) == pa.PA_ERR_INVALID  # misaligned
+
+
+def test_gather_read_rejects_bad_arguments_before_launch():
+    L = pa._lib()
+    assert L.pa_gather_read(FAKE, 4, 3000, FAKE, None) == pa.PA_ERR_INVALID  # tile size
+    assert L.pa_gather_read(FAKE, 4, 16384, FAKE, None) == pa.PA_ERR_INVALID
+    assert L.pa_gather_read(FAKE, -1, 4096, FAKE, None) == pa.PA_ERR_INVALID
+    assert L.pa_gather_read(None, 4, 4096, FAKE, None) == pa.PA_ERR_INVALID
+    assert L.pa_gather_read(FAKE, 4, 4096, None, None) == pa.PA_ERR_INVALID
+    assert L.pa_gather_read(None, 0, 4096, None, None) == pa.PA_OK  # nothing to read, nothing launched
