@@ -256,6 +256,47 @@ int pa_decode_fp8_append(void *out, const void *query, const void *new_key, cons
                          int variant, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Decode attention for batches whose sequences share leading blocks ([cpai] §6 and
+ * [wmrh] "paged attention": forked samples of one prompt hold the prompt's physical
+ * blocks with a reference count, so their tables start with the same block ids).  The
+ * result is that of pa_decode_append (new_key, new_value given: each sequence's newest
+ * K/V stored at position ctx - 1, then attended) or of pa_decode (both NULL) with the
+ * same partition_size, up to rounding order; the shared blocks are read once per group
+ * instead of once per sequence.
+ *
+ * Groups are runs of consecutive sequences: group j holds sequences group_start[j] ..
+ * group_start[j + 1] - 1 (device int32 [num_groups + 1], ascending, group_start[0] = 0,
+ * group_start[num_groups] = num_seqs), at most max_group_size (1..16) of them, whose first
+ * group_parts[j] partitions (device int32 [num_groups]; partitions of partition_size
+ * tokens) are reached through the same table entries.  Those partitions run once per
+ * (group, KV head) on the matrix cores, every member's query a row of the product; the
+ * rest of each context runs on the partitioned vector kernel, which also stores the
+ * newest token; the partition merge combines both.
+ *
+ * A sequence is served by its group only when the group is well formed (at most
+ * max_group_size members, 1 <= group_parts[j] <= max_group_parts), its shared
+ * partitions end before its newest token (group_parts[j] * partition_size <= ctx - 1)
+ * and its table entries for them equal the group's first sequence's and lie in the pool
+ * (a device-side plan kernel checks this); any other sequence is attended in full by the
+ * vector kernel, so a wrong group description costs speed, not results.
+ *
+ * Supported: one query head per KV head (num_q_heads == num_kv_heads), f16 or bf16,
+ * head_dim 64 or 128, block_size 16..128 dividing partition_size (> 0), max_group_parts
+ * * partition_size <= max_context_len (0: no shared-prefix pass).  variant: PA_VARIANT_AUTO
+ * or PA_VARIANT_VALU, optionally | PA_DECODE_SHARED_KV.  workspace: at least
+ * pa_decode_grouped_workspace_bytes(...) bytes.  Other errors as pa_decode.
+ */
+size_t pa_decode_grouped_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                         int max_context_len, int partition_size);
+int pa_decode_grouped(void *out, const void *query, const void *new_key, const void *new_value,
+                      void *key_cache, void *value_cache, const int32_t *block_tables, int max_blocks_per_seq,
+                      const int32_t *context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int max_context_len, float scale, int dtype,
+                      int partition_size, const int32_t *group_start, const int32_t *group_parts,
+                      int num_groups, int max_group_size, int max_group_parts, int variant, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
  * Measurement helper, not part of the attention path: reads `bytes` bytes of device
  * memory at buf once (16-byte non-temporal loads spread over the whole device) and
  * folds them into a value that is stored to *sink (device, 4 bytes) only when it

@@ -29,7 +29,8 @@ EXPORTS = (
     "pa_status_str", "pa_last_error", "pa_abi_version", "pa_decode_workspace_bytes", "pa_decode",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_check_tables",
     "pa_reshape_and_cache_fp8", "pa_decode_fp8", "pa_multi_query", "pa_decode_append",
-    "pa_decode_fp8_append", "pa_stream_read", "pa_gather_read",
+    "pa_decode_fp8_append", "pa_stream_read", "pa_gather_read", "pa_decode_grouped",
+    "pa_decode_grouped_workspace_bytes",
     "pa_check_copy_pairs", "pa_alloc_adopt",
     "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_set_free_order", "pa_alloc_new_seq",
     "pa_alloc_append_slot", "pa_alloc_append_slots", "pa_alloc_fork", "pa_alloc_free_seq",
@@ -85,6 +86,9 @@ def _lib():
         "pa_swap_blocks": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]),
         "pa_stream_read": (i32, [vp, sz, vp, vp]),
         "pa_gather_read": (i32, [vp, i32, i32, vp, vp]),
+        "pa_decode_grouped_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
+        "pa_decode_grouped": (i32, [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    f32, i32, i32, vp, vp, i32, i32, i32, i32, vp, sz, vp]),
         "pa_alloc_adopt": (i32, [vp, i32, i64p, i32p, i32]),
         "pa_check_tables": (i32, [i32p, i32p, i32, i32, i32, i32]),
         "pa_check_copy_pairs": (i32, [i32p, i32p, i32, i32]),
@@ -202,6 +206,53 @@ def pa_multi_query(out, query, key_cache, value_cache, block_tables, context_len
         _dev(query_start, "query_start", torch.int32), S, T, int(max_query_len), Hq, Hkv, d, B, nb,
         float(scale), dtype_code(query), _stream(stream))
     _check(rc, "pa_multi_query")
+    return out
+
+
+def pa_decode_grouped_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                      max_context_len: int, partition_size: int) -> int:
+    return _lib().pa_decode_grouped_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                    max_context_len, partition_size)
+
+
+def pa_decode_grouped(out, query, key_cache, value_cache, block_tables, context_lens, scale: float,
+                      group_start, group_parts, max_group_size: int, max_group_parts: int,
+                      max_context_len: int, partition_size: int, new_key=None, new_value=None,
+                      variant: int = PA_VARIANT_AUTO, workspace=None, stream=None):
+    """Decode over shared-prefix groups of consecutive sequences (group_start int32
+    [G + 1], group_parts int32 [G], both on the device); with new_key / new_value
+    ([S][H_kv][d]) the newest tokens are stored and attended in the same call."""
+    torch = _torch()
+    S, Hq, d = query.shape
+    nb, Hkv, B, d2 = key_cache.shape
+    if d2 != d or value_cache.shape != key_cache.shape or out.shape != query.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables / context_lens shape")
+    if group_start.dim() != 1 or group_parts.shape != (group_start.numel() - 1,):
+        raise ValueError("group_start [G + 1] and group_parts [G]")
+    for t in (query, key_cache, value_cache, out):
+        if t.dtype != query.dtype:
+            raise ValueError("query, pools and out must share one dtype")
+    if (new_key is None) != (new_value is None):
+        raise ValueError("new_key and new_value: both or neither")
+    if new_key is not None and (new_key.shape != (S, Hkv, d) or new_value.shape != new_key.shape
+                                or new_key.dtype != query.dtype or new_value.dtype != query.dtype):
+        raise ValueError("new_key / new_value must be [S][H_kv][d] of the query's dtype")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    nk = None if new_key is None else _dev(new_key, "new_key")
+    nv = None if new_value is None else _dev(new_value, "new_value")
+    rc = _lib().pa_decode_grouped(
+        _dev(out, "out"), _dev(query, "query"), nk, nv, _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, d, B, nb, int(max_context_len),
+        float(scale), dtype_code(query), int(partition_size), _dev(group_start, "group_start", torch.int32),
+        _dev(group_parts, "group_parts", torch.int32), group_parts.numel(), int(max_group_size),
+        int(max_group_parts), int(variant), ws_ptr, ws_bytes, _stream(stream))
+    _check(rc, "pa_decode_grouped")
     return out
 
 

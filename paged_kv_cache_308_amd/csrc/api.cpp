@@ -74,6 +74,12 @@ int launch_decode_mfma(const DecodeArgs &a) {
     return fail(PA_ERR_UNSUPPORTED, "MFMA dtype %d", a.dtype);
 }
 
+int launch_decode_mfma_grouped(const DecodeArgs &a) {
+    if (a.dtype == PA_F16) return launch_decode_mfma_grouped_f16(a);
+    if (a.dtype == PA_BF16) return launch_decode_mfma_grouped_bf16(a);
+    return fail(PA_ERR_UNSUPPORTED, "MFMA dtype %d", a.dtype);
+}
+
 size_t workspace_layout(int S, int Hq, int d, int P, void *ws, float **m, float **l, float **acc) {
     const size_t n = (size_t)S * Hq * P;
     const size_t bm = align256(n * sizeof(float));
@@ -195,6 +201,26 @@ static int decode_common(DecodeArgs &a, int max_context_len, float scale, int va
     const int kernel_choice = variant & 15;
     if (kernel_choice > PA_VARIANT_MFMA || (variant & ~(15 | PA_DECODE_SHARED_KV)))
         return fail(PA_ERR_INVALID, "variant %d", variant);
+    const bool grouped = a.group_start != nullptr;
+    if (grouped) {
+        if (partition_size <= 0)
+            return fail(PA_ERR_INVALID, "shared-prefix groups need partitions (partition_size %d)", partition_size);
+        if (group != 1 || a.kv_fp8 || (dtype != PA_F16 && dtype != PA_BF16))
+            return fail(PA_ERR_UNSUPPORTED, "shared-prefix groups take f16/bf16 pools with one query head per "
+                                            "KV head (group %d, dtype %d)", group, dtype);
+        if (kernel_choice == PA_VARIANT_MFMA)
+            return fail(PA_ERR_UNSUPPORTED, "shared-prefix groups run their private tokens on the vector kernel");
+        if (!a.group_parts) return fail(PA_ERR_INVALID, "NULL group_parts");
+        if (a.num_groups < 1) return fail(PA_ERR_INVALID, "num_groups %d", a.num_groups);
+        if (a.group_rows < 1 || a.group_rows > 16)
+            return fail(PA_ERR_INVALID, "max_group_size %d (1..16)", a.group_rows);
+        if (a.max_group_parts < 0 || (int64_t)a.max_group_parts * partition_size > max_context_len)
+            return fail(PA_ERR_INVALID, "max_group_parts %d with partitions of %d and max_context_len %d",
+                        a.max_group_parts, partition_size, max_context_len);
+        if (a.max_group_parts > 0 && (int64_t)a.num_groups * num_kv_heads * a.max_group_parts > INT32_MAX)
+            return fail(PA_ERR_UNSUPPORTED, "too many group partitions");
+        a.group_rows = a.group_rows <= 2 ? 2 : a.group_rows <= 4 ? 4 : a.group_rows <= 8 ? 8 : 16;
+    }
     const bool mfma_ok = !a.kv_fp8 && mfma_supported(dtype, head_dim, block_size, group);
     const bool on_mfma = mfma_ok && (kernel_choice == PA_VARIANT_MFMA ||
                                      (kernel_choice == PA_VARIANT_AUTO && group >= 2));
@@ -222,12 +248,26 @@ static int decode_common(DecodeArgs &a, int max_context_len, float scale, int va
         workspace_layout_balanced(num_seqs, num_q_heads, num_kv_heads, head_dim, w, workspace, &a.ws_hdr,
                                   &a.ws_max, &a.ws_sum, &a.ws_acc);
     } else if (partition_size > 0) {
-        const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, a.max_partitions,
+        const size_t base = workspace_layout(num_seqs, num_q_heads, head_dim, a.max_partitions,
                                              nullptr, nullptr, nullptr, nullptr);
-        if (!workspace || workspace_bytes < need)
-            return fail(PA_ERR_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+        const size_t plan = grouped ? 2 * align256((size_t)num_seqs * sizeof(int32_t)) : 0;
+        if (!workspace || workspace_bytes < base + plan)
+            return fail(PA_ERR_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, base + plan);
         workspace_layout(num_seqs, num_q_heads, head_dim, a.max_partitions, workspace, &a.ws_max,
                          &a.ws_sum, &a.ws_acc);
+        if (grouped) {
+            a.seq_group = (int32_t *)((char *)workspace + base);
+            a.seq_parts = (int32_t *)((char *)workspace + base + align256((size_t)num_seqs * sizeof(int32_t)));
+        }
+    }
+    if (grouped) {
+        if (a.max_group_parts > 0) {
+            int rc = launch_group_plan(a);
+            if (rc == PA_OK) rc = launch_decode_mfma_grouped(a);
+            if (rc != PA_OK) return rc;
+            a.skip_parts = a.seq_parts;
+        }
+        return launch_decode_valu(a);
     }
     if (kernel_choice == PA_VARIANT_MFMA) {
         if (a.kv_fp8) return fail(PA_ERR_UNSUPPORTED, "E4M3 pools run on the vector kernel");
@@ -292,6 +332,41 @@ int pa_decode_append(void *out, const void *query, const void *new_key, const vo
     a.new_value = new_value;
     a.key_out = key_cache;
     a.value_out = value_cache;
+    return decode_common(a, max_context_len, scale, variant, workspace, workspace_bytes);
+}
+
+size_t pa_decode_grouped_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                         int max_context_len, int partition_size) {
+    const size_t base = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                  max_context_len, partition_size);
+    if (base == 0 || partition_size <= 0) return 0;
+    return base + 2 * align256((size_t)num_seqs * sizeof(int32_t));
+}
+
+int pa_decode_grouped(void *out, const void *query, const void *new_key, const void *new_value,
+                      void *key_cache, void *value_cache, const int32_t *block_tables, int max_blocks_per_seq,
+                      const int32_t *context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int max_context_len, float scale, int dtype,
+                      int partition_size, const int32_t *group_start, const int32_t *group_parts,
+                      int num_groups, int max_group_size, int max_group_parts, int variant, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    clear_error();
+    if (num_seqs > 0 && !group_start) return fail(PA_ERR_INVALID, "NULL group_start");
+    if (num_seqs > 0 && (!new_key) != (!new_value)) return fail(PA_ERR_INVALID, "new_key and new_value: both or neither");
+    DecodeArgs a = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                               context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               num_blocks, dtype, partition_size, stream);
+    if (new_key) {
+        a.new_key = new_key;
+        a.new_value = new_value;
+        a.key_out = key_cache;
+        a.value_out = value_cache;
+    }
+    a.group_start = group_start;
+    a.group_parts = group_parts;
+    a.num_groups = num_groups;
+    a.group_rows = max_group_size;
+    a.max_group_parts = max_group_parts;
     return decode_common(a, max_context_len, scale, variant, workspace, workspace_bytes);
 }
 

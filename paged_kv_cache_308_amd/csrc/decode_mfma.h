@@ -215,6 +215,20 @@ __device__ __forceinline__ void load_q(u32x4 (&qb)[Geom<D>::NKK], const uint8_t 
     }
 }
 
+// Q^T operand with one query row per member of a group of consecutive sequences (one
+// query head per KV head): row n, when bit n of `rows` is set, is the query of head kvh
+// of sequence s + n; other rows are zero
+template <int D>
+__device__ __forceinline__ void load_q_rows(u32x4 (&qb)[Geom<D>::NKK], const uint8_t *query, int s, int kvh,
+                                            int num_q_heads, uint32_t rows, int n, int q) {
+#pragma unroll
+    for (int kk = 0; kk < Geom<D>::NKK; ++kk) {
+        qb[kk] = u32x4{0, 0, 0, 0};
+        if ((rows >> n) & 1u)
+            qb[kk] = *(const u32x4 *)(query + ((int64_t)((s + n) * num_q_heads + kvh) * D + 32 * kk + 8 * q) * 2);
+    }
+}
+
 // Per-wave online-softmax state of one range: m (running max of head n, same in the 4
 // lanes of a column), lsum (this lane's share of the normaliser), o (O^T fragments).
 template <int D>
@@ -242,7 +256,8 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
                                              int num_kv_heads, int log2_block, int num_blocks, int start,
                                              int end, float scale_log2, int wave, int lane,
                                              const uint8_t *new_k = nullptr, const uint8_t *new_v = nullptr,
-                                             uint8_t *key_out = nullptr, uint8_t *value_out = nullptr) {
+                                             uint8_t *key_out = nullptr, uint8_t *value_out = nullptr,
+                                             uint32_t group_rows = 0) {
     using Gm = Geom<D>;
     constexpr int ROW = Gm::ROW;
     constexpr int NKK = Gm::NKK;
@@ -254,7 +269,10 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
     const int64_t block_bytes = (int64_t)num_kv_heads * block_size * ROW;
 
     u32x4 qb[NKK];
-    load_q<D, G>(qb, query, s, kvh, num_q_heads, n, q);
+    if (group_rows)  // one query row per sequence of a group (shared-prefix pass)
+        load_q_rows<D>(qb, query, s, kvh, num_kv_heads, group_rows, n, q);
+    else
+        load_q<D, G>(qb, query, s, kvh, num_q_heads, n, q);
 
     st.m = -INFINITY;
     st.lsum = 0.f;
@@ -379,12 +397,12 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
 // Merge the waves' states through LDS (the staging area; every wave's loads of the range
 // are complete) and write, per query head g of the group, either the normalised output
 // row out_row0 + g (ws_max == nullptr) or the partial (max, sum, weighted value sums)
-// at index idx0 + g * idx_stride of the workspace arrays.  Called by every thread;
-// leaves LDS free for the next range.
+// at index idx0 + g * idx_stride of the workspace arrays; rows outside row_mask are not
+// written.  Called by every thread; leaves LDS free for the next range.
 template <typename T, int D, int G>
 __device__ __forceinline__ void finish(const WaveState<D> &st, uint8_t *lds, int *sm_bad, int wave, int lane,
                                        void *out, int64_t out_row0, float *ws_max, float *ws_sum, float *ws_acc,
-                                       int64_t idx0, int64_t idx_stride) {
+                                       int64_t idx0, int64_t idx_stride, uint32_t row_mask = 0xffffffffu) {
     constexpr int NN = Geom<D>::NN;
     const int n = lane & 15;
     const int q = lane >> 4;
@@ -410,6 +428,7 @@ __device__ __forceinline__ void finish(const WaveState<D> &st, uint8_t *lds, int
     for (int t = threadIdx.x; t < G * D; t += MW * 64) {
         const int g = t / D;
         const int j = t - g * D;
+        if (!((row_mask >> g) & 1u)) continue;  // a row this workgroup does not own
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < MW; ++w) M = fmaxf(M, sm_m[w * G + g]);
@@ -594,6 +613,86 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_balanced_kernel(
             } while (__builtin_amdgcn_readfirstlane(context_lens[s]) <= 0);
         }
     }
+}
+
+// Shared-prefix pass (pa_decode_grouped): one workgroup per (group, KV head, shared
+// partition).  A group is a run of consecutive sequences whose tables start with the
+// same physical blocks ([cpai] §6: forked sequences share their prompt's blocks); each
+// shared partition's K/V tiles are read once for all members, whose queries (one query
+// head per KV head) fill the rows of the score product, and each served member's
+// partial for that partition goes to the partition workspace, where the partitioned
+// vector kernel leaves it alone and the log-sum-exp merge takes it.  Which members a
+// partition serves was decided by group_plan_kernel: seq_group[s] == j and
+// seq_parts[s] > p.
+template <typename T, int D, int G, bool NT>
+__global__ __launch_bounds__(MW * 64) void decode_mfma_grouped_kernel(
+    const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
+    const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ group_start, const int32_t *__restrict__ group_parts,
+    const int32_t *__restrict__ seq_group, const int32_t *__restrict__ seq_parts, float *__restrict__ ws_max,
+    float *__restrict__ ws_sum, float *__restrict__ ws_acc, int max_blocks_per_seq, int num_seqs,
+    int num_kv_heads, int log2_block, int num_blocks, int partition_size, int max_partitions,
+    int max_group_parts, float scale_log2) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int p = blockIdx.x % max_group_parts;
+    const int rest = blockIdx.x / max_group_parts;
+    const int kvh = rest % num_kv_heads;
+    const int j = rest / num_kv_heads;
+    const int s0 = group_start[j];
+    const int members = group_start[j + 1] - s0;
+    if (s0 < 0 || members < 1 || members > G || s0 > num_seqs - members) return;
+    if (p >= group_parts[j]) return;
+    uint32_t rows = 0;
+    for (int i = 0; i < members; ++i)
+        if (seq_group[s0 + i] == j && seq_parts[s0 + i] > p) rows |= 1u << i;
+    rows = __builtin_amdgcn_readfirstlane(rows);
+    if (rows == 0) return;
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds[MW * Geom<D>::WAVE_LDS];
+    static_assert((2 * MW * G + MW * G * D) * 4 <= MW * Geom<D>::WAVE_LDS, "merge area must fit the staging area");
+    __shared__ int sm_bad;
+    WaveState<D> st;
+    st.bad = false;
+    attend_range<T, D, G, NT>(st, lds + wave * Geom<D>::WAVE_LDS, query, key_cache, value_cache,
+                              block_tables + (int64_t)s0 * max_blocks_per_seq, max_blocks_per_seq, s0, kvh,
+                              num_kv_heads, log2_block, num_blocks, p * partition_size,
+                              (p + 1) * partition_size, scale_log2, wave, lane, nullptr, nullptr, nullptr,
+                              nullptr, rows);
+    // member i's partial: (sequence s0 + i, head kvh, partition p)
+    const int64_t idx0 = ((int64_t)s0 * num_kv_heads + kvh) * max_partitions + p;
+    finish<T, D, G>(st, lds, &sm_bad, wave, lane, nullptr, 0, ws_max, ws_sum, ws_acc, idx0,
+                    (int64_t)num_kv_heads * max_partitions, rows);
+}
+
+template <typename T, int D, int G>
+int launch_grouped_t(const DecodeArgs &a) {
+    const unsigned grid = (unsigned)a.num_groups * a.num_kv_heads * a.max_group_parts;
+    auto kernel = a.cached_kv ? decode_mfma_grouped_kernel<T, D, G, false> : decode_mfma_grouped_kernel<T, D, G, true>;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(MW * 64), 0, (hipStream_t)a.stream, (const uint8_t *)a.query,
+                       (const uint8_t *)a.key_cache, (const uint8_t *)a.value_cache, a.block_tables,
+                       a.group_start, a.group_parts, a.seq_group, a.seq_parts, a.ws_max, a.ws_sum, a.ws_acc,
+                       a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads, __builtin_ctz(a.block_size),
+                       a.num_blocks, a.partition_size, a.max_partitions, a.max_group_parts, a.scale_log2);
+    return check_launch("decode_mfma_grouped");
+}
+
+template <typename T, int D>
+int launch_grouped_d(const DecodeArgs &a) {
+    switch (a.group_rows) {
+        case 2: return launch_grouped_t<T, D, 2>(a);
+        case 4: return launch_grouped_t<T, D, 4>(a);
+        case 8: return launch_grouped_t<T, D, 8>(a);
+        case 16: return launch_grouped_t<T, D, 16>(a);
+    }
+    return fail(PA_ERR_UNSUPPORTED, "group rows %d", a.group_rows);
+}
+
+template <typename T>
+int launch_grouped(const DecodeArgs &a) {
+    if (a.head_dim == 64) return launch_grouped_d<T, 64>(a);
+    if (a.head_dim == 128) return launch_grouped_d<T, 128>(a);
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d", a.head_dim);
 }
 
 template <typename T, int D, int G, bool NT>

@@ -4,5 +4,6 @@
 namespace pa {
 
 int launch_decode_mfma_bf16(const DecodeArgs &a) { return mfma::by_dim<BF16>(a); }
+int launch_decode_mfma_grouped_bf16(const DecodeArgs &a) { return mfma::launch_grouped<BF16>(a); }
 
 }  // namespace pa

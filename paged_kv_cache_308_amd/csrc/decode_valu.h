@@ -290,7 +290,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     float *__restrict__ ws_acc, int max_blocks_per_seq, int num_seqs, int num_kv_heads,
     int log2_block, int num_blocks, int partition_size, int max_partitions, float scale_log2,
     const uint8_t *__restrict__ new_key, const uint8_t *__restrict__ new_value, uint8_t *key_out,
-    uint8_t *value_out) {
+    uint8_t *value_out, const int32_t *__restrict__ skip_parts) {
     using T = typename KV::Q;
     constexpr int NWG = waves_per_group<KV, G>();
     constexpr int QB = T::bytes;            // query / output element bytes
@@ -336,6 +336,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     if (SPLIT) {
         start = part * partition_size;
         if (ctx < 0 || start >= ctx) return;  // nothing here (the merge handles bad lengths)
+        // leading partitions a shared-prefix pass already wrote (pa_decode_grouped)
+        if (skip_parts != nullptr && part < skip_parts[s]) return;
         end = min(ctx, start + partition_size);
     }
 
@@ -910,7 +912,7 @@ int launch_t(const DecodeArgs &a) {
                            a.context_lens, a.ws_max, a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs,
                            a.num_kv_heads, log2b, a.num_blocks, a.partition_size, a.max_partitions,
                            a.scale_log2, (const uint8_t *)a.new_key, (const uint8_t *)a.new_value,
-                           (uint8_t *)a.key_out, (uint8_t *)a.value_out);
+                           (uint8_t *)a.key_out, (uint8_t *)a.value_out, a.skip_parts);
         const int rc = check_launch("decode_valu (partitions)");
         if (rc != PA_OK) return rc;
         return launch_lse_merge(a);
@@ -921,7 +923,7 @@ int launch_t(const DecodeArgs &a) {
                        (const uint8_t *)a.value_cache, a.k_scales, a.v_scales, a.block_tables,
                        a.context_lens, nullptr, nullptr, nullptr, a.max_blocks_per_seq, a.num_seqs,
                        a.num_kv_heads, log2b, a.num_blocks, 0, 1, a.scale_log2, (const uint8_t *)a.new_key,
-                       (const uint8_t *)a.new_value, (uint8_t *)a.key_out, (uint8_t *)a.value_out);
+                       (const uint8_t *)a.new_value, (uint8_t *)a.key_out, (uint8_t *)a.value_out, nullptr);
     return check_launch("decode_valu");
 }
 

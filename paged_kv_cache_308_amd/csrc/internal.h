@@ -51,6 +51,15 @@ struct DecodeArgs {
     const int32_t *query_start;  // [S + 1]: the sequence's rows of query / out
     int num_query_tokens;        // rows of query / out
     int max_query_len;           // bound on query_start[s + 1] - query_start[s]
+    // shared-prefix groups (pa_decode_grouped)
+    const int32_t *group_start;  // [num_groups + 1]: group j is sequences group_start[j] ..
+    const int32_t *group_parts;  // [num_groups]: leading partitions its members share
+    int32_t *seq_group;          // workspace [S]: group serving sequence s (-1: none)
+    int32_t *seq_parts;          // workspace [S]: leading partitions served by its group
+    const int32_t *skip_parts;   // for the partitioned vector kernel: partitions already done
+    int num_groups;
+    int max_group_parts;         // bound on group_parts[j] (grid extent)
+    int group_rows;              // rows of the grouped score product: 2, 4, 8 or 16
     void *stream;
 };
 
@@ -83,6 +92,9 @@ int launch_reshape_and_cache_fp8(const void *key, const void *value, void *key_c
                                  void *stream);
 int launch_stream_read(const void *buf, size_t bytes, void *sink, void *stream);
 int launch_gather_read(const uint64_t *tile_addrs, int num_tiles, int tile_bytes, void *sink, void *stream);
+// Which sequences a group serves and for how many partitions (seq_group, seq_parts).
+int launch_group_plan(const DecodeArgs &a);
+int launch_decode_mfma_grouped(const DecodeArgs &a);
 int launch_move_blocks(const void *src_key, const void *src_value, void *dst_key, void *dst_value,
                        const int32_t *src, const int32_t *dst, int num_pairs, int num_kv_heads,
                        int head_dim, int block_size, int src_blocks, int dst_blocks, int elem_bytes,
@@ -101,6 +113,8 @@ int launch_decode_mfma_f16(const DecodeArgs &a);
 int launch_multi_query_f16(const DecodeArgs &a);
 int launch_multi_query_bf16(const DecodeArgs &a);
 int launch_decode_mfma_bf16(const DecodeArgs &a);
+int launch_decode_mfma_grouped_f16(const DecodeArgs &a);
+int launch_decode_mfma_grouped_bf16(const DecodeArgs &a);
 
 // Map a HIP error after a launch to PA_ERR_HIP with its text.
 int check_launch(const char *what);

@@ -33,6 +33,52 @@ def _scale_pools(k_scales: torch.Tensor, v_scales: torch.Tensor):
     return k_scales.view(nb, h, 1, 1), v_scales.view(nb, h, 1, 1)
 
 
+def prefix_groups(host_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
+                  partition_size: int, max_group_size: int = 16):
+    """Shared-prefix groups for pa_decode_grouped, from the step's host tables: runs of
+    consecutive sequences whose tables start with the same block ids ("PagedAttention"
+    concept report (compassingai.com) §6: forked sequences hold their prompt's blocks).
+    A sequence joins the current group when it shares at least one whole partition with
+    the group's first sequence; the group's shared partitions are the fewest any member
+    has (shared leading blocks, ending before each member's newest token).  Returns
+    (group_start int32 [G + 1], group_parts int32 [G], largest group size, largest
+    group_parts).  Host bookkeeping only: the device re-checks every member."""
+    S = len(context_lens)
+    bpp = partition_size // block_size
+    ctx = np.asarray(context_lens, np.int64)
+
+    def own_parts(s):  # partitions wholly before the newest token
+        return max(0, int(ctx[s] - 1)) // partition_size
+
+    def common_parts(a, b):
+        n = min(own_parts(a), own_parts(b)) * bpp
+        if n == 0:
+            return 0
+        eq = host_tables[a, :n] == host_tables[b, :n]
+        k = n if eq.all() else int(np.argmin(eq))
+        return k // bpp
+
+    starts, parts = [0], []
+    i = 0
+    while i < S:
+        g = own_parts(i)
+        j = i + 1
+        while j < S and j - i < max_group_size:
+            c = common_parts(i, j)
+            if c < 1:
+                break
+            g = min(g, c)
+            j += 1
+        if j - i == 1:
+            g = 0
+        parts.append(g)
+        starts.append(j)
+        i = j
+    start = np.asarray(starts, np.int32)
+    gp = np.asarray(parts, np.int32)
+    return start, gp, int(np.max(np.diff(start))) if S else 1, int(gp.max()) if len(gp) else 0
+
+
 class PagedKVCache:
     """Device K/V pools of one layer and the host allocator.  dtype=torch.uint8 holds
     E4M3 codes, with k_scales / v_scales float32 [num_blocks][H_kv] (one per block and

@@ -1,0 +1,209 @@
+"""Decode over shared-prefix groups (pa_decode_grouped) against the oracle on the GPU.
+
+Each group's sequences are forks of one prompt: their tables start with the prompt's
+full blocks (the same ids), the prompt's partly filled last block is copied into each
+member's own block (copy-on-write), and each member then has private tokens.  The
+oracle attends through each sequence's table as usual; the grouped call must give the
+same attention (bar 2e-2, f16 / bf16 output against binary64) whether or not the
+device plan lets a group serve a sequence, and store the newest tokens bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_308_amd as pa
+import workloads as W
+from paged_kv_cache_308_amd.engine import prefix_groups, to_torch
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class GroupCase:
+    """Groups of forked sequences placed in a pool through a random block permutation;
+    unused slots hold NaN.  ctx includes the newest token, whose slot is NaN too (the
+    grouped call with new tokens must store it first)."""
+
+    def __init__(self, rng, groups, H, d, B, dtype):
+        # groups: list of (prompt_len, [private lens of the members])
+        self.H, self.d, self.B, self.dtype = H, d, B, dtype
+        npd = W.storage_np_dtype(dtype)
+        logical = []  # per sequence: (k, v) [n][H][d]
+        self.ctx = []
+        shared_blocks = []
+        for prompt, privs in groups:
+            pk = W.round_to(rng.standard_normal((prompt, H, d), dtype=np.float32), dtype)
+            pv = W.round_to(rng.standard_normal((prompt, H, d), dtype=np.float32), dtype)
+            for n in privs:
+                k = W.round_to(rng.standard_normal((n, H, d), dtype=np.float32), dtype)
+                v = W.round_to(rng.standard_normal((n, H, d), dtype=np.float32), dtype)
+                logical.append((np.concatenate([pk, k]), np.concatenate([pv, v])))
+                self.ctx.append(prompt + n)
+                shared_blocks.append(prompt // B)
+        S = len(logical)
+        nblk = [-(-c // B) for c in self.ctx]
+        need = sum(nblk)  # more than enough (shared blocks counted per member)
+        self.num_blocks = need + 3
+        ids = rng.permutation(self.num_blocks)
+        self.tables = np.full((S, max(nblk)), -1, np.int32)
+        pos, s = 0, 0
+        for prompt, privs in groups:
+            sb = prompt // B
+            shared = ids[pos:pos + sb]
+            pos += sb
+            for _ in privs:
+                own = nblk[s] - sb
+                self.tables[s, :sb] = shared
+                self.tables[s, sb:nblk[s]] = ids[pos:pos + own]
+                pos += own
+                s += 1
+        assert pos <= self.num_blocks
+        fill = W.nan_bits(dtype)
+        shape = (self.num_blocks, H, B, d)
+        self.kc = np.full(shape, fill, npd)
+        self.vc = np.full(shape, fill, npd)
+        for s, (k, v) in enumerate(logical):
+            for t in range(self.ctx[s]):
+                b, o = self.tables[s, t // B], t % B
+                self.kc[b, :, o, :] = k[t]
+                self.vc[b, :, o, :] = v[t]
+        self.ctx = np.asarray(self.ctx, np.int32)
+        self.q = W.round_to(rng.standard_normal((S, H, d), dtype=np.float32), dtype)
+        self.new_k = np.stack([k[-1] for k, _ in logical])
+        self.new_v = np.stack([v[-1] for _, v in logical])
+        self.scale = float(np.float32(1.0 / np.sqrt(d)))
+
+    def oracle_out(self):
+        return oracle.default().decode(self.q, self.kc, self.vc, self.tables, self.ctx, self.scale, self.dtype)
+
+    def poisoned_newest(self):
+        """The pools with every sequence's newest slot set to NaN."""
+        kc, vc = self.kc.copy(), self.vc.copy()
+        fill = W.nan_bits(self.dtype)
+        for s, c in enumerate(self.ctx):
+            b, o = self.tables[s, (c - 1) // self.B], (c - 1) % self.B
+            kc[b, :, o, :] = fill
+            vc[b, :, o, :] = fill
+        return kc, vc
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().double().cpu().numpy()
+
+
+def bits(t: torch.Tensor) -> bytes:
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy().tobytes()
+
+
+def run_grouped(c: GroupCase, P, group_start, group_parts, max_group_size, max_group_parts,
+                append: bool, tables=None):
+    dev = lambda a: to_torch(a, c.dtype).cuda()
+    kc0, vc0 = c.poisoned_newest() if append else (c.kc, c.vc)
+    kc, vc = dev(kc0), dev(vc0)
+    q = dev(c.q)
+    bt = torch.from_numpy(c.tables if tables is None else tables).cuda()
+    cl = torch.from_numpy(c.ctx).cuda()
+    gs = torch.from_numpy(np.asarray(group_start, np.int32)).cuda()
+    gp = torch.from_numpy(np.asarray(group_parts, np.int32)).cuda()
+    out = torch.empty_like(q)
+    mc = int(c.ctx.max())
+    ws = torch.empty(pa.pa_decode_grouped_workspace_bytes(q.shape[0], c.H, c.H, c.d, mc, P),
+                     dtype=torch.uint8, device="cuda")
+    nk = dev(c.new_k) if append else None
+    nv = dev(c.new_v) if append else None
+    pa.pa_decode_grouped(out, q, kc, vc, bt, cl, c.scale, gs, gp, max_group_size, max_group_parts, mc, P,
+                         new_key=nk, new_value=nv, workspace=ws)
+    torch.cuda.synchronize()
+    return out, kc, vc
+
+
+GROUPS = [
+    (100, [5, 1, 40, 7, 3]),   # 5 samples of a 100-token prompt
+    (64, [1]),                 # a lone sequence
+    (129, [2, 9]),
+    (40, [30, 1, 1, 20]),      # prompt shorter than a partition
+    (200, [1] * 16),           # the largest group
+    (256, [3, 60, 17]),        # prompt ends on a partition boundary
+]
+SHAPES = [(4, 128, 16, "f16", 64), (2, 64, 32, "bf16", 64), (2, 128, 16, "bf16", 32), (3, 128, 64, "f16", 128)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+@pytest.mark.parametrize("append", [False, True])
+def test_grouped_matches_oracle(shape, append):
+    H, d, B, dt, P = shape
+    rng = np.random.default_rng(hash(shape) % 1000 + append)
+    c = GroupCase(rng, GROUPS, H, d, B, dt)
+    want = c.oracle_out()
+    gs, gp, gmax, pmax = prefix_groups(c.tables, c.ctx, B, P)
+    assert pmax >= 1
+    say(f"[gpu] grouped {shape} append={append}: {len(gp)} groups, parts {gp.tolist()}")
+    got, kc, vc = run_grouped(c, P, gs, gp, gmax, pmax, append)
+    err = np.max(np.abs(f64(got) - want))
+    assert err <= TOL, err
+    if append:  # the newest tokens stored bit for bit
+        assert bits(kc) == np.ascontiguousarray(c.kc).tobytes()
+        assert bits(vc) == np.ascontiguousarray(c.vc).tobytes()
+
+
+def test_grouped_falls_back_for_sequences_it_cannot_serve():
+    """Descriptions the device plan rejects only cost speed: a member whose table leaves
+    the shared blocks, a group claiming more shared partitions than a member's context
+    holds, groups larger than max_group_size, ranges past the batch, and no shared
+    partitions at all all give the oracle's attention."""
+    H, d, B, dt, P = 2, 128, 16, "f16", 64
+    rng = np.random.default_rng(31)
+    c = GroupCase(rng, GROUPS, H, d, B, dt)
+    want = c.oracle_out()
+    gs, gp, gmax, pmax = prefix_groups(c.tables, c.ctx, B, P)
+    cases = []
+    # member 2 of group 0 reads a copy of a shared block through another id
+    t = c.tables.copy()
+    spare = c.num_blocks - 1
+    c2 = GroupCase.__new__(GroupCase)
+    c2.__dict__.update(c.__dict__)
+    c2.kc, c2.vc = c.kc.copy(), c.vc.copy()
+    c2.kc[spare], c2.vc[spare] = c.kc[t[2, 1]], c.vc[t[2, 1]]
+    t[2, 1] = spare
+    c2.tables = t
+    cases.append(("table differs", c2, gs, gp, gmax, pmax))
+    gp2 = gp.copy()
+    gp2[0] = pmax  # more than the shortest member of group 0 holds
+    cases.append(("too many parts", c, gs, gp2, gmax, pmax))
+    cases.append(("group too large", c, gs, gp, 4, pmax))
+    gs3 = gs.copy()
+    gs3[-1] = len(c.ctx) + 5  # the last range runs past the batch
+    cases.append(("range past the batch", c, gs3, gp, gmax, pmax))
+    cases.append(("no shared pass", c, gs, np.zeros_like(gp), gmax, 0))
+    for name, cc, a, b, g, m in cases:
+        w = want if cc is c else cc.oracle_out()
+        say(f"[gpu] grouped fallback: {name}")
+        got, _, _ = run_grouped(cc, P, a, b, g, m, append=True)
+        err = np.max(np.abs(f64(got) - w))
+        assert err <= TOL, (name, err)
+
+
+def test_grouped_equals_partitioned_decode_closely():
+    """Same partitions, same merge: the grouped result is the partitioned decode's up to
+    the order of the shared partitions' sums (matrix-core products, weights rounded to
+    the storage type)."""
+    H, d, B, dt, P = 4, 128, 16, "bf16", 64
+    rng = np.random.default_rng(47)
+    c = GroupCase(rng, GROUPS, H, d, B, dt)
+    gs, gp, gmax, pmax = prefix_groups(c.tables, c.ctx, B, P)
+    got, _, _ = run_grouped(c, P, gs, gp, gmax, pmax, append=False)
+    q = to_torch(c.q, dt).cuda()
+    ref = torch.empty_like(q)
+    mc = int(c.ctx.max())
+    ws = torch.empty(pa.pa_decode_workspace_bytes(q.shape[0], H, H, d, mc, P), dtype=torch.uint8, device="cuda")
+    pa.pa_decode(ref, q, to_torch(c.kc, dt).cuda(), to_torch(c.vc, dt).cuda(), torch.from_numpy(c.tables).cuda(),
+                 torch.from_numpy(c.ctx).cuda(), c.scale, max_context_len=mc, partition_size=P, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(f64(got) - f64(ref))) <= TOL
