@@ -89,6 +89,9 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="store the newest tokens with their own launch even where the attention "
                          "launch can do it")
+    ap.add_argument("--no-grouped", action="store_true",
+                    help="batches of forked sequences: attend per sequence (pa_decode_append) instead of "
+                         "reading each shared partition once per group (pa_decode_grouped)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-stream", action="store_true",
                     help="skip the read-bandwidth probes (pa_stream_read over 4 GiB, pa_gather_read over the step's tiles)")
@@ -139,6 +142,9 @@ def build_replicas(args, w, batch, identity: bool):
         src = torch.from_numpy(db.cow_src).cuda()
         dst = torch.from_numpy(db.cow_dst).cuda()
         out = torch.empty_like(db.query)
+        if args.grouped:
+            ws = db.grouped_workspace(args.P)
+            db.group_args = db.groups(args.P)
         reps.append((db, ws, src, dst, out))
     torch.cuda.synchronize()
     return reps
@@ -167,7 +173,9 @@ def run_steps(args, reps, n_steps: int, record: bool):
             db.cache.write(db.new_key, db.new_value, db.slot_mapping, st)
         if record:
             evs[k][1].record(st)
-        if args.fused:  # the newest tokens' store rides in the attention launch
+        if args.grouped:  # shared partitions once per group, the newest tokens stored
+            db.step_grouped(args.P, db.group_args, out=out, workspace=ws, stream=st, variant=args.variant)
+        elif args.fused:  # the newest tokens' store rides in the attention launch
             db.step(args.P, args.variant, out=out, workspace=ws, stream=st)
         else:
             db.attend(args.P, args.variant, out=out, workspace=ws, stream=st)
@@ -499,6 +507,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = W.WORKLOADS[args.workload]
     args.P = w.partition_size if args.partition_size is None else args.partition_size
+    # batches of forked sequences (shared prompts) take the grouped path by default
+    args.grouped = (w.lengths == "prefix" and not args.no_grouped and args.P > 0 and w.kv != "fp8"
+                    and w.num_q_heads == w.num_kv_heads and w.dtype in ("f16", "bf16"))
     log(args, f"[bench] {w.name}: generating inputs")
     batch = W.make_batch(w)
     ctx = batch.lengths.context_lens
@@ -513,7 +524,8 @@ def main():
     reps = build_replicas(args, w, batch, identity=False)
     # tokens held in the pool (a block shared by several sequences counts once)
     ab = algorithmic_bytes(w, ctx, reps[0][0].cache.alloc.stats()["stored_tokens"])
-    args.fused = not args.unfused and reps[0][0].cache.fused_step_ok(w.num_q_heads, args.P, args.variant)
+    args.fused = args.grouped or (not args.unfused and
+                                  reps[0][0].cache.fused_step_ok(w.num_q_heads, args.P, args.variant))
     if args.fused:  # the attention launch also stores the newest K/V into the pool
         newest = 2 * w.num_seqs * w.num_kv_heads * w.head_dim * w.kv_elem_bytes
         ab["total"] += newest
@@ -550,7 +562,9 @@ def main():
     achieved = ab["total_unique"] / (dec_avg * 1e-3) / 1e9
     g = w.num_q_heads // w.num_kv_heads
     mfma = w.kv != "fp8" and (args.variant == 2 or (args.variant == 0 and g >= 2 and w.dtype != "f32"))
-    if args.P < 0:
+    if args.grouped:
+        kernels = "group_plan_kernel + decode_mfma_grouped_kernel + decode_valu_kernel + lse_merge_kernel"
+    elif args.P < 0:
         kernels = ("decode_mfma_balanced_kernel" if mfma else "decode_balanced_kernel") + " + balanced_merge_kernel"
     else:
         kernels = ("decode_mfma_kernel" if mfma else "decode_valu_kernel") + (" + lse_merge_kernel" if args.P else "")
@@ -588,11 +602,13 @@ def main():
         "mfma_util": round(4.0 * float(ctx.sum()) * w.num_q_heads * w.head_dim / (dec_avg * 1e-3) / 1e12 /
                            MFMA_PEAK_TFLOPS[w.dtype], 4) if mfma else None,
         "fused_store": args.fused,
+        "grouped": args.grouped,
         "pre_decode_us": round(float(np.mean(pre_ms)) * 1e3, 2),
         "decode_kv_gbs": round(ab["kv"] / (dec_avg * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": kernels, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": ab["total_unique"], "traffic": measured_traffic(w.name)},
+                     "bytes_per_launch": ab["total_unique"],
+                     "traffic": measured_traffic(w.name + ("_grouped" if args.grouped else ""))},
         "identity_decode_us": None if ident is None else round(ident * 1e3, 2),
         "paged_vs_identity": None if ident is None else round(ident / dec_avg, 4),
         "host_alloc_us_per_step": round(alloc_us, 2),

@@ -615,15 +615,16 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_balanced_kernel(
     }
 }
 
-// Shared-prefix pass (pa_decode_grouped): one workgroup per (group, KV head, shared
-// partition).  A group is a run of consecutive sequences whose tables start with the
-// same physical blocks ([cpai] §6: forked sequences share their prompt's blocks); each
-// shared partition's K/V tiles are read once for all members, whose queries (one query
-// head per KV head) fill the rows of the score product, and each served member's
-// partial for that partition goes to the partition workspace, where the partitioned
-// vector kernel leaves it alone and the log-sum-exp merge takes it.  Which members a
-// partition serves was decided by group_plan_kernel: seq_group[s] == j and
-// seq_parts[s] > p.
+// Shared-prefix pass (pa_decode_grouped): one workgroup per (group, KV head).  A group
+// is a run of consecutive sequences whose tables start with the same physical blocks
+// ([cpai] §6: forked sequences share their prompt's blocks); the workgroup reads the K/V
+// tiles of the group's shared partitions once for all members, whose queries (one query
+// head per KV head) fill the rows of the score product, and writes each served member's
+// partial for the whole shared span into its partition 0 slot and empty partials (max
+// -inf, sums 0) into the slots of its other shared partitions, which the partitioned
+// vector kernel leaves alone and the log-sum-exp merge then weighs 0.  Which members
+// the pass serves was decided by group_plan_kernel: seq_group[s] == j (then
+// seq_parts[s] == group_parts[j]).
 template <typename T, int D, int G, bool NT>
 __global__ __launch_bounds__(MW * 64) void decode_mfma_grouped_kernel(
     const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
@@ -635,17 +636,16 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_grouped_kernel(
     int max_group_parts, float scale_log2) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int p = blockIdx.x % max_group_parts;
-    const int rest = blockIdx.x / max_group_parts;
-    const int kvh = rest % num_kv_heads;
-    const int j = rest / num_kv_heads;
+    const int kvh = blockIdx.x % num_kv_heads;
+    const int j = blockIdx.x / num_kv_heads;
     const int s0 = group_start[j];
     const int members = group_start[j + 1] - s0;
     if (s0 < 0 || members < 1 || members > G || s0 > num_seqs - members) return;
-    if (p >= group_parts[j]) return;
+    const int parts = group_parts[j];
+    if (parts < 1 || parts > max_group_parts) return;
     uint32_t rows = 0;
     for (int i = 0; i < members; ++i)
-        if (seq_group[s0 + i] == j && seq_parts[s0 + i] > p) rows |= 1u << i;
+        if (seq_group[s0 + i] == j && seq_parts[s0 + i] == parts) rows |= 1u << i;
     rows = __builtin_amdgcn_readfirstlane(rows);
     if (rows == 0) return;
 
@@ -656,18 +656,31 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_grouped_kernel(
     st.bad = false;
     attend_range<T, D, G, NT>(st, lds + wave * Geom<D>::WAVE_LDS, query, key_cache, value_cache,
                               block_tables + (int64_t)s0 * max_blocks_per_seq, max_blocks_per_seq, s0, kvh,
-                              num_kv_heads, log2_block, num_blocks, p * partition_size,
-                              (p + 1) * partition_size, scale_log2, wave, lane, nullptr, nullptr, nullptr,
-                              nullptr, rows);
-    // member i's partial: (sequence s0 + i, head kvh, partition p)
-    const int64_t idx0 = ((int64_t)s0 * num_kv_heads + kvh) * max_partitions + p;
-    finish<T, D, G>(st, lds, &sm_bad, wave, lane, nullptr, 0, ws_max, ws_sum, ws_acc, idx0,
-                    (int64_t)num_kv_heads * max_partitions, rows);
+                              num_kv_heads, log2_block, num_blocks, 0, parts * partition_size, scale_log2, wave,
+                              lane, nullptr, nullptr, nullptr, nullptr, rows);
+    // member i's partial: (sequence s0 + i, head kvh, partition 0) ...
+    const int64_t stride = (int64_t)num_kv_heads * max_partitions;
+    const int64_t idx0 = ((int64_t)s0 * num_kv_heads + kvh) * max_partitions;
+    finish<T, D, G>(st, lds, &sm_bad, wave, lane, nullptr, 0, ws_max, ws_sum, ws_acc, idx0, stride, rows);
+    // ... and empty partials in its partitions 1 .. parts - 1
+    for (int t = threadIdx.x; t < G * (parts - 1) * D; t += MW * 64) {
+        const int i = t / ((parts - 1) * D);
+        const int r = t - i * (parts - 1) * D;
+        const int p = 1 + r / D;
+        const int e = r - (p - 1) * D;
+        if (!((rows >> i) & 1u)) continue;
+        const int64_t pi = idx0 + i * stride + p;
+        if (e == 0) {
+            ws_max[pi] = -INFINITY;
+            ws_sum[pi] = 0.f;
+        }
+        ws_acc[pi * D + e] = 0.f;
+    }
 }
 
 template <typename T, int D, int G>
 int launch_grouped_t(const DecodeArgs &a) {
-    const unsigned grid = (unsigned)a.num_groups * a.num_kv_heads * a.max_group_parts;
+    const unsigned grid = (unsigned)a.num_groups * a.num_kv_heads;
     auto kernel = a.cached_kv ? decode_mfma_grouped_kernel<T, D, G, false> : decode_mfma_grouped_kernel<T, D, G, true>;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(MW * 64), 0, (hipStream_t)a.stream, (const uint8_t *)a.query,
                        (const uint8_t *)a.key_cache, (const uint8_t *)a.value_cache, a.block_tables,

@@ -14,8 +14,8 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-from . import PA_DECODE_SHARED_KV, PA_VARIANT_AUTO
-from .engine import TORCH_DTYPE, PagedKVCache, to_torch
+from . import PA_DECODE_SHARED_KV, PA_VARIANT_AUTO, pa_decode_grouped, pa_decode_grouped_workspace_bytes
+from .engine import TORCH_DTYPE, PagedKVCache, prefix_groups, to_torch
 
 
 @dataclasses.dataclass
@@ -50,6 +50,30 @@ class DeviceBatch:
                                    workspace=workspace, stream=stream)
         self.cache.write(self.new_key, self.new_value, self.slot_mapping, stream)
         return self.attend(partition_size, variant & ~PA_DECODE_SHARED_KV, out, workspace, stream)
+
+    def groups(self, partition_size: int):
+        """Shared-prefix groups of the batch (host tables) as device arrays, with the
+        largest group and the most shared partitions, for step_grouped."""
+        gs, gp, gmax, pmax = prefix_groups(self.host_tables, self.host_context_lens, self.cache.block_size,
+                                           partition_size)
+        dev = self.block_tables.device
+        return torch.from_numpy(gs).to(dev), torch.from_numpy(gp).to(dev), gmax, pmax
+
+    def grouped_workspace(self, partition_size: int) -> torch.Tensor:
+        n = pa_decode_grouped_workspace_bytes(self.query.shape[0], self.query.shape[1], self.cache.num_kv_heads,
+                                              self.cache.head_dim, self.max_context_len, partition_size)
+        return torch.empty(n, dtype=torch.uint8, device=self.block_tables.device)
+
+    def step_grouped(self, partition_size: int, groups, out=None, workspace=None, stream=None,
+                     variant: int = PA_VARIANT_AUTO) -> torch.Tensor:
+        """The decode step over shared-prefix groups (pa_decode_grouped): the newest
+        K/V stored, shared partitions read once per group."""
+        gs, gp, gmax, pmax = groups
+        out = torch.empty_like(self.query) if out is None else out
+        return pa_decode_grouped(out, self.query, self.cache.key_cache, self.cache.value_cache, self.block_tables,
+                                 self.context_lens, self.scale, gs, gp, gmax, pmax, self.max_context_len,
+                                 partition_size, new_key=self.new_key, new_value=self.new_value,
+                                 variant=variant, workspace=workspace, stream=stream)
 
     def attend(self, partition_size: int = 0, variant: int = PA_VARIANT_AUTO, out=None,
                workspace=None, stream=None) -> torch.Tensor:

@@ -717,6 +717,27 @@ def test_full_size_sampled(name, P):
     assert err <= TOL[w.dtype]
 
 
+def test_full_size_prefix_sharing_grouped():
+    """The prefix-sharing workload through pa_decode_grouped, as the benchmark runs it:
+    16 groups of 5 forks, each sharing its prompt's two whole 512-token partitions;
+    all 80 sequences against the oracle."""
+    w = W.WORKLOADS["prefix_sharing"]
+    say("[gpu] full-size prefix_sharing grouped: generating")
+    batch = W.make_batch(w)
+    db = replay(batch)
+    groups = db.groups(w.partition_size)
+    gs, gp, gmax, pmax = groups
+    assert gs.tolist() == list(range(0, 81, 5)) and gp.tolist() == [2] * 16 and gmax == 5 and pmax == 2
+    say("[gpu] full-size prefix_sharing grouped: step")
+    got = f64(db.step_grouped(w.partition_size, groups, workspace=db.grouped_workspace(w.partition_size)))
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(got))
+    want, _ = place.decode_step(batch)
+    err = np.max(np.abs(got - want))
+    say(f"[gpu] full-size prefix_sharing grouped: max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("tile", [1024, 2048, 4096, 8192])
 def test_gather_read_probe_reads_without_writing(tile):
     """pa_gather_read reads the listed tiles (addresses inside one zero buffer, in random
