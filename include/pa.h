@@ -260,22 +260,23 @@ int pa_decode_fp8_append(void *out, const void *query, const void *new_key, cons
  * [wmrh] "paged attention": forked samples of one prompt hold the prompt's physical
  * blocks with a reference count, so their tables start with the same block ids).  The
  * result is that of pa_decode_append (new_key, new_value given: each sequence's newest
- * K/V stored at position ctx - 1, then attended) or of pa_decode (both NULL) with the
- * same partition_size, up to rounding order; the shared blocks are read once per group
- * instead of once per sequence.
+ * K/V stored at position ctx - 1, then attended) or of pa_decode (both NULL), up to
+ * rounding order; the shared blocks are read once per group instead of once per
+ * sequence.
  *
  * Groups are runs of consecutive sequences: group j holds sequences group_start[j] ..
  * group_start[j + 1] - 1 (device int32 [num_groups + 1], ascending, group_start[0] = 0,
  * group_start[num_groups] = num_seqs), at most max_group_size (1..16) of them, whose first
- * group_parts[j] partitions (device int32 [num_groups]; partitions of partition_size
- * tokens) are reached through the same table entries.  Those partitions run once per
- * (group, KV head) on the matrix cores, every member's query a row of the product; the
- * rest of each context runs on the partitioned vector kernel, which also stores the
- * newest token; the partition merge combines both.
+ * group_parts[j] spans of partition_size tokens (device int32 [num_groups]) are reached
+ * through the same table entries.  Those spans run once per (group, KV head) on the
+ * matrix cores, every member's query a row of the product, leaving a partial (max, sum,
+ * weighted value sums) per member and head in the workspace; the rest of each context
+ * runs in one pass on the vector kernel, which also stores the newest token and folds
+ * the partial in.
  *
  * A sequence is served by its group only when the group is well formed (at most
  * max_group_size members, 1 <= group_parts[j] <= max_group_parts), its shared
- * partitions end before its newest token (group_parts[j] * partition_size <= ctx - 1)
+ * spans end before its newest token (group_parts[j] * partition_size <= ctx - 1)
  * and its table entries for them equal the group's first sequence's and lie in the pool
  * (a device-side plan kernel checks this); any other sequence is attended in full by the
  * vector kernel, so a wrong group description costs speed, not results.

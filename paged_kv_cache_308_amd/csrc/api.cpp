@@ -109,6 +109,18 @@ size_t workspace_layout_balanced(int S, int Hq, int Hkv, int d, int W, void *ws,
     return bh + 2 * bm + bacc;
 }
 
+// pa_decode_grouped: the shared-prefix partials (one partition) then seq_group, seq_parts.
+size_t grouped_workspace_layout(int S, int Hq, int d, void *ws, DecodeArgs *a) {
+    const size_t base = workspace_layout(S, Hq, d, 1, nullptr, nullptr, nullptr, nullptr);
+    const size_t plan = align256((size_t)S * sizeof(int32_t));
+    if (ws) {
+        workspace_layout(S, Hq, d, 1, ws, &a->ws_max, &a->ws_sum, &a->ws_acc);
+        a->seq_group = (int32_t *)((char *)ws + base);
+        a->seq_parts = (int32_t *)((char *)ws + base + plan);
+    }
+    return base + 2 * plan;
+}
+
 int device_max_waves() {
     int dev = 0, cus = 0, threads = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -247,20 +259,25 @@ static int decode_common(DecodeArgs &a, int max_context_len, float scale, int va
         a.max_workers = w;
         workspace_layout_balanced(num_seqs, num_q_heads, num_kv_heads, head_dim, w, workspace, &a.ws_hdr,
                                   &a.ws_max, &a.ws_sum, &a.ws_acc);
+    } else if (grouped) {
+        // one partial per (sequence, query head) from the shared-prefix pass, then the plan
+        const size_t need = grouped_workspace_layout(num_seqs, num_q_heads, head_dim, nullptr, &a);
+        if (!workspace || workspace_bytes < need)
+            return fail(PA_ERR_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+        grouped_workspace_layout(num_seqs, num_q_heads, head_dim, workspace, &a);
     } else if (partition_size > 0) {
-        const size_t base = workspace_layout(num_seqs, num_q_heads, head_dim, a.max_partitions,
+        const size_t need = workspace_layout(num_seqs, num_q_heads, head_dim, a.max_partitions,
                                              nullptr, nullptr, nullptr, nullptr);
-        const size_t plan = grouped ? 2 * align256((size_t)num_seqs * sizeof(int32_t)) : 0;
-        if (!workspace || workspace_bytes < base + plan)
-            return fail(PA_ERR_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, base + plan);
+        if (!workspace || workspace_bytes < need)
+            return fail(PA_ERR_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
         workspace_layout(num_seqs, num_q_heads, head_dim, a.max_partitions, workspace, &a.ws_max,
                          &a.ws_sum, &a.ws_acc);
-        if (grouped) {
-            a.seq_group = (int32_t *)((char *)workspace + base);
-            a.seq_parts = (int32_t *)((char *)workspace + base + align256((size_t)num_seqs * sizeof(int32_t)));
-        }
     }
     if (grouped) {
+        // spans of partition_size tokens; the private tokens run in one pass
+        a.group_span = partition_size;
+        a.partition_size = 0;
+        a.max_partitions = 1;
         if (a.max_group_parts > 0) {
             int rc = launch_group_plan(a);
             if (rc == PA_OK) rc = launch_decode_mfma_grouped(a);
@@ -337,10 +354,11 @@ int pa_decode_append(void *out, const void *query, const void *new_key, const vo
 
 size_t pa_decode_grouped_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                          int max_context_len, int partition_size) {
-    const size_t base = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                  max_context_len, partition_size);
-    if (base == 0 || partition_size <= 0) return 0;
-    return base + 2 * align256((size_t)num_seqs * sizeof(int32_t));
+    (void)max_context_len;
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_q_heads % num_kv_heads ||
+        partition_size <= 0)
+        return 0;
+    return grouped_workspace_layout(num_seqs, num_q_heads, head_dim, nullptr, nullptr);
 }
 
 int pa_decode_grouped(void *out, const void *query, const void *new_key, const void *new_value,

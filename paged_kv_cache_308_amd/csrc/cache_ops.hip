@@ -349,7 +349,7 @@ int launch_group_plan(const DecodeArgs &a) {
     hipLaunchKernelGGL(group_plan_kernel, dim3((unsigned)a.num_seqs), dim3(64), 0, (hipStream_t)a.stream,
                        a.block_tables, a.context_lens, a.group_start, a.group_parts, a.seq_group, a.seq_parts,
                        a.num_seqs, a.num_groups, a.max_blocks_per_seq, __builtin_ctz(a.block_size), a.num_blocks,
-                       a.partition_size, a.group_rows, a.max_group_parts);
+                       a.group_span, a.group_rows, a.max_group_parts);
     return check_launch("group_plan");
 }
 

@@ -620,11 +620,10 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_balanced_kernel(
 // ([cpai] §6: forked sequences share their prompt's blocks); the workgroup reads the K/V
 // tiles of the group's shared partitions once for all members, whose queries (one query
 // head per KV head) fill the rows of the score product, and writes each served member's
-// partial for the whole shared span into its partition 0 slot and empty partials (max
-// -inf, sums 0) into the slots of its other shared partitions, which the partitioned
-// vector kernel leaves alone and the log-sum-exp merge then weighs 0.  Which members
-// the pass serves was decided by group_plan_kernel: seq_group[s] == j (then
-// seq_parts[s] == group_parts[j]).
+// partial (max, sum, weighted value sums) for the whole shared span at (sequence, head)
+// of ws_max / ws_sum / ws_acc, which the one-pass vector kernel folds into its own state
+// for the member's later tokens.  Which members the pass serves was decided by
+// group_plan_kernel: seq_group[s] == j (then seq_parts[s] == group_parts[j]).
 template <typename T, int D, int G, bool NT>
 __global__ __launch_bounds__(MW * 64) void decode_mfma_grouped_kernel(
     const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
@@ -632,8 +631,8 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_grouped_kernel(
     const int32_t *__restrict__ group_start, const int32_t *__restrict__ group_parts,
     const int32_t *__restrict__ seq_group, const int32_t *__restrict__ seq_parts, float *__restrict__ ws_max,
     float *__restrict__ ws_sum, float *__restrict__ ws_acc, int max_blocks_per_seq, int num_seqs,
-    int num_kv_heads, int log2_block, int num_blocks, int partition_size, int max_partitions,
-    int max_group_parts, float scale_log2) {
+    int num_kv_heads, int log2_block, int num_blocks, int partition_size, int max_group_parts,
+    float scale_log2) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kvh = blockIdx.x % num_kv_heads;
@@ -658,24 +657,9 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_grouped_kernel(
                               block_tables + (int64_t)s0 * max_blocks_per_seq, max_blocks_per_seq, s0, kvh,
                               num_kv_heads, log2_block, num_blocks, 0, parts * partition_size, scale_log2, wave,
                               lane, nullptr, nullptr, nullptr, nullptr, rows);
-    // member i's partial: (sequence s0 + i, head kvh, partition 0) ...
-    const int64_t stride = (int64_t)num_kv_heads * max_partitions;
-    const int64_t idx0 = ((int64_t)s0 * num_kv_heads + kvh) * max_partitions;
-    finish<T, D, G>(st, lds, &sm_bad, wave, lane, nullptr, 0, ws_max, ws_sum, ws_acc, idx0, stride, rows);
-    // ... and empty partials in its partitions 1 .. parts - 1
-    for (int t = threadIdx.x; t < G * (parts - 1) * D; t += MW * 64) {
-        const int i = t / ((parts - 1) * D);
-        const int r = t - i * (parts - 1) * D;
-        const int p = 1 + r / D;
-        const int e = r - (p - 1) * D;
-        if (!((rows >> i) & 1u)) continue;
-        const int64_t pi = idx0 + i * stride + p;
-        if (e == 0) {
-            ws_max[pi] = -INFINITY;
-            ws_sum[pi] = 0.f;
-        }
-        ws_acc[pi * D + e] = 0.f;
-    }
+    // member i's partial at (sequence s0 + i, head kvh)
+    finish<T, D, G>(st, lds, &sm_bad, wave, lane, nullptr, 0, ws_max, ws_sum, ws_acc,
+                    (int64_t)s0 * num_kv_heads + kvh, num_kv_heads, rows);
 }
 
 template <typename T, int D, int G>
@@ -686,7 +670,7 @@ int launch_grouped_t(const DecodeArgs &a) {
                        (const uint8_t *)a.key_cache, (const uint8_t *)a.value_cache, a.block_tables,
                        a.group_start, a.group_parts, a.seq_group, a.seq_parts, a.ws_max, a.ws_sum, a.ws_acc,
                        a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads, __builtin_ctz(a.block_size),
-                       a.num_blocks, a.partition_size, a.max_partitions, a.max_group_parts, a.scale_log2);
+                       a.num_blocks, a.group_span, a.max_group_parts, a.scale_log2);
     return check_launch("decode_mfma_grouped");
 }
 

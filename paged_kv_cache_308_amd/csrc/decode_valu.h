@@ -336,9 +336,16 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     if (SPLIT) {
         start = part * partition_size;
         if (ctx < 0 || start >= ctx) return;  // nothing here (the merge handles bad lengths)
-        // leading partitions a shared-prefix pass already wrote (pa_decode_grouped)
-        if (skip_parts != nullptr && part < skip_parts[s]) return;
         end = min(ctx, start + partition_size);
+    }
+    // One pass after a shared-prefix pass (pa_decode_grouped): that pass attended to the
+    // first skip_parts[s] spans of partition_size tokens of this sequence and left its
+    // partial in ws_max / ws_sum / ws_acc at (s, query head); this workgroup starts after
+    // them and folds the partial in at the end.  The plan guarantees start <= ctx - 1.
+    int prefix_spans = 0;
+    if (!SPLIT && skip_parts != nullptr) {
+        prefix_spans = __builtin_amdgcn_readfirstlane(skip_parts[s]);
+        if (prefix_spans > 0) start = prefix_spans * partition_size;
     }
 
     const int block_size = 1 << log2_block;
@@ -571,9 +578,20 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     for (int t = threadIdx.x; t < G * D; t += NWG * 64) {
         const int g = t / D;
         const int j = t - g * D;
+        const int h = kvh * G + g;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NWG; ++w) M = fmaxf(M, sm_m[w][g]);
+        float m0 = -INFINITY, l0 = 0.f, a0 = 0.f;  // the shared-prefix partial, if any
+        bool bad0 = false;
+        if (!SPLIT && prefix_spans > 0) {
+            const int64_t pi = (int64_t)s * num_q_heads + h;
+            m0 = ws_max[pi];
+            l0 = ws_sum[pi];
+            a0 = ws_acc[pi * D + j];
+            bad0 = m0 != m0;
+            M = fmaxf(M, m0);
+        }
         const float Ms = M == -INFINITY ? 0.f : M;
         float Lsum = 0.f, A = 0.f;
 #pragma unroll
@@ -582,7 +600,11 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
             Lsum += sm_l[w][g] * f;
             A += sm_acc[w][g][j] * f;
         }
-        const int h = kvh * G + g;
+        if (!SPLIT && prefix_spans > 0 && !bad0) {
+            const float f = fast_exp2(m0 - Ms);
+            Lsum += l0 * f;
+            A += a0 * f;
+        }
         if (SPLIT) {
             const int64_t pi = ((int64_t)s * num_q_heads + h) * max_partitions + part;
             if (j == 0) {
@@ -592,7 +614,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
             ws_acc[pi * D + j] = A;
         } else {
             float o = Lsum > 0.f ? A / Lsum : 0.f;
-            if (any_bad) o = NAN;
+            if (any_bad || bad0) o = NAN;
             store_out<T>(out, ((int64_t)s * num_q_heads + h) * D + j, o);
         }
     }
@@ -912,7 +934,7 @@ int launch_t(const DecodeArgs &a) {
                            a.context_lens, a.ws_max, a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs,
                            a.num_kv_heads, log2b, a.num_blocks, a.partition_size, a.max_partitions,
                            a.scale_log2, (const uint8_t *)a.new_key, (const uint8_t *)a.new_value,
-                           (uint8_t *)a.key_out, (uint8_t *)a.value_out, a.skip_parts);
+                           (uint8_t *)a.key_out, (uint8_t *)a.value_out, nullptr);
         const int rc = check_launch("decode_valu (partitions)");
         if (rc != PA_OK) return rc;
         return launch_lse_merge(a);
@@ -921,9 +943,10 @@ int launch_t(const DecodeArgs &a) {
                        dim3(waves_per_group<KV, G>() * 64), 0, st,
                        a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
                        (const uint8_t *)a.value_cache, a.k_scales, a.v_scales, a.block_tables,
-                       a.context_lens, nullptr, nullptr, nullptr, a.max_blocks_per_seq, a.num_seqs,
-                       a.num_kv_heads, log2b, a.num_blocks, 0, 1, a.scale_log2, (const uint8_t *)a.new_key,
-                       (const uint8_t *)a.new_value, (uint8_t *)a.key_out, (uint8_t *)a.value_out, nullptr);
+                       a.context_lens, a.ws_max, a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs,
+                       a.num_kv_heads, log2b, a.num_blocks, a.group_span, 1, a.scale_log2,
+                       (const uint8_t *)a.new_key, (const uint8_t *)a.new_value, (uint8_t *)a.key_out,
+                       (uint8_t *)a.value_out, a.skip_parts);
     return check_launch("decode_valu");
 }
 

@@ -53,13 +53,14 @@ struct DecodeArgs {
     int max_query_len;           // bound on query_start[s + 1] - query_start[s]
     // shared-prefix groups (pa_decode_grouped)
     const int32_t *group_start;  // [num_groups + 1]: group j is sequences group_start[j] ..
-    const int32_t *group_parts;  // [num_groups]: leading partitions its members share
+    const int32_t *group_parts;  // [num_groups]: leading spans its members share
     int32_t *seq_group;          // workspace [S]: group serving sequence s (-1: none)
-    int32_t *seq_parts;          // workspace [S]: leading partitions served by its group
-    const int32_t *skip_parts;   // for the partitioned vector kernel: partitions already done
+    int32_t *seq_parts;          // workspace [S]: leading spans served by its group
+    const int32_t *skip_parts;   // for the one-pass vector kernel: spans already attended
     int num_groups;
     int max_group_parts;         // bound on group_parts[j] (grid extent)
     int group_rows;              // rows of the grouped score product: 2, 4, 8 or 16
+    int group_span;              // tokens per shared span (0 outside pa_decode_grouped)
     void *stream;
 };
 
@@ -70,6 +71,10 @@ size_t workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_par
 size_t workspace_layout_balanced(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                  int max_workers, void *ws, int32_t **hdr, float **m, float **l,
                                  float **acc);
+// pa_decode_grouped: one shared-prefix partial per (sequence, query head), then the plan's
+// seq_group and seq_parts (pointers set in *a when ws is given); returns bytes needed.
+struct DecodeArgs;
+size_t grouped_workspace_layout(int num_seqs, int num_q_heads, int head_dim, void *ws, DecodeArgs *a);
 // Most waves the current device can hold at once (0 if unknown).
 int device_max_waves();
 constexpr int kBalancedMaxSeqs = 4096;
