@@ -270,9 +270,16 @@ __device__ inline void merge_rows(float (&m)[G], float (&l)[G], float (&acc)[G][
 #ifndef PA_FP8_WAVES_PER_EU
 #define PA_FP8_WAVES_PER_EU 1
 #endif
-template <typename KV, int G>
+// Pools in the query's type: 4-wave workgroups for one pass (4 per CU at 115 registers),
+// 8 for partitions.  Measured: llama-7B-shaped batches 122.4 against 123.0 us with 8 waves
+// in one pass; the private tokens of grouped shared-prefix batches (items of ~140 tokens)
+// 99 against 107 us per step; partitions of 512 tokens 306 against 309 us with 8 waves.
+#ifndef PA_VALU_WAVES_ONE_PASS
+#define PA_VALU_WAVES_ONE_PASS 4
+#endif
+template <typename KV, int G, bool SPLIT>
 constexpr int waves_per_group() {
-    return KV::scaled ? PA_FP8_WAVES : NW;
+    return KV::scaled ? PA_FP8_WAVES : (SPLIT ? NW : PA_VALU_WAVES_ONE_PASS);
 }
 // Waves per SIMD the register allocation must allow (1 = no constraint).
 template <typename KV, int G>
@@ -281,7 +288,7 @@ constexpr int min_waves_per_eu() {
 }
 
 template <typename KV, int D, int G, bool SPLIT, bool NT>
-__global__ __launch_bounds__((waves_per_group<KV, G>() * 64))
+__global__ __launch_bounds__((waves_per_group<KV, G, SPLIT>() * 64))
 __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu_kernel(
     void *__restrict__ out, const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
     const uint8_t *__restrict__ value_cache, const float *__restrict__ k_scales,
@@ -292,7 +299,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     const uint8_t *__restrict__ new_key, const uint8_t *__restrict__ new_value, uint8_t *key_out,
     uint8_t *value_out, const int32_t *__restrict__ skip_parts) {
     using T = typename KV::Q;
-    constexpr int NWG = waves_per_group<KV, G>();
+    constexpr int NWG = waves_per_group<KV, G, SPLIT>();
     constexpr int QB = T::bytes;            // query / output element bytes
     constexpr int EPL = KV::epl;            // elements per lane per row
     constexpr int SB = KV::slice_bytes;
@@ -928,7 +935,7 @@ int launch_t(const DecodeArgs &a) {
     hipStream_t st = (hipStream_t)a.stream;
     if (split) {
         hipLaunchKernelGGL((decode_valu_kernel<KV, D, G, true, NT>), dim3(grid),
-                           dim3(waves_per_group<KV, G>() * 64), 0, st,
+                           dim3(waves_per_group<KV, G, true>() * 64), 0, st,
                            a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
                            (const uint8_t *)a.value_cache, a.k_scales, a.v_scales, a.block_tables,
                            a.context_lens, a.ws_max, a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs,
@@ -940,7 +947,7 @@ int launch_t(const DecodeArgs &a) {
         return launch_lse_merge(a);
     }
     hipLaunchKernelGGL((decode_valu_kernel<KV, D, G, false, NT>), dim3(grid),
-                       dim3(waves_per_group<KV, G>() * 64), 0, st,
+                       dim3(waves_per_group<KV, G, false>() * 64), 0, st,
                        a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
                        (const uint8_t *)a.value_cache, a.k_scales, a.v_scales, a.block_tables,
                        a.context_lens, a.ws_max, a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs,

@@ -308,11 +308,11 @@ def test_bad_table_entry_gives_nan_for_that_sequence_only(P, kernel):
         assert bits(got[0]) == bits(clean[0]) and bits(got[2]) == bits(clean[2])
 
 
-@pytest.mark.parametrize("S", [1, 2, 63, 64, 65, 300, 512, 513, 700])
+@pytest.mark.parametrize("S", [1, 2, 63, 64, 65, 256, 257, 300, 512, 513, 700])
 def test_one_pass_batch_sizes_and_longest_first_order(S):
     """The one-pass vector kernel runs sequences longest first (a sort of the lengths
-    inside every workgroup: one wave up to 64 sequences, the whole workgroup up to 512,
-    index order beyond).  Outputs must not depend on it: every row against the oracle,
+    inside every workgroup: one wave up to 64 sequences, the whole 4-wave workgroup up
+    to 256, index order beyond; f32 pools too).  Outputs must not depend on it: every row against the oracle,
     many equal lengths (ties), and a negative length (NaN for that sequence only)."""
     rng = np.random.default_rng(100 + S)
     lens = rng.integers(0, 49, S)
