@@ -207,3 +207,23 @@ def test_grouped_equals_partitioned_decode_closely():
                  torch.from_numpy(c.ctx).cuda(), c.scale, max_context_len=mc, partition_size=P, workspace=ws)
     torch.cuda.synchronize()
     assert np.max(np.abs(f64(got) - f64(ref))) <= TOL
+
+
+def test_grouped_bad_private_entry_gives_nan_for_that_member_only():
+    """A table entry outside the pool among one member's own tokens: that sequence's
+    output is NaN, its group's other members and everyone else are unaffected."""
+    H, d, B, dt, P = 2, 128, 16, "f16", 64
+    rng = np.random.default_rng(53)
+    c = GroupCase(rng, GROUPS, H, d, B, dt)
+    gs, gp, gmax, pmax = prefix_groups(c.tables, c.ctx, B, P)
+    clean, _, _ = run_grouped(c, P, gs, gp, gmax, pmax, append=False)
+    s_bad = 2  # group 0's third member; its own blocks start after the shared ones
+    k = int(c.ctx[s_bad] - 1) // B
+    assert k >= gp[0] * P // B
+    t = c.tables.copy()
+    t[s_bad, k] = c.num_blocks + 7
+    say("[gpu] grouped: bad private entry")
+    got, _, _ = run_grouped(c, P, gs, gp, gmax, pmax, append=False, tables=t)
+    assert torch.isnan(got[s_bad]).all()
+    keep = torch.arange(len(c.ctx), device="cuda") != s_bad
+    assert bits(got[keep]) == bits(clean[keep])
