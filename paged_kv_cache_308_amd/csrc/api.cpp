@@ -229,8 +229,8 @@ static int decode_common(DecodeArgs &a, int max_context_len, float scale, int va
         if (a.max_group_parts < 0 || (int64_t)a.max_group_parts * partition_size > max_context_len)
             return fail(PA_ERR_INVALID, "max_group_parts %d with partitions of %d and max_context_len %d",
                         a.max_group_parts, partition_size, max_context_len);
-        if (a.max_group_parts > 0 && (int64_t)a.num_groups * num_kv_heads * a.max_group_parts > INT32_MAX)
-            return fail(PA_ERR_UNSUPPORTED, "too many group partitions");
+        if ((int64_t)a.num_groups * num_kv_heads > INT32_MAX)  // one workgroup per (group, KV head)
+            return fail(PA_ERR_UNSUPPORTED, "too many groups");
         a.group_rows = a.group_rows <= 2 ? 2 : a.group_rows <= 4 ? 4 : a.group_rows <= 8 ? 8 : 16;
     }
     const bool mfma_ok = !a.kv_fp8 && mfma_supported(dtype, head_dim, block_size, group);
