@@ -340,6 +340,14 @@ int pa_check_copy_pairs(const int32_t *src, const int32_t *dst, int num_pairs, i
  */
 typedef struct pa_allocator pa_allocator;
 
+/* Pool figures for monitoring.  The rates are those "vLLM PagedAttention 技术深度解析"
+ * (kwkr.cn) §1.4.1 names, with the paged pool's quantities: blocks in use over all
+ * blocks; shared blocks over all blocks; memory that is free but unusable over all
+ * memory, where in a paged pool any free block serves any request, so the unusable part
+ * is the allocated slots no token fills (the tails of last blocks); and the effective
+ * memory utilisation of the "PagedAttention" concept report (compassingai.com) §7:
+ * KV that requests need over KV allocated to them, here stored tokens over the slots of
+ * the blocks in use (a shared block counted once; 0 with no block in use). */
 typedef struct pa_alloc_stats {
     int64_t total_blocks;
     int64_t used_blocks;    /* reference count > 0 */
@@ -349,6 +357,10 @@ typedef struct pa_alloc_stats {
     int64_t logical_tokens; /* sum of context lengths */
     int64_t stored_tokens;  /* filled slots, counting a shared block once */
     int64_t wasted_slots;   /* used_blocks * B - stored_tokens */
+    double block_utilisation;  /* used_blocks / total_blocks */
+    double sharing_rate;       /* shared_blocks / total_blocks */
+    double fragmentation_rate; /* wasted_slots / (total_blocks * B) */
+    double emu;                /* stored_tokens / (used_blocks * B) */
 } pa_alloc_stats;
 
 int pa_alloc_create(int num_blocks, int block_size, pa_allocator **out);
@@ -368,8 +380,12 @@ int pa_alloc_append_slot(pa_allocator *a, int64_t seq, int32_t *slot, int32_t *c
                          int32_t *cow_dst);
 /*
  * n appends in order (seqs[i] may repeat).  slots[i] receives each slot; the copies
- * raised are written to cow_src/cow_dst (capacity n) and counted in *num_cow.  Stops at
- * the first failure; *num_done (may be NULL) = appends that succeeded.
+ * raised are written to cow_src/cow_dst (capacity n) and counted in *num_cow.  All or
+ * nothing ([cpai] §13: running work stays untouched by an out-of-memory error): when an
+ * append fails (PA_ERR_OOM, or PA_ERR_INVALID for an unknown sequence) the appends
+ * before it are taken back, the allocator is left exactly as before the call (free
+ * stack order included), *num_cow and *num_done are 0 and pa_last_error names the
+ * failing append.  On success *num_done (may be NULL) = n.
  */
 int pa_alloc_append_slots(pa_allocator *a, const int64_t *seqs, int n, int32_t *slots,
                           int32_t *cow_src, int32_t *cow_dst, int *num_cow, int *num_done);

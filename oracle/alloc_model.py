@@ -20,7 +20,8 @@ What the pages fix:
 Readings (pages silent): the free list is a LIFO stack whose pops initially return
 0, 1, 2, ... (or a given order); blocks released by free_seq are pushed in table
 order; copy-on-write copies the whole block and moves the writer to the copy; the
-last holder writes in place; an out-of-memory append changes nothing.
+last holder writes in place; an out-of-memory append changes nothing, and a batch of
+appends that runs out part-way changes nothing either (append_slots).
 """
 from __future__ import annotations
 
@@ -93,6 +94,24 @@ class ModelAllocator:
         self.ctx[sid] = n + 1
         return last * B + n % B, None
 
+    def append_slots(self, sids) -> Tuple[List[int], List[Tuple[int, int]]]:
+        """Appends in order, all or nothing: if one runs out of blocks (or names an
+        unknown sequence) the allocator is restored to its state before the call, free
+        list order included, and the error is raised."""
+        saved = (list(self.free), list(self.ref), {k: list(v) for k, v in self.tables.items()},
+                 dict(self.ctx))
+        slots, cow = [], []
+        try:
+            for sid in sids:
+                slot, c = self.append_slot(sid)
+                slots.append(slot)
+                if c is not None:
+                    cow.append(c)
+        except (OutOfBlocks, InvalidOp):
+            self.free, self.ref, self.tables, self.ctx = saved
+            raise
+        return slots, cow
+
     def adopt(self, num_tokens: int):
         """A sequence of num_tokens tokens on fresh blocks (the receiving end of a swap)."""
         n = -(-num_tokens // self.block_size)
@@ -143,6 +162,7 @@ class ModelAllocator:
             for j, b in enumerate(table):
                 fill[b] = max(fill[b], min(B, n - j * B))
         stored = sum(fill)
+        wasted = used * B - stored
         return {
             "total_blocks": self.num_blocks,
             "used_blocks": used,
@@ -151,5 +171,13 @@ class ModelAllocator:
             "num_seqs": len(self.tables),
             "logical_tokens": sum(self.ctx.values()),
             "stored_tokens": stored,
-            "wasted_slots": used * B - stored,
+            "wasted_slots": wasted,
+            # kwkr.cn §1.4.1: blocks in use / all blocks; shared blocks / all blocks;
+            # free-but-unusable memory / all memory (in a paged pool every free block is
+            # usable, so the unusable part is the allocated slots no token fills)
+            "block_utilisation": used / self.num_blocks,
+            "sharing_rate": shared / self.num_blocks,
+            "fragmentation_rate": wasted / (self.num_blocks * B),
+            # compassingai.com §7: KV the requests need / KV allocated to them
+            "emu": stored / (used * B) if used else 0.0,
         }

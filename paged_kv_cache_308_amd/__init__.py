@@ -47,7 +47,8 @@ class PaError(RuntimeError):
 class _Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "total_blocks", "used_blocks", "free_blocks", "shared_blocks", "num_seqs",
-        "logical_tokens", "stored_tokens", "wasted_slots")]
+        "logical_tokens", "stored_tokens", "wasted_slots")] + [(n, ctypes.c_double) for n in (
+        "block_utilisation", "sharing_rate", "fragmentation_rate", "emu")]
 
 
 _L = None
@@ -500,7 +501,8 @@ class Allocator:
         return slot.value, ((cs.value, cd.value) if cs.value >= 0 else None)
 
     def append_slots(self, seqs):
-        """Appends in order; returns (slots int32 [n], cow_src int32 [k], cow_dst int32 [k])."""
+        """Appends in order, all or nothing (a failure leaves the allocator as it was);
+        returns (slots int32 [n], cow_src int32 [k], cow_dst int32 [k])."""
         s = np.ascontiguousarray(np.asarray(seqs), dtype=np.int64)
         n = len(s)
         slots = np.empty(n, np.int32)
@@ -510,7 +512,7 @@ class Allocator:
         rc = _lib().pa_alloc_append_slots(
             self._h, s.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, _p32(slots), _p32(cs),
             _p32(cd), ctypes.byref(ncow), ctypes.byref(done))
-        _check(rc, f"pa_alloc_append_slots (done {done.value} of {n})")
+        _check(rc, "pa_alloc_append_slots")
         return slots, cs[:ncow.value].copy(), cd[:ncow.value].copy()
 
     def adopt(self, num_tokens: int):

@@ -9,7 +9,9 @@
 // pool is an explicit out-of-memory error that leaves running work untouched.
 //
 // Every operation is O(1) except fork/free/table export (O(table length)) and the
-// statistics (O(blocks in use)).  One mutex per allocator serialises callers.
+// statistics (O(blocks in use)).  One mutex per allocator serialises callers.  A batch
+// of appends is all or nothing: each append records what it changed, and a failure
+// part-way undoes the earlier ones in reverse order (free stack order included).
 #include <algorithm>
 #include <mutex>
 #include <new>
@@ -38,8 +40,16 @@ struct pa_allocator {
         return b;
     }
 
-    // One append; caller holds the mutex.
-    int append(int64_t sid, int32_t *slot, int32_t *cow_src, int32_t *cow_dst) {
+    // What one append changed, enough to undo it: the sequence, whether it pushed a
+    // fresh block onto its table, and the block a copy-on-write replaced (-1: none).
+    struct Undo {
+        Seq *seq;
+        bool pushed;
+        int32_t replaced;
+    };
+
+    // One append; caller holds the mutex.  With `undo`, records the change.
+    int append(int64_t sid, int32_t *slot, int32_t *cow_src, int32_t *cow_dst, Undo *undo = nullptr) {
         auto it = seqs.find(sid);
         if (it == seqs.end()) return pa::fail(PA_ERR_INVALID, "unknown sequence %lld", (long long)sid);
         Seq &s = it->second;
@@ -47,11 +57,13 @@ struct pa_allocator {
         const int32_t off = s.ctx % B;
         *cow_src = -1;
         *cow_dst = -1;
+        if (undo) *undo = Undo{&s, false, -1};
         if (off == 0) {
             if (free_stack.empty()) return pa::fail(PA_ERR_OOM, "no free block for sequence %lld", (long long)sid);
             const int32_t b = pop();
             s.table.push_back(b);
             *slot = b * B;
+            if (undo) undo->pushed = true;
         } else {
             const int32_t last = s.table.back();
             if (refs[last] > 1) {
@@ -62,12 +74,32 @@ struct pa_allocator {
                 *cow_src = last;
                 *cow_dst = b;
                 *slot = b * B + off;
+                if (undo) undo->replaced = last;
             } else {
                 *slot = last * B + off;
             }
         }
         s.ctx += 1;
         return PA_OK;
+    }
+
+    // Reverse one recorded append (appends are undone newest first, so every block
+    // returns to the free stack at the position it was popped from).
+    void revert(const Undo &u) {
+        Seq &s = *u.seq;
+        s.ctx -= 1;
+        if (u.pushed) {
+            const int32_t b = s.table.back();
+            s.table.pop_back();
+            refs[b] = 0;
+            free_stack.push_back(b);
+        } else if (u.replaced >= 0) {
+            const int32_t b = s.table.back();
+            s.table.back() = u.replaced;
+            refs[u.replaced] += 1;
+            refs[b] = 0;
+            free_stack.push_back(b);
+        }
     }
 };
 
@@ -132,13 +164,21 @@ int pa_alloc_append_slots(pa_allocator *a, const int64_t *seqs, int n, int32_t *
     if (!a || n < 0 || (n && (!seqs || !slots || !cow_src || !cow_dst)) || !num_cow)
         return pa::fail(PA_ERR_INVALID, "NULL argument or n < 0");
     std::lock_guard<std::mutex> g(a->mu);
+    std::vector<pa_allocator::Undo> undo;
+    try {
+        undo.resize((size_t)n);
+    } catch (const std::bad_alloc &) {
+        return pa::fail(PA_ERR_OOM, "host allocation failed");
+    }
     int ncow = 0;
     for (int i = 0; i < n; ++i) {
         int32_t s, cs, cd;
-        const int rc = a->append(seqs[i], &s, &cs, &cd);
+        const int rc = a->append(seqs[i], &s, &cs, &cd, &undo[(size_t)i]);
         if (rc != PA_OK) {
-            *num_cow = ncow;
-            if (num_done) *num_done = i;
+            // all or nothing: take back appends 0 .. i-1, newest first
+            for (int j = i - 1; j >= 0; --j) a->revert(undo[(size_t)j]);
+            pa::fail(rc, "append %d of %d (sequence %lld): %s; no append kept", i, n, (long long)seqs[i],
+                     rc == PA_ERR_OOM ? "no free block" : "unknown sequence");
             return rc;
         }
         slots[i] = s;
@@ -266,6 +306,14 @@ int pa_alloc_get_stats(pa_allocator *a, pa_alloc_stats *out) {
     }
     for (const auto &kv : fill) s.stored_tokens += kv.second;
     s.wasted_slots = s.used_blocks * B - s.stored_tokens;
+    // kwkr.cn §1.4.1 monitoring figures and compassingai.com §7 EMU (ratios of the
+    // counts above, each 0 when its denominator is)
+    const double slots_total = (double)s.total_blocks * B;
+    const double slots_used = (double)s.used_blocks * B;
+    s.block_utilisation = (double)s.used_blocks / (double)s.total_blocks;
+    s.sharing_rate = (double)s.shared_blocks / (double)s.total_blocks;
+    s.fragmentation_rate = (double)s.wasted_slots / slots_total;
+    s.emu = s.used_blocks > 0 ? (double)s.stored_tokens / slots_used : 0.0;
     *out = s;
     return PA_OK;
 }

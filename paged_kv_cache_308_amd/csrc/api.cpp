@@ -150,7 +150,7 @@ const char *pa_status_str(int status) {
 
 const char *pa_last_error(void) { return g_err; }
 
-int pa_abi_version(void) { return 3; }
+int pa_abi_version(void) { return 4; }
 
 static int max_partitions_for(int max_context_len, int partition_size) {
     if (partition_size == 0) return 1;

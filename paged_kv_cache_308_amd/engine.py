@@ -79,6 +79,57 @@ def prefix_groups(host_tables: np.ndarray, context_lens: np.ndarray, block_size:
     return start, gp, int(np.max(np.diff(start))) if S else 1, int(gp.max()) if len(gp) else 0
 
 
+class StepUploader:
+    """Host -> device upload of a decode step's index data: the newest tokens' slots
+    (int32 [S]), the block tables (int32 [S][max_blocks]) and the context lengths
+    (int32 [S]) ("PagedAttention" concept report (compassingai.com) §5: the tables are
+    plain integer arrays handed to the kernel).
+
+    The arrays are packed into one pinned host staging buffer and copied into one device
+    buffer with a single asynchronous copy on the caller's stream, so the step's kernels,
+    queued after it on that stream, see them without a host synchronisation.  `depth`
+    stagings (pinned and device) are used in turn; before a staging is packed again the
+    host waits for the event recorded after its previous copy, so a copy still in flight
+    never reads a half-written staging, and the device views a call returned stay valid
+    until `depth` - 1 further uploads have been made.  Buffers are allocated once, for
+    up to max_seqs sequences of max_blocks_per_seq table entries."""
+
+    def __init__(self, max_seqs: int, max_blocks_per_seq: int, device="cuda", depth: int = 2):
+        import torch as _t
+        self.max_seqs, self.max_blocks = int(max_seqs), int(max_blocks_per_seq)
+        n = 2 * self.max_seqs + self.max_seqs * self.max_blocks
+        self._host = [_t.empty(n, dtype=_t.int32, pin_memory=True) for _ in range(depth)]
+        self._dev = [_t.empty(n, dtype=_t.int32, device=device) for _ in range(depth)]
+        self._done = [None] * depth
+        self._next = 0
+
+    def upload(self, slots, block_tables, context_lens, stream=None):
+        """Returns device int32 views (slots [S], block_tables [S][mb], context_lens [S])
+        whose contents arrive in stream order."""
+        import torch as _t
+        tb = np.asarray(block_tables, np.int32)
+        S, mb = tb.shape
+        if S > self.max_seqs or mb > self.max_blocks:
+            raise ValueError(f"{S} sequences of {mb} blocks exceed the uploader's {self.max_seqs} x {self.max_blocks}")
+        st = stream if stream is not None else _t.cuda.current_stream()
+        i = self._next
+        self._next = (i + 1) % len(self._host)
+        if self._done[i] is not None:
+            self._done[i].synchronize()  # the staging's previous copy has read it
+        h = self._host[i].numpy()
+        n = 2 * S + S * mb
+        h[:S] = np.asarray(slots, np.int32)
+        h[S:2 * S] = np.asarray(context_lens, np.int32)
+        h[2 * S:n] = tb.reshape(-1)
+        d = self._dev[i]
+        with _t.cuda.stream(st):
+            d[:n].copy_(self._host[i][:n], non_blocking=True)
+            ev = _t.cuda.Event()
+            ev.record(st)
+        self._done[i] = ev
+        return d[:S], d[2 * S:n].view(S, mb), d[S:2 * S]
+
+
 class PagedKVCache:
     """Device K/V pools of one layer and the host allocator.  dtype=torch.uint8 holds
     E4M3 codes, with k_scales / v_scales float32 [num_blocks][H_kv] (one per block and

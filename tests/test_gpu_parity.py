@@ -259,17 +259,112 @@ def test_edge_lengths(shape):
             assert bits(got[1]) == bits(v1.repeat_interleave(g, dim=0))
 
 
-@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
-def test_identity_and_permuted_tables_are_bit_identical(dt):
-    lens = [100, 37, 513, 16, 1]
-    outs = []
-    for identity in (True, False):
-        rng = np.random.default_rng(11)
-        c = Case(rng, lens, 8, 2, 128, 16, dt, identity=identity)
+def _relabel(tables, pools, perm):
+    """The same cache with physical block b moved to perm[b]: pools (and per-block
+    arrays) permuted along their first axis, table entries mapped (padding kept)."""
+    t = tables.copy()
+    t[t >= 0] = perm[t[t >= 0]]
+    moved = []
+    for a in pools:
+        m = np.empty_like(a)
+        m[perm] = a
+        moved.append(m)
+    return t, moved
+
+
+def _identity_perm(tables, num_blocks):
+    """A relabelling that makes the tables physically consecutive (block ids in table
+    order: the contiguous layout); blocks no table uses go after them."""
+    used = [int(b) for b in tables.reshape(-1) if b >= 0]
+    perm = np.full(num_blocks, -1, np.int64)
+    nxt = 0
+    for b in used:
+        if perm[b] < 0:
+            perm[b] = nxt
+            nxt += 1
+    for b in range(num_blocks):
+        if perm[b] < 0:
+            perm[b] = nxt
+            nxt += 1
+    return perm
+
+
+@pytest.mark.parametrize("dt,Hq,Hkv,v", [("f32", 8, 2, VALU), ("f16", 8, 2, VALU), ("bf16", 8, 2, VALU),
+                                         ("bf16", 64, 8, MFMA), ("f16", 16, 2, MFMA), ("bf16", 32, 32, VALU)])
+def test_identity_and_permuted_tables_are_bit_identical(dt, Hq, Hkv, v):
+    """Where the blocks sit changes nothing ("PagedAttention" concept report §5: the
+    table maps logical blocks to any physical ones): the same cache laid out
+    contiguously (identity tables) and under a random relabelling of the physical blocks
+    gives bit-identical output on every kernel form (one pass, partitions, balanced
+    split), the matrix-core kernel with 8 query heads per KV head included."""
+    lens = [100, 37, 513, 16, 1, 700, 129]
+    c = Case(np.random.default_rng(11), lens, Hq, Hkv, 128, 16, dt)
+    perm_id = _identity_perm(c.tables, c.num_blocks)
+    perm_rand = np.random.default_rng(12).permutation(c.num_blocks)
+    outs = {}
+    for lay, perm in (("paged", None), ("identity", perm_id), ("relabelled", perm_rand)):
+        t, kc, vc = c.tables, c.kc, c.vc
+        if perm is not None:
+            t, (kc, vc) = _relabel(c.tables, (c.kc, c.vc), perm)
+        if lay == "identity":  # physically consecutive
+            nb = [-(-n // c.B) for n in lens]
+            assert [t[s, :nb[s]].tolist() for s in range(len(lens))] == \
+                [list(range(sum(nb[:s]), sum(nb[:s + 1]))) for s in range(len(lens))]
+        c2 = Case.__new__(Case)
+        c2.__dict__.update(c.__dict__)
+        c2.tables, c2.kc, c2.vc = t, kc, vc
         for P in (0, 64, BAL):
-            say(f"[gpu] identity={identity} {dt} P={P}")
-            outs.append((P, bits(_run_case(c, P, VALU))))
-    assert outs[0] == outs[3] and outs[1] == outs[4] and outs[2] == outs[5]
+            say(f"[gpu] layout {lay} {dt} g={Hq // Hkv} variant={v} P={P}")
+            outs[(lay, P)] = bits(_run_case(c2, P, v))
+    for P in (0, 64, BAL):
+        assert outs[("paged", P)] == outs[("identity", P)] == outs[("relabelled", P)], P
+
+
+def test_fp8_identity_and_permuted_tables_are_bit_identical():
+    """E4M3 pools: moving every block together with its scales leaves the output
+    bit-identical (one pass, partitions, balanced split; 1 and 4 query heads per KV head)."""
+    for Hq, Hkv in ((8, 8), (16, 4)):
+        c = Fp8Case(np.random.default_rng(13), [100, 37, 513, 16, 1, 300], Hq, Hkv, 128, 16, "bf16")
+        perm_id = _identity_perm(c.tables, c.num_blocks)
+        perm_rand = np.random.default_rng(14).permutation(c.num_blocks)
+        res = {}
+        for lay, perm in (("paged", None), ("identity", perm_id), ("relabelled", perm_rand)):
+            arrays = (c.kc, c.vc, c.ks, c.vs)
+            t = c.tables
+            if perm is not None:
+                t, arrays = _relabel(c.tables, arrays, perm)
+            kc, vc, ks, vs = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in arrays)
+            q = to_torch(c.q, "bf16").cuda()
+            bt, cl = torch.from_numpy(t).cuda(), torch.from_numpy(c.ctx).cuda()
+            for P in (0, 64, BAL):
+                out = torch.empty_like(q)
+                ws = None
+                if P:
+                    ws = torch.empty(pa.pa_decode_workspace_bytes(q.shape[0], Hq, Hkv, 128, int(c.ctx.max()), P),
+                                     dtype=torch.uint8, device="cuda")
+                say(f"[gpu] fp8 layout {lay} g={Hq // Hkv} P={P}")
+                pa.pa_decode_fp8(out, q, kc, vc, ks, vs, bt, cl, c.scale, max_context_len=int(c.ctx.max()),
+                                 partition_size=P, workspace=ws)
+                torch.cuda.synchronize()
+                res[(lay, P)] = bits(out)
+        for P in (0, 64, BAL):
+            assert res[("paged", P)] == res[("identity", P)] == res[("relabelled", P)], (Hq, Hkv, P)
+
+
+def test_grouped_decode_identity_and_permuted_layouts_are_bit_identical():
+    """pa_decode_grouped over the same forked batch placed by the allocator from a
+    permuted free list and from the identity free list: bit-identical outputs."""
+    w = SMALL["prefix_f16"]
+    outs = []
+    for identity in (False, True):
+        batch = W.make_batch(w, identity=identity)
+        db = replay(batch)
+        groups = db.groups(w.partition_size)
+        assert groups[1].max() >= 1  # some partitions are shared
+        say(f"[gpu] grouped layout identity={identity}")
+        outs.append(bits(db.step_grouped(w.partition_size, groups, workspace=db.grouped_workspace(w.partition_size))))
+        torch.cuda.synchronize()
+    assert outs[0] == outs[1]
 
 
 def test_shared_kv_hint_changes_nothing_but_the_cache_policy():
@@ -654,90 +749,6 @@ def bits_rows(b: bytes, rows, w) -> bytes:
     return b"".join(b[r * per:(r + 1) * per] for r in rows)
 
 
-# ------------------------------------------------------------ full-size workloads
-
-
-def _sample(ctx: np.ndarray, k: int = 6):
-    order = np.argsort(ctx, kind="stable")
-    pick = {int(order[0]), int(order[-1])}
-    rng = np.random.default_rng(99)
-    for s in rng.permutation(len(ctx)):
-        if len(pick) >= k:
-            break
-        pick.add(int(s))
-    return sorted(pick)
-
-
-def _sub_batch_scales(w, batch, sub, seqs):
-    """Block scales for a sub-batch placed by the oracle in its own pool: each of its
-    blocks takes the scale of the block that holds the same tokens in the full batch."""
-    ks_full, vs_full = W.fp8_scales(w)
-    a_full, sids, _, _ = place.replay(batch)
-    a_sub, sids_sub, _, _ = place.replay(sub)
-    ks, vs = ks_full.copy(), vs_full.copy()
-    for i, s in enumerate(seqs):
-        full_t, _ = a_full.block_table(sids[s])
-        sub_t, _ = a_sub.block_table(sids_sub[i])
-        for fb, sb in zip(full_t, sub_t):
-            ks[sb] = ks_full[fb]
-            vs[sb] = vs_full[fb]
-    return ks, vs
-
-
-FULL_SIZE = [("llama7b", None), ("llama13b_long", None), ("llama70b_gqa", None),
-             ("llama70b_gqa", 0), ("prefix_sharing", None), ("llama7b_fp8", None)]
-
-
-@pytest.mark.parametrize("name,P", FULL_SIZE, ids=lambda x: str(x))
-def test_full_size_sampled(name, P):
-    """Whole batch on the GPU in the benchmark's launch setup (P None: the workload's
-    partition setting); oracle on a sample of sequences (attention does not depend on
-    where blocks sit, so the oracle may place its sub-batch in its own pool)."""
-    w = W.WORKLOADS[name]
-    P = w.partition_size if P is None else P
-    say(f"[gpu] full-size {name}: generating")
-    batch = W.make_batch(w)
-    db = replay(batch)
-    variant = AUTO
-    say(f"[gpu] full-size {name}: step P={P}")
-    got = f64(db.step(partition_size=P, variant=variant))
-    torch.cuda.synchronize()
-    assert np.all(np.isfinite(got))
-    if w.lengths == "prefix":
-        want, p = place.decode_step(batch)
-        assert np.array_equal(db.host_tables, p.block_tables) and len(db.cow_src) == 64
-        err = np.max(np.abs(got - want))
-    else:
-        seqs = _sample(batch.lengths.context_lens)
-        sub = W.make_batch(w, seqs=seqs)
-        scales = _sub_batch_scales(w, batch, sub, seqs) if w.kv == "fp8" else None
-        want, _ = place.decode_step(sub, fp8_scales=scales)
-        err = np.max(np.abs(got[seqs] - want))
-    say(f"[gpu] full-size {name}: max abs err {err:.3e}")
-    assert err <= TOL[w.dtype]
-
-
-def test_full_size_prefix_sharing_grouped():
-    """The prefix-sharing workload through pa_decode_grouped, as the benchmark runs it:
-    16 groups of 5 forks, each sharing its prompt's two whole 512-token partitions;
-    all 80 sequences against the oracle."""
-    w = W.WORKLOADS["prefix_sharing"]
-    say("[gpu] full-size prefix_sharing grouped: generating")
-    batch = W.make_batch(w)
-    db = replay(batch)
-    groups = db.groups(w.partition_size)
-    gs, gp, gmax, pmax = groups
-    assert gs.tolist() == list(range(0, 81, 5)) and gp.tolist() == [2] * 16 and gmax == 5 and pmax == 2
-    say("[gpu] full-size prefix_sharing grouped: step")
-    got = f64(db.step_grouped(w.partition_size, groups, workspace=db.grouped_workspace(w.partition_size)))
-    torch.cuda.synchronize()
-    assert np.all(np.isfinite(got))
-    want, _ = place.decode_step(batch)
-    err = np.max(np.abs(got - want))
-    say(f"[gpu] full-size prefix_sharing grouped: max abs err {err:.3e}")
-    assert err <= TOL[w.dtype]
-
-
 @pytest.mark.parametrize("tile", [1024, 2048, 4096, 8192])
 def test_gather_read_probe_reads_without_writing(tile):
     """pa_gather_read reads the listed tiles (addresses inside one zero buffer, in random
@@ -767,3 +778,47 @@ def test_stream_read_probe_reads_without_writing():
     pa.pa_stream_read(small, sink)
     torch.cuda.synchronize()
     assert sink.tolist() == [7, 7, 7, 7]
+
+
+def test_step_upload_equals_host_arrays():
+    """A step's slots, tables and lengths, packed into pinned staging and copied on the
+    stream (engine.StepUploader), arrive equal to the host arrays; with two stagings the
+    views of the previous upload stay intact while the next one is packed and copied."""
+    from paged_kv_cache_308_amd.engine import StepUploader
+    rng = np.random.default_rng(77)
+    up = StepUploader(64, 300)
+    prev = None
+    for k in range(8):
+        S, mb = int(rng.integers(1, 65)), int(rng.integers(1, 301))
+        tb = rng.integers(-1, 40000, (S, mb)).astype(np.int32)
+        sl = rng.integers(-1, 1 << 20, S).astype(np.int32)
+        cl = rng.integers(0, 4097, S).astype(np.int32)
+        say(f"[gpu] step upload {k}: S={S} max_blocks={mb}")
+        got = up.upload(sl, tb, cl)
+        torch.cuda.synchronize()
+        for g, want in zip(got, (sl, tb, cl)):
+            assert g.is_contiguous() and np.array_equal(g.cpu().numpy(), want)
+        if prev is not None:  # the previous upload's views are still intact
+            for g, want in zip(*prev):
+                assert np.array_equal(g.cpu().numpy(), want)
+        prev = (got, (sl, tb, cl))
+    with pytest.raises(ValueError):
+        up.upload(np.zeros(65, np.int32), np.zeros((65, 1), np.int32), np.zeros(65, np.int32))
+
+
+def test_step_upload_drives_decode():
+    """The allocator's step (slots, tables, lengths) through the pinned upload feeds the
+    decode launch: the result is bit-identical to the same step with the tables uploaded
+    by a plain synchronous copy."""
+    from paged_kv_cache_308_amd.engine import StepUploader
+    w = SMALL["mha_f16"]
+    batch = W.make_batch(w)
+    db = replay(batch)
+    ref = bits(db.step(partition_size=0, variant=VALU))
+    up = StepUploader(w.num_seqs, db.host_tables.shape[1])
+    slots = db.slot_mapping.cpu().numpy()
+    sl, bt, cl = up.upload(slots, db.host_tables, db.host_context_lens)
+    db2 = replay(batch)
+    db2.slot_mapping, db2.block_tables, db2.context_lens = sl, bt, cl
+    say("[gpu] decode through uploaded step data")
+    assert bits(db2.step(partition_size=0, variant=VALU)) == ref

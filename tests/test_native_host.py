@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(pa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert pa.abi_version() == 3
+    assert pa.abi_version() == 4
 
 
 # -------------------------------------------------------------- allocator parity
@@ -60,6 +60,20 @@ def _run_both(num_blocks, B, ops, order=None):
                     assert e.value.status == pa.PA_ERR_OOM
                     break
                 assert nat.append_slot(a) == want
+        elif kind == "batch":
+            # one append for each of the first n live sequences, then for the picked one
+            # again: all or nothing on both sides
+            pairs = [live[i % len(live)] for i in range(n)] + [live[pick % len(live)]]
+            try:
+                want_slots, want_cow = mod.append_slots([b for _, b in pairs])
+            except OutOfBlocks:
+                with pytest.raises(pa.PaError) as e:
+                    nat.append_slots([a for a, _ in pairs])
+                assert e.value.status == pa.PA_ERR_OOM
+            else:
+                slots, cs, cd = nat.append_slots([a for a, _ in pairs])
+                assert slots.tolist() == want_slots
+                assert list(zip(cs.tolist(), cd.tolist())) == want_cow
         elif kind == "fork":
             a, b = live[pick % len(live)]
             live.append((nat.fork(a), mod.fork(b)))
@@ -87,7 +101,7 @@ def _run_both(num_blocks, B, ops, order=None):
 
 
 @settings(max_examples=80, deadline=None)
-@given(st.lists(st.tuples(st.sampled_from(["new", "append", "fork", "free", "adopt"]),
+@given(st.lists(st.tuples(st.sampled_from(["new", "append", "fork", "free", "adopt", "batch"]),
                           st.integers(0, 50), st.integers(1, 12)), max_size=50),
        st.sampled_from([1, 4, 16]), st.booleans())
 def test_native_allocator_matches_model(ops, B, permuted):
@@ -134,8 +148,87 @@ def test_native_out_of_blocks_leaves_state():
     before = (nat.stats(), nat.block_table(s))
     with pytest.raises(pa.PaError) as e:
         nat.append_slots([s, s])
-    assert e.value.status == pa.PA_ERR_OOM and "done 0 of 2" in str(e.value)
+    assert e.value.status == pa.PA_ERR_OOM and "append 0 of 2" in str(e.value)
     assert (nat.stats(), nat.block_table(s)) == before
+
+
+def test_batch_append_out_of_blocks_midway_keeps_nothing():
+    """A batch that runs out of blocks part-way keeps none of its appends ("PagedAttention"
+    concept report §13: an out-of-memory error leaves running work untouched), including
+    a copy-on-write of a shared partly filled block earlier in the batch; the free stack
+    order is restored too, so the next pops are the same blocks."""
+    B = 4
+    for Alloc in (lambda: pa.Allocator(5, B), lambda: ModelAllocator(5, B)):
+        a = Alloc()
+        p = a.new_seq()
+        for _ in range(6):  # blocks 0, 1; block 1 holds 2 of 4 slots
+            a.append_slot(p)
+        c = a.fork(p)  # block 1 shared (count 2), partly filled
+        q = a.new_seq()
+        for _ in range(8):  # blocks 2, 3 (full)
+            a.append_slot(q)
+        # 1 free block left (4).  Batch: p writes into shared block 1 -> copy-on-write
+        # takes block 4; q's next token needs a fresh block -> out of blocks.
+        snap = (a.stats(), a.block_table(p), a.block_table(c), a.block_table(q),
+                [a.refcount(b) for b in range(5)])
+        assert snap[4] == [2, 2, 1, 1, 0]
+        if isinstance(a, ModelAllocator):
+            with pytest.raises(OutOfBlocks):
+                a.append_slots([p, c, q])
+        else:
+            with pytest.raises(pa.PaError) as e:
+                a.append_slots([p, c, q])
+            assert e.value.status == pa.PA_ERR_OOM and "append 2 of 3" in str(e.value)
+        assert snap == (a.stats(), a.block_table(p), a.block_table(c), a.block_table(q),
+                        [a.refcount(b) for b in range(5)])
+        # the pool is as it was: p's write still copies into block 4
+        if isinstance(a, ModelAllocator):
+            assert a.append_slot(p) == (4 * B + 2, (1, 4))
+        else:
+            assert a.append_slot(p) == (4 * B + 2, (1, 4))
+    # an unknown sequence late in a batch also takes the earlier appends back
+    nat = pa.Allocator(4, B)
+    s = nat.new_seq()
+    before = (nat.stats(), nat.block_table(s))
+    with pytest.raises(pa.PaError) as e:
+        nat.append_slots([s, s, 12345])
+    assert e.value.status == pa.PA_ERR_INVALID
+    assert (nat.stats(), nat.block_table(s)) == before
+
+
+def test_monitoring_rates():
+    """kwkr.cn §1.4.1 rates and the compassingai.com §7 EMU from the native allocator,
+    on a hand-counted pool: 10 blocks of 4 slots; sequence a holds 6 tokens (blocks 0, 1),
+    its fork b shares both, then b writes a token (copy-on-write of block 1 into block 2);
+    sequence c holds 1 token (block 3)."""
+    nat = pa.Allocator(10, 4)
+    a = nat.new_seq()
+    nat.append_slots([a] * 6)
+    b = nat.fork(a)
+    nat.append_slot(b)
+    c = nat.new_seq()
+    nat.append_slot(c)
+    st_ = nat.stats()
+    # used blocks 0, 1, 2, 3; shared: block 0 (count 2); stored: 4 + 2 + 3 + 1 = 10
+    assert (st_["used_blocks"], st_["shared_blocks"], st_["stored_tokens"]) == (4, 1, 10)
+    assert st_["block_utilisation"] == 4 / 10
+    assert st_["sharing_rate"] == 1 / 10
+    assert st_["fragmentation_rate"] == 6 / 40
+    assert st_["emu"] == 10 / 16
+    assert st_ == {**ModelAllocator_replay_stats()}
+    empty = pa.Allocator(3, 16).stats()
+    assert empty["emu"] == 0.0 and empty["block_utilisation"] == 0.0
+
+
+def ModelAllocator_replay_stats():
+    m = ModelAllocator(10, 4)
+    a = m.new_seq()
+    m.append_slots([a] * 6)
+    b = m.fork(a)
+    m.append_slot(b)
+    c = m.new_seq()
+    m.append_slot(c)
+    return m.stats()
 
 
 def test_native_invalid_calls():

@@ -128,3 +128,50 @@ def test_fp8_prefix_step_equals_attention_over_dequantised_tokens():
             torch.from_numpy(vq).permute(1, 0, 2)[None].contiguous(), scale=w.scale,
             enable_gqa=g > 1)[0, :, 0].numpy()
     assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+# ------------------------------------------- the full-size tests' threaded oracle
+
+
+@pytest.mark.parametrize("name,changes", [
+    ("llama7b_fp8", dict(num_seqs=9, num_q_heads=8, num_kv_heads=8, num_blocks=1500)),
+    ("prefix_sharing", dict(num_seqs=10, groups=2, samples=5, num_q_heads=4, num_kv_heads=4,
+                            prefix_base=40, private_max=30, num_blocks=200)),
+    ("llama70b_gqa", dict(num_seqs=5, num_q_heads=16, num_kv_heads=2, low=100, high=600,
+                          block_size=16, num_blocks=300)),
+])
+def test_threaded_oracle_equals_plain_oracle(name, changes):
+    """The full-size tests' oracle (its own compact pool, sequences split over threads)
+    gives exactly the plain oracle step in the workload's own pool: the split changes no
+    arithmetic and attention does not depend on where blocks sit (E4M3 scales travel
+    with their tokens)."""
+    import oracle_threads as OT
+    w = W.scaled(W.WORKLOADS[name], **changes)
+    batch = W.make_batch(w)
+    want, _ = place.decode_step(batch)
+    got = OT.decode_step(batch)
+    assert np.array_equal(got, want)
+
+
+def test_threaded_multi_query_rows_equal_the_whole_call():
+    """Rows picked from a chunked-prefill batch through the threaded helper (runs cut into
+    pieces whose context ends at the piece's last row) equal the same rows of one oracle
+    call over the whole batch, bit for bit."""
+    import oracle
+    import oracle_threads as OT
+    w = W.scaled(W.WORKLOADS["chunked_prefill"], num_seqs=3, num_q_heads=4, num_kv_heads=2,
+                 low=80, high=200, query_len=70, num_blocks=64)
+    batch = W.make_batch(w)
+    ctx = batch.lengths.context_lens.astype(np.int64)
+    nq = np.minimum(ctx, w.query_len)
+    qstart = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    qrows = [W.chunk_queries(w, s, int(n)) for s, n in enumerate(nq)]
+    p = OT.compact_place(batch)
+    p.write(p.new_key, p.new_value, p.slot_mapping, w.dtype)
+    whole = oracle.default().multi_query(np.concatenate(qrows), p.key_cache, p.value_cache, p.block_tables,
+                                         p.context_lens, qstart, w.scale, w.dtype)
+    picks = [OT.RowPick(0, np.arange(int(nq[0]))), OT.RowPick(1, np.array([0, 1, 5, 6, 7, 40, int(nq[1]) - 1])),
+             OT.RowPick(2, np.array([3]))]
+    got = OT.multi_query_rows(picks, qrows, p, w, nq)
+    for pk, g in zip(picks, got):
+        assert np.array_equal(g, whole[qstart[pk.seq] + pk.rows])
