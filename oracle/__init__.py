@@ -65,7 +65,8 @@ class Oracle:
     """ctypes view of one compiled oracle library."""
 
     def __init__(self, path: Optional[str] = None):
-        path = path or _LIB
+        # ORACLE_LIBRARY: another build of oracle.c (the sanitizer build of the tests)
+        path = path or os.environ.get("ORACLE_LIBRARY") or _LIB
         if path == _LIB and _needs_build(path):
             build()
         self._lib = ctypes.CDLL(path)

@@ -107,7 +107,11 @@ def _lib():
         "pa_alloc_get_stats": (i32, [vp, ctypes.POINTER(_Stats)]),
     }
     for name, (res, args) in sig.items():
-        f = getattr(L, name)
+        # a host-only build (the sanitizer build of the allocator) lacks the device entry
+        # points: they stay unbound and raise AttributeError when called
+        f = getattr(L, name, None)
+        if f is None:
+            continue
         f.restype = res
         f.argtypes = args
     _L = L

@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "libpa")
 LIB = os.path.join(HERE, "libpa.so")
 
-SOURCES = ["api.cpp", "allocator.cpp", "cache_ops.hip", "decode_valu_f32.hip", "decode_valu_f16.hip",
+SOURCES = ["api.cpp", "host_api.cpp", "allocator.cpp", "cache_ops.hip", "decode_valu_f32.hip", "decode_valu_f16.hip",
            "decode_valu_bf16.hip", "decode_valu_fp8_f16.hip", "decode_valu_fp8_bf16.hip",
            "decode_mfma_f16.hip", "decode_mfma_bf16.hip", "multi_query_mfma_f16.hip",
            "multi_query_mfma_bf16.hip"]
