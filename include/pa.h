@@ -298,6 +298,29 @@ int pa_decode_grouped(void *out, const void *query, const void *new_key, const v
                       size_t workspace_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under graph capture, serving
+ * loops that must not allocate, harnesses that forbid allocation): pa_decode with its
+ * partials (partitions or the balanced split) kept in a fixed device array of the
+ * library instead of a caller workspace.  The call allocates and frees nothing.
+ *
+ * Every GPU the library runs on holds its own copy of that array, PA_NOALLOC_SCRATCH_BYTES
+ * bytes, from the first use of the library on it until the process ends.  A call whose
+ * partials need more (pa_decode_workspace_bytes(...) > PA_NOALLOC_SCRATCH_BYTES) returns
+ * PA_ERR_INVALID before anything is enqueued.  All calls on one GPU share its array and
+ * its contents are whatever the last call left (the kernels write every partial before
+ * reading it, so nothing needs clearing): calls that can overlap on one GPU (several
+ * streams, several host threads) race on it and must be serialised by the caller.
+ * partition_size == 0 uses no scratch.  Arguments, results and errors otherwise as
+ * pa_decode.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int pa_decode_noalloc(void *out, const void *query, const void *key_cache, const void *value_cache,
+                      const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_context_len, float scale, int dtype, int partition_size,
+                      int variant, void *stream);
+
+/*
  * Measurement helper, not part of the attention path: reads `bytes` bytes of device
  * memory at buf once (16-byte non-temporal loads spread over the whole device) and
  * folds them into a value that is stored to *sink (device, 4 bytes) only when it

@@ -23,6 +23,7 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_VARIANT_AUTO, PA_VARIANT_VALU, PA_VARIANT_MFMA = 0, 1, 2
 PA_DECODE_SHARED_KV = 16
 PA_PARTITION_BALANCED = -1
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20  # the fixed device scratch of pa_decode_noalloc
 
 # Every symbol include/pa.h declares (checked by the tests).
 EXPORTS = (
@@ -30,7 +31,7 @@ EXPORTS = (
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_check_tables",
     "pa_reshape_and_cache_fp8", "pa_decode_fp8", "pa_multi_query", "pa_decode_append",
     "pa_decode_fp8_append", "pa_stream_read", "pa_gather_read", "pa_decode_grouped",
-    "pa_decode_grouped_workspace_bytes",
+    "pa_decode_grouped_workspace_bytes", "pa_decode_noalloc",
     "pa_check_copy_pairs", "pa_alloc_adopt",
     "pa_alloc_create", "pa_alloc_destroy", "pa_alloc_set_free_order", "pa_alloc_new_seq",
     "pa_alloc_append_slot", "pa_alloc_append_slots", "pa_alloc_fork", "pa_alloc_free_seq",
@@ -72,6 +73,8 @@ def _lib():
         "pa_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
         "pa_decode": (i32, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                             i32, i32, i32, vp, sz, vp]),
+        "pa_decode_noalloc": (i32, [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                    i32, i32, i32, vp]),
         "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
         "pa_reshape_and_cache_fp8": (i32, [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                            vp]),
@@ -185,6 +188,31 @@ def pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, sc
         int(max_context_len), float(scale), dtype_code(query), int(partition_size), int(variant),
         ws_ptr, ws_bytes, _stream(stream))
     _check(rc, "pa_decode")
+    return out
+
+
+def pa_decode_noalloc(out, query, key_cache, value_cache, block_tables, context_lens, scale: float,
+                      max_context_len: int = 0, partition_size: int = 0, variant: int = PA_VARIANT_AUTO,
+                      stream=None):
+    """pa_decode with its partials in the library's fixed device scratch (no workspace,
+    nothing allocated); calls that may overlap on one GPU must be serialised."""
+    torch = _torch()
+    S, Hq, d = query.shape
+    nb, Hkv, B, d2 = key_cache.shape
+    if d2 != d or value_cache.shape != key_cache.shape or out.shape != query.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables / context_lens shape")
+    for t in (query, key_cache, value_cache, out):
+        if t.dtype != query.dtype:
+            raise ValueError("query, pools and out must share one dtype")
+    rc = _lib().pa_decode_noalloc(
+        _dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, d, B, nb,
+        int(max_context_len), float(scale), dtype_code(query), int(partition_size), int(variant),
+        _stream(stream))
+    _check(rc, "pa_decode_noalloc")
     return out
 
 

@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libpa.so")
 SOURCES = ["api.cpp", "host_api.cpp", "allocator.cpp", "cache_ops.hip", "decode_valu_f32.hip", "decode_valu_f16.hip",
            "decode_valu_bf16.hip", "decode_valu_fp8_f16.hip", "decode_valu_fp8_bf16.hip",
            "decode_mfma_f16.hip", "decode_mfma_bf16.hip", "multi_query_mfma_f16.hip",
-           "multi_query_mfma_bf16.hip"]
+           "multi_query_mfma_bf16.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]

@@ -499,3 +499,13 @@ def test_grouped_decode_rejects_bad_arguments_before_launch():
     # one shared-prefix partial per (sequence, head) plus the plan's two int32 arrays
     assert pa.pa_decode_grouped_workspace_bytes(4, 4, 4, 128, 256, 64) >= 4 * 4 * 130 * 4 + 2 * 16
     assert pa.pa_decode_grouped_workspace_bytes(4, 4, 4, 128, 256, 0) == 0
+
+
+def test_noalloc_rejects_partials_beyond_its_scratch_before_launching():
+    """pa_decode_noalloc refuses a call whose partials exceed its fixed scratch with an
+    argument error, before touching the device (here there is none)."""
+    need = pa.pa_decode_workspace_bytes(4096, 64, 8, 128, 1 << 16, 512)
+    assert need > pa.PA_NOALLOC_SCRATCH_BYTES
+    rc = pa._lib().pa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, 4096, 64, 8, 128, 16, 1 << 20,
+                                     1 << 16, 0.1, pa.PA_F16, 512, 0, None)
+    assert rc == pa.PA_ERR_INVALID and b"fixed scratch" in pa._lib().pa_last_error()
