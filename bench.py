@@ -86,6 +86,10 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--variant", type=int, default=0)
     ap.add_argument("--no-identity", action="store_true")
+    ap.add_argument("--layout", choices=("paged", "identity"), default="paged",
+                    help="physical placement of the timed batch: the allocator's seeded random free order "
+                         "(paged), or every sequence on consecutive blocks (identity; for profiling the "
+                         "contiguous comparison point)")
     ap.add_argument("--unfused", action="store_true",
                     help="store the newest tokens with their own launch even where the attention "
                          "launch can do it")
@@ -543,7 +547,7 @@ def main():
         print(json.dumps(mq_bench(args, w, batch)), flush=True)
         return
     log(args, f"[bench] placing {REPLICAS} replicas")
-    reps = build_replicas(args, w, batch, identity=False)
+    reps = build_replicas(args, w, batch, identity=args.layout == "identity")
     # tokens held in the pool (a block shared by several sequences counts once)
     ab = algorithmic_bytes(w, ctx, reps[0][0].cache.alloc.stats()["stored_tokens"])
     args.fused = args.grouped or (not args.unfused and
@@ -565,14 +569,17 @@ def main():
     gather = None if args.no_stream else gather_read_gbs(w, reps)
     upload = upload_cost(w, reps[0][0])
 
-    ident = None
-    if not args.no_identity:
+    ident = ident_gather = None
+    if not args.no_identity and args.layout == "paged":
         del reps
         torch.cuda.empty_cache()
         reps_i = build_replicas(args, w, batch, identity=True)
         run_steps(args, reps_i, args.warmup, record=False)
         _, dec_i, _ = run_steps(args, reps_i, args.steps, record=True)
         ident = float(np.mean(dec_i))
+        # the same read probe over the identity layout's tiles: separates the memory
+        # system's response to the address pattern from the kernel's
+        ident_gather = None if args.no_stream else gather_read_gbs(w, reps_i)
         del reps_i
         torch.cuda.empty_cache()
         log(args, f"[bench] identity layout decode {ident * 1e3:.1f} us")
@@ -609,7 +616,7 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "num_blocks": w.num_blocks,
                    "sum_context_lens": int(ctx.sum()), "max_context_len": int(ctx.max()),
-                   "partition_size": args.P, "variant": args.variant,
+                   "partition_size": args.P, "variant": args.variant, "layout": args.layout,
                    "kv_bytes_per_step": ab["kv"], "replicas": REPLICAS},
         # against the nominal peak on the bytes HBM must deliver: a block shared by several
         # sequences counts once (equal to value's bytes when nothing is shared)
@@ -637,6 +644,13 @@ def main():
                      "traffic": measured_traffic(w.name + ("_grouped" if args.grouped else ""))},
         "identity_decode_us": None if ident is None else round(ident * 1e3, 2),
         "paged_vs_identity": None if ident is None else round(ident / dec_avg, 4),
+        "identity_gather_read_gbs": None if ident_gather is None else round(ident_gather["gbs"], 1),
+        # physically consecutive blocks read the same bytes (counters) but more slowly, the
+        # read probe as much as the kernel: the contiguous layout concentrates the concurrent
+        # workgroups' reads on neighbouring addresses; against its own probe the kernel is as
+        # close on either layout
+        "identity_pct_of_gather_read": None if ident is None or ident_gather is None else
+        round(100 * ab["total_unique"] / (ident * 1e-3) / 1e9 / ident_gather["gbs"], 2),
         "host_alloc_us_per_step": round(alloc_us, 2),
         "upload_us": upload["us"],
         "upload_bytes": upload["bytes"],

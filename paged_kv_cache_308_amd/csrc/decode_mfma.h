@@ -21,8 +21,11 @@
 //  * V must be read transposed (8 tokens of one d per lane): each wave copies its V
 //    rows HBM -> LDS with direct 16-byte LDS loads (global_load_lds_dwordx4, no
 //    register staging) into its own double-buffered region, 1 KiB per wave load with
-//    32 bytes of padding after each KiB so the four rows read together fall in
-//    different banks, and reads them back 16 bits at a time.
+//    32 bytes of padding after each KiB, and reads the V^T operand with gfx950's LDS
+//    transpose read ds_read_b64_tr_b16 (two per operand).  The tokens of a 16-token
+//    tile are taken in the order tile_row gives (the K operand's rows are loaded in that
+//    order, which permutes rows within one load instruction), so the four rows one
+//    16-lane group reads together lie in different padded KiB groups: different banks.
 // Softmax runs in fp32 (online, exp2 domain).  P enters the second product rounded to
 // the storage type; the normaliser sums the rounded weights, so numerator and
 // denominator use the same weights.  Accumulation is fp32.
@@ -101,8 +104,25 @@ __device__ inline uint8_t *v_at(uint8_t *stage, int r, int col) {
     return stage + (r / Gm::RPK) * Gm::KSTR + (r % Gm::RPK) * Gm::ROW + col;
 }
 
+// Token (row of a 16-token tile) in k slot m of lane group a (a, m in 0..3) of the score
+// and value products.  S^T row 4a + m holds this token, and the transpose read of lane
+// group a returns V rows tile_row(a, 0..3).  Chosen so that the four rows a group reads
+// lie at different bank offsets of the LDS stage (KiB groups padded by 32 bytes):
+// d = 128 (4 rows per KiB): rows a, a + 4, a + 8, a + 12, one per KiB group;
+// d = 64 (8 rows per KiB): rows 2a, 2a + 1, 2a + 8, 2a + 9 (two groups, odd and even rows
+// half a KiB-period apart).
+template <int D>
+__device__ inline int tile_row(int a, int m) {
+    static_assert(D == 64 || D == 128, "head dim");
+    if constexpr (D == 128)
+        return 4 * m + a;
+    else
+        return 8 * (m >> 1) + (m & 1) + 2 * a;
+}
+
 // Loads of one chunk: tile tt's 16 rows start at byte base[tt] of the pools.  Its V
-// rows go to LDS stage `stage` (direct loads), its K operands to k.
+// rows go to LDS stage `stage` (direct loads, in token order), its K operands to k
+// (lane (n, q) supplies row n of the score product: token tile_row(n / 4, n % 4)).
 template <int D, bool NT>
 __device__ __forceinline__ void issue_chunk(u32x4 (&k)[2][Geom<D>::NKK], uint8_t *stage, const int64_t (&base)[2],
                                             const uint8_t *key_cache, const uint8_t *value_cache, int lane,
@@ -117,7 +137,8 @@ __device__ __forceinline__ void issue_chunk(u32x4 (&k)[2][Geom<D>::NKK], uint8_t
                 (__attribute__((address_space(3))) void *)(stage + (tt * Gm::VL + i) * Gm::KSTR), 16, 0, 0);
 #pragma unroll
         for (int kk = 0; kk < Gm::NKK; ++kk)
-            k[tt][kk] = kv_load<NT>((const u32x4 *)(key_cache + base[tt] + n * Gm::ROW + (32 * kk + 8 * q) * 2));
+            k[tt][kk] = kv_load<NT>((const u32x4 *)(key_cache + base[tt] + tile_row<D>(n >> 2, n & 3) * Gm::ROW +
+                                                    (32 * kk + 8 * q) * 2));
     }
 }
 
@@ -130,7 +151,7 @@ __device__ __forceinline__ void consume_chunk(const u32x4 (&k)[2][Geom<D>::NKK],
                                               int n, int q, float &m, float &lsum, f32x4 (&o)[Geom<D>::NN]) {
     using Gm = Geom<D>;
     const bool tail = tok0 + CT > end;
-    // scores S^T: lane holds tokens 16 tt + 4 q + i of head n
+    // scores S^T: lane holds tokens 16 tt + tile_row(q, i) of head n
     float sc[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -139,7 +160,7 @@ __device__ __forceinline__ void consume_chunk(const u32x4 (&k)[2][Geom<D>::NKK],
         for (int kk = 0; kk < Gm::NKK; ++kk) acc = Mma<T>::run(k[tt][kk], qb[kk], acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool ok = !tail || (tok0 + 16 * tt + 4 * q + i < end);
+            const bool ok = !tail || (tok0 + 16 * tt + tile_row<D>(q, i) < end);
             sc[tt][i] = ok ? acc[i] * scale_log2 : -INFINITY;
         }
     }
@@ -153,7 +174,8 @@ __device__ __forceinline__ void consume_chunk(const u32x4 (&k)[2][Geom<D>::NKK],
     const float ms = mn == -INFINITY ? 0.f : mn;
     const float alpha = fast_exp2(m - ms);
     m = mn;
-    // P^T operand: k slot j < 4 -> token 4q + j (tile 0), j >= 4 -> token 16 + 4q + j - 4
+    // P^T operand: k slot j < 4 -> token tile_row(q, j) (tile 0), j >= 4 -> token
+    // 16 + tile_row(q, j - 4) (tile 1)
     uint32_t pk[4];
     float psum = 0.f;
 #pragma unroll
@@ -183,18 +205,23 @@ __device__ __forceinline__ void consume_chunk(const u32x4 (&k)[2][Geom<D>::NKK],
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    // V^T operand per 16-row d fragment: lane reads V[t(q, j)][16 nn + n]
+    // V^T operand per 16-row d fragment: lane (n, q) needs V[token of k slot j][16 nn + n].
+    // ds_read_b64_tr_b16 (lane mapping checked on gfx950): within each 16-lane group,
+    // lane j receives element j % 4 of the 8-byte reads of lanes 4k + j / 4, k = 0..3.
+    // Lane (n, q) reads 8 bytes of row tile_row(q, n / 4) at d = 16 nn + 4 (n % 4), so it
+    // receives V[tile_row(q, k)][16 nn + n] for k = 0..3: tile 0's k slots; the same
+    // read 16 rows further gives tile 1's.
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int vrow = tile_row<D>(q, n >> 2);
 #pragma unroll
     for (int nn = 0; nn < Gm::NN; ++nn) {
-        uint32_t vk[4];
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-            const int t0 = j < 4 ? 4 * q + j : 16 + 4 * q + (j - 4);
-            const uint16_t a = *(const uint16_t *)v_at<D>(stage, t0, (16 * nn + n) * 2);
-            const uint16_t c2 = *(const uint16_t *)v_at<D>(stage, t0 + 1, (16 * nn + n) * 2);
-            vk[j / 2] = (uint32_t)a | ((uint32_t)c2 << 16);
-        }
-        o[nn] = Mma<T>::run(u32x4{vk[0], vk[1], vk[2], vk[3]}, pb, o[nn]);
+        const int col = (16 * nn + 4 * (n & 3)) * 2;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)v_at<D>(stage, vrow, col));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)v_at<D>(stage, 16 + vrow, col));
+        const uint2 lw = __builtin_bit_cast(uint2, lo), hw = __builtin_bit_cast(uint2, hi);
+        o[nn] = Mma<T>::run(u32x4{lw.x, lw.y, hw.x, hw.y}, pb, o[nn]);
     }
     // the stage is rewritten by a later chunk's loads: finish reading it first
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

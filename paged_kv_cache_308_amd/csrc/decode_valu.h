@@ -287,7 +287,16 @@ constexpr int min_waves_per_eu() {
     return KV::scaled ? PA_FP8_WAVES_PER_EU : PA_VALU_WAVES_PER_EU;
 }
 
-template <typename KV, int D, int G, bool SPLIT, bool NT>
+// One pass with one wave per work item (SOLO): each wave streams a whole (sequence, KV
+// head) item and writes its output from registers; a workgroup holds NWG consecutive
+// items.  For batches of short items (the private tokens after a shared-prefix pass,
+// ~140 tokens each), where splitting an item over the workgroup's waves leaves each wave
+// two chunks and the cross-wave merge, the sort and the launch of many small
+// workgroups dominate.
+#ifndef PA_VALU_SOLO
+#define PA_VALU_SOLO 0  // 0: one wave per item after a shared-prefix pass only; 1: always; -1: never
+#endif
+template <typename KV, int D, int G, bool SPLIT, bool NT, bool SOLO = false>
 __global__ __launch_bounds__((waves_per_group<KV, G, SPLIT>() * 64))
 __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu_kernel(
     void *__restrict__ out, const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
@@ -309,11 +318,15 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     constexpr int NLK = loads_per_chunk<KV, G>();
     constexpr int C = NLK * TPW;             // tokens per chunk
 
+    static_assert(!(SOLO && SPLIT), "one wave per item is a one-pass form");
     const int lane = threadIdx.x & 63;
     // wave-uniform: keeps table lookups on the scalar unit and branches scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row = lane / LPT;
     const int col = lane % LPT;
+    // the waves that share this wave's work item, and this wave's place among them
+    constexpr int NWI = SOLO ? 1 : NWG;
+    const int iw = SOLO ? 0 : wave;
 
     int part = 0, s, kvh;
     if constexpr (SPLIT) {
@@ -330,11 +343,28 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
         // longest first, so the longest items start in the first round and the last
         // rounds hold short ones (no tail of one long sequence).  Workgroup w runs on
         // XCD w % 8: with a multiple of 8 KV heads, one head's sequences share an XCD.
-        kvh = blockIdx.x % num_kv_heads;
-        const int rank = blockIdx.x / num_kv_heads;
+        const int item = SOLO ? (int)blockIdx.x * NWG + wave : (int)blockIdx.x;
+        kvh = item % num_kv_heads;
+        int rank = item / num_kv_heads;
+        if constexpr (KV::scaled && !SOLO) {
+            // E4M3 pools read a K and a V scale per (block, KV head); a block's heads share one
+            // line of each scale array.  In head-fastest order XCD x (workgroup w = 8k + x) runs
+            // heads x, x + 8, ... of every sequence and fetches the whole line of every block;
+            // here it runs the contiguous heads hx x .. hx x + hx - 1 (hx = H_kv / 8) and
+            // fetches only their part.  Sequences still start in longest-first order.
+            if (num_kv_heads % 8 == 0) {
+                const int hx = num_kv_heads / 8;
+                const int k = item / 8;
+                rank = k / hx;
+                kvh = hx * (item % 8) + k % hx;
+            }
+        }
+        if (SOLO && rank >= num_seqs) rank = num_seqs - 1;  // past the batch: sorts with the rest, then leaves
         __shared__ uint32_t sm_order[NWG * 64];
         s = num_seqs <= NWG * 64 ? longest_first<NWG * 64>(context_lens, num_seqs, rank, sm_order) : rank;
         s = __builtin_amdgcn_readfirstlane(s);
+        // no barrier follows in the one-wave-per-item form
+        if (SOLO && item >= num_seqs * num_kv_heads) return;
     }
     const int num_q_heads = num_kv_heads * G;
 
@@ -361,7 +391,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     const int64_t block_bytes = (int64_t)num_kv_heads * block_size * ROW_BYTES;
     // This wave's first table entry, read beside the context length instead of after it
     // (the first chunk's position does not depend on the length).
-    const int lb0 = (start + wave * C) >> log2_block;
+    const int lb0 = (start + iw * C) >> log2_block;
     const int32_t pb0 = lb0 < max_blocks_per_seq ? table[lb0] : -1;
 
     // this lane's slice of every query head of the group
@@ -397,7 +427,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     // behind the loop); after the loop it stores them into the pool (E4M3: rounded by
     // all 64 lanes, D / 64 elements each) and attends to them with row 0 of its lanes
     // (the other rows masked).  The loop never reads that slot.
-    const bool app_here = append && wave == (nfull + (has_tail ? 1 : 0)) % NWG;
+    const bool app_here = append && iw == (nfull + (has_tail ? 1 : 0)) % NWI;
     constexpr int AP = D / 64;  // E4M3: elements of the newest row per lane
     static_assert(AP * 64 == D, "head_dim");
     typename KV::Word app_k[1] = {typename KV::Word{}}, app_v[1] = {typename KV::Word{}};
@@ -494,30 +524,30 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
                                           acc);
     };
 
-    // This wave's full chunks are wave, wave + NWG, ...  The steady-state loop always
+    // This wave's full chunks are iw, iw + NWI, ...  The steady-state loop always
     // has a next chunk to prefetch, so its loads are unconditional and the compiler
     // waits only for the chunk being reduced; the last one or two run after it.
     {
-        const int mine = nfull > wave ? (nfull - wave + NWG - 1) / NWG : 0;
+        const int mine = nfull > iw ? (nfull - iw + NWI - 1) / NWI : 0;
         Chunk A, Bf;
         if (mine > 0) {
-            issue(A, wave);
+            issue(A, iw);
             int j = 0;
             for (; j + 2 < mine; j += 2) {
-                issue(Bf, wave + (j + 1) * NWG);
-                consume(A, wave + j * NWG, false);
-                issue(A, wave + (j + 2) * NWG);
-                consume(Bf, wave + (j + 1) * NWG, false);
+                issue(Bf, iw + (j + 1) * NWI);
+                consume(A, iw + j * NWI, false);
+                issue(A, iw + (j + 2) * NWI);
+                consume(Bf, iw + (j + 1) * NWI, false);
             }
             if (j + 1 < mine) {
-                issue(Bf, wave + (j + 1) * NWG);
-                consume(A, wave + j * NWG, false);
-                consume(Bf, wave + (j + 1) * NWG, false);
+                issue(Bf, iw + (j + 1) * NWI);
+                consume(A, iw + j * NWI, false);
+                consume(Bf, iw + (j + 1) * NWI, false);
             } else {
-                consume(A, wave + j * NWG, false);
+                consume(A, iw + j * NWI, false);
             }
         }
-        if (has_tail && (nfull % NWG) == wave) {
+        if (has_tail && (nfull % NWI) == iw) {
             issue(A, nfull);
             consume(A, nfull, true);
         }
@@ -525,7 +555,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
 
     if (app_here) {
         if constexpr (KV::scaled) {
-            __shared__ __align__(16) uint8_t sm_new[2][D];
+            __shared__ __align__(16) uint8_t sm_new_all[SOLO ? NWG : 1][2][D];
+            uint8_t(&sm_new)[2][D] = sm_new_all[SOLO ? wave : 0];
             const uint32_t ck = KV::template encode_run<AP>(app_rk, app_ks);
             const uint32_t cv = KV::template encode_run<AP>(app_rv, app_vs);
             if constexpr (AP == 2) {
@@ -562,6 +593,40 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     end = end_all;
 
     merge_rows<G, EPL, LPT>(m, l, acc);
+
+    if constexpr (SOLO) {
+        // the item's only wave: row 0 writes its slices of every head's output, after
+        // folding in the shared-prefix partial if there is one
+        if (row == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int h = kvh * G + g;
+                const int64_t pi = (int64_t)s * num_q_heads + h;
+                float M = m[g], m0 = -INFINITY, l0 = 0.f;
+                bool bad0 = false;
+                if (prefix_spans > 0) {
+                    m0 = ws_max[pi];
+                    l0 = ws_sum[pi];
+                    bad0 = m0 != m0;
+                    if (!bad0) M = fmaxf(M, m0);
+                }
+                const float Ms = M == -INFINITY ? 0.f : M;
+                const float f = fast_exp2(m[g] - Ms);
+                const float f0 = prefix_spans > 0 && !bad0 ? fast_exp2(m0 - Ms) : 0.f;
+                const float Lsum = l[g] * f + l0 * f0;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    const int j = col * EPL + e;
+                    float A = acc[g][e] * f;
+                    if (prefix_spans > 0 && !bad0) A += ws_acc[pi * D + j] * f0;
+                    float o = Lsum > 0.f ? A / Lsum : 0.f;
+                    if (bad || bad0) o = NAN;
+                    store_out<T>(out, pi * D + j, o);
+                }
+            }
+        }
+        return;
+    }
 
     // merge the waves through LDS
     __shared__ float sm_m[NWG][G], sm_l[NWG][G], sm_acc[NWG][G][D];
@@ -946,15 +1011,23 @@ int launch_t(const DecodeArgs &a) {
         if (rc != PA_OK) return rc;
         return launch_lse_merge(a);
     }
-    hipLaunchKernelGGL((decode_valu_kernel<KV, D, G, false, NT>), dim3(grid),
-                       dim3(waves_per_group<KV, G, false>() * 64), 0, st,
+    // one wave per item for the private tokens after a shared-prefix pass (short items;
+    // pa_decode_grouped takes one query head per KV head and 16-bit pools)
+    constexpr bool solo_built = PA_VALU_SOLO > 0 || (PA_VALU_SOLO == 0 && G == 1 && !KV::scaled);
+    const bool solo = solo_built && (PA_VALU_SOLO > 0 || a.skip_parts != nullptr);
+    constexpr int NWG1 = waves_per_group<KV, G, false>();
+    auto kernel = decode_valu_kernel<KV, D, G, false, NT, false>;
+    if constexpr (solo_built)
+        if (solo) kernel = decode_valu_kernel<KV, D, G, false, NT, true>;
+    const unsigned grid1 = solo ? (unsigned)(((int64_t)a.num_seqs * a.num_kv_heads + NWG1 - 1) / NWG1) : grid;
+    hipLaunchKernelGGL(kernel, dim3(grid1), dim3(NWG1 * 64), 0, st,
                        a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
                        (const uint8_t *)a.value_cache, a.k_scales, a.v_scales, a.block_tables,
                        a.context_lens, a.ws_max, a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs,
                        a.num_kv_heads, log2b, a.num_blocks, a.group_span, 1, a.scale_log2,
                        (const uint8_t *)a.new_key, (const uint8_t *)a.new_value, (uint8_t *)a.key_out,
                        (uint8_t *)a.value_out, a.skip_parts);
-    return check_launch("decode_valu");
+    return check_launch(solo ? "decode_valu (one wave per item)" : "decode_valu");
 }
 
 template <typename KV, int D, int G>
