@@ -694,39 +694,87 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
 
 // Log-sum-exp merge of the partition partials of one (sequence, query head):
 //   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  out = sum_p 2^(m_p - M) acc_p / L.
+// The merge is latency-bound (a few KB per wave), so the loads are issued together:
+// lane p holds partition p's max and sum (64 partitions a round), the first 8
+// partitions' value sums are loaded before the context length is even known (every
+// slot below max_partitions lies in the workspace; unused ones are never counted), and
+// later value sums 8 partitions at a time.  Weights reach the other lanes by readlane.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void lse_merge_kernel(
     void *__restrict__ out, const float *__restrict__ ws_max, const float *__restrict__ ws_sum,
     const float *__restrict__ ws_acc, const int32_t *__restrict__ context_lens, int num_q_heads,
     int partition_size, int max_partitions) {
+    constexpr int JP = D / 64;  // output elements per lane
+    constexpr int PB = 8;       // partitions whose value sums are loaded together
+    const int lane = threadIdx.x;
     const int sh = blockIdx.x;  // s * H_q + h
     const int s = sh / num_q_heads;
-    const int ctx = context_lens[s];
     const int64_t obase = (int64_t)sh * D;
-    const int n = ctx <= 0 ? 0 : (ctx + partition_size - 1) / partition_size;
-    if (ctx < 0 || n > max_partitions) {
-        for (int j = threadIdx.x; j < D; j += 64) store_out<T>(out, obase + j, NAN);
-        return;
-    }
     const float *mp = ws_max + (int64_t)sh * max_partitions;
     const float *lp = ws_sum + (int64_t)sh * max_partitions;
+    const float *ap = ws_acc + (int64_t)sh * max_partitions * D + lane;
+    float a0[PB][JP];
+#pragma unroll
+    for (int u = 0; u < PB; ++u)
+#pragma unroll
+        for (int jj = 0; jj < JP; ++jj) a0[u][jj] = u < max_partitions ? ap[u * D + 64 * jj] : 0.f;
+    const int ctx = context_lens[s];
+    const int n = ctx <= 0 ? 0 : (ctx + partition_size - 1) / partition_size;
+    if (ctx < 0 || n > max_partitions) {
+        for (int j = lane; j < D; j += 64) store_out<T>(out, obase + j, NAN);
+        return;
+    }
+    // the maximum (and any NaN partial, from a bad table entry) over every partition
+    float xf = -INFINITY, lf = 0.f;  // this lane's partition of the first round
     float M = -INFINITY;
     bool bad = false;
-    for (int p = 0; p < n; ++p) {
-        const float x = mp[p];
+    for (int p0 = 0; p0 < n; p0 += 64) {
+        const int p = p0 + lane;
+        const float x = p < n ? mp[p] : -INFINITY;
+        if (p0 == 0) {
+            xf = x;
+            lf = p < n ? lp[p] : 0.f;
+        }
         bad |= x != x;
         M = fmaxf(M, x);
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const bool any_bad = __any(bad);
     const float Ms = M == -INFINITY ? 0.f : M;
-    float Lsum = 0.f;
-    for (int p = 0; p < n; ++p) Lsum += lp[p] * fast_exp2(mp[p] - Ms);
-    for (int j = threadIdx.x; j < D; j += 64) {
-        float A = 0.f;
-        for (int p = 0; p < n; ++p)
-            A += fast_exp2(mp[p] - Ms) * ws_acc[((int64_t)sh * max_partitions + p) * D + j];
-        float o = Lsum > 0.f ? A / Lsum : 0.f;
-        if (bad) o = NAN;
-        store_out<T>(out, obase + j, o);
+    float Lsum = 0.f, A[JP];
+#pragma unroll
+    for (int jj = 0; jj < JP; ++jj) A[jj] = 0.f;
+    for (int p0 = 0; p0 < n; p0 += 64) {
+        const int p = p0 + lane;
+        const float x = p0 == 0 ? xf : (p < n ? mp[p] : -INFINITY);
+        const float l = p0 == 0 ? lf : (p < n ? lp[p] : 0.f);
+        const float w = p < n ? fast_exp2(x - Ms) : 0.f;
+        Lsum += l * w;
+        const int cnt = min(64, n - p0);
+        for (int i = 0; i < cnt; i += PB) {
+            float a[PB][JP];
+#pragma unroll
+            for (int u = 0; u < PB; ++u)
+#pragma unroll
+                for (int jj = 0; jj < JP; ++jj)
+                    a[u][jj] = p0 + i == 0 ? a0[u][jj] : (i + u < cnt ? ap[(int64_t)(p0 + i + u) * D + 64 * jj] : 0.f);
+#pragma unroll
+            for (int u = 0; u < PB; ++u) {
+                if (i + u >= cnt) break;
+                const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i + u));
+#pragma unroll
+                for (int jj = 0; jj < JP; ++jj) A[jj] += wu * a[u][jj];
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) Lsum += __shfl_xor(Lsum, o);
+#pragma unroll
+    for (int jj = 0; jj < JP; ++jj) {
+        float o = Lsum > 0.f ? A[jj] / Lsum : 0.f;
+        if (any_bad) o = NAN;
+        store_out<T>(out, obase + lane + 64 * jj, o);
     }
 }
 
