@@ -59,6 +59,15 @@ constexpr int MW = 4;  // waves per workgroup
 #ifndef PA_MQ_WAVES_PER_EU
 #define PA_MQ_WAVES_PER_EU 3  // waves per SIMD the register allocation must allow
 #endif
+// Tuning switches: PA_MQ_VPREFETCH reads a tile's V^T operands right after the score
+// product, before the softmax (their LDS latency behind the exponentials); PA_MQ_PRIO
+// raises the wave's issue priority around its runs of matrix-core instructions.
+#ifndef PA_MQ_VPREFETCH
+#define PA_MQ_VPREFETCH 0
+#endif
+#ifndef PA_MQ_PRIO
+#define PA_MQ_PRIO 0
+#endif
 // 16-row query fragments per wave.  Four halve the LDS reads per product but need more
 // than 256 registers (one wave per SIMD), which measured 1.4x slower than two.
 constexpr int RF = PA_MQ_FRAGS;
@@ -282,6 +291,7 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
         const int k0 = t * KT;
         // scores S^T: lane holds keys k0 + 16 tt + 4 q + i of row n of each fragment
         float sc[RF][NT][4];
+        if (PA_MQ_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             f32x4 acc[RF];
@@ -297,6 +307,23 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
             for (int f = 0; f < RF; ++f)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[f][tt][i] = acc[f][i];
+        }
+        if (PA_MQ_PRIO) __builtin_amdgcn_s_setprio(0);
+        // V^T operand reads for this tile (see below), issued before the softmax
+        auto read_v = [&](int nn, int h) -> u32x4 {
+            const uint8_t *r0 = buf + KBYTES + vrd0 + (32 * h) * VROW + 32 * nn;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(r0));
+            const s16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(r0 + 16 * VROW));
+            const uint2 lw = __builtin_bit_cast(uint2, lo), hw = __builtin_bit_cast(uint2, hi);
+            return u32x4{lw.x, lw.y, hw.x, hw.y};
+        };
+        u32x4 vpre[PA_MQ_VPREFETCH ? NN : 1][NH];
+        if (PA_MQ_VPREFETCH) {
+#pragma unroll
+            for (int nn = 0; nn < (PA_MQ_VPREFETCH ? NN : 1); ++nn)
+#pragma unroll
+                for (int h = 0; h < NH; ++h) vpre[nn][h] = read_v(nn, h);
         }
         if (k0 + KT - 1 > wave_first_pos) {  // a diagonal tile: mask keys past each row
 #pragma unroll
@@ -339,8 +366,7 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
             }
         }
         // V^T operand per 16-row d fragment and half: keys 32h + 4q..+3 and 32h + 16 + 4q..+3
-        // of d = 16 nn + n (two transpose reads of the V rows), shared by the fragments
-        uint8_t *vt = (uint8_t *)buf + KBYTES;
+        // of d = 16 nn + n (two transpose reads of the V rows, read_v), shared by the fragments
         // rescale only when some row's reference moved (otherwise every alpha is 1)
         if (__any(grow)) {
 #pragma unroll
@@ -350,6 +376,7 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
                 for (int nn = 0; nn < NN; ++nn) o[f][nn] *= alpha[f];
             }
         }
+        if (PA_MQ_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -359,17 +386,12 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
                 // keys 32h + 4q .. +3, then 32h + 16 + 4q .. +3, of d = 16 nn + n
-                const uint8_t *r0 = vt + vrd0 + (32 * h) * VROW + 32 * nn;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4 *)(r0));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4 *)(r0 + 16 * VROW));
-                const uint2 lw = __builtin_bit_cast(uint2, lo), hw = __builtin_bit_cast(uint2, hi);
-                const u32x4 va = u32x4{lw.x, lw.y, hw.x, hw.y};
+                const u32x4 va = PA_MQ_VPREFETCH ? vpre[PA_MQ_VPREFETCH ? nn : 0][h] : read_v(nn, h);
 #pragma unroll
                 for (int f = 0; f < RF; ++f) o[f][nn] = Mma<T>::run(va, pb[f][h], o[f][nn]);
             }
         }
+        if (PA_MQ_PRIO) __builtin_amdgcn_s_setprio(0);
     };
 
     // While tile t is used from LDS, tile t + 1 is being loaded into registers (and with
