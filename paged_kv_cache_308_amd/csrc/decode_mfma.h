@@ -142,12 +142,46 @@ __device__ __forceinline__ void issue_chunk(u32x4 (&k)[2][Geom<D>::NKK], uint8_t
     }
 }
 
+// V^T operands of one chunk, read from its LDS stage into registers: fragment nn of
+// lane (n, q) holds V[token of k slot j][d = 16 nn + n], k slot j < 4 -> token
+// tile_row(q, j) (tile 0), j >= 4 -> token 16 + tile_row(q, j - 4) (tile 1).
+// ds_read_b64_tr_b16 (lane mapping checked on gfx950): within each 16-lane group, lane j
+// receives element j % 4 of the 8-byte reads of lanes 4k + j / 4, k = 0..3.  Lane (n, q)
+// reads 8 bytes of row tile_row(q, n / 4) at d = 16 nn + 4 (n % 4), so it receives
+// V[tile_row(q, k)][16 nn + n] for k = 0..3: tile 0's k slots; the same read 16 rows
+// further gives tile 1's.
+//
+// The operands are read before the next chunk's loads are issued: an LDS read after a
+// direct-to-LDS load waits for every load in flight (the compiler cannot tell the stages
+// apart), so reading first leaves the next chunk's loads in flight while this one is used.
+template <int D>
+__device__ __forceinline__ void read_vt(u32x4 (&vt)[Geom<D>::NN], uint8_t *stage, int n, int q) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int vrow = tile_row<D>(q, n >> 2);
+#pragma unroll
+    for (int nn = 0; nn < Geom<D>::NN; ++nn) {
+        const int col = (16 * nn + 4 * (n & 3)) * 2;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)v_at<D>(stage, vrow, col));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)v_at<D>(stage, 16 + vrow, col));
+        const uint2 lw = __builtin_bit_cast(uint2, lo), hw = __builtin_bit_cast(uint2, hi);
+        vt[nn] = u32x4{lw.x, lw.y, hw.x, hw.y};
+    }
+}
+
+// Wait until this wave's LDS reads have completed (before direct loads rewrite a stage
+// they read).  s_waitcnt with only the LGKM count at 0 (gfx9 encoding: vmcnt 63,
+// expcnt 7, lgkmcnt 0).
+__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // One chunk of CT tokens starting at position tok0 (rows at or past `end` masked)
 // folded into a wave's online-softmax state: m (running max of head n), lsum (this
-// lane's share of the normaliser) and o (O^T fragments).
+// lane's share of the normaliser) and o (O^T fragments).  k: the chunk's K operands;
+// vt: its V^T operands (read_vt), from registers only.
 template <typename T, int D>
 __device__ __forceinline__ void consume_chunk(const u32x4 (&k)[2][Geom<D>::NKK], const u32x4 (&qb)[Geom<D>::NKK],
-                                              uint8_t *stage, int tok0, int end, float scale_log2, int lane,
+                                              u32x4 (&vt)[Geom<D>::NN], int tok0, int end, float scale_log2,
                                               int n, int q, float &m, float &lsum, f32x4 (&o)[Geom<D>::NN]) {
     using Gm = Geom<D>;
     const bool tail = tok0 + CT > end;
@@ -192,41 +226,21 @@ __device__ __forceinline__ void consume_chunk(const u32x4 (&k)[2][Geom<D>::NKK],
     const u32x4 pb = u32x4{pk[0], pk[1], pk[2], pk[3]};
 #pragma unroll
     for (int nn = 0; nn < Gm::NN; ++nn) o[nn] *= alpha;
-    // this chunk's V rows have landed in LDS: its V loads were issued before its K
-    // loads, which the score product above already waited for
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (tail) {
-        // rows past `end` as zeros: 0 * NaN would poison the product
-        for (int r = max(0, end - tok0); r < CT; ++r)
-            for (int col = lane * 4; col < Gm::ROW; col += 256) *(uint32_t *)v_at<D>(stage, r, col) = 0u;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    // V^T operand per 16-row d fragment: lane (n, q) needs V[token of k slot j][16 nn + n].
-    // ds_read_b64_tr_b16 (lane mapping checked on gfx950): within each 16-lane group,
-    // lane j receives element j % 4 of the 8-byte reads of lanes 4k + j / 4, k = 0..3.
-    // Lane (n, q) reads 8 bytes of row tile_row(q, n / 4) at d = 16 nn + 4 (n % 4), so it
-    // receives V[tile_row(q, k)][16 nn + n] for k = 0..3: tile 0's k slots; the same
-    // read 16 rows further gives tile 1's.
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    const int vrow = tile_row<D>(q, n >> 2);
+        // V of rows past `end` as zeros (whatever was read there): 0 * NaN would poison
+        // the product.  Word w of a fragment holds k slots 2w (low half) and 2w + 1.
+        u32x4 keep;
 #pragma unroll
-    for (int nn = 0; nn < Gm::NN; ++nn) {
-        const int col = (16 * nn + 4 * (n & 3)) * 2;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)v_at<D>(stage, vrow, col));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)v_at<D>(stage, 16 + vrow, col));
-        const uint2 lw = __builtin_bit_cast(uint2, lo), hw = __builtin_bit_cast(uint2, hi);
-        o[nn] = Mma<T>::run(u32x4{lw.x, lw.y, hw.x, hw.y}, pb, o[nn]);
+        for (int w = 0; w < 4; ++w) {
+            const int t0 = (w < 2 ? 0 : 16) + tile_row<D>(q, (2 * w) & 3);
+            const int t1 = (w < 2 ? 0 : 16) + tile_row<D>(q, (2 * w + 1) & 3);
+            keep[w] = (tok0 + t0 < end ? 0x0000ffffu : 0u) | (tok0 + t1 < end ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int nn = 0; nn < Gm::NN; ++nn) vt[nn] &= keep;
     }
-    // the stage is rewritten by a later chunk's loads: finish reading it first
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int nn = 0; nn < Gm::NN; ++nn) o[nn] = Mma<T>::run(vt[nn], pb, o[nn]);
 }
 
 // Q^T operand of (sequence s, KV head kvh): lane holds Q[head n][32 kk + 8 q .. +8];
@@ -267,7 +281,8 @@ struct WaveState {
 
 // The workgroup's MW waves over tokens [start, end) of (sequence s, KV head kvh):
 // wave w takes the CT-token chunks w, w + MW, ... of the range through a double-
-// buffered pipeline (K operands in registers, V rows in its LDS stages).
+// buffered pipeline (K operands in registers, V rows in its LDS stages, one chunk's
+// loads in flight while the previous chunk is used).
 //
 // Newest token given (new_k non-null; the range ends at the context's end): the chunks
 // stop before position end - 1, and the wave that would take the next chunk then stores
@@ -275,7 +290,7 @@ struct WaveState {
 // slot and folds it into its state from registers: the score by vector dot products
 // over the 4 lanes of each head's column, the weight rounded to T as the matrix-core
 // path rounds it.  A wave whose 16-row tile holds that slot treats the row as past the
-// end (score -inf, V row zeroed in LDS), whichever value it read.
+// end (score -inf, V operand zeroed), whichever value it read.
 template <typename T, int D, int G, bool NT>
 __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds, const uint8_t *query,
                                              const uint8_t *key_cache, const uint8_t *value_cache,
@@ -341,32 +356,43 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
             base[tt] = tile_base(c, tt);
             base[tt] = base[tt] < 0 ? 0 : base[tt];
         }
+        // the stage was last read two chunks ago (its operands long used); the wait makes
+        // the order explicit before the loads rewrite it
+        wait_lds_reads();
         issue_chunk<D, NT>(b.k, wave_lds + stage * Gm::STAGE, base, key_cache, value_cache, lane, n, q);
     };
-    auto consume = [&](const Chunk &b, int c, int stage) {
-        consume_chunk<T, D>(b.k, qb, wave_lds + stage * Gm::STAGE, start + c * CT, end, scale_log2, lane, n, q,
-                            st.m, st.lsum, st.o);
+    u32x4 vt[Gm::NN];
+    auto consume = [&](const Chunk &b, int c) {
+        consume_chunk<T, D>(b.k, qb, vt, start + c * CT, end, scale_log2, n, q, st.m, st.lsum, st.o);
     };
+    auto stage_at = [&](int stage) { return wave_lds + stage * Gm::STAGE; };
 
-    // this wave's chunks are wave, wave + MW, ...; the steady-state loop always has a
-    // next chunk to prefetch (see tile_base), the last one or two run after it
+    // This wave's chunks are wave, wave + MW, ...  Per chunk: its V^T operands are read
+    // from LDS (once its loads have landed), the next chunk's loads are issued, then the
+    // chunk is used from registers while they are in flight.  The steady-state loop always
+    // has a next chunk to prefetch (see tile_base); the last one or two run after it.
     const int mine = nchunks > wave ? (nchunks - wave + MW - 1) / MW : 0;
     Chunk A, Bf;
     if (mine > 0) {
         issue(A, wave, 0);
         int j = 0;
         for (; j + 2 < mine; j += 2) {
+            read_vt<D>(vt, stage_at(0), n, q);
             issue(Bf, wave + (j + 1) * MW, 1);
-            consume(A, wave + j * MW, 0);
+            consume(A, wave + j * MW);
+            read_vt<D>(vt, stage_at(1), n, q);
             issue(A, wave + (j + 2) * MW, 0);
-            consume(Bf, wave + (j + 1) * MW, 1);
+            consume(Bf, wave + (j + 1) * MW);
         }
         if (j + 1 < mine) {
+            read_vt<D>(vt, stage_at(0), n, q);
             issue(Bf, wave + (j + 1) * MW, 1);
-            consume(A, wave + j * MW, 0);
-            consume(Bf, wave + (j + 1) * MW, 1);
+            consume(A, wave + j * MW);
+            read_vt<D>(vt, stage_at(1), n, q);
+            consume(Bf, wave + (j + 1) * MW);
         } else {
-            consume(A, wave + j * MW, 0);
+            read_vt<D>(vt, stage_at(0), n, q);
+            consume(A, wave + j * MW);
         }
     }
     if (append && wave == nchunks % MW) {
