@@ -11,9 +11,11 @@
 // share the KV head.  Each of its four waves owns 32 rows (two 16-row fragments that
 // share every operand read).  The workgroup walks the keys its rows can see ([0, last
 // row's position]) in tiles of 32 keys (64 at d = 64, the same bytes); every tile is
-// loaded from HBM once, through the block table, into double-buffered LDS (K and V rows
-// on padded strides) while the previous tile is being used,
-// and all four waves read it there.  Per tile and wave:
+// loaded once, through the block table, straight from HBM into one of three LDS buffers
+// (global_load_lds, 1 KiB per load, no register staging) two tiles ahead of use, and all
+// four waves read it there.  In LDS a row's 16-byte pieces are permuted (an XOR of the
+// piece index with a function of the row), which keeps both operand reads below free
+// of bank conflicts without padding.  Per tile and wave:
 //
 //   S^T[t][r]  = sum_d K[t][d] Q[r][d]          A = K rows (16 keys x 32 d), B = Q^T
 //   O^T[d][r] += sum_t V[t][d] P[r][t]          A = V^T (16 d x 32 keys),   B = P^T
@@ -22,8 +24,8 @@
 // B[8(l/16)..+8][l%16] and receives D[4(l/16)..+4][l%16], so the score fragment holds,
 // per lane, one row's scores for keys 4q..4q+3 and 16+4q..16+4q+3: exactly a P^T
 // operand once the V^T operand uses the same k order (two LDS transpose reads,
-// ds_read_b64_tr_b16, of the V rows).  The causal mask compares each key's position with its row's; a
-// wave skips tiles past its own last row.  Softmax is fp32 online in the exp2 domain;
+// ds_read_b64_tr_b16, of the V rows).  The causal mask compares each key's position with
+// its row's.  Softmax is fp32 online in the exp2 domain;
 // P enters the second product rounded to the storage type and the normaliser sums the
 // rounded weights (on the matrix cores, P against a ones operand).  Rows are written by
 // the wave that owns them (no merge).
@@ -42,34 +44,23 @@ namespace mq {
 
 using mfma::Mma;
 using mfma::f32x4;
-constexpr int MW = 4;  // waves per workgroup
+#ifndef PA_MQ_WAVES
+#define PA_MQ_WAVES 4
+#endif
+constexpr int MW = PA_MQ_WAVES;  // waves per workgroup
 #ifndef PA_MQ_FRAGS
 #define PA_MQ_FRAGS 2
 #endif
 #ifndef PA_MQ_KEYS
 #define PA_MQ_KEYS 32
 #endif
-// The loop is latency-bound (each wave's chain of LDS reads, score products, max,
-// exponentials and value products), so occupancy wins over prefetch depth: one key tile
-// in flight and registers held to 168 so that 3 waves share each SIMD (388 us against
-// 455 us with two tiles in flight at 2 waves; a few bytes of spill at d = 128).
-#ifndef PA_MQ_DEPTH
-#define PA_MQ_DEPTH 1  // key tiles in flight beyond the one in use (1 or 2)
-#endif
 #ifndef PA_MQ_WAVES_PER_EU
 #define PA_MQ_WAVES_PER_EU 3  // waves per SIMD the register allocation must allow
 #endif
-// Tuning switches: PA_MQ_VPREFETCH reads a tile's V^T operands right after the score
-// product, before the softmax (their LDS latency behind the exponentials); PA_MQ_PRIO
-// raises the wave's issue priority around its runs of matrix-core instructions.
-#ifndef PA_MQ_VPREFETCH
-#define PA_MQ_VPREFETCH 0
-#endif
-#ifndef PA_MQ_PRIO
-#define PA_MQ_PRIO 0
-#endif
 // 16-row query fragments per wave.  Four halve the LDS reads per product but need more
-// than 256 registers (one wave per SIMD), which measured 1.4x slower than two.
+// than 256 registers (one wave per SIMD), which measured 1.4x slower than two; one (8
+// waves of 16 rows, 4 waves per SIMD) measured 0.239 of the matrix-core peak against
+// 0.277 with two.
 constexpr int RF = PA_MQ_FRAGS;
 constexpr int ROWS = 16 * RF * MW;   // query rows per workgroup
 static_assert(PA_MQ_KEYS % 32 == 0 && (RF == 1 || RF == 2 || RF == 4), "tile shape");
@@ -104,15 +95,10 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
     constexpr int NN = D / 16;             // 16-row d fragments of the output
     constexpr int NT = KT / 16;            // 16-key score operands per tile
     constexpr int NH = KT / 32;            // 32-key value products per tile
-    constexpr int KROW = ROW + 16;         // LDS stride of a key row (16 lanes x 16 bytes: no bank conflict)
-    constexpr int KBYTES = KT * KROW;
-    // V rows as they are, read transposed by ds_read_b64_tr_b16; a 32-byte pad keeps the
-    // 16 rows one operand read touches in different banks
-    constexpr int VROW = ROW + 32;
-    constexpr int BUF = KBYTES + KT * VROW;  // one tile: K rows, then V rows
-    constexpr int PARTS = ROW / 16;        // 16-byte pieces of a row
-    constexpr int NCH = KT * PARTS / (MW * 64);  // pieces of K (and of V) per thread per tile
-    static_assert(NCH * MW * 64 == KT * PARTS && NCH % 2 == 0, "tile pieces must divide over the workgroup");
+    // rows unpadded, their 16-byte pieces permuted (swz): every 1 KiB of a tile is one
+    // direct load of the workgroup
+    constexpr int KBYTES = KT * ROW;
+    constexpr int BUF = 2 * KBYTES;  // one tile: K rows, then V rows
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -149,11 +135,14 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
         orow[f] = (int64_t)q0 + ti;
         io_ok[f] = ok && orow[f] >= 0 && orow[f] < num_query_tokens;
     }
-    const int wave_end = wrow0 < rows ? ctx - nq + (min(rows, wrow0 + 16 * RF) - 1) / G + 1 : 0;
     const int wg_last = min(rows, ROWS * tile + ROWS) - 1;
     const int end = bad_len ? 0 : ctx - nq + wg_last / G + 1;  // keys the workgroup reads
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
+    // three buffers, each its own variable: the compiler then tells a buffer's LDS reads
+    // from direct loads into another and does not wait for those
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[BUF];
 
     const int block_size = 1 << log2_block;
     const int32_t *table = block_tables + (int64_t)s * max_blocks_per_seq;
@@ -205,36 +194,19 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
         for (int i = 0; i < NN; ++i) o[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     bool bad = bad_len;
+    // per fragment: the raw product above which a row's reference must move
+    const float inv_sl = 1.f / sl;
+    float bound[RF];
+#pragma unroll
+    for (int f = 0; f < RF; ++f) bound[f] = -INFINITY;
 
     const int ntiles = (end + KT - 1) / KT;
 
-    // Global loads of key tile t: this thread's NCH pieces of K and of V.  Each 16-key
-    // group lies in one block (B >= 16); the NT block ids are looked up once per tile
-    // (scalar loads).  Keys at or past `end`, and pieces of a bad block, load block 0's
-    // first row instead (inside the pool) and are stored as zeros.
-    struct Stage {
-        u32x4 k[NCH], v[NCH];
-        bool ok[NCH];
-        bool full;  // every piece of the tile is valid (uniform): no zeroing needed
-    };
-    // Pieces 2i and 2i+1 of a thread are the same 16 bytes of two neighbouring keys.
-    // Everything that depends only on the thread is computed once: a piece's key, its
-    // byte offset inside its 16-key group of rows, and its LDS destinations.
-    int pkey[NCH], prow[NCH], kst[NCH], vst[NCH / 2];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = threadIdx.x + (i / 2) * MW * 64;  // pair index over the tile
-        const int part = c % PARTS;
-        pkey[i] = 2 * (c / PARTS) + (i & 1);
-        prow[i] = (pkey[i] & 15) * ROW + part * 16;
-        kst[i] = pkey[i] * KROW + part * 16;
-        if ((i & 1) == 0) vst[i / 2] = pkey[i] * VROW + part * 16;  // the pair's second key: + VROW
-    }
-    auto load_tile = [&](Stage &st, int t) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    // byte offset of the first row of each 16-key group of tile t (uniform), -1 if not valid
+    auto group_bases = [&](int t, int64_t (&base)[NT]) {
         const int k0 = t * KT;
-        // byte offset of each 16-key group's first row (uniform), -1 if not valid
-        int64_t base[NT];
-        bool full = k0 + KT <= end;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
             base[j] = -1;
@@ -248,50 +220,109 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
                 }
                 if (base[j] < 0) bad = true;
             }
-            full = full && base[j] >= 0;
         }
-        st.full = full;
+    };
+    // Piece permutation: piece c of row r (16 bytes) sits at piece c ^ swz(r % 16) of the
+    // row.  The 16 rows one K operand read touches (same piece), and the 8 rows half a V
+    // transpose read touches (32 bytes each), then lie in different banks.
+    auto swz = [](int r) -> int {
+        r &= 15;
+        return D == 128 ? 2 * (r & 7) + ((r >> 3) & 1) : 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+    };
+    // Direct loads: a tile's K (then V) is KBYTES / 1024 loads of 1 KiB, NI per wave; load j
+    // fills rows j * RPL .. + RPL (one 16-key group); lane l writes LDS bytes 16 l of it, so
+    // it fetches the global piece that the permutation puts there.
+    constexpr int RPL = 1024 / ROW;           // rows per load
+    constexpr int NI = KBYTES / 1024 / MW;    // loads of K (and of V) per wave and tile
+    static_assert(NI * MW * 1024 == KBYTES && RPL <= 16, "a tile must divide into 1 KiB loads per wave");
+    uint32_t gofs[NI];                        // lane's byte offset in its 16-key group
+    int ggrp[NI];                             // the group (uniform)
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
+    for (int i = 0; i < NI; ++i) {
+        const int j = wave * NI + i;
+        const int r = j * RPL + (16 * lane) / ROW;
+        const int p = ((16 * lane) % ROW) / 16;
+        gofs[i] = (uint32_t)((r & 15) * ROW + 16 * (p ^ swz(r)));
+        ggrp[i] = __builtin_amdgcn_readfirstlane(r >> 4);
+    }
+    // issue tile t's loads into buf (block 0's rows where a group has no data: inside the
+    // pool; masked, and V rows past the end zeroed once landed)
+    auto issue = [&](uint8_t *buf, int t) {
+        int64_t base[NT];
+        group_bases(t, base);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
             int64_t b = base[0];
 #pragma unroll
-            for (int j = 1; j < NT; ++j)
-                if ((pkey[i] >> 4) == j) b = base[j];
-            st.ok[i] = k0 + pkey[i] < end && b >= 0;
-            const int64_t off = st.ok[i] ? b + prow[i] : 0;
-            st.k[i] = *(const u32x4 *)(key_cache + off);
-            st.v[i] = *(const u32x4 *)(value_cache + off);
+            for (int g = 1; g < NT; ++g)
+                if (ggrp[i] == g) b = base[g];
+            b = b >= 0 ? b : 0;
+            const int j = wave * NI + i;
+            __builtin_amdgcn_global_load_lds((const void *)(key_cache + b + gofs[i]),
+                                             (__attribute__((address_space(3))) void *)(buf + j * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(value_cache + b + gofs[i]),
+                                             (__attribute__((address_space(3))) void *)(buf + KBYTES + j * 1024), 16,
+                                             0, 0);
         }
     };
-    // K and V rows as they are (padded strides)
-    auto store_tile = [&](const Stage &st, uint8_t *buf) {
-#pragma unroll
-        for (int i = 0; i < NCH; i += 2) {
-            u32x4 k0w = st.k[i], k1w = st.k[i + 1], v0w = st.v[i], v1w = st.v[i + 1];
-            if (!st.full) {
-                if (!st.ok[i]) k0w = v0w = u32x4{0, 0, 0, 0};
-                if (!st.ok[i + 1]) k1w = v1w = u32x4{0, 0, 0, 0};
-            }
-            *(u32x4 *)(buf + kst[i]) = k0w;
-            *(u32x4 *)(buf + kst[i + 1]) = k1w;
-            uint8_t *vt = buf + KBYTES + vst[i / 2];
-            *(u32x4 *)vt = v0w;
-            *(u32x4 *)(vt + VROW) = v1w;
-        }
+    // this wave's loads of every tile but the newest issued have landed (2 NI loads per
+    // tile in flight at most: s_waitcnt vmcnt(2 NI), gfx9 encoding with expcnt 7, lgkmcnt 15)
+    auto wait_previous = [&]() {
+        constexpr int V = 2 * NI;
+        __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
     };
-    // V^T operand reads: d = 16 nn + n, keys of group g = 8h + q (+4): the swizzle of
-    // d depends on nn only, so a lane needs one base per swizzle value
-    // ds_read_b64_tr_b16 (checked on gfx950): within each 16-lane group, lane j receives
-    // element j % 4 of the 8-byte reads of lanes 4k + j / 4, k = 0..3.  Lane (n, q) reads
-    // row 4q + n / 4, columns 16 nn + 4 (n % 4) .. +3, so lane (n, q) receives
-    // V[keys 4q .. 4q + 3][d = 16 nn + n]: the V^T operand's k order.
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    const int vrd0 = (4 * q + (n >> 2)) * VROW + 8 * (n & 3);
-    auto compute_tile = [&](const uint8_t *buf, int t) {
+    // Workgroup barrier that leaves the newest tile's loads in flight: __syncthreads()
+    // would wait for every load (its release fence covers loads into LDS).  Each wave has
+    // already waited for its own loads of the tile the others read next (wait_previous);
+    // it waits for its own LDS operations (zeroing, reads of the buffer about to be
+    // refilled), then meets the others.  The signal fences keep the compiler from moving
+    // memory operations across.
+    auto barrier = [&]() {
+        __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    // V rows of tile t at or past `end` as zeros (this wave's pieces, once landed): their
+    // weight is 0, and 0 * NaN would poison the product
+    auto zero_tail = [&](uint8_t *buf, int t) {
         const int k0 = t * KT;
-        // scores S^T: lane holds keys k0 + 16 tt + 4 q + i of row n of each fragment
-        float sc[RF][NT][4];
-        if (PA_MQ_PRIO) __builtin_amdgcn_s_setprio(1);
+        if (k0 + KT > end) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int j = wave * NI + i;
+                const int r = j * RPL + (16 * lane) / ROW;
+                if (k0 + r >= end) *(u32x4 *)(buf + KBYTES + j * 1024 + 16 * lane) = u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    // operand read offsets of the lane (constant over tiles): K piece 4 kk + q of row n;
+    // V 8 bytes of row 4 q + n / 4 at byte 32 nn + 8 (n % 4) (the rows 16 and 32 further
+    // share the permutation)
+    uint32_t kofs[NKK], vofs[NN];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) kofs[kk] = (uint32_t)(n * ROW + 16 * ((4 * kk + q) ^ swz(n)));
+#pragma unroll
+    for (int nn = 0; nn < NN; ++nn) {
+        const int r = 4 * q + (n >> 2);
+        vofs[nn] = (uint32_t)(KBYTES + r * ROW + 16 * ((2 * nn + ((n & 3) >> 1)) ^ swz(r)) + 8 * (n & 1));
+    }
+    auto k_at = [&](const uint8_t *buf, int tt, int kk) -> u32x4 {
+        return *(const u32x4 *)(buf + 16 * tt * ROW + kofs[kk]);
+    };
+    auto v_base = [&](const uint8_t *buf) -> const uint8_t * { return buf; };
+    auto read_v = [&](const uint8_t *vb, int nn, int h) -> u32x4 {
+        const lds_u8 *r0 = (const lds_u8 *)vb + vofs[nn] + 32 * h * ROW;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(r0));
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(r0 + 16 * ROW));
+        const uint2 lw = __builtin_bit_cast(uint2, lo), hw = __builtin_bit_cast(uint2, hi);
+        return u32x4{lw.x, lw.y, hw.x, hw.y};
+    };
+    typedef float Scores[RF][NT][4];
+    // scores S^T of the tile in buf: lane holds keys 16 tt + 4 q + i of row n of each
+    // fragment (raw products; the scale enters at the exponent)
+    auto scores = [&](const uint8_t *buf, Scores &sc) {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             f32x4 acc[RF];
@@ -299,7 +330,7 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
             for (int f = 0; f < RF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
-                const u32x4 ka = *(const u32x4 *)(buf + (16 * tt + n) * KROW + (32 * kk + 8 * q) * 2);
+                const u32x4 ka = k_at(buf, tt, kk);
 #pragma unroll
                 for (int f = 0; f < RF; ++f) acc[f] = Mma<T>::run(ka, qb[f][kk], acc[f]);
             }
@@ -308,24 +339,12 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[f][tt][i] = acc[f][i];
         }
-        if (PA_MQ_PRIO) __builtin_amdgcn_s_setprio(0);
-        // V^T operand reads for this tile (see below), issued before the softmax
-        auto read_v = [&](int nn, int h) -> u32x4 {
-            const uint8_t *r0 = buf + KBYTES + vrd0 + (32 * h) * VROW + 32 * nn;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(r0));
-            const s16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(r0 + 16 * VROW));
-            const uint2 lw = __builtin_bit_cast(uint2, lo), hw = __builtin_bit_cast(uint2, hi);
-            return u32x4{lw.x, lw.y, hw.x, hw.y};
-        };
-        u32x4 vpre[PA_MQ_VPREFETCH ? NN : 1][NH];
-        if (PA_MQ_VPREFETCH) {
-#pragma unroll
-            for (int nn = 0; nn < (PA_MQ_VPREFETCH ? NN : 1); ++nn)
-#pragma unroll
-                for (int h = 0; h < NH; ++h) vpre[nn][h] = read_v(nn, h);
-        }
-        if (k0 + KT - 1 > wave_first_pos) {  // a diagonal tile: mask keys past each row
+    };
+    // causal mask of tile t: keys past each row's position (only tiles that reach past the
+    // wave's first row need it)
+    auto mask = [&](Scores &sc, int t) {
+        const int k0 = t * KT;
+        if (k0 + KT - 1 > wave_first_pos) {
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
@@ -334,11 +353,24 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
                     for (int i = 0; i < 4; ++i)
                         if (k0 + 16 * tt + 4 * q + i > pos[f]) sc[f][tt][i] = -INFINITY;
         }
-        // P^T operands per 32-key half h: k slot j < 4 -> key 32h + 4q + j,
-        // j >= 4 -> key 32h + 16 + 4q + j - 4
-        u32x4 pb[RF][NH];
-        float alpha[RF];
-        bool grow = false;
+    };
+    auto rescale = [&](const float (&alpha)[RF]) {
+#pragma unroll
+        for (int f = 0; f < RF; ++f) {
+            osum[f] *= alpha[f];
+#pragma unroll
+            for (int nn = 0; nn < NN; ++nn) o[f][nn] *= alpha[f];
+        }
+    };
+    // online softmax of a tile's (masked) scores, first half: the reference a row's weights
+    // are taken against only moves when the row's scores pass it by more than
+    // 2^RESCALE_LOG2.  Each lane compares its own scores with that bound (raw products
+    // against (m + RESCALE_LOG2) / sl); only when some lane's pass does the wave take the
+    // rows' maxima over their 4 lanes and move the references (alpha: the factor for the
+    // sums so far).  ms: the reference the weights are taken against.
+    auto row_max = [&](const Scores &sc, float (&alpha)[RF], float (&ms)[RF]) {
+        bool pass = false;
+        float lm[RF];
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
             float cm = sc[f][0][0];
@@ -346,13 +378,29 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[f][tt][i]);
-            cm = max_over_column(cm);
-            const float mt = cm * sl;  // this tile's max of the row (-inf: nothing visible)
-            const bool g = mt > m[f] + RESCALE_LOG2;
-            alpha[f] = g ? fast_exp2(m[f] - mt) : 1.f;
-            m[f] = g ? mt : m[f];
-            grow |= g;
-            const float ms = m[f] == -INFINITY ? 0.f : m[f];
+            lm[f] = cm;
+            pass |= cm > bound[f];
+            alpha[f] = 1.f;
+        }
+        if (__any(pass)) {
+#pragma unroll
+            for (int f = 0; f < RF; ++f) {
+                const float mt = max_over_column(lm[f]) * sl;  // the tile's max of the row
+                const bool g = mt > m[f] + RESCALE_LOG2;
+                alpha[f] = g ? fast_exp2(m[f] - mt) : 1.f;
+                m[f] = g ? mt : m[f];
+                bound[f] = (m[f] + RESCALE_LOG2) * inv_sl;
+            }
+            rescale(alpha);
+        }
+#pragma unroll
+        for (int f = 0; f < RF; ++f) ms[f] = m[f] == -INFINITY ? 0.f : m[f];
+    };
+    // second half: the weights, as P^T operands per 32-key half h (k slot j < 4 -> key
+    // 32h + 4q + j, j >= 4 -> key 32h + 16 + 4q + j - 4)
+    auto weights = [&](const Scores &sc, const float (&ms)[RF], u32x4 (&pb)[RF][NH]) {
+#pragma unroll
+        for (int f = 0; f < RF; ++f)
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
                 uint32_t pk[4];
@@ -360,23 +408,14 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
                     for (int i = 0; i < 4; i += 2)
-                        pk[2 * u + i / 2] = round2<T>(fast_exp2(fmaf(sc[f][2 * h + u][i], sl, -ms)),
-                                                      fast_exp2(fmaf(sc[f][2 * h + u][i + 1], sl, -ms)));
+                        pk[2 * u + i / 2] = round2<T>(fast_exp2(fmaf(sc[f][2 * h + u][i], sl, -ms[f])),
+                                                      fast_exp2(fmaf(sc[f][2 * h + u][i + 1], sl, -ms[f])));
                 pb[f][h] = u32x4{pk[0], pk[1], pk[2], pk[3]};
             }
-        }
-        // V^T operand per 16-row d fragment and half: keys 32h + 4q..+3 and 32h + 16 + 4q..+3
-        // of d = 16 nn + n (two transpose reads of the V rows, read_v), shared by the fragments
-        // rescale only when some row's reference moved (otherwise every alpha is 1)
-        if (__any(grow)) {
-#pragma unroll
-            for (int f = 0; f < RF; ++f) {
-                osum[f] *= alpha[f];
-#pragma unroll
-                for (int nn = 0; nn < NN; ++nn) o[f][nn] *= alpha[f];
-            }
-        }
-        if (PA_MQ_PRIO) __builtin_amdgcn_s_setprio(1);
+    };
+    // the normaliser (P against a ones operand) and the value product of the tile in buf
+    auto values = [&](const uint8_t *buf, const u32x4 (&pb)[RF][NH]) {
+        const auto vb = v_base(buf);
 #pragma unroll
         for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -386,44 +425,48 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
                 // keys 32h + 4q .. +3, then 32h + 16 + 4q .. +3, of d = 16 nn + n
-                const u32x4 va = PA_MQ_VPREFETCH ? vpre[PA_MQ_VPREFETCH ? nn : 0][h] : read_v(nn, h);
+                const u32x4 va = read_v(vb, nn, h);
 #pragma unroll
                 for (int f = 0; f < RF; ++f) o[f][nn] = Mma<T>::run(va, pb[f][h], o[f][nn]);
             }
         }
-        if (PA_MQ_PRIO) __builtin_amdgcn_s_setprio(0);
     };
 
-    // While tile t is used from LDS, tile t + 1 is being loaded into registers (and with
-    // PA_MQ_DEPTH 2, tile t + 2 as well).  Loads past the last tile read block 0's first
-    // row (all masked) instead of being skipped, so the compiler's waits stay exact.
-    if (PA_MQ_DEPTH == 1 && ntiles > 0) {
-        Stage st;
-        load_tile(st, 0);
-        store_tile(st, lds);
-        __syncthreads();
-        for (int t = 0; t < ntiles; ++t) {
-            load_tile(st, t + 1);
-            if (t * KT < wave_end) compute_tile(lds + (t & 1) * BUF, t);
-            if (t + 1 < ntiles) store_tile(st, lds + ((t + 1) & 1) * BUF);
-            __syncthreads();
-        }
-    } else if (ntiles > 0) {
-        Stage sa, sb;
-        load_tile(sa, 0);
-        load_tile(sb, 1);
-        store_tile(sa, lds);
-        __syncthreads();
-        // next: the stage holding tile t + 1; spare: free, receives tile t + 2
-        auto step = [&](Stage &next, Stage &spare, int t) {
-            load_tile(spare, t + 2);
-            if (t * KT < wave_end) compute_tile(lds + (t & 1) * BUF, t);
-            if (t + 1 < ntiles) store_tile(next, lds + ((t + 1) & 1) * BUF);
-            __syncthreads();
+    // a wave skips the tiles past its own last row
+    const int wave_end = wrow0 < rows ? ctx - nq + (min(rows, wrow0 + 16 * RF) - 1) / G + 1 : 0;
+    auto compute = [&](const uint8_t *buf, int t) {
+        if (t * KT >= wave_end) return;
+        Scores sc;
+        scores(buf, sc);
+        mask(sc, t);
+        float alpha[RF], ms[RF];
+        row_max(sc, alpha, ms);
+        u32x4 pb[RF][NH];
+        weights(sc, ms, pb);
+        values(buf, pb);
+    };
+    // Three buffers, tile t in buffer t % 3, loaded directly from HBM into LDS two tiles
+    // ahead of use.  Step t: tile t + 2's loads are issued into the buffer tile t - 1 left,
+    // tile t is used, the wave waits for its own loads of tile t + 1 (zeroing V rows past
+    // the end), and one barrier makes every wave's loads of tile t + 1 visible and frees
+    // buffer t % 3.  Loads past the last tile read block 0's rows and are never used.
+    if (ntiles > 0) {
+        issue(lds0, 0);
+        issue(lds1, 1);
+        wait_previous();
+        zero_tail(lds0, 0);
+        barrier();
+        auto step = [&](uint8_t *cur, uint8_t *nxt, uint8_t *fre, int t) {
+            issue(fre, t + 2);
+            compute(cur, t);
+            wait_previous();
+            zero_tail(nxt, t + 1);
+            barrier();
         };
-        for (int t = 0; t < ntiles; t += 2) {
-            step(sb, sa, t);
-            if (t + 1 < ntiles) step(sa, sb, t + 1);
+        for (int t = 0; t < ntiles; t += 3) {
+            step(lds0, lds1, lds2, t);
+            if (t + 1 < ntiles) step(lds1, lds2, lds0, t + 1);
+            if (t + 2 < ntiles) step(lds2, lds0, lds1, t + 2);
         }
     }
 
