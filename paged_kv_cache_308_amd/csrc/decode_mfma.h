@@ -44,6 +44,9 @@ namespace mfma {
 #ifndef PA_MFMA_WAVES
 #define PA_MFMA_WAVES 4
 #endif
+#ifndef PA_MFMA_VREG
+#define PA_MFMA_VREG 1  // V through registers, two chunks ahead (0: direct-to-LDS loads, one ahead)
+#endif
 #ifndef PA_MFMA_BAL_PER_CU
 #define PA_MFMA_BAL_PER_CU 0  // balanced split: workgroups per CU (0: as many as fit)
 #endif
@@ -243,6 +246,79 @@ __device__ __forceinline__ void consume_chunk(const u32x4 (&k)[2][Geom<D>::NKK],
     for (int nn = 0; nn < Gm::NN; ++nn) o[nn] = Mma<T>::run(vt[nn], pb, o[nn]);
 }
 
+// As consume_chunk, with the V^T operands read from the chunk's LDS stage fragment by
+// fragment (read_vt's lane mapping) instead of from registers read beforehand: fewer live
+// registers, for the form that stages V through registers.
+template <typename T, int D>
+__device__ __forceinline__ void consume_chunk_lds(const u32x4 (&k)[2][Geom<D>::NKK], const u32x4 (&qb)[Geom<D>::NKK],
+                                                  uint8_t *stage, int tok0, int end, float scale_log2, int n, int q,
+                                                  float &m, float &lsum, f32x4 (&o)[Geom<D>::NN]) {
+    using Gm = Geom<D>;
+    const bool tail = tok0 + CT > end;
+    float sc[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < Gm::NKK; ++kk) acc = Mma<T>::run(k[tt][kk], qb[kk], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = !tail || (tok0 + 16 * tt + tile_row<D>(q, i) < end);
+            sc[tt][i] = ok ? acc[i] * scale_log2 : -INFINITY;
+        }
+    }
+    float cm = sc[0][0];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[tt][i]);
+    cm = max_over_column(cm);
+    const float mn = fmaxf(m, cm);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(m - ms);
+    m = mn;
+    uint32_t pk[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            float b0, b1;
+            const uint32_t h0 = Mma<T>::round(fast_exp2(sc[tt][i] - ms), b0);
+            const uint32_t h1 = Mma<T>::round(fast_exp2(sc[tt][i + 1] - ms), b1);
+            psum += b0 + b1;
+            pk[2 * tt + i / 2] = h0 | (h1 << 16);
+        }
+    lsum = lsum * alpha + psum;
+    const u32x4 pb = u32x4{pk[0], pk[1], pk[2], pk[3]};
+#pragma unroll
+    for (int nn = 0; nn < Gm::NN; ++nn) o[nn] *= alpha;
+    // rows past `end` as zeros (0 * NaN would poison the product); word w of an operand
+    // holds k slots 2w (low half) and 2w + 1
+    u32x4 keep = u32x4{~0u, ~0u, ~0u, ~0u};
+    if (tail) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int t0 = (w < 2 ? 0 : 16) + tile_row<D>(q, (2 * w) & 3);
+            const int t1 = (w < 2 ? 0 : 16) + tile_row<D>(q, (2 * w + 1) & 3);
+            keep[w] = (tok0 + t0 < end ? 0x0000ffffu : 0u) | (tok0 + t1 < end ? 0xffff0000u : 0u);
+        }
+    }
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int vrow = tile_row<D>(q, n >> 2);
+#pragma unroll
+    for (int nn = 0; nn < Gm::NN; ++nn) {
+        const int col = (16 * nn + 4 * (n & 3)) * 2;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)v_at<D>(stage, vrow, col));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)v_at<D>(stage, 16 + vrow, col));
+        const uint2 lw = __builtin_bit_cast(uint2, lo), hw = __builtin_bit_cast(uint2, hi);
+        const u32x4 va = u32x4{lw.x, lw.y, hw.x, hw.y} & keep;
+        o[nn] = Mma<T>::run(va, pb, o[nn]);
+    }
+}
+
 // Q^T operand of (sequence s, KV head kvh): lane holds Q[head n][32 kk + 8 q .. +8];
 // heads past the group are zero
 template <int D, int G>
@@ -349,13 +425,50 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
     struct Chunk {
         u32x4 k[2][NKK];
     };
-    auto issue = [&](Chunk &b, int c, int stage) {
-        int64_t base[2];
+    auto bases = [&](int c, int64_t (&base)[2]) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             base[tt] = tile_base(c, tt);
             base[tt] = base[tt] < 0 ? 0 : base[tt];
         }
+    };
+#if PA_MFMA_VREG
+    // V rows through registers (ordinary loads, like K): with every load of one kind the
+    // compiler's waits count exactly, so V can run two chunks ahead.  (A direct-to-LDS
+    // load in flight makes every wait for a register load wait for all loads.)
+    struct VSet {
+        u32x4 v[2 * Gm::VL];
+    };
+    auto issue_vr = [&](VSet &b, int c) {
+        int64_t base[2];
+        bases(c, base);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < Gm::VL; ++i)
+                b.v[tt * Gm::VL + i] = kv_load<NT>((const u32x4 *)(value_cache + base[tt] + i * 1024 + lane * 16));
+    };
+    // into the wave's stage, in the layout the direct loads used (1 KiB groups padded by 32 B);
+    // the stage's previous chunk was read out two chunks ago (LDS operations of a wave run in order)
+    auto stage_vr = [&](const VSet &b, int stage) {
+        uint8_t *sp = wave_lds + stage * Gm::STAGE;
+#pragma unroll
+        for (int j = 0; j < 2 * Gm::VL; ++j) *(u32x4 *)(sp + j * Gm::KSTR + lane * 16) = b.v[j];
+    };
+    auto issue_kr = [&](Chunk &b, int c) {
+        int64_t base[2];
+        bases(c, base);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+                b.k[tt][kk] = kv_load<NT>((const u32x4 *)(key_cache + base[tt] + tile_row<D>(n >> 2, n & 3) * ROW +
+                                                          (32 * kk + 8 * q) * 2));
+    };
+#endif
+    auto issue = [&](Chunk &b, int c, int stage) {
+        int64_t base[2];
+        bases(c, base);
         // the stage was last read two chunks ago (its operands long used); the wait makes
         // the order explicit before the loads rewrite it
         wait_lds_reads();
@@ -366,12 +479,58 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
         consume_chunk<T, D>(b.k, qb, vt, start + c * CT, end, scale_log2, n, q, st.m, st.lsum, st.o);
     };
     auto stage_at = [&](int stage) { return wave_lds + stage * Gm::STAGE; };
+    auto consume_lds = [&](const Chunk &b, int c, int stage) {
+        consume_chunk_lds<T, D>(b.k, qb, stage_at(stage), start + c * CT, end, scale_log2, n, q, st.m, st.lsum, st.o);
+    };
 
+    const int mine = nchunks > wave ? (nchunks - wave + MW - 1) / MW : 0;
+    auto cidx = [&](int i) { return wave + i * MW; };
+#if PA_MFMA_VREG
+    // This wave's chunks are c_i = wave + i MW, i < mine.  Chunk i's V rows are loaded two
+    // chunks ahead into register set i % 2 and stored into stage i % 2 once the stage's
+    // previous chunk has been read out; its K operands are loaded one chunk ahead into K
+    // set i % 2; then the chunk is used (K from registers, V^T read from the stage).  The
+    // loop starts with loads and ends with the next chunk's store, so the compiler's waits
+    // for register loads fall inside an iteration, where it counts them exactly.  Loads in
+    // the steady-state loop are unconditional (no branch around a load); the last one to
+    // three chunks run after it; loads past the range read block 0's rows, never used.
+    Chunk K0, K1;
+    VSet V0, V1;
+    if (mine > 0) {
+        issue_vr(V0, cidx(0));
+        issue_vr(V1, cidx(1));
+        issue_kr(K0, cidx(0));
+        stage_vr(V0, 0);
+        int i = 0;
+        for (; i + 3 < mine; i += 2) {
+            issue_vr(V0, cidx(i + 2));
+            issue_kr(K1, cidx(i + 1));
+            consume_lds(K0, cidx(i), 0);
+            stage_vr(V1, 1);
+            issue_vr(V1, cidx(i + 3));
+            issue_kr(K0, cidx(i + 2));
+            consume_lds(K1, cidx(i + 1), 1);
+            stage_vr(V0, 0);
+        }
+        const int left = mine - i;  // 1 to 3; chunk i's V is in stage 0, chunk i + 1's in V1
+        if (left == 3) issue_vr(V0, cidx(i + 2));
+        if (left >= 2) issue_kr(K1, cidx(i + 1));
+        consume_lds(K0, cidx(i), 0);
+        if (left >= 2) {
+            stage_vr(V1, 1);
+            if (left == 3) issue_kr(K0, cidx(i + 2));
+            consume_lds(K1, cidx(i + 1), 1);
+        }
+        if (left == 3) {
+            stage_vr(V0, 0);
+            consume_lds(K0, cidx(i + 2), 0);
+        }
+    }
+#else
     // This wave's chunks are wave, wave + MW, ...  Per chunk: its V^T operands are read
     // from LDS (once its loads have landed), the next chunk's loads are issued, then the
     // chunk is used from registers while they are in flight.  The steady-state loop always
     // has a next chunk to prefetch (see tile_base); the last one or two run after it.
-    const int mine = nchunks > wave ? (nchunks - wave + MW - 1) / MW : 0;
     Chunk A, Bf;
     if (mine > 0) {
         issue(A, wave, 0);
@@ -395,6 +554,7 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
             consume(A, wave + j * MW);
         }
     }
+#endif
     if (append && wave == nchunks % MW) {
         const int lb = tnew >> log2_block;
         int64_t base = -1;
@@ -510,7 +670,7 @@ __device__ __forceinline__ void finish(const WaveState<D> &st, uint8_t *lds, int
 }
 
 template <typename T, int D, int G, bool SPLIT, bool NT>
-__global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
+__global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(
     void *__restrict__ out, const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
     const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, float *__restrict__ ws_max, float *__restrict__ ws_sum,
@@ -563,7 +723,7 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_kernel(
 // take the range's chunks in turn, as the one-pass kernel does for a whole context,
 // and at the item's end they merge and write the item's partial.
 template <typename T, int D, int G, bool NT>
-__global__ __launch_bounds__(MW * 64) void decode_mfma_balanced_kernel(
+__global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_balanced_kernel(
     const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
     const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int32_t *__restrict__ ws_hdr, float *__restrict__ ws_max,
@@ -678,7 +838,7 @@ __global__ __launch_bounds__(MW * 64) void decode_mfma_balanced_kernel(
 // for the member's later tokens.  Which members the pass serves was decided by
 // group_plan_kernel: seq_group[s] == j (then seq_parts[s] == group_parts[j]).
 template <typename T, int D, int G, bool NT>
-__global__ __launch_bounds__(MW * 64) void decode_mfma_grouped_kernel(
+__global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_grouped_kernel(
     const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
     const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ group_start, const int32_t *__restrict__ group_parts,
