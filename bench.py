@@ -593,7 +593,7 @@ def main():
     g = w.num_q_heads // w.num_kv_heads
     mfma = w.kv != "fp8" and (args.variant == 2 or (args.variant == 0 and g >= 2 and w.dtype != "f32"))
     if args.grouped:
-        kernels = "group_plan_kernel + decode_mfma_grouped_kernel + decode_valu_kernel"
+        kernels = "decode_mfma_grouped_kernel (with the plan) + decode_valu_kernel"
     elif args.P < 0:
         kernels = ("decode_mfma_balanced_kernel" if mfma else "decode_balanced_kernel") + " + balanced_merge_kernel"
     else:

@@ -249,8 +249,8 @@ static int decode_common(DecodeArgs &a, int max_context_len, float scale, int va
         a.partition_size = 0;
         a.max_partitions = 1;
         if (a.max_group_parts > 0) {
-            int rc = launch_group_plan(a);
-            if (rc == PA_OK) rc = launch_decode_mfma_grouped(a);
+            // the plan (which sequences each group serves) and the shared spans, one launch
+            const int rc = launch_decode_mfma_grouped(a);
             if (rc != PA_OK) return rc;
             a.skip_parts = a.seq_parts;
         }

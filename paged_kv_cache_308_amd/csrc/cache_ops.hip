@@ -291,66 +291,5 @@ int launch_gather_read(const uint64_t *tile_addrs, int num_tiles, int tile_bytes
     return check_launch("gather_read");
 }
 
-// Shared-prefix groups (pa_decode_grouped): for each sequence s, the group whose range
-// holds s (group_start read as an ascending array) and whether that group's
-// shared-prefix pass serves it: the group has at most group_rows members, shares
-// 1 <= parts <= max_group_parts leading partitions, the shared tokens end before the
-// newest one (parts * P <= ctx - 1), and s reaches every shared block through the same
-// table entry as the group's first sequence, inside the pool.  seq_parts[s] = parts
-// when served, else 0 and seq_group[s] = -1: the partitioned kernel then attends to the
-// whole context of s itself, so a group described wrongly costs speed, never results.
-__global__ __launch_bounds__(64) void group_plan_kernel(
-    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-    const int32_t *__restrict__ group_start, const int32_t *__restrict__ group_parts,
-    int32_t *__restrict__ seq_group, int32_t *__restrict__ seq_parts, int num_seqs, int num_groups,
-    int max_blocks_per_seq, int log2_block, int num_blocks, int partition_size, int group_rows,
-    int max_group_parts) {
-    // one wave per sequence; every lookup spread over the lanes
-    const int s = blockIdx.x;
-    const int lane = threadIdx.x;
-    // j = (number of group starts <= s) - 1: the last such group when the starts ascend
-    int count = 0;
-    for (int base = 0; base < num_groups; base += 64) {
-        const int i = base + lane;
-        count += __popcll(__ballot(i < num_groups && group_start[i] <= s));
-    }
-    const int j = count - 1;
-    bool ok = j >= 0;
-    int parts = 0, s0 = 0;
-    if (ok) {
-        s0 = group_start[j];
-        const int s1 = group_start[j + 1];
-        parts = group_parts[j];
-        ok = s0 >= 0 && s0 <= s && s < s1 && s1 <= num_seqs && s1 - s0 <= group_rows && parts >= 1 &&
-             parts <= max_group_parts;
-    }
-    const int ctx = context_lens[s];
-    const int64_t shared = (int64_t)parts * partition_size;
-    ok = ok && ctx >= 1 && shared <= (int64_t)ctx - 1;
-    const int64_t nblk = shared >> log2_block;  // the partition size is a multiple of the block size
-    ok = ok && nblk <= max_blocks_per_seq;
-    if (ok) {
-        const int32_t *ts = block_tables + (int64_t)s * max_blocks_per_seq;
-        const int32_t *t0 = block_tables + (int64_t)s0 * max_blocks_per_seq;
-        bool bad = false;
-        for (int k = lane; k < (int)nblk; k += 64) {
-            const int32_t b = ts[k];
-            bad |= b != t0[k] || b < 0 || b >= num_blocks;
-        }
-        ok = !__any(bad);
-    }
-    if (lane == 0) {
-        seq_group[s] = ok ? j : -1;
-        seq_parts[s] = ok ? parts : 0;
-    }
-}
-
-int launch_group_plan(const DecodeArgs &a) {
-    hipLaunchKernelGGL(group_plan_kernel, dim3((unsigned)a.num_seqs), dim3(64), 0, (hipStream_t)a.stream,
-                       a.block_tables, a.context_lens, a.group_start, a.group_parts, a.seq_group, a.seq_parts,
-                       a.num_seqs, a.num_groups, a.max_blocks_per_seq, __builtin_ctz(a.block_size), a.num_blocks,
-                       a.group_span, a.group_rows, a.max_group_parts);
-    return check_launch("group_plan");
-}
 
 }  // namespace pa

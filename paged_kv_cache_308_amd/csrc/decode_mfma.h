@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include "balanced.h"
+#include "group_plan.h"
 #include "internal.h"
 #include "kernel_common.h"
 
@@ -835,41 +836,63 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 // head per KV head) fill the rows of the score product, and writes each served member's
 // partial (max, sum, weighted value sums) for the whole shared span at (sequence, head)
 // of ws_max / ws_sum / ws_acc, which the one-pass vector kernel folds into its own state
-// for the member's later tokens.  Which members the pass serves was decided by
-// group_plan_kernel: seq_group[s] == j (then seq_parts[s] == group_parts[j]).
+// for the member's later tokens.  Which members are served is group_serves's decision:
+// each workgroup checks its own members (one wave per member), and the same launch
+// carries ceil(S / MW) more workgroups that record the decision for every sequence in
+// seq_group / seq_parts (one wave per sequence) for the vector kernel that follows.
 template <typename T, int D, int G, bool NT>
 __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_grouped_kernel(
     const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
-    const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
-    const int32_t *__restrict__ group_start, const int32_t *__restrict__ group_parts,
-    const int32_t *__restrict__ seq_group, const int32_t *__restrict__ seq_parts, float *__restrict__ ws_max,
-    float *__restrict__ ws_sum, float *__restrict__ ws_acc, int max_blocks_per_seq, int num_seqs,
-    int num_kv_heads, int log2_block, int num_blocks, int partition_size, int max_group_parts,
-    float scale_log2) {
+    const uint8_t *__restrict__ value_cache, GroupPlanArgs plan, int32_t *__restrict__ seq_group,
+    int32_t *__restrict__ seq_parts, float *__restrict__ ws_max, float *__restrict__ ws_sum,
+    float *__restrict__ ws_acc, int num_kv_heads, float scale_log2) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ngw = plan.num_groups * num_kv_heads;  // shared-span workgroups
+    if ((int)blockIdx.x >= ngw) {
+        // the plan: one wave per sequence
+        const int s = ((int)blockIdx.x - ngw) * MW + wave;
+        if (s >= plan.num_seqs) return;
+        int j, parts;
+        const bool ok = group_serves(plan, s, lane, j, parts);
+        if (lane == 0) {
+            seq_group[s] = ok ? j : -1;
+            seq_parts[s] = ok ? parts : 0;
+        }
+        return;
+    }
     const int kvh = blockIdx.x % num_kv_heads;
     const int j = blockIdx.x / num_kv_heads;
-    const int s0 = group_start[j];
-    const int members = group_start[j + 1] - s0;
-    if (s0 < 0 || members < 1 || members > G || s0 > num_seqs - members) return;
-    const int parts = group_parts[j];
-    if (parts < 1 || parts > max_group_parts) return;
-    uint32_t rows = 0;
-    for (int i = 0; i < members; ++i)
-        if (seq_group[s0 + i] == j && seq_parts[s0 + i] == parts) rows |= 1u << i;
-    rows = __builtin_amdgcn_readfirstlane(rows);
-    if (rows == 0) return;
+    const int s0 = plan.group_start[j];
+    const int members = plan.group_start[j + 1] - s0;
+    if (s0 < 0 || members < 1 || members > G || s0 > plan.num_seqs - members) return;
+    const int parts = plan.group_parts[j];
+    if (parts < 1 || parts > plan.max_group_parts) return;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[MW * Geom<D>::WAVE_LDS];
     static_assert((2 * MW * G + MW * G * D) * 4 <= MW * Geom<D>::WAVE_LDS, "merge area must fit the staging area");
     __shared__ int sm_bad;
+    __shared__ uint32_t sm_rows[MW];
+    // the members this pass serves: member i checked by wave i mod MW
+    uint32_t mine_rows = 0;
+    for (int i = wave; i < members; i += MW) {
+        int jj, pp;
+        if (group_serves(plan, s0 + i, lane, jj, pp) && jj == j && pp == parts) mine_rows |= 1u << i;
+    }
+    if (lane == 0) sm_rows[wave] = mine_rows;
+    __syncthreads();
+    uint32_t rows = 0;
+#pragma unroll
+    for (int w = 0; w < MW; ++w) rows |= sm_rows[w];
+    rows = __builtin_amdgcn_readfirstlane(rows);
+    if (rows == 0) return;
+
     WaveState<D> st;
     st.bad = false;
     attend_range<T, D, G, NT>(st, lds + wave * Geom<D>::WAVE_LDS, query, key_cache, value_cache,
-                              block_tables + (int64_t)s0 * max_blocks_per_seq, max_blocks_per_seq, s0, kvh,
-                              num_kv_heads, log2_block, num_blocks, 0, parts * partition_size, scale_log2, wave,
-                              lane, nullptr, nullptr, nullptr, nullptr, rows);
+                              plan.block_tables + (int64_t)s0 * plan.max_blocks_per_seq, plan.max_blocks_per_seq,
+                              s0, kvh, num_kv_heads, plan.log2_block, plan.num_blocks, 0, parts * plan.span,
+                              scale_log2, wave, lane, nullptr, nullptr, nullptr, nullptr, rows);
     // member i's partial at (sequence s0 + i, head kvh)
     finish<T, D, G>(st, lds, &sm_bad, wave, lane, nullptr, 0, ws_max, ws_sum, ws_acc,
                     (int64_t)s0 * num_kv_heads + kvh, num_kv_heads, rows);
@@ -877,13 +900,25 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 template <typename T, int D, int G>
 int launch_grouped_t(const DecodeArgs &a) {
-    const unsigned grid = (unsigned)a.num_groups * a.num_kv_heads;
+    GroupPlanArgs plan;
+    plan.block_tables = a.block_tables;
+    plan.context_lens = a.context_lens;
+    plan.group_start = a.group_start;
+    plan.group_parts = a.group_parts;
+    plan.num_seqs = a.num_seqs;
+    plan.num_groups = a.num_groups;
+    plan.max_blocks_per_seq = a.max_blocks_per_seq;
+    plan.log2_block = __builtin_ctz(a.block_size);
+    plan.num_blocks = a.num_blocks;
+    plan.span = a.group_span;
+    plan.group_rows = a.group_rows;
+    plan.max_group_parts = a.max_group_parts;
+    const int64_t grid = (int64_t)a.num_groups * a.num_kv_heads + (a.num_seqs + MW - 1) / MW;
+    if (grid > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "grid of %lld workgroups", (long long)grid);
     auto kernel = a.cached_kv ? decode_mfma_grouped_kernel<T, D, G, false> : decode_mfma_grouped_kernel<T, D, G, true>;
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(MW * 64), 0, (hipStream_t)a.stream, (const uint8_t *)a.query,
-                       (const uint8_t *)a.key_cache, (const uint8_t *)a.value_cache, a.block_tables,
-                       a.group_start, a.group_parts, a.seq_group, a.seq_parts, a.ws_max, a.ws_sum, a.ws_acc,
-                       a.max_blocks_per_seq, a.num_seqs, a.num_kv_heads, __builtin_ctz(a.block_size),
-                       a.num_blocks, a.group_span, a.max_group_parts, a.scale_log2);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(MW * 64), 0, (hipStream_t)a.stream, (const uint8_t *)a.query,
+                       (const uint8_t *)a.key_cache, (const uint8_t *)a.value_cache, plan, a.seq_group, a.seq_parts,
+                       a.ws_max, a.ws_sum, a.ws_acc, a.num_kv_heads, a.scale_log2);
     return check_launch("decode_mfma_grouped");
 }
 

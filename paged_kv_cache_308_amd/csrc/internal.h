@@ -97,8 +97,6 @@ int launch_reshape_and_cache_fp8(const void *key, const void *value, void *key_c
                                  void *stream);
 int launch_stream_read(const void *buf, size_t bytes, void *sink, void *stream);
 int launch_gather_read(const uint64_t *tile_addrs, int num_tiles, int tile_bytes, void *sink, void *stream);
-// Which sequences a group serves and for how many partitions (seq_group, seq_parts).
-int launch_group_plan(const DecodeArgs &a);
 int launch_decode_mfma_grouped(const DecodeArgs &a);
 int launch_move_blocks(const void *src_key, const void *src_value, void *dst_key, void *dst_value,
                        const int32_t *src, const int32_t *dst, int num_pairs, int num_kv_heads,
