@@ -18,11 +18,13 @@
 //    which is exactly a P^T operand once the k order is chosen to match (no shuffle);
 //  * the O^T fragment holds one head per lane column, so the online-softmax rescale
 //    and the final division use per-lane values;
-//  * V must be read transposed (8 tokens of one d per lane): each wave copies its V
-//    rows HBM -> LDS with direct 16-byte LDS loads (global_load_lds_dwordx4, no
-//    register staging) into its own double-buffered region, 1 KiB per wave load with
-//    32 bytes of padding after each KiB, and reads the V^T operand with gfx950's LDS
-//    transpose read ds_read_b64_tr_b16 (two per operand).  The tokens of a 16-token
+//  * V must be read transposed (8 tokens of one d per lane): each wave loads its V rows
+//    into registers two chunks ahead (16-byte loads, 1 KiB per wave load), stores them
+//    into its own double-buffered LDS region with 32 bytes of padding after each KiB,
+//    and reads the V^T operand with gfx950's LDS transpose read ds_read_b64_tr_b16 (two
+//    per operand).  (Direct HBM -> LDS loads would save the stores, but while one is in
+//    flight the compiler turns every wait for a register load into a wait for all
+//    loads, which limits the pipeline to one chunk ahead.)  The tokens of a 16-token
 //    tile are taken in the order tile_row gives (the K operand's rows are loaded in that
 //    order, which permutes rows within one load instruction), so the four rows one
 //    16-lane group reads together lie in different padded KiB groups: different banks.
@@ -44,9 +46,6 @@ namespace mfma {
 
 #ifndef PA_MFMA_WAVES
 #define PA_MFMA_WAVES 4
-#endif
-#ifndef PA_MFMA_VREG
-#define PA_MFMA_VREG 1  // V through registers, two chunks ahead (0: direct-to-LDS loads, one ahead)
 #endif
 #ifndef PA_MFMA_BAL_PER_CU
 #define PA_MFMA_BAL_PER_CU 0  // balanced split: workgroups per CU (0: as many as fit)
@@ -124,134 +123,18 @@ __device__ inline int tile_row(int a, int m) {
         return 8 * (m >> 1) + (m & 1) + 2 * a;
 }
 
-// Loads of one chunk: tile tt's 16 rows start at byte base[tt] of the pools.  Its V
-// rows go to LDS stage `stage` (direct loads, in token order), its K operands to k
-// (lane (n, q) supplies row n of the score product: token tile_row(n / 4, n % 4)).
-template <int D, bool NT>
-__device__ __forceinline__ void issue_chunk(u32x4 (&k)[2][Geom<D>::NKK], uint8_t *stage, const int64_t (&base)[2],
-                                            const uint8_t *key_cache, const uint8_t *value_cache, int lane,
-                                            int n, int q) {
-    using Gm = Geom<D>;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int i = 0; i < Gm::VL; ++i)
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(value_cache + base[tt] + i * 1024 + lane * 16),
-                (__attribute__((address_space(3))) void *)(stage + (tt * Gm::VL + i) * Gm::KSTR), 16, 0, 0);
-#pragma unroll
-        for (int kk = 0; kk < Gm::NKK; ++kk)
-            k[tt][kk] = kv_load<NT>((const u32x4 *)(key_cache + base[tt] + tile_row<D>(n >> 2, n & 3) * Gm::ROW +
-                                                    (32 * kk + 8 * q) * 2));
-    }
-}
-
-// V^T operands of one chunk, read from its LDS stage into registers: fragment nn of
-// lane (n, q) holds V[token of k slot j][d = 16 nn + n], k slot j < 4 -> token
-// tile_row(q, j) (tile 0), j >= 4 -> token 16 + tile_row(q, j - 4) (tile 1).
+// One chunk of CT tokens starting at position tok0 (rows at or past `end` masked) folded
+// into a wave's online-softmax state: m (running max of head n), lsum (this lane's share
+// of the normaliser) and o (O^T fragments).  k: the chunk's K operands; its V rows are
+// in the LDS stage, read as V^T operands fragment by fragment.
 // ds_read_b64_tr_b16 (lane mapping checked on gfx950): within each 16-lane group, lane j
 // receives element j % 4 of the 8-byte reads of lanes 4k + j / 4, k = 0..3.  Lane (n, q)
 // reads 8 bytes of row tile_row(q, n / 4) at d = 16 nn + 4 (n % 4), so it receives
 // V[tile_row(q, k)][16 nn + n] for k = 0..3: tile 0's k slots; the same read 16 rows
-// further gives tile 1's.
-//
-// The operands are read before the next chunk's loads are issued: an LDS read after a
-// direct-to-LDS load waits for every load in flight (the compiler cannot tell the stages
-// apart), so reading first leaves the next chunk's loads in flight while this one is used.
-template <int D>
-__device__ __forceinline__ void read_vt(u32x4 (&vt)[Geom<D>::NN], uint8_t *stage, int n, int q) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    const int vrow = tile_row<D>(q, n >> 2);
-#pragma unroll
-    for (int nn = 0; nn < Geom<D>::NN; ++nn) {
-        const int col = (16 * nn + 4 * (n & 3)) * 2;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)v_at<D>(stage, vrow, col));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)v_at<D>(stage, 16 + vrow, col));
-        const uint2 lw = __builtin_bit_cast(uint2, lo), hw = __builtin_bit_cast(uint2, hi);
-        vt[nn] = u32x4{lw.x, lw.y, hw.x, hw.y};
-    }
-}
-
-// Wait until this wave's LDS reads have completed (before direct loads rewrite a stage
-// they read).  s_waitcnt with only the LGKM count at 0 (gfx9 encoding: vmcnt 63,
-// expcnt 7, lgkmcnt 0).
-__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// One chunk of CT tokens starting at position tok0 (rows at or past `end` masked)
-// folded into a wave's online-softmax state: m (running max of head n), lsum (this
-// lane's share of the normaliser) and o (O^T fragments).  k: the chunk's K operands;
-// vt: its V^T operands (read_vt), from registers only.
+// further gives tile 1's.  P^T operand: k slot j < 4 -> token tile_row(q, j) (tile 0),
+// j >= 4 -> token 16 + tile_row(q, j - 4) (tile 1).
 template <typename T, int D>
 __device__ __forceinline__ void consume_chunk(const u32x4 (&k)[2][Geom<D>::NKK], const u32x4 (&qb)[Geom<D>::NKK],
-                                              u32x4 (&vt)[Geom<D>::NN], int tok0, int end, float scale_log2,
-                                              int n, int q, float &m, float &lsum, f32x4 (&o)[Geom<D>::NN]) {
-    using Gm = Geom<D>;
-    const bool tail = tok0 + CT > end;
-    // scores S^T: lane holds tokens 16 tt + tile_row(q, i) of head n
-    float sc[2][4];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < Gm::NKK; ++kk) acc = Mma<T>::run(k[tt][kk], qb[kk], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok = !tail || (tok0 + 16 * tt + tile_row<D>(q, i) < end);
-            sc[tt][i] = ok ? acc[i] * scale_log2 : -INFINITY;
-        }
-    }
-    float cm = sc[0][0];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[tt][i]);
-    cm = max_over_column(cm);
-    const float mn = fmaxf(m, cm);
-    const float ms = mn == -INFINITY ? 0.f : mn;
-    const float alpha = fast_exp2(m - ms);
-    m = mn;
-    // P^T operand: k slot j < 4 -> token tile_row(q, j) (tile 0), j >= 4 -> token
-    // 16 + tile_row(q, j - 4) (tile 1)
-    uint32_t pk[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-            float b0, b1;
-            const uint32_t h0 = Mma<T>::round(fast_exp2(sc[tt][i] - ms), b0);
-            const uint32_t h1 = Mma<T>::round(fast_exp2(sc[tt][i + 1] - ms), b1);
-            psum += b0 + b1;
-            pk[2 * tt + i / 2] = h0 | (h1 << 16);
-        }
-    lsum = lsum * alpha + psum;
-    const u32x4 pb = u32x4{pk[0], pk[1], pk[2], pk[3]};
-#pragma unroll
-    for (int nn = 0; nn < Gm::NN; ++nn) o[nn] *= alpha;
-    if (tail) {
-        // V of rows past `end` as zeros (whatever was read there): 0 * NaN would poison
-        // the product.  Word w of a fragment holds k slots 2w (low half) and 2w + 1.
-        u32x4 keep;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int t0 = (w < 2 ? 0 : 16) + tile_row<D>(q, (2 * w) & 3);
-            const int t1 = (w < 2 ? 0 : 16) + tile_row<D>(q, (2 * w + 1) & 3);
-            keep[w] = (tok0 + t0 < end ? 0x0000ffffu : 0u) | (tok0 + t1 < end ? 0xffff0000u : 0u);
-        }
-#pragma unroll
-        for (int nn = 0; nn < Gm::NN; ++nn) vt[nn] &= keep;
-    }
-#pragma unroll
-    for (int nn = 0; nn < Gm::NN; ++nn) o[nn] = Mma<T>::run(vt[nn], pb, o[nn]);
-}
-
-// As consume_chunk, with the V^T operands read from the chunk's LDS stage fragment by
-// fragment (read_vt's lane mapping) instead of from registers read beforehand: fewer live
-// registers, for the form that stages V through registers.
-template <typename T, int D>
-__device__ __forceinline__ void consume_chunk_lds(const u32x4 (&k)[2][Geom<D>::NKK], const u32x4 (&qb)[Geom<D>::NKK],
                                                   uint8_t *stage, int tok0, int end, float scale_log2, int n, int q,
                                                   float &m, float &lsum, f32x4 (&o)[Geom<D>::NN]) {
     using Gm = Geom<D>;
@@ -357,9 +240,9 @@ struct WaveState {
 };
 
 // The workgroup's MW waves over tokens [start, end) of (sequence s, KV head kvh):
-// wave w takes the CT-token chunks w, w + MW, ... of the range through a double-
-// buffered pipeline (K operands in registers, V rows in its LDS stages, one chunk's
-// loads in flight while the previous chunk is used).
+// wave w takes the CT-token chunks w, w + MW, ... of the range through a pipeline: K
+// operands loaded one chunk ahead into registers, V rows two chunks ahead into registers
+// and then into the wave's two LDS stages.
 //
 // Newest token given (new_k non-null; the range ends at the context's end): the chunks
 // stop before position end - 1, and the wave that would take the next chunk then stores
@@ -433,10 +316,8 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
             base[tt] = base[tt] < 0 ? 0 : base[tt];
         }
     };
-#if PA_MFMA_VREG
     // V rows through registers (ordinary loads, like K): with every load of one kind the
-    // compiler's waits count exactly, so V can run two chunks ahead.  (A direct-to-LDS
-    // load in flight makes every wait for a register load wait for all loads.)
+    // compiler's waits count exactly, so V can run two chunks ahead.
     struct VSet {
         u32x4 v[2 * Gm::VL];
     };
@@ -449,8 +330,9 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
             for (int i = 0; i < Gm::VL; ++i)
                 b.v[tt * Gm::VL + i] = kv_load<NT>((const u32x4 *)(value_cache + base[tt] + i * 1024 + lane * 16));
     };
-    // into the wave's stage, in the layout the direct loads used (1 KiB groups padded by 32 B);
-    // the stage's previous chunk was read out two chunks ago (LDS operations of a wave run in order)
+    // into the wave's stage, 1 KiB groups padded by 32 B (the layout tile_row's bank spread
+    // assumes); the stage's previous chunk was read two chunks ago (a wave's LDS operations
+    // run in order)
     auto stage_vr = [&](const VSet &b, int stage) {
         uint8_t *sp = wave_lds + stage * Gm::STAGE;
 #pragma unroll
@@ -466,27 +348,13 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
                 b.k[tt][kk] = kv_load<NT>((const u32x4 *)(key_cache + base[tt] + tile_row<D>(n >> 2, n & 3) * ROW +
                                                           (32 * kk + 8 * q) * 2));
     };
-#endif
-    auto issue = [&](Chunk &b, int c, int stage) {
-        int64_t base[2];
-        bases(c, base);
-        // the stage was last read two chunks ago (its operands long used); the wait makes
-        // the order explicit before the loads rewrite it
-        wait_lds_reads();
-        issue_chunk<D, NT>(b.k, wave_lds + stage * Gm::STAGE, base, key_cache, value_cache, lane, n, q);
-    };
-    u32x4 vt[Gm::NN];
-    auto consume = [&](const Chunk &b, int c) {
-        consume_chunk<T, D>(b.k, qb, vt, start + c * CT, end, scale_log2, n, q, st.m, st.lsum, st.o);
-    };
     auto stage_at = [&](int stage) { return wave_lds + stage * Gm::STAGE; };
     auto consume_lds = [&](const Chunk &b, int c, int stage) {
-        consume_chunk_lds<T, D>(b.k, qb, stage_at(stage), start + c * CT, end, scale_log2, n, q, st.m, st.lsum, st.o);
+        consume_chunk<T, D>(b.k, qb, stage_at(stage), start + c * CT, end, scale_log2, n, q, st.m, st.lsum, st.o);
     };
 
     const int mine = nchunks > wave ? (nchunks - wave + MW - 1) / MW : 0;
     auto cidx = [&](int i) { return wave + i * MW; };
-#if PA_MFMA_VREG
     // This wave's chunks are c_i = wave + i MW, i < mine.  Chunk i's V rows are loaded two
     // chunks ahead into register set i % 2 and stored into stage i % 2 once the stage's
     // previous chunk has been read out; its K operands are loaded one chunk ahead into K
@@ -527,35 +395,6 @@ __device__ __forceinline__ void attend_range(WaveState<D> &st, uint8_t *wave_lds
             consume_lds(K0, cidx(i + 2), 0);
         }
     }
-#else
-    // This wave's chunks are wave, wave + MW, ...  Per chunk: its V^T operands are read
-    // from LDS (once its loads have landed), the next chunk's loads are issued, then the
-    // chunk is used from registers while they are in flight.  The steady-state loop always
-    // has a next chunk to prefetch (see tile_base); the last one or two run after it.
-    Chunk A, Bf;
-    if (mine > 0) {
-        issue(A, wave, 0);
-        int j = 0;
-        for (; j + 2 < mine; j += 2) {
-            read_vt<D>(vt, stage_at(0), n, q);
-            issue(Bf, wave + (j + 1) * MW, 1);
-            consume(A, wave + j * MW);
-            read_vt<D>(vt, stage_at(1), n, q);
-            issue(A, wave + (j + 2) * MW, 0);
-            consume(Bf, wave + (j + 1) * MW);
-        }
-        if (j + 1 < mine) {
-            read_vt<D>(vt, stage_at(0), n, q);
-            issue(Bf, wave + (j + 1) * MW, 1);
-            consume(A, wave + j * MW);
-            read_vt<D>(vt, stage_at(1), n, q);
-            consume(Bf, wave + (j + 1) * MW);
-        } else {
-            read_vt<D>(vt, stage_at(0), n, q);
-            consume(A, wave + j * MW);
-        }
-    }
-#endif
     if (append && wave == nchunks % MW) {
         const int lb = tnew >> log2_block;
         int64_t base = -1;
