@@ -360,8 +360,10 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
             }
         }
         if (SOLO && rank >= num_seqs) rank = num_seqs - 1;  // past the batch: sorts with the rest, then leaves
+        // (one wave per item: every item of such a batch is resident at once, so the order
+        // does not matter and the sort is skipped)
         __shared__ uint32_t sm_order[NWG * 64];
-        s = num_seqs <= NWG * 64 ? longest_first<NWG * 64>(context_lens, num_seqs, rank, sm_order) : rank;
+        s = !SOLO && num_seqs <= NWG * 64 ? longest_first<NWG * 64>(context_lens, num_seqs, rank, sm_order) : rank;
         s = __builtin_amdgcn_readfirstlane(s);
         // no barrier follows in the one-wave-per-item form
         if (SOLO && item >= num_seqs * num_kv_heads) return;
@@ -383,6 +385,21 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     if (!SPLIT && skip_parts != nullptr) {
         prefix_spans = __builtin_amdgcn_readfirstlane(skip_parts[s]);
         if (prefix_spans > 0) start = prefix_spans * partition_size;
+    }
+    // one wave per item: the shared-prefix partial (written by the previous launch) is
+    // loaded now, its latency behind the loop, rather than after it
+    float pre_m[SOLO ? G : 1], pre_l[SOLO ? G : 1], pre_a[SOLO ? G : 1][SOLO ? EPL : 1];
+    if constexpr (SOLO) {
+        if (skip_parts != nullptr) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int64_t pi = (int64_t)s * num_kv_heads * G + kvh * G + g;
+                pre_m[g] = ws_max[pi];
+                pre_l[g] = ws_sum[pi];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) pre_a[g][e] = ws_acc[pi * D + col * EPL + e];
+            }
+        }
     }
 
     const int block_size = 1 << log2_block;
@@ -605,8 +622,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
                 float M = m[g], m0 = -INFINITY, l0 = 0.f;
                 bool bad0 = false;
                 if (prefix_spans > 0) {
-                    m0 = ws_max[pi];
-                    l0 = ws_sum[pi];
+                    m0 = pre_m[g];
+                    l0 = pre_l[g];
                     bad0 = m0 != m0;
                     if (!bad0) M = fmaxf(M, m0);
                 }
@@ -618,7 +635,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
                 for (int e = 0; e < EPL; ++e) {
                     const int j = col * EPL + e;
                     float A = acc[g][e] * f;
-                    if (prefix_spans > 0 && !bad0) A += ws_acc[pi * D + j] * f0;
+                    if (prefix_spans > 0 && !bad0) A += pre_a[g][e] * f0;
                     float o = Lsum > 0.f ? A / Lsum : 0.f;
                     if (bad || bad0) o = NAN;
                     store_out<T>(out, pi * D + j, o);
