@@ -30,9 +30,9 @@
 // rounded weights (on the matrix cores, P against a ones operand).  Rows are written by
 // the wave that owns them (no merge).
 //
-// Row tiles are numbered fastest, then sequence, then KV head, and spread over the XCDs
-// in contiguous ranges, so the row tiles that read the same sequence's blocks share an
-// XCD's L2 (K and V are read with cacheable loads).
+// Workgroups are spread over the XCDs in contiguous ranges with the row tiles numbered
+// fastest, so the row tiles that read the same sequence's blocks share an XCD's L2 (K and V
+// are read with cacheable loads); within a range the sequences run longest first.
 #include <hip/hip_runtime.h>
 
 #include "decode_mfma.h"
@@ -53,6 +53,9 @@ constexpr int MW = PA_MQ_WAVES;  // waves per workgroup
 #endif
 #ifndef PA_MQ_KEYS
 #define PA_MQ_KEYS 32
+#endif
+#ifndef PA_MQ_LPT
+#define PA_MQ_LPT 1
 #endif
 #ifndef PA_MQ_WAVES_PER_EU
 #define PA_MQ_WAVES_PER_EU 3  // waves per SIMD the register allocation must allow
@@ -105,11 +108,26 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
     const int n = lane & 15;  // query row of a fragment / key row within a 16-key operand
     const int q = lane >> 4;  // k group
 
+    // Contiguous ranges of workgroups per XCD; within an XCD's range the row tiles run
+    // fastest, then its KV heads, then the sequences longest first (the last workgroups
+    // dispatched are the shortest).  Batches of up to MW * 64 sequences are sorted.
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = L % tiles_per_seq;
     const int rest = L / tiles_per_seq;
-    const int s = rest % num_seqs;
-    const int kvh = rest / num_seqs;
+    int rank, kvh;
+    if (PA_MQ_LPT && num_kv_heads % 8 == 0) {
+        const int hx = num_kv_heads / 8;  // KV heads per XCD
+        const int per_xcd = num_seqs * hx;
+        const int r = rest % per_xcd;
+        rank = r / hx;
+        kvh = (rest / per_xcd) * hx + r % hx;
+    } else {
+        rank = rest % num_seqs;
+        kvh = rest / num_seqs;
+    }
+    __shared__ uint32_t sm_order[MW * 64];
+    int s = PA_MQ_LPT && num_seqs <= MW * 64 ? longest_first<MW * 64>(context_lens, num_seqs, rank, sm_order) : rank;
+    s = __builtin_amdgcn_readfirstlane(s);
     const int num_q_heads = num_kv_heads * G;
 
     const int ctx = context_lens[s];
