@@ -222,24 +222,6 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
 
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
-    // byte offset of the first row of each 16-key group of tile t (uniform), -1 if not valid
-    auto group_bases = [&](int t, int64_t (&base)[NT]) {
-        const int k0 = t * KT;
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            base[j] = -1;
-            const int kj = k0 + 16 * j;
-            if (kj < end) {
-                const int lb = kj >> log2_block;
-                if (lb < max_blocks_per_seq) {
-                    const int32_t pb = table[lb];
-                    if (pb >= 0 && pb < num_blocks)
-                        base[j] = (int64_t)pb * block_bytes + head_off + (int64_t)(kj & (block_size - 1)) * ROW;
-                }
-                if (base[j] < 0) bad = true;
-            }
-        }
-    };
     // Piece permutation: piece c of row r (16 bytes) sits at piece c ^ swz(r % 16) of the
     // row.  The 16 rows one K operand read touches (same piece), and the 8 rows half a V
     // transpose read touches (32 bytes each), then lie in different banks.
@@ -254,27 +236,40 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
     constexpr int NI = KBYTES / 1024 / MW;    // loads of K (and of V) per wave and tile
     static_assert(NI * MW * 1024 == KBYTES && RPL <= 16, "a tile must divide into 1 KiB loads per wave");
     uint32_t gofs[NI];                        // lane's byte offset in its 16-key group
-    int ggrp[NI];                             // the group (uniform)
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int j = wave * NI + i;
         const int r = j * RPL + (16 * lane) / ROW;
         const int p = ((16 * lane) % ROW) / 16;
         gofs[i] = (uint32_t)((r & 15) * ROW + 16 * (p ^ swz(r)));
-        ggrp[i] = __builtin_amdgcn_readfirstlane(r >> 4);
     }
+    // The table entry of this wave's 16-key group of the next tile to issue (a wave's
+    // loads of a tile lie in one group), looked up one tile ahead so that no issue waits
+    // for it: the entry, -1 (no data) or -2 (past the table row).
+    static_assert(NI * RPL <= 16 && 16 % (NI * RPL) == 0, "a wave's loads of a tile share one 16-key group");
+    const int wgrp = __builtin_amdgcn_readfirstlane((wave * NI * RPL) >> 4);
+    int32_t ent = -1;
+    auto lookup = [&](int t) {
+        const int kj = t * KT + 16 * wgrp;
+        ent = -1;
+        if (kj < end) {
+            const int lb = kj >> log2_block;
+            ent = lb < max_blocks_per_seq ? table[lb] : -2;
+        }
+    };
     // issue tile t's loads into buf (block 0's rows where a group has no data: inside the
-    // pool; masked, and V rows past the end zeroed once landed)
+    // pool; masked, and V rows past the end zeroed once landed), then look up tile t + 1
     auto issue = [&](uint8_t *buf, int t) {
-        int64_t base[NT];
-        group_bases(t, base);
+        const int kj = t * KT + 16 * wgrp;
+        int64_t b = 0;
+        if (ent != -1) {
+            if (ent >= 0 && ent < num_blocks)
+                b = (int64_t)ent * block_bytes + head_off + (int64_t)(kj & (block_size - 1)) * ROW;
+            else
+                bad = true;
+        }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            int64_t b = base[0];
-#pragma unroll
-            for (int g = 1; g < NT; ++g)
-                if (ggrp[i] == g) b = base[g];
-            b = b >= 0 ? b : 0;
             const int j = wave * NI + i;
             __builtin_amdgcn_global_load_lds((const void *)(key_cache + b + gofs[i]),
                                              (__attribute__((address_space(3))) void *)(buf + j * 1024), 16, 0, 0);
@@ -282,6 +277,7 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
                                              (__attribute__((address_space(3))) void *)(buf + KBYTES + j * 1024), 16,
                                              0, 0);
         }
+        lookup(t + 1);
     };
     // this wave's loads of every tile but the newest issued have landed (2 NI loads per
     // tile in flight at most: s_waitcnt vmcnt(2 NI), gfx9 encoding with expcnt 7, lgkmcnt 15)
@@ -469,6 +465,7 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
     // the end), and one barrier makes every wave's loads of tile t + 1 visible and frees
     // buffer t % 3.  Loads past the last tile read block 0's rows and are never used.
     if (ntiles > 0) {
+        lookup(0);
         issue(lds0, 0);
         issue(lds1, 1);
         wait_previous();
@@ -481,11 +478,17 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
             zero_tail(nxt, t + 1);
             barrier();
         };
-        for (int t = 0; t < ntiles; t += 3) {
+        // whole rounds of three steps, then the last one or two: no path back into the loop
+        // skips a step, so the compiler's wait before each buffer's reads stays exact (a
+        // skipped step would leave that buffer's loads apparently in flight)
+        int t = 0;
+        for (; t + 2 < ntiles; t += 3) {
             step(lds0, lds1, lds2, t);
-            if (t + 1 < ntiles) step(lds1, lds2, lds0, t + 1);
-            if (t + 2 < ntiles) step(lds2, lds0, lds1, t + 2);
+            step(lds1, lds2, lds0, t + 1);
+            step(lds2, lds0, lds1, t + 2);
         }
+        if (t < ntiles) step(lds0, lds1, lds2, t);
+        if (t + 1 < ntiles) step(lds1, lds2, lds0, t + 1);
     }
 
     __shared__ int sm_bad;
