@@ -140,19 +140,19 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
     // this lane's rows (one per fragment f: token ti, head g) and their positions; the
     // wave's and the workgroup's last positions bound the keys they read
     const int wrow0 = ROWS * tile + 16 * RF * wave;  // first row of the wave
-    int pos[RF], gh[RF];
-    int64_t orow[RF];
-    bool io_ok[RF];
-#pragma unroll
-    for (int f = 0; f < RF; ++f) {
+    // this lane's row of fragment f: its query-token row of query / out (-1: none) and
+    // query head, computed where needed (not held through the key loop)
+    auto row_io = [&](int f, int &gh) -> int64_t {
         const int r = wrow0 + 16 * f + n;
         const bool ok = r < rows;
         const int ti = (ok ? r : rows - 1) / G;
-        gh[f] = (ok ? r : rows - 1) % G;
-        pos[f] = ctx - nq + ti;
-        orow[f] = (int64_t)q0 + ti;
-        io_ok[f] = ok && orow[f] >= 0 && orow[f] < num_query_tokens;
-    }
+        gh = (ok ? r : rows - 1) % G;
+        const int64_t orow = (int64_t)q0 + ti;
+        return ok && orow >= 0 && orow < num_query_tokens ? orow : -1;
+    };
+    int pos[RF];
+#pragma unroll
+    for (int f = 0; f < RF; ++f) pos[f] = ctx - nq + (min(wrow0 + 16 * f + n, rows - 1)) / G;
     const int wg_last = min(rows, ROWS * tile + ROWS) - 1;
     const int end = bad_len ? 0 : ctx - nq + wg_last / G + 1;  // keys the workgroup reads
 
@@ -171,14 +171,16 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
     // sequence are zero
     u32x4 qb[RF][NKK];
 #pragma unroll
-    for (int f = 0; f < RF; ++f)
+    for (int f = 0; f < RF; ++f) {
+        int gh;
+        const int64_t orow = row_io(f, gh);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             qb[f][kk] = u32x4{0, 0, 0, 0};
-            if (io_ok[f])
-                qb[f][kk] = *(const u32x4 *)(query + ((orow[f] * num_q_heads + kvh * G + gh[f]) * D + 32 * kk +
-                                                      8 * q) * 2);
+            if (orow >= 0)
+                qb[f][kk] = *(const u32x4 *)(query + ((orow * num_q_heads + kvh * G + gh) * D + 32 * kk + 8 * q) * 2);
         }
+    }
 
     // Scores stay unscaled until the exponent: exp2(s * x - m) with s = |scale * log2 e| > 0,
     // so the running max can be taken on raw products (a negative scale flips the sign
@@ -261,6 +263,8 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
     // pool; masked, and V rows past the end zeroed once landed), then look up tile t + 1
     auto issue = [&](uint8_t *buf, int t) {
         const int kj = t * KT + 16 * wgrp;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) asm volatile("" : "+v"(gofs[i]));
         int64_t b = 0;
         if (ent != -1) {
             if (ent >= 0 && ent < num_blocks)
@@ -450,6 +454,13 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
     const int wave_end = wrow0 < rows ? ctx - nq + (min(rows, wrow0 + 16 * RF) - 1) / G + 1 : 0;
     auto compute = [&](const uint8_t *buf, int t) {
         if (t * KT >= wave_end) return;
+        // The operand offsets are opaque at each step (an empty asm): the compiler then folds
+        // the buffer's constant LDS address into each read's offset field instead of keeping
+        // offset + address copies per buffer live through the loop.
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(kofs[kk]));
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn) asm volatile("" : "+v"(vofs[nn]));
         Scores sc;
         scores(buf, sc);
         mask(sc, t);
@@ -501,9 +512,11 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(PA_MQ_W
 #pragma unroll
     for (int f = 0; f < RF; ++f) {
         const float l = osum[f][0];
-        if (!io_ok[f]) continue;
+        int gh;
+        const int64_t orow = row_io(f, gh);
+        if (orow < 0) continue;
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        const int64_t obase = (orow[f] * num_q_heads + kvh * G + gh[f]) * D;
+        const int64_t obase = (orow * num_q_heads + kvh * G + gh) * D;
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn)
 #pragma unroll
