@@ -227,3 +227,48 @@ def test_grouped_bad_private_entry_gives_nan_for_that_member_only():
     assert torch.isnan(got[s_bad]).all()
     keep = torch.arange(len(c.ctx), device="cuda") != s_bad
     assert bits(got[keep]) == bits(clean[keep])
+
+
+def _relabelled(c: GroupCase, perm) -> GroupCase:
+    """The same cache with physical block b moved to perm[b] (pools permuted along their
+    first axis, table entries mapped)."""
+    c2 = GroupCase.__new__(GroupCase)
+    c2.__dict__.update(c.__dict__)
+    t = c.tables.copy()
+    t[t >= 0] = perm[t[t >= 0]]
+    c2.tables = t
+    for name in ("kc", "vc"):
+        a = getattr(c, name)
+        m = np.empty_like(a)
+        m[perm] = a
+        setattr(c2, name, m)
+    return c2
+
+
+def test_grouped_identity_and_relabelled_tables_are_bit_identical():
+    """Where the blocks sit changes nothing ("PagedAttention" concept report §5 and §6:
+    sequences reach shared and private blocks only through their tables): the grouped
+    call over the same forked cache laid out in table order (shared blocks once, then
+    each member's own) and under a random relabelling gives bit-identical output, with
+    the newest tokens stored in the same launch."""
+    H, d, B, dt, P = 4, 128, 16, "f16", 64
+    rng = np.random.default_rng(61)
+    c = GroupCase(rng, GROUPS, H, d, B, dt)
+    gs, gp, gmax, pmax = prefix_groups(c.tables, c.ctx, B, P)
+    used = []
+    for b in c.tables.reshape(-1):
+        if b >= 0 and int(b) not in used:
+            used.append(int(b))
+    ident = np.full(c.num_blocks, -1, np.int64)
+    ident[used] = np.arange(len(used))
+    ident[ident < 0] = np.arange(len(used), c.num_blocks)
+    outs = []
+    for name, perm in (("paged", None), ("table order", ident),
+                       ("relabelled", np.random.default_rng(62).permutation(c.num_blocks))):
+        cc = c if perm is None else _relabelled(c, perm)
+        g2 = prefix_groups(cc.tables, cc.ctx, B, P)
+        assert np.array_equal(g2[0], gs) and np.array_equal(g2[1], gp)
+        say(f"[gpu] grouped layout {name}")
+        got, _, _ = run_grouped(cc, P, gs, gp, gmax, pmax, append=True)
+        outs.append(bits(got))
+    assert outs[0] == outs[1] == outs[2]

@@ -155,3 +155,36 @@ def test_chunked_prefill_step_through_the_cache():
     torch.cuda.synchronize()
     want = c.run_mq(oracle.default())
     assert np.max(np.abs(out.float().cpu().numpy() - want)) <= TOL
+
+
+def test_multi_query_identity_and_relabelled_tables_are_bit_identical():
+    """Where the blocks sit changes nothing ("PagedAttention" concept report §5): the same
+    cache laid out in table order and under a random relabelling of the physical blocks
+    gives bit-identical multi-query output (1 and 4 query heads per KV head)."""
+    for Hq, Hkv, d, dt in ((4, 4, 128, "f16"), (8, 2, 64, "bf16")):
+        c = MQCase(np.random.default_rng(71), [300, 37, 513, 16, 1], [300, 5, 200, 16, 1], Hq, Hkv, d, 16, dt)
+        used = []
+        for b in c.tables.reshape(-1):
+            if b >= 0 and int(b) not in used:
+                used.append(int(b))
+        ident = np.full(c.num_blocks, -1, np.int64)
+        ident[used] = np.arange(len(used))
+        ident[ident < 0] = np.arange(len(used), c.num_blocks)
+        outs = []
+        for name, perm in (("paged", None), ("table order", ident),
+                           ("relabelled", np.random.default_rng(72).permutation(c.num_blocks))):
+            cc = c
+            if perm is not None:
+                cc = MQCase.__new__(MQCase)
+                cc.__dict__.update(c.__dict__)
+                t = c.tables.copy()
+                t[t >= 0] = perm[t[t >= 0]]
+                cc.tables = t
+                for nm in ("kc", "vc"):
+                    a = getattr(c, nm)
+                    m = np.empty_like(a)
+                    m[perm] = a
+                    setattr(cc, nm, m)
+            say(f"[gpu] multi_query layout {name} g={Hq // Hkv} d={d}")
+            outs.append(run_mq(cc).cpu().contiguous().view(torch.uint8).numpy().tobytes())
+        assert outs[0] == outs[1] == outs[2], (Hq, Hkv, d)
