@@ -702,11 +702,14 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
     const int kvh = blockIdx.x % num_kv_heads;
     const int j = blockIdx.x / num_kv_heads;
+    // the group's record, read together
     const int s0 = plan.group_start[j];
-    const int members = plan.group_start[j + 1] - s0;
-    if (s0 < 0 || members < 1 || members > G || s0 > plan.num_seqs - members) return;
+    const int s1 = plan.group_start[j + 1];
     const int parts = plan.group_parts[j];
-    if (parts < 1 || parts > plan.max_group_parts) return;
+    const int members = s1 - s0;
+    if ((s0 < 0) | (members < 1) | (members > G) | (s0 > plan.num_seqs - members) | (parts < 1) |
+        (parts > plan.max_group_parts))
+        return;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[MW * Geom<D>::WAVE_LDS];
     static_assert((2 * MW * G + MW * G * D) * 4 <= MW * Geom<D>::WAVE_LDS, "merge area must fit the staging area");
@@ -714,10 +717,8 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     __shared__ uint32_t sm_rows[MW];
     // the members this pass serves: member i checked by wave i mod MW
     uint32_t mine_rows = 0;
-    for (int i = wave; i < members; i += MW) {
-        int jj, pp;
-        if (group_serves(plan, s0 + i, lane, jj, pp) && jj == j && pp == parts) mine_rows |= 1u << i;
-    }
+    for (int i = wave; i < members; i += MW)
+        if (group_serves_in(plan, s0 + i, j, s0, s0 + members, parts, lane)) mine_rows |= 1u << i;
     if (lane == 0) sm_rows[wave] = mine_rows;
     __syncthreads();
     uint32_t rows = 0;

@@ -70,4 +70,51 @@ __device__ inline bool group_serves(const GroupPlanArgs &p, int s, int lane, int
     return ok;
 }
 
+// The same decision for a sequence s that the caller already places in group j (the
+// group's start s0, next start s1 and parts read by the caller): true exactly when
+// group_serves(p, s, ...) holds with that j and parts.  Every load it needs is known up
+// front (the group starts, s's length, both tables' shared entries), so they are issued
+// together: one memory round trip instead of three dependent ones.  The caller
+// guarantees 0 <= s0, s < num_seqs (the loads are made with clamped indices, without a
+// branch, and their results ignored where out of range).
+__device__ inline bool group_serves_in(const GroupPlanArgs &p, int s, int j, int s0, int s1, int parts,
+                                       int lane) {
+    const int64_t shared = (int64_t)parts * p.span;
+    const int64_t nblk = shared >> p.log2_block;
+    const bool shape_ok = s0 >= 0 && s0 <= s && s < s1 && s1 <= p.num_seqs && s1 - s0 <= p.group_rows &&
+                          parts >= 1 && parts <= p.max_group_parts && nblk <= p.max_blocks_per_seq;
+    if (p.num_groups <= 64 && nblk <= 64) {
+        // one lookup of each kind per lane, all issued before any is used
+        const int32_t *ts = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+        const int32_t *t0 = p.block_tables + (int64_t)s0 * p.max_blocks_per_seq;
+        const bool lk = shape_ok && lane < (int)nblk;
+        const int kl = lk ? lane : 0;  // index 0 lies in every table row and group array
+        const int32_t b = ts[kl];
+        const int32_t b0 = t0[kl];
+        const int gs = p.group_start[lane < p.num_groups ? lane : 0];
+        const int ctx = p.context_lens[s];
+        // every term evaluated (no short circuit, which would sink the table loads behind
+        // the group-start comparison)
+        const bool bad = __any(lk & ((b != b0) | (b < 0) | (b >= p.num_blocks)));
+        const int count = __popcll(__ballot((lane < p.num_groups) & (gs <= s)));
+        return shape_ok & (count - 1 == j) & (ctx >= 1) & (shared <= (int64_t)ctx - 1) & !bad;
+    }
+    bool bad = !shape_ok;
+    if (shape_ok) {
+        const int32_t *ts = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+        const int32_t *t0 = p.block_tables + (int64_t)s0 * p.max_blocks_per_seq;
+        for (int k = lane; k < (int)nblk; k += 64) {
+            const int32_t b = ts[k];
+            bad |= b != t0[k] || b < 0 || b >= p.num_blocks;
+        }
+    }
+    const int ctx = shape_ok ? p.context_lens[s] : 0;
+    int count = 0;
+    for (int base = 0; base < p.num_groups; base += 64) {
+        const int i = base + lane;
+        count += __popcll(__ballot(i < p.num_groups && p.group_start[i] <= s));
+    }
+    return shape_ok && count - 1 == j && ctx >= 1 && shared <= (int64_t)ctx - 1 && !__any(bad);
+}
+
 }  // namespace pa
