@@ -188,3 +188,19 @@ def test_multi_query_identity_and_relabelled_tables_are_bit_identical():
             say(f"[gpu] multi_query layout {name} g={Hq // Hkv} d={d}")
             outs.append(run_mq(cc).cpu().contiguous().view(torch.uint8).numpy().tobytes())
         assert outs[0] == outs[1] == outs[2], (Hq, Hkv, d)
+
+
+@pytest.mark.parametrize("S", [65, 100, 257, 300])
+def test_multi_query_large_batches_around_the_sort_limits(S):
+    """Batches past one wave's sort (64 sequences: the workgroup sorts through LDS) and
+    past the workgroup's (256: sequences in index order), with 8 KV heads (each XCD's
+    range of workgroups takes one head's sequences longest first) and 2 heads."""
+    rng = np.random.default_rng(80 + S)
+    lens = rng.integers(1, 60, S).tolist()
+    qlens = [int(rng.integers(0, n + 1)) for n in lens]
+    for Hq, Hkv in ((8, 8), (4, 2)):
+        c = MQCase(rng, lens, qlens, Hq, Hkv, 64, 16, "f16")
+        say(f"[gpu] multi_query S={S} Hq={Hq} Hkv={Hkv}")
+        got = run_mq(c).double().cpu().numpy()
+        want = c.run_mq(oracle.default())
+        assert np.max(np.abs(got - want)) <= TOL, (S, Hq, Hkv)
