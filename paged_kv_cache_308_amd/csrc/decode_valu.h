@@ -521,7 +521,10 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
         typename KV::Word k[NLK], v[NLK];
         float ksl[NLK], vsc[NLK];
     };
-    auto issue = [&](Chunk &b, int c) {
+    // tail: the chunk that holds `end`; there a lane whose row lies at or past `end` reads
+    // block 0's first rows instead (cached after the first such read; masked like any row
+    // past the end), so the rows past the context in the last block are not fetched
+    auto issue = [&](Chunk &b, int c, bool tail = false) {
 #pragma unroll
         for (int i = 0; i < NLK; ++i) {
             int64_t off = load_offset(c, i);
@@ -532,6 +535,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
                 b.vsc[i] = off < 0 ? 0.f : cached_vs;
             }
             off = off < 0 ? 0 : off;
+            if (tail && start + c * C + i * TPW + row >= end) off = 0;
             b.k[i] = kv_load<NT>((const typename KV::Word *)(key_cache + off + lane * SB));
             b.v[i] = kv_load<NT>((const typename KV::Word *)(value_cache + off + lane * SB));
         }
@@ -565,7 +569,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
             }
         }
         if (has_tail && (nfull % NWI) == iw) {
-            issue(A, nfull);
+            issue(A, nfull, true);
             consume(A, nfull, true);
         }
     }
