@@ -272,3 +272,30 @@ def test_grouped_identity_and_relabelled_tables_are_bit_identical():
         got, _, _ = run_grouped(cc, P, gs, gp, gmax, pmax, append=True)
         outs.append(bits(got))
     assert outs[0] == outs[1] == outs[2]
+
+
+@pytest.mark.parametrize("case", ["70 groups", "96 shared blocks"])
+def test_grouped_many_groups_and_long_shared_prompts(case):
+    """Past the one-load-per-lane check (at most 64 groups and 64 shared blocks): 70
+    groups of two forks, and two groups whose members share 3 spans of 512 tokens (96
+    blocks of 16); both give the oracle's attention with the newest tokens stored."""
+    if case == "70 groups":
+        H, d, B, dt, P = 2, 64, 16, "f16", 32
+        groups = [(40 + (i % 7), [3 + (i % 5), 1 + (i % 3)]) for i in range(70)]
+    else:
+        H, d, B, dt, P = 2, 128, 16, "bf16", 512
+        groups = [(1700, [9, 1, 40]), (1600, [20, 3])]
+    rng = np.random.default_rng(91 if case == "70 groups" else 92)
+    c = GroupCase(rng, groups, H, d, B, dt)
+    want = c.oracle_out()
+    gs, gp, gmax, pmax = prefix_groups(c.tables, c.ctx, B, P)
+    say(f"[gpu] grouped {case}: {len(gp)} groups, parts up to {pmax}")
+    if case == "70 groups":
+        assert len(gp) > 64
+    else:
+        assert pmax * P // B > 64
+    got, kc, vc = run_grouped(c, P, gs, gp, gmax, pmax, append=True)
+    err = np.max(np.abs(f64(got) - want))
+    assert err <= TOL, (case, err)
+    assert bits(kc) == np.ascontiguousarray(c.kc).tobytes()
+    assert bits(vc) == np.ascontiguousarray(c.vc).tobytes()
