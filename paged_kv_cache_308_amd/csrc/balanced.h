@@ -11,9 +11,10 @@
 // log-sum-exp weights ("PagedAttention" concept report (compassingai.com) §8 defines
 // the attention; the split changes only the order of the sums).
 //
-// Workspace header (int32), written by workgroup 0 of the decode launch: [0] chunks per
-// KV head, [1] chunks per worker, [2] workers, [4 + s] chunks of the sequences before s
-// (s = 0..S).
+// Workspace header (int32), written by workgroup 0 of the decode launch: [0] units per
+// KV head, [1] units per worker, [2] workers, [3] units ahead of each non-empty item's
+// chunks (a share of the list that stands for the cost of starting an item; no worker
+// reads anything for them), [4 + s] units of the sequences before s (s = 0..S).
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -41,13 +42,15 @@ __global__ __launch_bounds__(64) void balanced_merge_kernel(
     const int ctx = context_lens[s];
     const int per_head = ws_hdr[0];
     const int per = ws_hdr[1];
+    const int ov = ws_hdr[3];
     const int first = ws_hdr[BAL_HDR + s];
-    const int n = ws_hdr[BAL_HDR + s + 1] - first;
+    const int units = ws_hdr[BAL_HDR + s + 1] - first;
+    const int n = units > ov ? units - ov : 0;  // chunks after the item's start units
     if (ctx < 0 || n == 0) {
         for (int j = threadIdx.x; j < D; j += 64) store_out<T>(out, obase + j, ctx < 0 ? NAN : 0.f);
         return;
     }
-    const int g0 = kvh * per_head + first;
+    const int g0 = kvh * per_head + first + ov;
     const int w0 = g0 / per, w1 = (g0 + n - 1) / per;
     const int64_t item = (int64_t)kvh * num_seqs + s;
     // Partials in groups of four, every load of a group issued together, folded into a

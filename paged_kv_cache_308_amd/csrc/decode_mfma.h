@@ -44,6 +44,13 @@
 namespace pa {
 namespace mfma {
 
+// Cost of starting an item in the matrix-core balanced split, in chunks: the list gives
+// every item this many units before its chunks, so a worker whose range starts an item
+// takes that many chunks fewer (an item start drains the workgroup's load pipeline, merges
+// its waves and refills; about three chunks' time at 2 workgroups per CU).
+#ifndef PA_BAL_ITEM_UNITS
+#define PA_BAL_ITEM_UNITS 3
+#endif
 #ifndef PA_MFMA_WAVES
 #define PA_MFMA_WAVES 4
 #endif
@@ -559,9 +566,11 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // Balanced split on the matrix cores (balanced.h): CT-token chunks, one worker per
-// workgroup.  The workgroup walks its range item by item; within an item its waves
-// take the range's chunks in turn, as the one-pass kernel does for a whole context,
-// and at the item's end they merge and write the item's partial.
+// workgroup, and PA_BAL_ITEM_UNITS units ahead of each item's chunks in the list (a
+// range that holds only such units of an item skips it).  The workgroup walks its range
+// item by item; within an item its waves take the range's chunks in turn, as the
+// one-pass kernel does for a whole context, and at the item's end they merge and write
+// the item's partial.
 template <typename T, int D, int G, bool NT>
 __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_balanced_kernel(
     const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
@@ -573,6 +582,7 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = num_seqs;
+    constexpr int OV = PA_BAL_ITEM_UNITS;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[MW * Geom<D>::WAVE_LDS];
     static_assert((BAL_MAX_SEQS + 1) * 4 <= MW * Geom<D>::WAVE_LDS, "chunk prefix must fit the staging area");
@@ -587,7 +597,7 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int base = 0; base < S; base += 64) {
             const int s = base + lane;
             const int c = s < S ? context_lens[s] : 0;
-            int v = c > 0 ? (c + CT - 1) / CT : 0;
+            int v = c > 0 ? (c + CT - 1) / CT + OV : 0;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const int t = __shfl_up(v, o);
@@ -610,7 +620,7 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             ws_hdr[0] = per_head;
             ws_hdr[1] = per;
             ws_hdr[2] = W;
-            ws_hdr[3] = 0;
+            ws_hdr[3] = OV;
         }
         for (int t = threadIdx.x; t <= S; t += MW * 64) ws_hdr[BAL_HDR + t] = sm_pre[t];
     }
@@ -640,20 +650,24 @@ __global__ __launch_bounds__(MW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int g = g_begin; g < g_end;) {
         const int ctx = __builtin_amdgcn_readfirstlane(context_lens[s]);
         const int nc = (ctx + CT - 1) / CT;  // > 0: the list holds only non-empty items
-        const int take = min(nc - c, g_end - g);
-        WaveState<D> st;
-        st.bad = false;
-        const int seg_end = min(ctx, (c + take) * CT);
-        // the item's last segment holds the newest token
-        const bool app = new_key != nullptr && seg_end == ctx;
-        const int64_t nrow = (int64_t)(s * num_kv_heads + kvh) * Geom<D>::ROW;
-        attend_range<T, D, G, NT>(st, lds + wave * Geom<D>::WAVE_LDS, query, key_cache, value_cache,
-                                  block_tables + (int64_t)s * max_blocks_per_seq, max_blocks_per_seq, s, kvh,
-                                  num_kv_heads, log2_block, num_blocks, c * CT, seg_end, scale_log2, wave, lane,
-                                  app ? new_key + nrow : nullptr, app ? new_value + nrow : nullptr, key_out,
-                                  value_out);
-        const int64_t slot = (int64_t)w + (int64_t)kvh * S + s;
-        finish<T, D, G>(st, lds, &sm_bad, wave, lane, nullptr, 0, ws_max, ws_sum, ws_acc, slot * G, 1);
+        // units c .. c + take of the item: OV for its start, then its chunks
+        const int take = min(nc + OV - c, g_end - g);
+        const int c0 = max(c - OV, 0), c1 = c + take - OV;  // its chunks in this range
+        if (c1 > c0) {
+            WaveState<D> st;
+            st.bad = false;
+            const int seg_end = min(ctx, c1 * CT);
+            // the item's last segment holds the newest token
+            const bool app = new_key != nullptr && seg_end == ctx;
+            const int64_t nrow = (int64_t)(s * num_kv_heads + kvh) * Geom<D>::ROW;
+            attend_range<T, D, G, NT>(st, lds + wave * Geom<D>::WAVE_LDS, query, key_cache, value_cache,
+                                      block_tables + (int64_t)s * max_blocks_per_seq, max_blocks_per_seq, s,
+                                      kvh, num_kv_heads, log2_block, num_blocks, c0 * CT, seg_end, scale_log2,
+                                      wave, lane, app ? new_key + nrow : nullptr, app ? new_value + nrow : nullptr,
+                                      key_out, value_out);
+            const int64_t slot = (int64_t)w + (int64_t)kvh * S + s;
+            finish<T, D, G>(st, lds, &sm_bad, wave, lane, nullptr, 0, ws_max, ws_sum, ws_acc, slot * G, 1);
+        }
         g += take;
         // next non-empty item
         c = 0;
