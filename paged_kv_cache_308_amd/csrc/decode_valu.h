@@ -293,6 +293,13 @@ constexpr int min_waves_per_eu() {
 // ~140 tokens each), where splitting an item over the workgroup's waves leaves each wave
 // two chunks and the cross-wave merge, the sort and the launch of many small
 // workgroups dominate.
+// E4M3 pools: 1 reads a block's K/V scales with vector loads issued beside its codes and
+// applies them when the chunk is used; 0 reads them with scalar loads when the block is
+// looked up (a wait for any scalar load waits for all of them, so each chunk then waits
+// for the next block's scales before it can be used).
+#ifndef PA_FP8_VSCALE
+#define PA_FP8_VSCALE 1
+#endif
 #ifndef PA_VALU_SOLO
 #define PA_VALU_SOLO 0  // 0: one wave per item after a shared-prefix pass only; 1: always; -1: never
 #endif
@@ -491,6 +498,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     int cached_lb = -1;
     int64_t cached_base = -1;
     float cached_ks = 0.f, cached_vs = 0.f;  // E4M3 pools: the block's scales
+    int64_t cached_si = 0;                   // E4M3 pools: the block's place in the scale arrays
     auto load_offset = [&](int c, int i) -> int64_t {
         const int tok = start + c * C + i * TPW;
         if (tok >= end) return -1;
@@ -507,8 +515,11 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
                 } else {
                     cached_base = (int64_t)pb * block_bytes + head_off;
                     if constexpr (KV::scaled) {
-                        cached_ks = k_scales[(int64_t)pb * num_kv_heads + kvh];
-                        cached_vs = v_scales[(int64_t)pb * num_kv_heads + kvh];
+                        cached_si = (int64_t)pb * num_kv_heads + kvh;
+                        if (!PA_FP8_VSCALE) {
+                            cached_ks = k_scales[cached_si];
+                            cached_vs = v_scales[cached_si];
+                        }
                     }
                 }
             }
@@ -520,6 +531,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     struct Chunk {
         typename KV::Word k[NLK], v[NLK];
         float ksl[NLK], vsc[NLK];
+        bool sok[NLK];
     };
     // tail: the chunk that holds `end`; there a lane whose row lies at or past `end` reads
     // block 0's first rows instead (cached after the first such read; masked like any row
@@ -530,9 +542,20 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
             int64_t off = load_offset(c, i);
             b.ksl[i] = scale_log2;
             b.vsc[i] = 1.f;
+            b.sok[i] = off >= 0;
             if constexpr (KV::scaled) {
-                b.ksl[i] = off < 0 ? 0.f : scale_log2 * cached_ks;
-                b.vsc[i] = off < 0 ? 0.f : cached_vs;
+                if (PA_FP8_VSCALE) {
+                    // the block's scales by vector loads beside its codes, applied when the
+                    // chunk is used: vector loads are counted in order, so using this chunk
+                    // never waits for the next one's (scalar loads are waited for all at once)
+                    int64_t si = off < 0 ? 0 : cached_si;
+                    asm volatile("" : "+v"(si));
+                    b.ksl[i] = k_scales[si];
+                    b.vsc[i] = v_scales[si];
+                } else {
+                    b.ksl[i] = off < 0 ? 0.f : scale_log2 * cached_ks;
+                    b.vsc[i] = off < 0 ? 0.f : cached_vs;
+                }
             }
             off = off < 0 ? 0 : off;
             if (tail && start + c * C + i * TPW + row >= end) off = 0;
@@ -541,8 +564,18 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
         }
     };
     auto consume = [&](const Chunk &b, int c, bool tail) {
-        chunk_update<KV, G, NLK, LPT, TPW>(qv, b.k, b.v, b.ksl, b.vsc, start + c * C + row, end, tail, m, l,
-                                          acc);
+        if constexpr (KV::scaled && PA_FP8_VSCALE) {
+            float ksl[NLK], vsc[NLK];
+#pragma unroll
+            for (int i = 0; i < NLK; ++i) {
+                ksl[i] = b.sok[i] ? scale_log2 * b.ksl[i] : 0.f;
+                vsc[i] = b.sok[i] ? b.vsc[i] : 0.f;
+            }
+            chunk_update<KV, G, NLK, LPT, TPW>(qv, b.k, b.v, ksl, vsc, start + c * C + row, end, tail, m, l, acc);
+        } else {
+            chunk_update<KV, G, NLK, LPT, TPW>(qv, b.k, b.v, b.ksl, b.vsc, start + c * C + row, end, tail, m, l,
+                                              acc);
+        }
     };
 
     // This wave's full chunks are iw, iw + NWI, ...  The steady-state loop always
