@@ -626,7 +626,9 @@ def main():
         "decode_us": round(dec_avg * 1e3, 2),
         "decode_us_p10_median_p90": [round(float(np.percentile(dec_ms, x)) * 1e3, 2) for x in (10, 50, 90)],
         "stream_read_gbs": None if stream is None else round(stream, 1),
-        "pct_of_stream_read": None if stream is None else round(100 * gbs / stream, 2),
+        # the same unique bytes as pct_of_peak, against the measured streaming read
+        "pct_of_stream_read": None if stream is None else round(
+            100 * ab["kv_unique"] / (ms_step * 1e-3) / 1e9 / stream, 2),
         "gather_read_gbs": None if gather is None else round(gather["gbs"], 1),
         "gather_read": None if gather is None else {
             "bytes": gather["bytes"], "piece_bytes": gather["piece"], "us": round(gather["us"], 2),
