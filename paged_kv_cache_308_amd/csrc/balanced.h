@@ -2,10 +2,13 @@
 // Balanced split, shared by the vector and the matrix-core decode kernels.
 //
 // The batch's work is one ordered list of fixed-size chunks (KV head, then sequence,
-// then chunk of the sequence).  Each of W workers (waves) takes an equal contiguous
-// range of it; when a worker finishes the part of a (sequence, KV head) item that lies
-// in its range it writes that item's partial (running max, sum and weighted value sums
-// per query head) to slot `worker + item`.  Ranges and items are both ordered, so two
+// then chunk of the sequence), optionally with a few units ahead of each item's chunks
+// that stand for the cost of starting it.  Each of W workers (waves of the vector
+// kernel, workgroups of the matrix-core one) takes an equal contiguous range of it;
+// when a worker finishes the chunks of a (sequence, KV head) item that lie in its
+// range it writes that item's partial (running max, sum and weighted value sums per
+// query head) to slot `worker + item`; a range holding none of an item's chunks
+// writes nothing for it.  Ranges and items are both ordered, so two
 // (worker, item) pairs that share a slot would need a later worker on an earlier item,
 // which cannot happen.  balanced_merge_kernel combines each item's partials with
 // log-sum-exp weights ("PagedAttention" concept report (compassingai.com) §8 defines
