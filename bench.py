@@ -6,9 +6,10 @@ A step is one decode step of the whole batch on the device, inputs resident in
 HBM: the copy-on-write block copies the step raised (prefix_sharing only), the
 newest tokens' K/V stored into their slots, and decode attention over the block
 tables (with context partitions and their log-sum-exp merge when the workload uses
-them).  Where the vector kernel serves the step, the store rides in the attention
-launch (pa_decode_append / pa_decode_fp8_append); otherwise (--unfused, the matrix
-cores, the balanced split) it is its own launch (pa_reshape_and_cache).  Steps rotate over R replicas of
+them).  Where the attention launch can store the newest K/V (every kernel form but
+the vector kernel's balanced split), the store rides in it (pa_decode_append /
+pa_decode_fp8_append); otherwise (--unfused, or that balanced split) it is its own
+launch (pa_reshape_and_cache).  Steps rotate over R replicas of
 the batch in separate allocations, so no step finds the previous one's K/V in the
 last-level cache.
 
@@ -81,7 +82,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 100 untimed steps by default: after the GPU has been idle, the matrix-core-heavy
+    # multi-query kernel runs up to 40% slower for about its first hundred calls while the
+    # clocks settle (the decode kernels are steady from their first calls)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama7b")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--variant", type=int, default=0)
