@@ -158,13 +158,16 @@ def build_replicas(args, w, batch, identity: bool):
     return reps
 
 
-def run_steps(args, reps, n_steps: int, record: bool, attend_only: bool = False):
+def run_steps(args, reps, n_steps: int, record: bool, attend_only: bool = False, rewarm: int = 0):
     """Returns (total ms, per-step decode ms list, per-step pre-decode ms list).
     With record=False nothing but the two bracketing events touches the stream, so the
     total is the whole job's time; record=True adds events around each step's parts
     (for the decode-only figures), which themselves cost a few microseconds a step.
     attend_only: the decode calls alone, back to back (no copies, no separate scatter;
-    both are idempotent here, so the pools hold the same data either way)."""
+    both are idempotent here, so the pools hold the same data either way).
+    rewarm: untimed steps of the same kind enqueued right before the first event, with no
+    wait between them, so that the timed steps start in the state a steady run is in
+    rather than after the host's pause."""
     import torch
     st = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
@@ -172,16 +175,17 @@ def run_steps(args, reps, n_steps: int, record: bool, attend_only: bool = False)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0.record(st)
-    for k in range(n_steps):
+    for k in range(-rewarm, n_steps):
+        if k == 0:
+            t0.record(st)
         db, ws, src, dst, out = reps[k % len(reps)]
-        if record:
+        if record and k >= 0:
             evs[k][0].record(st)
         if src.numel() and not attend_only:
             db.cache.copy(src, dst, st)
         if not args.fused and not attend_only:
             db.cache.write(db.new_key, db.new_value, db.slot_mapping, st)
-        if record:
+        if record and k >= 0:
             evs[k][1].record(st)
         if args.grouped:  # shared partitions once per group, the newest tokens stored
             db.step_grouped(args.P, db.group_args, out=out, workspace=ws, stream=st, variant=args.variant)
@@ -189,7 +193,7 @@ def run_steps(args, reps, n_steps: int, record: bool, attend_only: bool = False)
             db.step(args.P, args.variant, out=out, workspace=ws, stream=st)
         else:
             db.attend(args.P, args.variant, out=out, workspace=ws, stream=st)
-        if record:
+        if record and k >= 0:
             evs[k][2].record(st)
     t1.record(st)
     torch.cuda.synchronize()
@@ -445,25 +449,29 @@ def mq_bench(args, w, batch) -> dict:
                      torch.from_numpy(qstart).cuda()))
     st = torch.cuda.current_stream()
 
-    def steps(n, record, attend_only=False):
+    def steps(n, record, attend_only=False, rewarm=0):
         """record=False: only the bracketing events (whole-job time); True: events
         around each step's scatter and attention as well.  attend_only: the attention
-        calls alone, back to back (the scatter writes the same tokens every step)."""
+        calls alone, back to back (the scatter writes the same tokens every step).
+        rewarm: untimed steps of the same kind enqueued right before the first event, with
+        no wait between them (after an idle stretch the kernel needs about a hundred calls
+        before its clocks settle)."""
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)] if record else None
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        t0.record(st)
-        for k in range(n):
+        for k in range(-rewarm, n):
+            if k == 0:
+                t0.record(st)
             db, q, out, sl, kk, vv, qs = reps[k % len(reps)]
-            if record:
+            if record and k >= 0:
                 evs[k][0].record(st)
             if not attend_only:
                 pa.pa_reshape_and_cache(kk, vv, db.cache.key_cache, db.cache.value_cache, sl, st)
-            if record:
+            if record and k >= 0:
                 evs[k][1].record(st)
             pa.pa_multi_query(out, q, db.cache.key_cache, db.cache.value_cache, db.block_tables,
                               db.context_lens, qs, w.scale, w.query_len, st)
-            if record:
+            if record and k >= 0:
                 evs[k][2].record(st)
         t1.record(st)
         torch.cuda.synchronize()
@@ -474,10 +482,10 @@ def mq_bench(args, w, batch) -> dict:
 
     steps(args.warmup, False)
     total, _, _ = steps(args.steps, False)
-    _, att, pre = steps(args.steps, True)
     # the attention calls alone, K back to back between two events: the call's duration
     # free of the markers the per-part events put between launches
-    att_total, _, _ = steps(args.steps, False, attend_only=True)
+    att_total, _, _ = steps(args.steps, False, attend_only=True, rewarm=args.warmup)
+    _, att, pre = steps(args.steps, True, rewarm=args.warmup)
     ms_step = total / args.steps
     att_ms = att_total / args.steps
     cpu = None
@@ -576,11 +584,11 @@ def main():
     run_steps(args, reps, args.warmup, record=False)
     log(args, f"[bench] timing {args.steps} steps")
     total_ms, _, _ = run_steps(args, reps, args.steps, record=False)
-    # the same steps again with events around each part: decode-only and scatter times
-    _, dec_ms, pre_ms = run_steps(args, reps, args.steps, record=True)
     # the decode calls alone, K of them back to back between two events: the call's duration
     # free of the markers the per-part events put between launches
-    att_ms, _, _ = run_steps(args, reps, args.steps, record=False, attend_only=True)
+    att_ms, _, _ = run_steps(args, reps, args.steps, record=False, attend_only=True, rewarm=args.warmup)
+    # the same steps again with events around each part: decode-only and scatter times
+    _, dec_ms, pre_ms = run_steps(args, reps, args.steps, record=True, rewarm=args.warmup)
     ms_step = total_ms / args.steps
     dec_avg = float(np.mean(dec_ms))
     dec_time = att_ms / args.steps
@@ -593,8 +601,7 @@ def main():
         del reps
         torch.cuda.empty_cache()
         reps_i = build_replicas(args, w, batch, identity=True)
-        run_steps(args, reps_i, args.warmup, record=False)
-        _, dec_i, _ = run_steps(args, reps_i, args.steps, record=True)
+        _, dec_i, _ = run_steps(args, reps_i, args.steps, record=True, rewarm=args.warmup)
         ident = float(np.mean(dec_i))
         # the same read probe over the identity layout's tiles: separates the memory
         # system's response to the address pattern from the kernel's
