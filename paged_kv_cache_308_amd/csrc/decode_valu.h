@@ -277,9 +277,16 @@ __device__ inline void merge_rows(float (&m)[G], float (&l)[G], float (&acc)[G][
 #ifndef PA_VALU_WAVES_ONE_PASS
 #define PA_VALU_WAVES_ONE_PASS 4
 #endif
-template <typename KV, int G, bool SPLIT>
+// Waves (one item each) per workgroup of the one-wave-per-item form.  One: the prefix
+// batch's 2,560 private items then spread over the CUs a wave at a time (about ten each)
+// instead of in workgroups of four, which left some CUs with twelve and others with
+// eight; measured 37.7 against 40.3 us for the pass (2 waves 39.6, 8 waves 56.0).
+#ifndef PA_VALU_SOLO_WAVES
+#define PA_VALU_SOLO_WAVES 1
+#endif
+template <typename KV, int G, bool SPLIT, bool SOLO = false>
 constexpr int waves_per_group() {
-    return KV::scaled ? PA_FP8_WAVES : (SPLIT ? NW : PA_VALU_WAVES_ONE_PASS);
+    return SOLO ? PA_VALU_SOLO_WAVES : (KV::scaled ? PA_FP8_WAVES : (SPLIT ? NW : PA_VALU_WAVES_ONE_PASS));
 }
 // Waves per SIMD the register allocation must allow (1 = no constraint).
 template <typename KV, int G>
@@ -304,7 +311,7 @@ constexpr int min_waves_per_eu() {
 #define PA_VALU_SOLO 0  // 0: one wave per item after a shared-prefix pass only; 1: always; -1: never
 #endif
 template <typename KV, int D, int G, bool SPLIT, bool NT, bool SOLO = false>
-__global__ __launch_bounds__((waves_per_group<KV, G, SPLIT>() * 64))
+__global__ __launch_bounds__((waves_per_group<KV, G, SPLIT, SOLO>() * 64))
 __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu_kernel(
     void *__restrict__ out, const uint8_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
     const uint8_t *__restrict__ value_cache, const float *__restrict__ k_scales,
@@ -315,7 +322,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu<KV, G>()))) void decode_valu
     const uint8_t *__restrict__ new_key, const uint8_t *__restrict__ new_value, uint8_t *key_out,
     uint8_t *value_out, const int32_t *__restrict__ skip_parts) {
     using T = typename KV::Q;
-    constexpr int NWG = waves_per_group<KV, G, SPLIT>();
+    constexpr int NWG = waves_per_group<KV, G, SPLIT, SOLO>();
     constexpr int QB = T::bytes;            // query / output element bytes
     constexpr int EPL = KV::epl;            // elements per lane per row
     constexpr int SB = KV::slice_bytes;
@@ -1118,11 +1125,12 @@ int launch_t(const DecodeArgs &a) {
     constexpr bool solo_built = PA_VALU_SOLO > 0 || (PA_VALU_SOLO == 0 && G == 1 && !KV::scaled);
     const bool solo = solo_built && (PA_VALU_SOLO > 0 || a.skip_parts != nullptr);
     constexpr int NWG1 = waves_per_group<KV, G, false>();
+    constexpr int NWS = waves_per_group<KV, G, false, true>();
     auto kernel = decode_valu_kernel<KV, D, G, false, NT, false>;
     if constexpr (solo_built)
         if (solo) kernel = decode_valu_kernel<KV, D, G, false, NT, true>;
-    const unsigned grid1 = solo ? (unsigned)(((int64_t)a.num_seqs * a.num_kv_heads + NWG1 - 1) / NWG1) : grid;
-    hipLaunchKernelGGL(kernel, dim3(grid1), dim3(NWG1 * 64), 0, st,
+    const unsigned grid1 = solo ? (unsigned)(((int64_t)a.num_seqs * a.num_kv_heads + NWS - 1) / NWS) : grid;
+    hipLaunchKernelGGL(kernel, dim3(grid1), dim3((solo ? NWS : NWG1) * 64), 0, st,
                        a.out, (const uint8_t *)a.query, (const uint8_t *)a.key_cache,
                        (const uint8_t *)a.value_cache, a.k_scales, a.v_scales, a.block_tables,
                        a.context_lens, a.ws_max, a.ws_sum, a.ws_acc, a.max_blocks_per_seq, a.num_seqs,
